@@ -1,0 +1,238 @@
+"""Dust gradient estimator -- CPU ORACLE. TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, fp64 statement of what the Dust estimator computes, used to check the HIP library.
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import this package. It shares no code with ``activation_perturbation_es_amd`` and never imports
+it. The element loops live in ``dust_oracle.c`` (plain C, fp64); this module marshals numpy
+arrays to it and states the two steps that are library primitives (a matrix product) or small
+closed forms (the tiny linear + softmax model) in numpy.
+
+Method source: the "Dust" explainer at cnblogs.com/32bin/p/23212811, sections
+"Credit assignment: one forward, two rewards" (noise, loss change, reward, error estimate,
+weight gradient) and "The real work: suppressing interference" (attention scoring, LM-head
+chunk). Generator: Philox4x32-10 (Salmon et al., SC'11) and Box-Muller; the counter layout is
+stated in ``dust_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "dust_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libdust_oracle.so")
+_lib = None
+
+_d = ctypes.POINTER(ctypes.c_double)
+_i64 = ctypes.c_int64
+_u32 = ctypes.c_uint32
+_u64 = ctypes.c_uint64
+
+
+def build(force: bool = False) -> str:
+    """Compile dust_oracle.c into libdust_oracle.so with gcc (fp64, OpenMP)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    lib.dust_or_philox4x32_10.argtypes = [ctypes.POINTER(_u32), ctypes.POINTER(_u32),
+                                          ctypes.POINTER(_u32)]
+    lib.dust_or_noise_words.argtypes = [_u64, _u32, _u32, _u32, _u32, ctypes.POINTER(_u32)]
+    lib.dust_or_uniform.argtypes = [_u32]
+    lib.dust_or_uniform.restype = ctypes.c_double
+    lib.dust_or_normal.argtypes = [_u64, _u32, _u32, _u32, _u64]
+    lib.dust_or_normal.restype = ctypes.c_double
+    lib.dust_or_normals.argtypes = [_u64, _u32, _u32, _u32, _i64, _i64, _i64, _i64, _d]
+    lib.dust_or_noise_inject.argtypes = [_d, _i64, _i64, _i64, _i64, _i64, ctypes.c_double, _u64,
+                                         _u32, _u32, _u32, _d]
+    lib.dust_or_loss_delta_loss.argtypes = [_d, _d, _i64, _i64, _d]
+    lib.dust_or_loss_delta_inner.argtypes = [_d, _d, _i64, _i64, _i64, _d]
+    lib.dust_or_reward_scan.argtypes = [_d, _i64, _i64, _i64, ctypes.c_double, _d]
+    lib.dust_or_error_estimate.argtypes = [_d, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
+                                           _u64, _u32, _u32, _u32, ctypes.c_int, _d]
+    lib.dust_or_error_estimate_at.argtypes = [_d, _i64, _i64, _i64, _i64, ctypes.c_double, _u64,
+                                              _u32, _u32, _u32, ctypes.POINTER(_i64),
+                                              ctypes.POINTER(_i64), _i64, _d]
+    lib.dust_or_head_ce_chunk.argtypes = [_d, ctypes.POINTER(ctypes.c_int32), _i64, _i64, _i64,
+                                          _i64, _i64, ctypes.c_double, _u64, _u32, _u32, _u32,
+                                          _d, _d]
+    lib.dust_or_round_bf16.argtypes = [ctypes.c_double]
+    lib.dust_or_round_bf16.restype = ctypes.c_double
+    _lib = lib
+    return lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a: np.ndarray):
+    return a.ctypes.data_as(_d)
+
+
+# ------------------------------------------------------------------------------ generator
+def philox4x32_10(counter, key) -> np.ndarray:
+    """Philox4x32-10 (SC'11) of one 4-word counter under a 2-word key."""
+    lib = _load()
+    c = (_u32 * 4)(*[int(x) & 0xFFFFFFFF for x in counter])
+    k = (_u32 * 2)(*[int(x) & 0xFFFFFFFF for x in key])
+    out = (_u32 * 4)()
+    lib.dust_or_philox4x32_10(c, k, out)
+    return np.array(list(out), dtype=np.uint32)
+
+
+def noise_words(seed: int, tag: int, draw: int, token: int, q: int) -> np.ndarray:
+    """Words carrying channels 4q..4q+3 of (draw, token): counter (q, token, draw, tag)."""
+    lib = _load()
+    out = (_u32 * 4)()
+    lib.dust_or_noise_words(seed, tag, draw, token, q, out)
+    return np.array(list(out), dtype=np.uint32)
+
+
+def uniform(w: int) -> float:
+    return _load().dust_or_uniform(int(w) & 0xFFFFFFFF)
+
+
+def normal(seed: int, tag: int, draw: int, token: int, ch: int) -> float:
+    """a^{(draw)}_{token, ch} ~ N(0, 1)."""
+    return _load().dust_or_normal(seed, tag, draw, token, ch)
+
+
+def normals(seed: int, tag: int, draw0: int, tok0: int, chan0: int, K: int, T: int, d: int) -> np.ndarray:
+    """Normals for draws draw0.., tokens tok0.., channels chan0..: array [K, T, d]."""
+    out = np.empty((K, T, d), dtype=np.float64)
+    _load().dust_or_normals(seed, tag, draw0, tok0, chan0, K, T, d, _p(out))
+    return out
+
+
+# ------------------------------------------------------------------------------ estimator steps
+def noise_inject(y, sigma: float, K: int, seed: int, tag: int, draw0: int = 0, tok0: int = 0,
+                 chan0: int = 0, d: int | None = None) -> np.ndarray:
+    """y'^{(i)}_t = y_t + sigma a^{(i)}_t for i = draw0 .. draw0+K-1: returns [K, T, d] fp64."""
+    y = _f64(y)
+    T, ld = y.shape
+    d = ld if d is None else d
+    out = np.empty((K, T, d), dtype=np.float64)
+    _load().dust_or_noise_inject(_p(y), T, d, ld, chan0, K, sigma, seed, tag, draw0, tok0, _p(out))
+    return out
+
+
+def loss_delta_loss(loss_clean, loss_pert) -> np.ndarray:
+    """c^{(i)}_t = l_clean,t - l^{(i)}_pert,t: returns [K, T]."""
+    lc, lp = _f64(loss_clean), _f64(loss_pert)
+    K, T = lp.shape
+    c = np.empty((K, T), dtype=np.float64)
+    _load().dust_or_loss_delta_loss(_p(lc), _p(lp), K, T, _p(c))
+    return c
+
+
+def loss_delta_inner(delta_o, g_o) -> np.ndarray:
+    """c^{(i)}_s = -<delta_o^{(i)}_s, g^o_s>: delta_o [K, T, d], g_o [T, d] -> [K, T]."""
+    do, go = _f64(delta_o), _f64(g_o)
+    K, T, d = do.shape
+    c = np.empty((K, T), dtype=np.float64)
+    _load().dust_or_loss_delta_inner(_p(do), _p(go), K, T, d, _p(c))
+    return c
+
+
+def reward_scan(c, seg_len: int, gamma: float) -> np.ndarray:
+    """r_t = sum_{s>=t in t's sequence} gamma^(s-t) c_s along the last axis of c [K, T]."""
+    c = _f64(c)
+    K, T = c.shape
+    assert T % seg_len == 0
+    r = np.empty_like(c)
+    _load().dust_or_reward_scan(_p(c), K, T, seg_len, gamma, _p(r))
+    return r
+
+
+def error_estimate(r, d: int, sigma: float, seed: int, tag: int, draw0: int = 0, tok0: int = 0,
+                   chan0: int = 0, K_total: int | None = None, g_in=None) -> np.ndarray:
+    """g_t = -(1/(K_total sigma)) sum_i r^{(i)}_t a^{(i)}_t (+ g_in): r [K, T] -> [T, d]."""
+    r = _f64(r)
+    K, T = r.shape
+    K_total = K if K_total is None else K_total
+    g = np.zeros((T, d), dtype=np.float64) if g_in is None else _f64(g_in).copy()
+    _load().dust_or_error_estimate(_p(r), K, K_total, T, d, chan0, sigma, seed, tag, draw0, tok0,
+                                   0 if g_in is None else 1, _p(g))
+    return g
+
+
+def error_estimate_at(r, tok, ch, sigma: float, seed: int, tag: int, draw0: int = 0, tok0: int = 0,
+                      chan0: int = 0, K_total: int | None = None) -> np.ndarray:
+    """g at chosen (token, channel) pairs only (no accumulate term)."""
+    r = _f64(r)
+    K, T = r.shape
+    K_total = K if K_total is None else K_total
+    tok = np.ascontiguousarray(tok, dtype=np.int64)
+    ch = np.ascontiguousarray(ch, dtype=np.int64)
+    out = np.empty(len(tok), dtype=np.float64)
+    _load().dust_or_error_estimate_at(_p(r), K, K_total, T, chan0, sigma, seed, tag, draw0, tok0,
+                                      tok.ctypes.data_as(ctypes.POINTER(_i64)),
+                                      ch.ctypes.data_as(ctypes.POINTER(_i64)), len(tok), _p(out))
+    return out
+
+
+def weight_grad(g_hat, x) -> np.ndarray:
+    """G_W = sum_t g_t x_t^T (explainer, "Credit assignment", weight-gradient outer product),
+    taken as one fp64 library matrix product: g_hat [T, d_out], x [T, d_in] -> [d_out, d_in]."""
+    return _f64(g_hat).T @ _f64(x)
+
+
+def head_ce_chunk(logits, targets, v0: int, C: int, K: int, sigma: float, seed: int, tag: int,
+                  draw0: int = 0, tok0: int = 0):
+    """Per-token cross-entropy with vocabulary chunk [v0, v0+C) perturbed, all other logits
+    clean: returns (loss_pert [K, T], loss_clean [T])."""
+    z = _f64(logits)
+    T, V = z.shape
+    y = np.ascontiguousarray(targets, dtype=np.int32)
+    lp = np.empty((K, T), dtype=np.float64)
+    lc = np.empty(T, dtype=np.float64)
+    _load().dust_or_head_ce_chunk(_p(z), y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), T, V, v0,
+                                  C, K, sigma, seed, tag, draw0, tok0, _p(lp), _p(lc))
+    return lp, lc
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 value (ties to even) of each element, as fp64."""
+    f = np.vectorize(_load().dust_or_round_bf16, otypes=[np.float64])
+    return f(_f64(x))
+
+
+# ------------------------------------------------------------------------------ tiny model
+def tiny_forward_losses(W, H, x, targets, y=None) -> np.ndarray:
+    """Per-token cross-entropy of the tiny linear + fixed-head model: y = x W^T (or the given
+    layer output y, any leading shape [..., T, d_out]), z = y H^T, l_t = CE(z_t, target_t)."""
+    if y is None:
+        y = _f64(x) @ _f64(W).T
+    z = _f64(y) @ _f64(H).T
+    m = z.max(axis=-1, keepdims=True)
+    lse = m[..., 0] + np.log(np.exp(z - m).sum(axis=-1))
+    tgt = np.asarray(targets, dtype=np.int64)
+    zy = z[..., np.arange(len(tgt)), tgt]
+    return lse - zy
+
+
+def tiny_analytic_grad(W, H, x, targets):
+    """Exact gradient of sum_t l_t for the tiny model: g_t = H^T (softmax(z_t) - e_target) is
+    dL/dy_t and G_W = sum_t g_t x_t^T. Returns (g [T, d_out], G_W [d_out, d_in])."""
+    x = _f64(x)
+    y = x @ _f64(W).T
+    z = y @ _f64(H).T
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    p[np.arange(len(targets)), np.asarray(targets)] -= 1.0
+    g = p @ _f64(H)
+    return g, g.T @ x

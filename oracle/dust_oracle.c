@@ -1,0 +1,272 @@
+/*
+ * Dust gradient estimator -- CPU ORACLE. TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously-correct fp64 statement of what the Dust estimator computes for one
+ * linear layer and for one vocabulary chunk of the LM head. Only the test suite, the smoke check
+ * and the CPU-baseline leg of the benchmark load this library; the product path (the HIP
+ * library and its Python binding) never links, imports or calls it, and shares no code with it.
+ *
+ * Sources (the "Dust" explainer at cnblogs.com/32bin/p/23212811, abbreviated "explainer"):
+ *   - section "Credit assignment: one forward, two rewards" (信用分配：一次前向，两种奖励):
+ *       noise a_t ~ N(0, I) scaled by sigma and added to the layer output y_t; the centred
+ *       per-token loss change c_s; the discounted reward r_t; the output-error estimate g_t;
+ *       the weight-gradient outer product G_W;
+ *   - section "The real work: suppressing interference" (真正的工作量：压住干扰):
+ *       attention internals scored by the inner product of the attention-output change with
+ *       that output's estimated error; the LM head perturbed on cached logits with only the
+ *       cross-entropy of one vocabulary chunk recomputed.
+ * The random numbers are Philox4x32-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers:
+ * As Easy as 1, 2, 3", SC'11) followed by the Box-Muller transform (Box & Muller, 1958). The
+ * pages fix neither the generator nor the index layout; the readings used here are:
+ *   key     = (seed mod 2^32, seed >> 32)
+ *   counter = (floor(ch / 4), token, draw, tag)      ch = global channel (vocab id for the head)
+ *   u(w)    = (floor(w / 2^9) + 1/2) * 2^-23          exact in fp32 and fp64, in (0, 1)
+ *   channel 4q+0 = rho(w0) cos(2 pi u(w1)), 4q+1 = rho(w0) sin(2 pi u(w1)),
+ *   channel 4q+2 = rho(w2) cos(2 pi u(w3)), 4q+3 = rho(w2) sin(2 pi u(w3)),
+ *   rho(w) = sqrt(-2 ln u(w)).
+ *
+ * Every loop below is the definition written out: no blocking, fusion or reordering of any
+ * sum. OpenMP splits only independent output elements across threads.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#ifndef M_PI
+#define M_PI 3.14159265358979323846
+#endif
+
+/* ---------------------------------------------------------------------------------------- */
+/* Philox4x32-10 (SC'11). One round maps (x0, x1, x2, x3) under key (k0, k1) to
+ *   (hi(B*x2) ^ x1 ^ k0,  lo(B*x2),  hi(A*x0) ^ x3 ^ k1,  lo(A*x0))
+ * with the multipliers A = 0xD2511F53 and B = 0xCD9E8D57; between rounds the key is advanced
+ * by the Weyl constants (0x9E3779B9, 0xBB67AE85). Ten rounds, nine key advances. */
+void dust_or_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4])
+{
+    uint32_t x0 = ctr[0], x1 = ctr[1], x2 = ctr[2], x3 = ctr[3];
+    uint32_t k0 = key[0], k1 = key[1];
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        uint64_t pa = (uint64_t)0xD2511F53u * (uint64_t)x0;
+        uint64_t pb = (uint64_t)0xCD9E8D57u * (uint64_t)x2;
+        uint32_t y0 = (uint32_t)(pb >> 32) ^ x1 ^ k0;
+        uint32_t y1 = (uint32_t)pb;
+        uint32_t y2 = (uint32_t)(pa >> 32) ^ x3 ^ k1;
+        uint32_t y3 = (uint32_t)pa;
+        x0 = y0; x1 = y1; x2 = y2; x3 = y3;
+    }
+    out[0] = x0; out[1] = x1; out[2] = x2; out[3] = x3;
+}
+
+/* The four words that carry the noise of channels 4q .. 4q+3 of (draw, token). */
+void dust_or_noise_words(uint64_t seed, uint32_t tag, uint32_t draw, uint32_t token, uint32_t q,
+                         uint32_t out[4])
+{
+    uint32_t ctr[4] = {q, token, draw, tag};
+    uint32_t key[2] = {(uint32_t)(seed & 0xFFFFFFFFu), (uint32_t)(seed >> 32)};
+    dust_or_philox4x32_10(ctr, key, out);
+}
+
+/* Uniform in (0, 1) from the top 23 bits of a word, centred in its bin. */
+double dust_or_uniform(uint32_t w)
+{
+    return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);
+}
+
+/* Standard normal a^{(draw)}_{token, ch}: explainer, "Credit assignment", a_t ~ N(0, I). */
+double dust_or_normal(uint64_t seed, uint32_t tag, uint32_t draw, uint32_t token, uint64_t ch)
+{
+    uint32_t w[4];
+    dust_or_noise_words(seed, tag, draw, token, (uint32_t)(ch / 4), w);
+    unsigned pair = (unsigned)((ch % 4) / 2);       /* words (0,1) or (2,3) */
+    double ua = dust_or_uniform(w[2 * pair]);
+    double ub = dust_or_uniform(w[2 * pair + 1]);
+    double rho = sqrt(-2.0 * log(ua));
+    double theta = 2.0 * M_PI * ub;
+    return (ch % 2 == 0) ? rho * cos(theta) : rho * sin(theta);
+}
+
+/* Bulk normals for (draw0 + k, token0 + t, chan0 + j): out[k][t][j], k < K, t < T, j < d. */
+void dust_or_normals(uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0, int64_t chan0,
+                     int64_t K, int64_t T, int64_t d, double *out)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < d; ++j)
+                out[(k * T + t) * d + j] = dust_or_normal(seed, tag, (uint32_t)(draw0 + k),
+                                                          (uint32_t)(tok0 + t),
+                                                          (uint64_t)(chan0 + j));
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Perturbed layer output y'^{(i)}_t = y_t + sigma a^{(i)}_t (explainer, "Credit assignment").
+ * y is [T, ld_y] (first d columns used); y_pert is [K, T, d]. */
+void dust_or_noise_inject(const double *y, int64_t T, int64_t d, int64_t ld_y, int64_t chan0,
+                          int64_t K, double sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                          uint32_t tok0, double *y_pert)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t t = 0; t < T; ++t)
+            for (int64_t j = 0; j < d; ++j)
+                y_pert[(k * T + t) * d + j] =
+                    y[t * ld_y + j] +
+                    sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k), (uint32_t)(tok0 + t),
+                                           (uint64_t)(chan0 + j));
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Per-token loss change, loss mode: c^{(i)}_t = l_clean,t - l^{(i)}_pert,t (explainer,
+ * "Credit assignment": the centred change, read as clean minus perturbed so that c is the
+ * reduction the noise produced). */
+void dust_or_loss_delta_loss(const double *loss_clean, const double *loss_pert, int64_t K,
+                             int64_t T, double *c)
+{
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t t = 0; t < T; ++t)
+            c[i * T + t] = loss_clean[t] - loss_pert[i * T + t];
+}
+
+/* Inner-product mode for attention internals: c^{(i)}_s = -<delta_o^{(i)}_s, g^o_s>
+ * (explainer, "The real work: suppressing interference", second measure). delta_o is
+ * [K, T, d], g_o is [T, d]. */
+void dust_or_loss_delta_inner(const double *delta_o, const double *g_o, int64_t K, int64_t T,
+                              int64_t d, double *c)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t s = 0; s < T; ++s) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                acc += delta_o[(i * T + s) * d + j] * g_o[s * d + j];
+            c[i * T + s] = -acc;
+        }
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Discounted reward r_t = sum_{s >= t, s in t's sequence} gamma^(s - t) c_s (explainer,
+ * "Credit assignment"). Tokens are T = B * seg_len, sequence b owns [b*seg_len, (b+1)*seg_len).
+ * Written as the backward recursion r_t = c_t + gamma r_{t+1}, r_last = c_last. */
+void dust_or_reward_scan(const double *c, int64_t K, int64_t T, int64_t seg_len, double gamma,
+                         double *r)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t b = 0; b < T / seg_len; ++b) {
+            int64_t first = b * seg_len, last = first + seg_len - 1;
+            r[i * T + last] = c[i * T + last];
+            for (int64_t t = last - 1; t >= first; --t)
+                r[i * T + t] = c[i * T + t] + gamma * r[i * T + t + 1];
+        }
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Output-error estimate g_t = -(1/(K sigma)) sum_i r^{(i)}_t a^{(i)}_t (explainer, "Credit
+ * assignment"). r is [K, T] holding draws draw0 .. draw0+K-1 of a population of K_total; g is
+ * [T, d] and, when accumulate != 0, the sum is added to the g passed in. */
+void dust_or_error_estimate(const double *r, int64_t K, int64_t K_total, int64_t T, int64_t d,
+                            int64_t chan0, double sigma, uint64_t seed, uint32_t tag,
+                            uint32_t draw0, uint32_t tok0, int accumulate, double *g)
+{
+    double scale = -1.0 / ((double)K_total * sigma);
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int64_t j = 0; j < d; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < K; ++i)
+                acc += r[i * T + t] * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),
+                                                     (uint32_t)(tok0 + t), (uint64_t)(chan0 + j));
+            double prev = accumulate ? g[t * d + j] : 0.0;
+            g[t * d + j] = prev + scale * acc;
+        }
+}
+
+/* The same quantity at n chosen (token, channel) pairs only: out[n] = g[tok[n], ch[n]]
+ * (without any accumulate term). */
+void dust_or_error_estimate_at(const double *r, int64_t K, int64_t K_total, int64_t T,
+                               int64_t chan0, double sigma, uint64_t seed, uint32_t tag,
+                               uint32_t draw0, uint32_t tok0, const int64_t *tok,
+                               const int64_t *ch, int64_t n, double *out)
+{
+    double scale = -1.0 / ((double)K_total * sigma);
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < n; ++m) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < K; ++i)
+            acc += r[i * T + tok[m]] * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),
+                                                      (uint32_t)(tok0 + tok[m]),
+                                                      (uint64_t)(chan0 + ch[m]));
+        out[m] = scale * acc;
+    }
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* LM head on cached logits (explainer, "The real work", third measure): for each draw only the
+ * logits of vocabulary chunk [v0, v0 + C) are perturbed, z'_j = z_j + sigma a_j, every other
+ * logit keeps its cached value, and the per-token cross-entropy over the whole vocabulary is
+ * recomputed: l = log sum_j exp(z'_j) - z'_{target}. logits is [T, V], loss_pert [K, T].
+ * loss_clean (may be NULL) receives the unperturbed cross-entropy. */
+void dust_or_head_ce_chunk(const double *logits, const int32_t *targets, int64_t T, int64_t V,
+                           int64_t v0, int64_t C, int64_t K, double sigma, uint64_t seed,
+                           uint32_t tag, uint32_t draw0, uint32_t tok0, double *loss_pert,
+                           double *loss_clean)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *z = logits + t * V;
+        int64_t y = targets[t];
+        if (loss_clean) {
+            double m = z[0];
+            for (int64_t j = 1; j < V; ++j) m = z[j] > m ? z[j] : m;
+            double s = 0.0;
+            for (int64_t j = 0; j < V; ++j) s += exp(z[j] - m);
+            loss_clean[t] = m + log(s) - z[y];
+        }
+        for (int64_t i = 0; i < K; ++i) {
+            /* the perturbed logit of entry j, written out for this draw */
+            double m = -INFINITY, zy = 0.0;
+            for (int64_t j = 0; j < V; ++j) {
+                double zj = z[j];
+                if (j >= v0 && j < v0 + C)
+                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),
+                                                 (uint32_t)(tok0 + t), (uint64_t)j);
+                if (zj > m) m = zj;
+                if (j == y) zy = zj;
+            }
+            double s = 0.0;
+            for (int64_t j = 0; j < V; ++j) {
+                double zj = z[j];
+                if (j >= v0 && j < v0 + C)
+                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),
+                                                 (uint32_t)(tok0 + t), (uint64_t)j);
+                s += exp(zj - m);
+            }
+            loss_pert[i * T + t] = m + log(s) - zy;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Round a double to the nearest bfloat16 value (8 significant bits, fp32 exponent range),
+ * ties to even, returned as a double. Used to state what a bf16 output must hold. */
+double dust_or_round_bf16(double x)
+{
+    if (x == 0.0 || isnan(x) || isinf(x)) return x;
+    double ax = fabs(x);
+    int e;
+    frexp(ax, &e);                     /* ax = m * 2^e, 0.5 <= m < 1 */
+    int qexp = e - 8;                  /* spacing of 8-bit significands in this binade */
+    if (qexp < -133) qexp = -133;      /* subnormal spacing of the fp32 exponent range */
+    double q = ldexp(1.0, qexp);
+    double n = ax / q;                 /* exact: a power-of-two scaling */
+    double fl = floor(n);
+    double rem = n - fl;
+    double rn = (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)) ? fl + 1.0 : fl;
+    double v = rn * q;
+    if (v > 3.3895313892515355e38) v = INFINITY;   /* beyond the largest finite bf16 */
+    return x < 0 ? -v : v;
+}
