@@ -1,0 +1,311 @@
+// Loss-change scoring and the discounted reward scan of the Dust estimator (gfx950).
+//
+// Explainer cnblogs.com/32bin/p/23212811:
+//  - "Credit assignment: one forward, two rewards": the per-token change c of the loss under
+//    each draw, and the reward r_t = sum_{s >= t} gamma^(s-t) c_s that credits a token's noise
+//    with its effect on later tokens;
+//  - "The real work: suppressing interference": attention internals are scored through the
+//    attention output by the inner product of the output change with that output's error.
+// All three kernels stream HBM once; none reuses data beyond a register tile.
+#include "dust_internal.hpp"
+
+namespace dust {
+namespace {
+
+// ---------------------------------------------------------------- loss mode: c = l_clean - l_pert
+template <bool VEC>
+__global__ __launch_bounds__(256) void loss_delta_loss_kernel(const float *__restrict__ lc,
+                                                              const float *__restrict__ lp,
+                                                              float *__restrict__ c, uint32_t T,
+                                                              uint32_t nb_row) {
+    const uint32_t i = blockIdx.x / nb_row;
+    const uint32_t tb = blockIdx.x % nb_row;
+    const uint64_t row = (uint64_t)i * T;
+    if constexpr (VEC) {
+        const uint32_t t = (tb * 256u + threadIdx.x) * 4u;
+        if (t >= T) return;
+        const float4 l = *(const float4 *)(lp + row + t);
+        const float4 k = *(const float4 *)(lc + t);
+        *(float4 *)(c + row + t) = make_float4(k.x - l.x, k.y - l.y, k.z - l.z, k.w - l.w);
+    } else {
+        const uint32_t t = tb * 256u + threadIdx.x;
+        if (t >= T) return;
+        c[row + t] = lc[t] - lp[row + t];
+    }
+}
+
+// ---------------------------------------------------------------- inner mode: c = -<dO, gO>
+// One wave per token s. The wave keeps g_o[s] in registers and streams the rows dO[i][s] of all
+// draws: lane l covers 16-byte pieces l, l+64, ... of the row (8 bf16 or 4 fp32 values each, or
+// single elements on the unaligned path). Each draw's 64 lane partials are summed with a
+// butterfly. UNROLL draws are loaded before any is reduced to keep loads in flight.
+template <bool BF16, bool VEC, int MAXM>
+__global__ __launch_bounds__(256) void loss_delta_inner_kernel(const void *__restrict__ dO_,
+                                                               const void *__restrict__ gO_,
+                                                               float *__restrict__ c,
+                                                               uint32_t Kc, uint32_t T,
+                                                               uint32_t d) {
+    constexpr int EPV = VEC ? (BF16 ? 8 : 4) : 1;   // elements per lane piece
+    constexpr int UNROLL = 4;
+    const uint32_t s = blockIdx.x * 4u + wave_in_block();
+    if (s >= T) return;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t nchunk = (d + 64u * EPV - 1u) / (64u * EPV);
+
+    float gv[MAXM][EPV];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) {
+        const uint32_t e0 = (m * 64u + lane) * EPV;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) gv[m][e] = 0.f;
+        if (m < (int)nchunk && e0 < d) {
+            if constexpr (BF16) {
+                const uint16_t *g = (const uint16_t *)gO_ + (uint64_t)s * d + e0;
+                if constexpr (VEC) {
+                    const uint4 v = *(const uint4 *)g;
+                    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        gv[m][2 * h] = __uint_as_float(w[h] << 16);
+                        gv[m][2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+                    }
+                } else {
+                    gv[m][0] = bf16_to_f32(g[0]);
+                }
+            } else {
+                const float *g = (const float *)gO_ + (uint64_t)s * d + e0;
+                if constexpr (VEC) {
+                    const float4 v = *(const float4 *)g;
+                    gv[m][0] = v.x; gv[m][1] = v.y; gv[m][2] = v.z; gv[m][3] = v.w;
+                } else {
+                    gv[m][0] = g[0];
+                }
+            }
+        }
+    }
+
+    const uint64_t draw_stride = (uint64_t)T * d;
+    for (uint32_t i0 = 0; i0 < Kc; i0 += UNROLL) {
+        float p[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            p[u] = 0.f;
+            const uint32_t i = i0 + u;
+            if (i >= Kc) continue;
+            const uint64_t rowoff = (uint64_t)i * draw_stride + (uint64_t)s * d;
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const uint32_t e0 = (m * 64u + lane) * EPV;
+                if (m >= (int)nchunk || e0 >= d) continue;
+                if constexpr (BF16) {
+                    const uint16_t *row = (const uint16_t *)dO_ + rowoff + e0;
+                    if constexpr (VEC) {
+                        const u32x4 v = __builtin_nontemporal_load((const u32x4 *)row);
+                        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int h = 0; h < 4; ++h) {
+                            p[u] = __builtin_fmaf(__uint_as_float(w[h] << 16), gv[m][2 * h], p[u]);
+                            p[u] = __builtin_fmaf(__uint_as_float(w[h] & 0xFFFF0000u),
+                                                  gv[m][2 * h + 1], p[u]);
+                        }
+                    } else {
+                        p[u] = __builtin_fmaf(bf16_to_f32(row[0]), gv[m][0], p[u]);
+                    }
+                } else {
+                    const float *row = (const float *)dO_ + rowoff + e0;
+                    if constexpr (VEC) {
+                        const f32x4 v = __builtin_nontemporal_load((const f32x4 *)row);
+                        p[u] = __builtin_fmaf(v.x, gv[m][0], p[u]);
+                        p[u] = __builtin_fmaf(v.y, gv[m][1], p[u]);
+                        p[u] = __builtin_fmaf(v.z, gv[m][2], p[u]);
+                        p[u] = __builtin_fmaf(v.w, gv[m][3], p[u]);
+                    } else {
+                        p[u] = __builtin_fmaf(row[0], gv[m][0], p[u]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            const float tot = wave_sum(p[u]);
+            if (lane == 0 && i0 + u < Kc) c[(uint64_t)(i0 + u) * T + s] = -tot;
+        }
+    }
+}
+
+// Same as above for rows too long to keep g_o in registers: g_o is re-read per draw (L1/L2).
+template <bool BF16>
+__global__ __launch_bounds__(256) void loss_delta_inner_long_kernel(const void *__restrict__ dO_,
+                                                                    const void *__restrict__ gO_,
+                                                                    float *__restrict__ c,
+                                                                    uint32_t Kc, uint32_t T,
+                                                                    uint32_t d) {
+    const uint32_t s = blockIdx.x * 4u + wave_in_block();
+    if (s >= T) return;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t draw_stride = (uint64_t)T * d;
+    for (uint32_t i = 0; i < Kc; ++i) {
+        float p = 0.f;
+        const uint64_t rowoff = (uint64_t)i * draw_stride + (uint64_t)s * d;
+        for (uint32_t j = lane; j < d; j += 64u) {
+            float a, b;
+            if constexpr (BF16) {
+                a = bf16_to_f32(((const uint16_t *)dO_)[rowoff + j]);
+                b = bf16_to_f32(((const uint16_t *)gO_)[(uint64_t)s * d + j]);
+            } else {
+                a = ((const float *)dO_)[rowoff + j];
+                b = ((const float *)gO_)[(uint64_t)s * d + j];
+            }
+            p = __builtin_fmaf(a, b, p);
+        }
+        const float tot = wave_sum(p);
+        if (lane == 0) c[(uint64_t)i * T + s] = -tot;
+    }
+}
+
+// ---------------------------------------------------------------- reverse segmented gamma-scan
+// One wave per (draw, sequence). The sequence is processed in chunks of 64*VEC elements from its
+// end towards its start. Inside a chunk each lane owns VEC consecutive elements and forms their
+// local suffix sums; the lanes then combine with a Hillis-Steele scan over the affine carry
+// (the block of lane l+off contributes gamma^(VEC*off) times its running sum), and the value at
+// the chunk's first element is carried into the next chunk. gamma powers come from repeated
+// squaring: gp[b] = gamma^(VEC * 2^b).
+template <int VEC>
+__global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float *r, uint32_t K,
+                                                          uint32_t T, uint32_t seg_len,
+                                                          float gamma) {
+    const uint32_t nseg = T / seg_len;
+    const uint64_t w = (uint64_t)blockIdx.x * 4u + wave_in_block();
+    if (w >= (uint64_t)K * nseg) return;
+    const uint32_t i = (uint32_t)(w / nseg);
+    const uint32_t b = (uint32_t)(w % nseg);
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint64_t seg_base = (uint64_t)i * T + (uint64_t)b * seg_len;
+
+    float gpow[VEC + 1];  // gamma^0 .. gamma^VEC
+    gpow[0] = 1.f;
+#pragma unroll
+    for (int e = 1; e <= VEC; ++e) gpow[e] = gpow[e - 1] * gamma;
+    float gp[7];          // gamma^(VEC * 2^b), b = 0..6
+    gp[0] = gpow[VEC];
+#pragma unroll
+    for (int k = 1; k < 7; ++k) gp[k] = gp[k - 1] * gp[k - 1];
+    // gamma^(VEC * (63 - lane)): product of gp[b] over the set bits of 63 - lane
+    float glane = 1.f;
+    {
+        const uint32_t j = 63u - lane;
+#pragma unroll
+        for (int k = 0; k < 6; ++k)
+            if (j & (1u << k)) glane *= gp[k];
+    }
+
+    constexpr uint32_t CH = 64u * VEC;
+    float carry = 0.f;  // r at the first element after the current chunk (0 past the end)
+    for (uint32_t done = 0; done < seg_len; done += CH) {
+        // chunk covers sequence positions [seg_len - done - CH, seg_len - done)
+        const int64_t start = (int64_t)seg_len - (int64_t)done - (int64_t)CH;
+        const int64_t pos = start + (int64_t)lane * VEC;   // first element of this lane
+        float v[VEC];
+        const bool in = pos >= 0;    // with VEC > 1, seg_len % VEC == 0, so a lane is all in or out
+        if constexpr (VEC == 4) {
+            if (in) {
+                const float4 x = *(const float4 *)(c + seg_base + pos);
+                v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+            } else {
+                v[0] = v[1] = v[2] = v[3] = 0.f;
+            }
+        } else {
+            v[0] = in ? c[seg_base + pos] : 0.f;
+        }
+        // local suffix sums inside the lane
+#pragma unroll
+        for (int e = VEC - 2; e >= 0; --e) v[e] = __builtin_fmaf(gamma, v[e + 1], v[e]);
+        // inclusive reverse scan over lanes: R_l = v0_l + gamma^VEC * R_{l+1}
+        float R = v[0];
+#pragma unroll
+        for (int k = 0; k < 6; ++k) {
+            const uint32_t off = 1u << k;
+            const float up = __shfl_down(R, off);
+            if (lane + off < 64u) R = __builtin_fmaf(gp[k], up, R);
+        }
+        // value just after this lane's block: R_{l+1} + gamma^(VEC*(63-l)) * carry
+        float after = __shfl_down(R, 1);
+        if (lane == 63u) after = 0.f;
+        after = __builtin_fmaf(glane, carry, after);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) v[e] = __builtin_fmaf(gpow[VEC - e], after, v[e]);
+        if (in) {
+            if constexpr (VEC == 4) {
+                *(float4 *)(r + seg_base + pos) = make_float4(v[0], v[1], v[2], v[3]);
+            } else {
+                r[seg_base + pos] = v[0];
+            }
+        }
+        carry = __shfl(v[0], 0);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_loss_delta_loss(const float *lc, const float *lp, float *c, int64_t Kc,
+                                  int64_t T, hipStream_t s) {
+    const bool vec = (T % 4 == 0) && aligned16(lc) && aligned16(lp) && aligned16(c);
+    const int64_t per_block = vec ? 1024 : 256;
+    const uint32_t nb_row = (uint32_t)((T + per_block - 1) / per_block);
+    const uint32_t blocks = (uint32_t)(nb_row * Kc);
+    if (vec)
+        loss_delta_loss_kernel<true><<<blocks, 256, 0, s>>>(lc, lp, c, (uint32_t)T, nb_row);
+    else
+        loss_delta_loss_kernel<false><<<blocks, 256, 0, s>>>(lc, lp, c, (uint32_t)T, nb_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_loss_delta_inner(const void *delta_o, const void *g_o, bool bf16, float *c,
+                                   int64_t Kc, int64_t T, int64_t d, hipStream_t s) {
+    const uint32_t blocks = (uint32_t)((T + 3) / 4);
+    const int epv = bf16 ? 8 : 4;
+    const bool vec = (d % epv == 0) && aligned16(delta_o) && aligned16(g_o);
+    const int64_t piece = vec ? 64 * epv : 64;
+    const int64_t nchunk = (d + piece - 1) / piece;
+#define DUST_INNER(B, V, M)                                                                    \
+    loss_delta_inner_kernel<B, V, M><<<blocks, 256, 0, s>>>(delta_o, g_o, c, (uint32_t)Kc,     \
+                                                            (uint32_t)T, (uint32_t)d)
+#define DUST_INNER_M(B, V)                                                                     \
+    do {                                                                                       \
+        if (nchunk <= 1) DUST_INNER(B, V, 1);                                                  \
+        else if (nchunk <= 2) DUST_INNER(B, V, 2);                                             \
+        else if (nchunk <= 4) DUST_INNER(B, V, 4);                                             \
+        else DUST_INNER(B, V, 8);                                                              \
+    } while (0)
+    if (nchunk > 8) {
+        if (bf16)
+            loss_delta_inner_long_kernel<true><<<blocks, 256, 0, s>>>(delta_o, g_o, c, (uint32_t)Kc,
+                                                                      (uint32_t)T, (uint32_t)d);
+        else
+            loss_delta_inner_long_kernel<false><<<blocks, 256, 0, s>>>(delta_o, g_o, c, (uint32_t)Kc,
+                                                                       (uint32_t)T, (uint32_t)d);
+    } else if (bf16) {
+        if (vec) DUST_INNER_M(true, true); else DUST_INNER_M(true, false);
+    } else {
+        if (vec) DUST_INNER_M(false, true); else DUST_INNER_M(false, false);
+    }
+#undef DUST_INNER_M
+#undef DUST_INNER
+    return hipGetLastError();
+}
+
+hipError_t launch_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
+                              float gamma, hipStream_t s) {
+    const int64_t waves = K * (T / seg_len);
+    const uint32_t blocks = (uint32_t)((waves + 3) / 4);
+    const bool vec = (seg_len % 4 == 0) && aligned16(c) && aligned16(r);
+    if (vec)
+        reward_scan_kernel<4><<<blocks, 256, 0, s>>>(c, r, (uint32_t)K, (uint32_t)T,
+                                                     (uint32_t)seg_len, gamma);
+    else
+        reward_scan_kernel<1><<<blocks, 256, 0, s>>>(c, r, (uint32_t)K, (uint32_t)T,
+                                                     (uint32_t)seg_len, gamma);
+    return hipGetLastError();
+}
+
+}  // namespace dust

@@ -1,0 +1,301 @@
+// C ABI of the Dust estimator: argument validation, then one launcher call per entry point.
+// Every check runs on the host before any HIP call, so a rejected call enqueues nothing and
+// touches no device state. The declarations and their contracts are in include/dust.h.
+#include "dust.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "dust_internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok() {
+    g_last_error[0] = '\0';
+    return DUST_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(DUST_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMax32 = 0xFFFFFFFFll;      // counter words are 32-bit
+constexpr int64_t kMaxIdx = 0x7FFFFFFFll;     // kernels index tokens / channels in 32 bits
+
+bool elem_aligned(const void *p, size_t elem) { return ((uintptr_t)p % elem) == 0; }
+
+dust::Key make_key(uint64_t seed, uint32_t tag) {
+    dust::Key k;
+    k.k0 = (uint32_t)(seed & 0xFFFFFFFFull);
+    k.k1 = (uint32_t)(seed >> 32);
+    k.tag = tag;
+    return k;
+}
+
+// Shared checks of the noise index ranges (see "Noise" in dust.h).
+int check_noise_ranges(const char *fn, int64_t T, int64_t d, int64_t chan0, int64_t K,
+                       uint32_t draw0, uint32_t tok0) {
+    if (chan0 < 0 || chan0 % 4 != 0)
+        return fail(DUST_ERR_INVALID, "%s: chan0=%lld must be >= 0 and a multiple of 4", fn,
+                    (long long)chan0);
+    if ((chan0 + d + 3) / 4 > kMax32 + 1)
+        return fail(DUST_ERR_INVALID, "%s: chan0 + d exceeds 2^34 channels", fn);
+    if ((int64_t)tok0 + T > kMax32 + 1)
+        return fail(DUST_ERR_INVALID, "%s: tok0 + T exceeds 2^32 tokens", fn);
+    if ((int64_t)draw0 + K > kMax32 + 1)
+        return fail(DUST_ERR_INVALID, "%s: draw0 + K exceeds 2^32 draws", fn);
+    return DUST_OK;
+}
+
+bool ranges_overlap(const void *a, size_t abytes, const void *b, size_t bbytes) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + bbytes && b0 < a0 + abytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dust_status_string(int status) {
+    switch (status) {
+        case DUST_OK: return "DUST_OK";
+        case DUST_ERR_INVALID: return "DUST_ERR_INVALID";
+        case DUST_ERR_UNSUPPORTED: return "DUST_ERR_UNSUPPORTED";
+        case DUST_ERR_WORKSPACE: return "DUST_ERR_WORKSPACE";
+        case DUST_ERR_HIP: return "DUST_ERR_HIP";
+        default: return "DUST_ERR_UNKNOWN";
+    }
+}
+
+const char *dust_last_error(void) { return g_last_error; }
+
+int dust_noise_inject(const void *y, void *y_pert, int dtype, int64_t T, int64_t d,
+                      int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, uint64_t seed,
+                      uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream) {
+    const char *fn = "dust_noise_inject";
+    if (dtype != DUST_F32 && dtype != DUST_BF16)
+        return fail(DUST_ERR_INVALID, "%s: dtype=%d is not DUST_F32 or DUST_BF16", fn, dtype);
+    if (T < 0 || d < 0 || Kc < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (T=%lld d=%lld Kc=%lld)", fn,
+                    (long long)T, (long long)d, (long long)Kc);
+    if (ld_y < d) return fail(DUST_ERR_INVALID, "%s: ld_y=%lld < d=%lld", fn, (long long)ld_y,
+                              (long long)d);
+    if (!std::isfinite(sigma)) return fail(DUST_ERR_INVALID, "%s: sigma is not finite", fn);
+    if (int rc = check_noise_ranges(fn, T, d, chan0, Kc, draw0, tok0)) return rc;
+    if (T == 0 || d == 0 || Kc == 0) return ok();
+    if (!y || !y_pert) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    const size_t es = dtype == DUST_BF16 ? 2 : 4;
+    if (!elem_aligned(y, es) || !elem_aligned(y_pert, es))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
+    if (T > kMaxIdx || d > kMaxIdx || Kc > kMaxIdx || ld_y > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if ((d + 3) / 4 >= 256 && ((d + 3) / 4 + 255) / 256 * T > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    if (ranges_overlap(y, (size_t)((T - 1) * ld_y + d) * es, y_pert, (size_t)(Kc * T * d) * es))
+        return fail(DUST_ERR_INVALID, "%s: y and y_pert overlap", fn);
+    return hip_status(dust::launch_noise_inject(y, y_pert, dtype == DUST_BF16, T, d, ld_y, chan0,
+                                                Kc, sigma, make_key(seed, tag), draw0, tok0,
+                                                (hipStream_t)stream),
+                      fn);
+}
+
+int dust_loss_delta(int mode, const float *loss_clean, const float *loss_pert,
+                    const void *delta_o, const void *g_o, int io_dtype, float *c, int64_t Kc,
+                    int64_t T, int64_t d, void *stream) {
+    const char *fn = "dust_loss_delta";
+    if (mode != DUST_DELTA_LOSS && mode != DUST_DELTA_INNER)
+        return fail(DUST_ERR_INVALID, "%s: mode=%d is not DUST_DELTA_LOSS or DUST_DELTA_INNER",
+                    fn, mode);
+    if (Kc < 0 || T < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (Kc=%lld T=%lld)", fn, (long long)Kc,
+                    (long long)T);
+    if (Kc > kMaxIdx || T > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (mode == DUST_DELTA_LOSS) {
+        if (Kc == 0 || T == 0) return ok();
+        if (!loss_clean || !loss_pert || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+        if (!elem_aligned(loss_clean, 4) || !elem_aligned(loss_pert, 4) || !elem_aligned(c, 4))
+            return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+        if (((T + 255) / 256) * Kc > kMaxIdx)
+            return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+        if (ranges_overlap(loss_clean, (size_t)T * 4, c, (size_t)(Kc * T) * 4))
+            return fail(DUST_ERR_INVALID, "%s: loss_clean and c overlap", fn);
+        if (loss_pert != c && ranges_overlap(loss_pert, (size_t)(Kc * T) * 4, c, (size_t)(Kc * T) * 4))
+            return fail(DUST_ERR_INVALID, "%s: loss_pert and c partially overlap", fn);
+        return hip_status(dust::launch_loss_delta_loss(loss_clean, loss_pert, c, Kc, T,
+                                                       (hipStream_t)stream),
+                          fn);
+    }
+    if (io_dtype != DUST_F32 && io_dtype != DUST_BF16)
+        return fail(DUST_ERR_INVALID, "%s: io_dtype=%d is not DUST_F32 or DUST_BF16", fn,
+                    io_dtype);
+    if (d < 1) return fail(DUST_ERR_INVALID, "%s: inner mode needs d >= 1 (d=%lld)", fn,
+                           (long long)d);
+    if (d > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: d beyond 2^31", fn);
+    if (Kc == 0 || T == 0) return ok();
+    if (!delta_o || !g_o || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    const size_t es = io_dtype == DUST_BF16 ? 2 : 4;
+    if (!elem_aligned(delta_o, es) || !elem_aligned(g_o, es) || !elem_aligned(c, 4))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
+    if (ranges_overlap(delta_o, (size_t)(Kc * T * d) * es, c, (size_t)(Kc * T) * 4) ||
+        ranges_overlap(g_o, (size_t)(T * d) * es, c, (size_t)(Kc * T) * 4))
+        return fail(DUST_ERR_INVALID, "%s: inputs and c overlap", fn);
+    return hip_status(dust::launch_loss_delta_inner(delta_o, g_o, io_dtype == DUST_BF16, c, Kc, T,
+                                                    d, (hipStream_t)stream),
+                      fn);
+}
+
+int dust_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
+                     float gamma, void *stream) {
+    const char *fn = "dust_reward_scan";
+    if (K < 0 || T < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (K=%lld T=%lld)", fn, (long long)K,
+                    (long long)T);
+    if (seg_len < 1) return fail(DUST_ERR_INVALID, "%s: seg_len=%lld < 1", fn, (long long)seg_len);
+    if (T % seg_len != 0)
+        return fail(DUST_ERR_INVALID, "%s: T=%lld is not a multiple of seg_len=%lld", fn,
+                    (long long)T, (long long)seg_len);
+    if (!(gamma >= 0.f && gamma <= 1.f))
+        return fail(DUST_ERR_INVALID, "%s: gamma=%g outside [0, 1]", fn, (double)gamma);
+    if (K == 0 || T == 0) return ok();
+    if (!c || !r) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(c, 4) || !elem_aligned(r, 4))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+    if (K > kMaxIdx || T > kMaxIdx || K * (T / seg_len) > 4 * kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (c != r && ranges_overlap(c, (size_t)(K * T) * 4, r, (size_t)(K * T) * 4))
+        return fail(DUST_ERR_INVALID, "%s: c and r partially overlap", fn);
+    return hip_status(dust::launch_reward_scan(c, r, K, T, seg_len, gamma, (hipStream_t)stream), fn);
+}
+
+int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_t K,
+                        int64_t K_total, int64_t T, int64_t d, int64_t chan0, float sigma,
+                        uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                        int accumulate, void *stream) {
+    const char *fn = "dust_error_estimate";
+    if (K < 0 || T < 0 || d < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (K=%lld T=%lld d=%lld)", fn,
+                    (long long)K, (long long)T, (long long)d);
+    if (K_total < 1 || K_total < K)
+        return fail(DUST_ERR_INVALID, "%s: K_total=%lld must be >= max(1, K=%lld)", fn,
+                    (long long)K_total, (long long)K);
+    if (!(sigma > 0.f) || !std::isfinite(sigma))
+        return fail(DUST_ERR_INVALID, "%s: sigma must be finite and > 0", fn);
+    if (int rc = check_noise_ranges(fn, T, d, chan0, K, draw0, tok0)) return rc;
+    if (T == 0 || d == 0) return ok();
+    if (!g_hat || (K > 0 && !r)) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(g_hat, 4) || (r && !elem_aligned(r, 4)) ||
+        (g_hat_t_bf16 && !elem_aligned(g_hat_t_bf16, 2)))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
+    if (T > kMaxIdx || d > kMaxIdx || K > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if ((T / 4 + 1) * ((d + 255) / 256) > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    if (r && ranges_overlap(r, (size_t)(K * T) * 4, g_hat, (size_t)(T * d) * 4))
+        return fail(DUST_ERR_INVALID, "%s: r and g_hat overlap", fn);
+    if (g_hat_t_bf16 && ranges_overlap(g_hat_t_bf16, (size_t)(T * d) * 2, g_hat, (size_t)(T * d) * 4))
+        return fail(DUST_ERR_INVALID, "%s: g_hat_t_bf16 and g_hat overlap", fn);
+    return hip_status(dust::launch_error_estimate(r, g_hat, (uint16_t *)g_hat_t_bf16, K, K_total, T,
+                                                  d, chan0, sigma, make_key(seed, tag), draw0,
+                                                  tok0, accumulate != 0, (hipStream_t)stream),
+                      fn);
+}
+
+size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in) {
+    return dust::weight_grad_workspace_bytes(T, d_out, d_in);
+}
+
+int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
+                     int64_t d_out, int64_t d_in, void *workspace, size_t ws_bytes,
+                     void *stream) {
+    const char *fn = "dust_weight_grad";
+    if (T < 0 || d_out < 0 || d_in < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (T=%lld d_out=%lld d_in=%lld)", fn,
+                    (long long)T, (long long)d_out, (long long)d_in);
+    if (d_out == 0 || d_in == 0) return ok();
+    if (!G || (T > 0 && (!g_hat_t_bf16 || !x_bf16)))
+        return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(G, 4) || (T > 0 && (!elem_aligned(g_hat_t_bf16, 2) || !elem_aligned(x_bf16, 2))))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
+    if (T > kMaxIdx || d_out > kMaxIdx || d_in > kMaxIdx || d_out * d_in > 256 * kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    const size_t need = dust::weight_grad_workspace_bytes(T, d_out, d_in);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need))
+        return fail(DUST_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && ((uintptr_t)workspace & 15u))
+        return fail(DUST_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    if (T > 0 && (ranges_overlap(G, (size_t)(d_out * d_in) * 4, g_hat_t_bf16, (size_t)(d_out * T) * 2) ||
+                  ranges_overlap(G, (size_t)(d_out * d_in) * 4, x_bf16, (size_t)(T * d_in) * 2)))
+        return fail(DUST_ERR_INVALID, "%s: G overlaps an input", fn);
+    if (need > 0 && ranges_overlap(G, (size_t)(d_out * d_in) * 4, workspace, need))
+        return fail(DUST_ERR_INVALID, "%s: G overlaps the workspace", fn);
+    return hip_status(dust::launch_weight_grad((const uint16_t *)g_hat_t_bf16,
+                                               (const uint16_t *)x_bf16, G, T, d_out, d_in,
+                                               workspace, (hipStream_t)stream),
+                      fn);
+}
+
+int dust_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
+                       float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
+                       int64_t Kc, float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                       uint32_t tok0, void *stream) {
+    const char *fn = "dust_head_ce_chunk";
+    if (T < 0 || Kc < 0 || V < 1)
+        return fail(DUST_ERR_INVALID, "%s: bad size (T=%lld V=%lld Kc=%lld)", fn, (long long)T,
+                    (long long)V, (long long)Kc);
+    if (v0 < 0 || C < 1 || v0 + C > V)
+        return fail(DUST_ERR_INVALID, "%s: chunk [%lld, %lld) outside [0, V=%lld)", fn,
+                    (long long)v0, (long long)(v0 + C), (long long)V);
+    if (!std::isfinite(sigma)) return fail(DUST_ERR_INVALID, "%s: sigma is not finite", fn);
+    if (int rc = check_noise_ranges(fn, T, C, v0, Kc, draw0, tok0)) return rc;
+    if (C > 4096) return fail(DUST_ERR_UNSUPPORTED, "%s: chunk size C=%lld > 4096", fn, (long long)C);
+    if (T > kMaxIdx || V > kMaxIdx || Kc > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (T == 0) return ok();
+    if (!logits || !targets || (Kc > 0 && !loss_pert))
+        return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(logits, 4) || !elem_aligned(targets, 4) ||
+        (loss_pert && !elem_aligned(loss_pert, 4)) || (loss_clean && !elem_aligned(loss_clean, 4)))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+    if (Kc == 0 && loss_clean == nullptr) return ok();
+    if (Kc > 0 && ranges_overlap(loss_pert, (size_t)(Kc * T) * 4, logits, (size_t)(T * V) * 4))
+        return fail(DUST_ERR_INVALID, "%s: loss_pert overlaps logits", fn);
+    return hip_status(dust::launch_head_ce_chunk(logits, targets, loss_pert, loss_clean, T, V, v0, C,
+                                                 Kc, sigma, make_key(seed, tag), draw0, tok0,
+                                                 (hipStream_t)stream),
+                      fn);
+}
+
+int dust_noise_words(uint32_t *words, int64_t Kc, int64_t T, int64_t G, uint32_t group0,
+                     uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream) {
+    const char *fn = "dust_noise_words";
+    if (Kc < 0 || T < 0 || G < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (Kc=%lld T=%lld G=%lld)", fn,
+                    (long long)Kc, (long long)T, (long long)G);
+    if ((int64_t)group0 + G > kMax32 + 1 || (int64_t)tok0 + T > kMax32 + 1 ||
+        (int64_t)draw0 + Kc > kMax32 + 1)
+        return fail(DUST_ERR_INVALID, "%s: counter range exceeds 2^32", fn);
+    if (Kc == 0 || T == 0 || G == 0) return ok();
+    if (!words) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!dust::aligned16(words)) return fail(DUST_ERR_INVALID, "%s: words must be 16-byte aligned", fn);
+    if (T > kMaxIdx || G > kMaxIdx || Kc > kMaxIdx || (G >= 256 && (G + 255) / 256 * T > kMaxIdx))
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    return hip_status(dust::launch_noise_words(words, Kc, T, G, group0, make_key(seed, tag), draw0,
+                                               tok0, (hipStream_t)stream),
+                      fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// Internal launcher interface between the C ABI (dust_api.cpp) and the HIP kernels.
+// Every launcher assumes its arguments were validated by the ABI layer and only enqueues work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dust_noise.hpp"
+
+namespace dust {
+
+// Native clang vectors (the nontemporal builtins take these, not HIP's struct vector types).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 storage is raw 16-bit words; conversions are explicit.
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+    return __uint_as_float((uint32_t)h << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    // round to nearest even via the compiler's bf16 conversion (v_cvt_pk_bf16_f32 on gfx950)
+    __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, b);
+}
+
+hipError_t launch_noise_inject(const void *y, void *y_pert, bool bf16, int64_t T, int64_t d,
+                               int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, Key key,
+                               uint32_t draw0, uint32_t tok0, hipStream_t s);
+
+hipError_t launch_noise_words(uint32_t *words, int64_t Kc, int64_t T, int64_t G, uint32_t group0,
+                              Key key, uint32_t draw0, uint32_t tok0, hipStream_t s);
+
+hipError_t launch_loss_delta_loss(const float *lc, const float *lp, float *c, int64_t Kc,
+                                  int64_t T, hipStream_t s);
+
+hipError_t launch_loss_delta_inner(const void *delta_o, const void *g_o, bool bf16, float *c,
+                                   int64_t Kc, int64_t T, int64_t d, hipStream_t s);
+
+hipError_t launch_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
+                              float gamma, hipStream_t s);
+
+hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t K,
+                                 int64_t K_total, int64_t T, int64_t d, int64_t chan0,
+                                 float sigma, Key key, uint32_t draw0, uint32_t tok0,
+                                 bool accumulate, hipStream_t s);
+
+size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in);
+
+hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, int64_t T,
+                              int64_t d_out, int64_t d_in, void *workspace, hipStream_t s);
+
+hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
+                                float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
+                                int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,
+                                hipStream_t s);
+
+inline bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Butterfly sum / max over the 64 lanes of a wave; every lane receives the result.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+// Index of the calling wave inside its block, as a wave-uniform (scalar) value.
+__device__ __forceinline__ uint32_t wave_in_block() {
+    return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+}  // namespace dust

@@ -1,0 +1,130 @@
+// LM-head chunk cross-entropy of the Dust estimator (gfx950).
+//
+// Explainer cnblogs.com/32bin/p/23212811, "The real work: suppressing interference": the head
+// is perturbed directly on its cached logits and only the cross-entropy involving one
+// vocabulary chunk is recomputed, which makes a far larger population affordable there. For
+// draw i and token t the chunk logits become z_j + sigma a_j; all other logits stay clean:
+//     l'_t = log( sum_{j not in chunk} e^{z_j} + sum_{j in chunk} e^{z_j + sigma a_j} ) - z'_y.
+// One wave per token. Pass 1 (once per token) reads the logit row: an online log-sum-exp over
+// the entries outside the chunk (running max and rescaled sum per lane, then merged across
+// lanes) and the chunk entries kept in registers as q_j = e^{z_j - M}. Pass 2 loops over the
+// draws: each lane regenerates the noise of its chunk channels (four per Philox call), forms
+// sum_j q_j 2^{sigma log2(e) a_j}, and the wave sums it. The target's perturbation is read from
+// the lane that owns the target channel. The loop is bound by the generator's ALU work; the
+// logits are read once per token.
+#include "dust_internal.hpp"
+
+namespace dust {
+namespace {
+
+constexpr float LOG2E = 1.44269504088896340736f;
+constexpr float LN2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
+__device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * LN2; }
+
+template <int GPL>  // channel groups (of 4) per lane: chunk size C <= 256 * GPL
+__global__ __launch_bounds__(256) void head_ce_kernel(
+    const float *__restrict__ logits, const int32_t *__restrict__ targets,
+    float *__restrict__ lp, float *__restrict__ lc, uint32_t T, uint32_t V, uint32_t v0,
+    uint32_t C, uint32_t Kc, float sigma, float sigma_log2e, Key key, uint32_t draw0,
+    uint32_t tok0) {
+    const uint32_t t = blockIdx.x * 4u + wave_in_block();
+    if (t >= T) return;
+    const uint32_t lane = threadIdx.x & 63u;
+    const float *z = logits + (uint64_t)t * V;
+    const int32_t y = targets[t];
+    const bool ybad = (y < 0) || ((uint32_t)y >= V);
+
+    // chunk logits of this lane: channels 4*(lane + 64 m) + e of the chunk
+    float q[GPL][4];
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < GPL; ++m) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t cc = 4u * (lane + 64u * m) + e;
+            q[m][e] = (cc < C) ? z[v0 + cc] : -INFINITY;
+            mloc = fmaxf(mloc, q[m][e]);
+        }
+    }
+    // online log-sum-exp over the entries outside the chunk
+    float mr = -INFINITY, sr = 0.f;
+    for (uint32_t j = lane; j < V; j += 64u) {
+        if (j - v0 < C) continue;   // inside the chunk (unsigned compare)
+        const float x = z[j];
+        if (x > mr) {
+            sr = sr * fast_exp(mr - x) + 1.f;
+            mr = x;
+        } else {
+            sr += fast_exp(x - mr);
+        }
+    }
+    const float M = wave_max(fmaxf(mloc, mr));
+    const float s_rest = wave_sum(mr == -INFINITY ? 0.f : sr * fast_exp(mr - M));
+    float qsum = 0.f;
+#pragma unroll
+    for (int m = 0; m < GPL; ++m)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            q[m][e] = (q[m][e] == -INFINITY) ? 0.f : fast_exp(q[m][e] - M);
+            qsum += q[m][e];
+        }
+    const float s_chunk = wave_sum(qsum);
+
+    const float zy = ybad ? __builtin_nanf("") : z[y];
+    const uint32_t cy = (uint32_t)y - v0;
+    const bool y_in = !ybad && cy < C;
+    const uint32_t owner = (cy >> 2) & 63u;
+    const uint32_t my = cy >> 8;        // group-of-lane index of the target channel
+    const uint32_t ey = cy & 3u;
+    if (lc != nullptr && lane == 0) lc[t] = M + fast_log(s_rest + s_chunk) - zy;
+
+    const uint32_t token = tok0 + t;
+    const uint32_t q0 = v0 / 4u;
+    for (uint32_t i = 0; i < Kc; ++i) {
+        const uint32_t draw = draw0 + i;
+        float s = 0.f, ysel = 0.f;
+#pragma unroll
+        for (int m = 0; m < GPL; ++m) {
+            const uint32_t grp = lane + 64u * m;
+            if (4u * grp >= C) continue;
+            const float4 n = noise4(key, q0 + grp, token, draw);
+            s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(sigma_log2e * n.x), s);
+            s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(sigma_log2e * n.y), s);
+            s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(sigma_log2e * n.z), s);
+            s = __builtin_fmaf(q[m][3], __builtin_amdgcn_exp2f(sigma_log2e * n.w), s);
+            if (y_in && (uint32_t)m == my)
+                ysel = ey == 0 ? n.x : (ey == 1 ? n.y : (ey == 2 ? n.z : n.w));
+        }
+        const float tot = wave_sum(s);
+        float ny = 0.f;
+        if (y_in) ny = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ysel), owner));
+        if (lane == 0)
+            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(sigma, ny, zy);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
+                                float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
+                                int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,
+                                hipStream_t s) {
+    const uint32_t blocks = (uint32_t)((T + 3) / 4);
+    const float sl2e = sigma * LOG2E;
+#define DUST_HEAD(G)                                                                           \
+    head_ce_kernel<G><<<blocks, 256, 0, s>>>(logits, targets, loss_pert, loss_clean,           \
+                                             (uint32_t)T, (uint32_t)V, (uint32_t)v0,           \
+                                             (uint32_t)C, (uint32_t)Kc, sigma, sl2e, key,      \
+                                             draw0, tok0)
+    if (C <= 256) DUST_HEAD(1);
+    else if (C <= 512) DUST_HEAD(2);
+    else if (C <= 1024) DUST_HEAD(4);
+    else if (C <= 2048) DUST_HEAD(8);
+    else DUST_HEAD(16);
+#undef DUST_HEAD
+    return hipGetLastError();
+}
+
+}  // namespace dust

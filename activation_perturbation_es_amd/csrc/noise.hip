@@ -1,0 +1,167 @@
+// Noise injection and raw-word kernels of the Dust estimator (gfx950).
+//
+// dust_noise_inject forms the perturbed layer outputs y'^{(i)}_t = y_t + sigma a^{(i)}_t for a
+// block of draws (explainer cnblogs.com/32bin/p/23212811, "Credit assignment: one forward, two
+// rewards"). One thread owns one group of four channels of one token: it loads those four y
+// values once and then, for every draw, regenerates the four normals with one Philox call and
+// writes the four perturbed values. A wave therefore writes 64 consecutive groups of one output
+// row per draw (fully coalesced), and y is read once per call, not once per draw. The kernel is
+// bound by the integer and transcendental ALU work of the generator, not by HBM.
+#include "dust_internal.hpp"
+
+namespace dust {
+namespace {
+
+// Thread -> (token, group) mapping shared by the noise kernels. When a row has fewer than 256
+// groups, one block covers several tokens; otherwise a row spans several blocks.
+struct RowMap {
+    uint32_t ngroups;   // groups per token row
+    uint32_t tpr_log2;  // log2(threads per row) when ngroups < 256, else 8
+    uint32_t nblk_g;    // blocks per row when ngroups >= 256
+};
+
+__device__ __forceinline__ bool map_thread(const RowMap &m, uint32_t T, uint32_t &t, uint32_t &g) {
+    if (m.tpr_log2 == 8) {
+        t = blockIdx.x / m.nblk_g;
+        g = (blockIdx.x % m.nblk_g) * 256u + threadIdx.x;
+    } else {
+        t = blockIdx.x * (256u >> m.tpr_log2) + (threadIdx.x >> m.tpr_log2);
+        g = threadIdx.x & ((1u << m.tpr_log2) - 1u);
+    }
+    return t < T && g < m.ngroups;
+}
+
+static RowMap make_rowmap(int64_t ngroups, int64_t T, uint32_t &blocks) {
+    RowMap m;
+    m.ngroups = (uint32_t)ngroups;
+    if (ngroups >= 256) {
+        m.tpr_log2 = 8;
+        m.nblk_g = (uint32_t)((ngroups + 255) / 256);
+        blocks = (uint32_t)(m.nblk_g * T);
+    } else {
+        uint32_t l = 0;
+        while ((1u << l) < (uint32_t)ngroups) ++l;
+        m.tpr_log2 = l;
+        m.nblk_g = 1;
+        const uint32_t rows_per_block = 256u >> l;
+        blocks = (uint32_t)((T + rows_per_block - 1) / rows_per_block);
+    }
+    return m;
+}
+
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_,
+                                                     void *__restrict__ yp_, uint32_t T,
+                                                     uint32_t d, uint64_t ld_y, uint32_t q0,
+                                                     uint32_t Kc, float sigma, Key key,
+                                                     uint32_t draw0, uint32_t tok0, RowMap m) {
+    uint32_t t, g;
+    if (!map_thread(m, T, t, g)) return;
+    const uint32_t j0 = 4u * g;
+    const uint32_t token = tok0 + t;
+    const uint32_t q = q0 + g;
+
+    float yv[4];
+    if constexpr (BF16) {
+        const uint16_t *y = (const uint16_t *)y_ + (uint64_t)t * ld_y + j0;
+        if constexpr (VEC) {
+            const uint2 v = *(const uint2 *)y;
+            yv[0] = __uint_as_float(v.x << 16);
+            yv[1] = __uint_as_float(v.x & 0xFFFF0000u);
+            yv[2] = __uint_as_float(v.y << 16);
+            yv[3] = __uint_as_float(v.y & 0xFFFF0000u);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yv[e] = (j0 + e < d) ? bf16_to_f32(y[e]) : 0.f;
+        }
+    } else {
+        const float *y = (const float *)y_ + (uint64_t)t * ld_y + j0;
+        if constexpr (VEC) {
+            const float4 v = *(const float4 *)y;
+            yv[0] = v.x; yv[1] = v.y; yv[2] = v.z; yv[3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) yv[e] = (j0 + e < d) ? y[e] : 0.f;
+        }
+    }
+
+    const uint64_t draw_stride = (uint64_t)T * d;
+    const uint64_t base = (uint64_t)t * d + j0;
+    for (uint32_t k = 0; k < Kc; ++k) {
+        const float4 n = noise4(key, q, token, draw0 + k);
+        const float o0 = __builtin_fmaf(sigma, n.x, yv[0]);
+        const float o1 = __builtin_fmaf(sigma, n.y, yv[1]);
+        const float o2 = __builtin_fmaf(sigma, n.z, yv[2]);
+        const float o3 = __builtin_fmaf(sigma, n.w, yv[3]);
+        const uint64_t off = (uint64_t)k * draw_stride + base;
+        if constexpr (BF16) {
+            uint16_t *out = (uint16_t *)yp_ + off;
+            if constexpr (VEC) {
+                uint2 v;
+                v.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
+                v.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
+                *(uint2 *)out = v;
+            } else {
+                const float o[4] = {o0, o1, o2, o3};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j0 + e < d) out[e] = f32_to_bf16(o[e]);
+            }
+        } else {
+            float *out = (float *)yp_ + off;
+            if constexpr (VEC) {
+                *(float4 *)out = make_float4(o0, o1, o2, o3);
+            } else {
+                const float o[4] = {o0, o1, o2, o3};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (j0 + e < d) out[e] = o[e];
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void words_kernel(uint4 *__restrict__ words, uint32_t T,
+                                                    uint32_t Kc, uint32_t group0, Key key,
+                                                    uint32_t draw0, uint32_t tok0, RowMap m) {
+    uint32_t t, g;
+    if (!map_thread(m, T, t, g)) return;
+    const uint64_t draw_stride = (uint64_t)T * m.ngroups;
+    for (uint32_t k = 0; k < Kc; ++k)
+        words[(uint64_t)k * draw_stride + (uint64_t)t * m.ngroups + g] =
+            noise_words(key, group0 + g, tok0 + t, draw0 + k);
+}
+
+}  // namespace
+
+hipError_t launch_noise_inject(const void *y, void *y_pert, bool bf16, int64_t T, int64_t d,
+                               int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, Key key,
+                               uint32_t draw0, uint32_t tok0, hipStream_t s) {
+    const int64_t ngroups = (d + 3) / 4;
+    uint32_t blocks = 0;
+    const RowMap m = make_rowmap(ngroups, T, blocks);
+    const bool vec = (d % 4 == 0) && (ld_y % 4 == 0) && aligned16(y) && aligned16(y_pert);
+    const uint32_t q0 = (uint32_t)(chan0 / 4);
+#define DUST_INJECT(B, V)                                                                      \
+    inject_kernel<B, V><<<blocks, 256, 0, s>>>(y, y_pert, (uint32_t)T, (uint32_t)d,            \
+                                               (uint64_t)ld_y, q0, (uint32_t)Kc, sigma, key,   \
+                                               draw0, tok0, m)
+    if (bf16) {
+        if (vec) DUST_INJECT(true, true); else DUST_INJECT(true, false);
+    } else {
+        if (vec) DUST_INJECT(false, true); else DUST_INJECT(false, false);
+    }
+#undef DUST_INJECT
+    return hipGetLastError();
+}
+
+hipError_t launch_noise_words(uint32_t *words, int64_t Kc, int64_t T, int64_t G, uint32_t group0,
+                              Key key, uint32_t draw0, uint32_t tok0, hipStream_t s) {
+    uint32_t blocks = 0;
+    const RowMap m = make_rowmap(G, T, blocks);
+    words_kernel<<<blocks, 256, 0, s>>>((uint4 *)words, (uint32_t)T, (uint32_t)Kc, group0, key,
+                                        draw0, tok0, m);
+    return hipGetLastError();
+}
+
+}  // namespace dust

@@ -1,0 +1,189 @@
+/*
+ * dust.h -- C ABI of the Dust gradient estimator on AMD Instinct MI355X (gfx950).
+ *
+ * Dust estimates a linear layer's weight gradient without backpropagation: it adds per-token
+ * Gaussian noise to the layer's output, scores every draw by the per-token change of the loss,
+ * folds those scores into discounted rewards, averages reward-weighted noise into an estimate
+ * of the output error, and contracts that estimate with the layer input. The LM-head variant
+ * perturbs cached logits and recomputes the cross-entropy for one vocabulary chunk only.
+ *
+ * Method source: the "Dust" explainer at cnblogs.com/32bin/p/23212811 ("explainer" below),
+ *   section "Credit assignment: one forward, two rewards" (信用分配：一次前向，两种奖励) and
+ *   section "The real work: suppressing interference" (真正的工作量：压住干扰).
+ *
+ * ------------------------------------------------------------------------------------------
+ * Conventions shared by every entry point
+ *   - Every data pointer is DEVICE memory owned by the caller (e.g. a torch tensor). The
+ *     library never allocates, frees, or synchronises; all work is enqueued on `stream`
+ *     (a hipStream_t; NULL = the legacy default stream) and runs asynchronously.
+ *   - Arrays are row-major and contiguous unless a leading dimension (ld_*) is given.
+ *   - Sizes are element counts. A size of zero is valid and enqueues nothing (the outputs are
+ *     left untouched, except where an entry point states otherwise).
+ *   - All arguments are validated on the host before any HIP call. Invalid arguments return
+ *     DUST_ERR_INVALID; shapes that are valid but outside what the kernels implement return
+ *     DUST_ERR_UNSUPPORTED; a short workspace returns DUST_ERR_WORKSPACE; a failed launch
+ *     returns DUST_ERR_HIP. dust_last_error() then holds a one-line description for the
+ *     calling thread. Nothing is enqueued when a call fails validation.
+ *   - Entry points are re-entrant and keep no state between calls.
+ *
+ * Noise (shared by inject, error estimate and head chunk; regenerated, never stored).
+ *   The explainer draws a_t ~ N(0, I) independently per token and per draw and adds sigma*a_t
+ *   to the layer output. The generator and the index layout are this library's definition:
+ *     key      = (seed mod 2^32, seed >> 32)
+ *     counter  = (floor(ch / 4), token, draw, tag)         -- Philox4x32-10 (Salmon et al.,
+ *                                                             SC'11) -> words w0..w3
+ *     u(w)     = (floor(w / 2^9) + 1/2) * 2^-23            -- uniform in (0, 1)
+ *     rho(w)   = sqrt(-2 ln u(w))                          -- Box-Muller radius
+ *     a[ch=4q+0] = rho(w0) cos(2 pi u(w1))   a[ch=4q+1] = rho(w0) sin(2 pi u(w1))
+ *     a[ch=4q+2] = rho(w2) cos(2 pi u(w3))   a[ch=4q+3] = rho(w2) sin(2 pi u(w3))
+ *   `ch` is the GLOBAL channel (chan0 + local channel; the vocabulary id for the head), `token`
+ *   is tok0 + local token and `draw` is draw0 + local draw, so the noise of an element does not
+ *   depend on how tokens, draws or channels are split across calls. `tag` separates
+ *   independent noise streams (layer types, perturbation passes).
+ *   Requirements: chan0 % 4 == 0; chan0 + d <= 2^34; tok0 + T <= 2^32; draw0 + K <= 2^32.
+ * ------------------------------------------------------------------------------------------
+ */
+#ifndef DUST_H_
+#define DUST_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DUST_OK = 0,
+    DUST_ERR_INVALID = 1,      /* bad pointer, size, alignment, or parameter */
+    DUST_ERR_UNSUPPORTED = 2,  /* valid, but outside what the kernels implement */
+    DUST_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+    DUST_ERR_HIP = 4           /* a HIP launch failed */
+} dust_status;
+
+typedef enum { DUST_F32 = 0, DUST_BF16 = 1 } dust_dtype;
+
+typedef enum { DUST_DELTA_LOSS = 0, DUST_DELTA_INNER = 1 } dust_delta_mode;
+
+/* Static name of a status code ("DUST_OK", ...). Never NULL. */
+const char *dust_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). Valid until the next
+ * call into the library from the same thread. */
+const char *dust_last_error(void);
+
+/*
+ * dust_noise_inject -- perturbed layer outputs for a block of draws.
+ * Explainer, "Credit assignment": the perturbed output of token t in draw i is
+ *     y'^{(i)}_t = y_t + sigma * a^{(i)}_t.
+ *   y       [T, ld_y] of `dtype` (the first d columns are used)         (in)
+ *   y_pert  [Kc, T, d] of `dtype`: y_pert[k][t][j] for draw draw0 + k    (out)
+ * Arithmetic in fp32; a bf16 output is rounded to nearest-even. dtype is DUST_F32 or DUST_BF16.
+ * Requires ld_y >= d and element-aligned pointers; 16-byte-aligned pointers with d and ld_y
+ * multiples of 4 take the vectorised path. sigma must be finite.
+ */
+int dust_noise_inject(const void *y, void *y_pert, int dtype, int64_t T, int64_t d,
+                      int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, uint64_t seed,
+                      uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);
+
+/*
+ * dust_loss_delta -- per-token score of every draw, c [Kc, T] fp32 (out).
+ * DUST_DELTA_LOSS (explainer, "Credit assignment": the centred per-token loss change, read as
+ *   clean minus perturbed so that c is the loss REDUCTION the noise caused):
+ *     c[i][t] = loss_clean[t] - loss_pert[i][t]
+ *   loss_clean [T] fp32, loss_pert [Kc, T] fp32 (in); delta_o, g_o, io_dtype and d unused.
+ * DUST_DELTA_INNER (explainer, "The real work": attention internals are scored through the
+ *   attention output by the inner product of the output change with that output's estimated
+ *   error; the sign is chosen so that c is again a first-order loss reduction):
+ *     c[i][s] = - sum_j delta_o[i][s][j] * g_o[s][j]
+ *   delta_o [Kc, T, d] and g_o [T, d] of io_dtype (DUST_F32 or DUST_BF16) (in); products
+ *   accumulate in fp32; loss_clean and loss_pert unused. d >= 1.
+ */
+int dust_loss_delta(int mode, const float *loss_clean, const float *loss_pert,
+                    const void *delta_o, const void *g_o, int io_dtype, float *c, int64_t Kc,
+                    int64_t T, int64_t d, void *stream);
+
+/*
+ * dust_reward_scan -- discounted rewards, r [K, T] fp32 (out) from c [K, T] fp32 (in).
+ * Explainer, "Credit assignment": r_t = sum_{s >= t} gamma^(s-t) c_s; gamma = 0 keeps each
+ * token's own score. The sum runs to the end of token t's own sequence: tokens form
+ * T / seg_len sequences of seg_len consecutive tokens and no reward crosses a sequence end.
+ * Requires seg_len >= 1, T % seg_len == 0, 0 <= gamma <= 1. r == c (in place) is allowed; any
+ * other overlap is rejected. fp32 arithmetic (a parallel scan, so rounding order differs from
+ * the sequential recursion).
+ */
+int dust_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
+                     float gamma, void *stream);
+
+/*
+ * dust_error_estimate -- output-error estimate g_hat [T, d] fp32 (out, or in/out).
+ * Explainer, "Credit assignment":
+ *     g_hat[t][j] = -(1 / (K_total * sigma)) * sum_{i < K} r[i][t] * a^{(draw0+i)}_{t, chan0+j}
+ *   r           [K, T] fp32 rewards of draws draw0 .. draw0+K-1                       (in)
+ *   g_hat       [T, d] fp32; with accumulate != 0 the sum is ADDED to its contents   (in/out)
+ *   g_hat_t_bf16  nullable; [d, T] bf16 transpose of the resulting g_hat (round to nearest
+ *               even), the operand dust_weight_grad takes                               (out)
+ * K_total is the whole population when draws arrive in chunks (K <= K_total); the noise is
+ * regenerated from (seed, tag) exactly as dust_noise_inject drew it. sigma > 0 and finite.
+ * The draw sum accumulates in fp32. K == 0 with accumulate == 0 writes zeros.
+ */
+int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_t K,
+                        int64_t K_total, int64_t T, int64_t d, int64_t chan0, float sigma,
+                        uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                        int accumulate, void *stream);
+
+/*
+ * dust_weight_grad_workspace -- bytes of device workspace dust_weight_grad needs for this
+ * shape (0 when none). Host-only; never fails.
+ */
+size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in);
+
+/*
+ * dust_weight_grad -- weight-gradient estimate G [d_out, d_in] fp32 (out).
+ * Explainer, "Credit assignment": G_W = sum_t g_hat_t x_t^T, the same outer product as
+ * backpropagation with the estimated output error in place of the chain-rule one:
+ *     G[o][i] = sum_t g_hat_t_bf16[o][t] * x_bf16[t][i]
+ *   g_hat_t_bf16  [d_out, T] bf16 (as written by dust_error_estimate)                  (in)
+ *   x_bf16        [T, d_in] bf16, the layer input                                      (in)
+ *   workspace     device scratch of at least dust_weight_grad_workspace(T, d_out, d_in)
+ *                 bytes (may be NULL when that is 0)
+ * bf16 matrix-core products with fp32 accumulation; split-T partial sums are reduced in a
+ * fixed order, so results are deterministic. T == 0 writes zeros.
+ */
+int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
+                     int64_t d_out, int64_t d_in, void *workspace, size_t ws_bytes,
+                     void *stream);
+
+/*
+ * dust_head_ce_chunk -- perturbed per-token cross-entropy of the LM head for one vocabulary
+ * chunk. Explainer, "The real work": the head is perturbed directly on cached logits and only
+ * the cross-entropy involving one chunk of the vocabulary is recomputed. For draw i and token t
+ * the logits of the chunk [v0, v0 + C) become z_j + sigma * a^{(i)}_{t, j} (global channel
+ * j = vocabulary id); every other logit keeps its cached value; the loss is the full-vocabulary
+ * cross-entropy  log sum_j exp(z'_j) - z'_{target}.
+ *   logits      [T, V] fp32 cached clean logits                                     (in)
+ *   targets     [T] int32 in [0, V); an out-of-range target yields NaN losses        (in)
+ *   loss_pert   [Kc, T] fp32, draws draw0 .. draw0+Kc-1                              (out)
+ *   loss_clean  nullable; [T] fp32 unperturbed cross-entropy                         (out)
+ * Requires 1 <= C <= 4096, v0 % 4 == 0, v0 + C <= V. Log-sum-exp is taken online in fp32.
+ */
+int dust_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
+                       float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
+                       int64_t Kc, float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                       uint32_t tok0, void *stream);
+
+/*
+ * dust_noise_words -- the raw Philox4x32-10 words behind the noise, for bit-exact checks of
+ * the generator and its indexing (the same device routine every noise kernel calls).
+ *   words  [Kc, T, G, 4] uint32: words[k][t][g][w] = word w of
+ *          counter (group0 + g, tok0 + t, draw0 + k, tag) under key (seed lo, seed hi)  (out)
+ * Requires group0 + G <= 2^32, tok0 + T <= 2^32, draw0 + Kc <= 2^32.
+ */
+int dust_noise_words(uint32_t *words, int64_t Kc, int64_t T, int64_t G, uint32_t group0,
+                     uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUST_H_ */

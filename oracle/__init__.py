@@ -69,6 +69,11 @@ def _load():
     lib.dust_or_head_ce_chunk.argtypes = [_d, ctypes.POINTER(ctypes.c_int32), _i64, _i64, _i64,
                                           _i64, _i64, ctypes.c_double, _u64, _u32, _u32, _u32,
                                           _d, _d]
+    _pi64 = ctypes.POINTER(_i64)
+    lib.dust_or_normals_at.argtypes = [_u64, _u32, _u32, _u32, _i64, _pi64, _pi64, _pi64, _i64, _d]
+    lib.dust_or_head_ce_at.argtypes = [_d, ctypes.POINTER(ctypes.c_int32), _i64, _i64, _i64, _i64,
+                                       ctypes.c_double, _u64, _u32, _u32, _u32, _pi64, _pi64, _i64,
+                                       _d]
     lib.dust_or_round_bf16.argtypes = [ctypes.c_double]
     lib.dust_or_round_bf16.restype = ctypes.c_double
     _lib = lib
@@ -115,6 +120,23 @@ def normals(seed: int, tag: int, draw0: int, tok0: int, chan0: int, K: int, T: i
     """Normals for draws draw0.., tokens tok0.., channels chan0..: array [K, T, d]."""
     out = np.empty((K, T, d), dtype=np.float64)
     _load().dust_or_normals(seed, tag, draw0, tok0, chan0, K, T, d, _p(out))
+    return out
+
+
+def _idx(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.int64)
+
+
+def _pidx(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(_i64))
+
+
+def normals_at(seed: int, tag: int, k, t, j, draw0: int = 0, tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """Normals at chosen local (draw, token, channel) triples."""
+    k, t, j = _idx(k), _idx(t), _idx(j)
+    out = np.empty(len(k), dtype=np.float64)
+    _load().dust_or_normals_at(seed, tag, draw0, tok0, chan0, _pidx(k), _pidx(t), _pidx(j), len(k),
+                               _p(out))
     return out
 
 
@@ -203,6 +225,19 @@ def head_ce_chunk(logits, targets, v0: int, C: int, K: int, sigma: float, seed: 
     _load().dust_or_head_ce_chunk(_p(z), y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), T, V, v0,
                                   C, K, sigma, seed, tag, draw0, tok0, _p(lp), _p(lc))
     return lp, lc
+
+
+def head_ce_at(logits, targets, v0: int, C: int, k, t, sigma: float, seed: int, tag: int,
+               draw0: int = 0, tok0: int = 0) -> np.ndarray:
+    """loss_pert of draw draw0 + k[m] at token t[m], for chosen pairs only."""
+    z = _f64(logits)
+    T, V = z.shape
+    y = np.ascontiguousarray(targets, dtype=np.int32)
+    k, t = _idx(k), _idx(t)
+    out = np.empty(len(k), dtype=np.float64)
+    _load().dust_or_head_ce_at(_p(z), y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), T, V, v0, C,
+                               sigma, seed, tag, draw0, tok0, _pidx(k), _pidx(t), len(k), _p(out))
+    return out
 
 
 def round_bf16(x) -> np.ndarray:

@@ -102,6 +102,17 @@ void dust_or_normals(uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
                                                           (uint64_t)(chan0 + j));
 }
 
+/* Normals at n chosen (draw, token, channel) triples: out[m] = a^{(draw0+k[m])}_{tok0+t[m], chan0+j[m]}. */
+void dust_or_normals_at(uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0, int64_t chan0,
+                        const int64_t *k, const int64_t *t, const int64_t *j, int64_t n,
+                        double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < n; ++m)
+        out[m] = dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]), (uint32_t)(tok0 + t[m]),
+                                (uint64_t)(chan0 + j[m]));
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Perturbed layer output y'^{(i)}_t = y_t + sigma a^{(i)}_t (explainer, "Credit assignment").
  * y is [T, ld_y] (first d columns used); y_pert is [K, T, d]. */
@@ -247,6 +258,39 @@ void dust_or_head_ce_chunk(const double *logits, const int32_t *targets, int64_t
             }
             loss_pert[i * T + t] = m + log(s) - zy;
         }
+    }
+}
+
+/* The same perturbed cross-entropy at n chosen (draw, token) pairs: out[m] is loss_pert of draw
+ * draw0 + k[m] at token t[m]. */
+void dust_or_head_ce_at(const double *logits, const int32_t *targets, int64_t T, int64_t V,
+                        int64_t v0, int64_t C, double sigma, uint64_t seed, uint32_t tag,
+                        uint32_t draw0, uint32_t tok0, const int64_t *k, const int64_t *t,
+                        int64_t n, double *out)
+{
+    (void)T;
+    #pragma omp parallel for schedule(static)
+    for (int64_t m = 0; m < n; ++m) {
+        const double *z = logits + t[m] * V;
+        int64_t y = targets[t[m]];
+        double mx = -INFINITY, zy = 0.0;
+        for (int64_t j = 0; j < V; ++j) {
+            double zj = z[j];
+            if (j >= v0 && j < v0 + C)
+                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),
+                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);
+            if (zj > mx) mx = zj;
+            if (j == y) zy = zj;
+        }
+        double s = 0.0;
+        for (int64_t j = 0; j < V; ++j) {
+            double zj = z[j];
+            if (j >= v0 && j < v0 + C)
+                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),
+                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);
+            s += exp(zj - mx);
+        }
+        out[m] = mx + log(s) - zy;
     }
 }
 
