@@ -24,6 +24,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, b);
 }
 
+// Two fp32 values -> packed bf16 pair (lo in bits 0..15), nearest-even, one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
 hipError_t launch_noise_inject(const void *y, void *y_pert, bool bf16, int64_t T, int64_t d,
                                int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, Key key,
                                uint32_t draw0, uint32_t tok0, hipStream_t s);
@@ -67,6 +75,14 @@ __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
     return x;
+}
+
+// Blocks are dispatched round-robin over the 8 XCDs (block b runs on XCD b % 8), each with its
+// own L2. This maps the hardware block index to a logical one so that each XCD receives one
+// contiguous eighth of the logical order; neighbouring logical blocks then share an L2.
+__device__ __forceinline__ uint32_t xcd_logical_block(uint32_t b, uint32_t nblocks) {
+    if (nblocks % 8u != 0u) return b;
+    return (b % 8u) * (nblocks / 8u) + b / 8u;
 }
 
 // Index of the calling wave inside its block, as a wave-uniform (scalar) value.

@@ -26,11 +26,16 @@ __device__ __forceinline__ uint64_t mul_wide(uint32_t a, uint32_t b) {
     return (uint64_t)a * (uint64_t)b;
 }
 
-// Ten Philox rounds on (c0, c1, c2, c3) under (k0, k1); results in place.
+// Three-input XOR in one VALU op: gfx950's v_bitop3_b32 with the parity truth table 0x96.
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
+// Ten Philox rounds on (c0, c1, c2, c3) under (k0, k1); results in place. The first round keeps
+// plain XORs so that wave-uniform counter words (draw, tag, often token) stay on the scalar unit.
 __device__ __forceinline__ void philox4x32_10(uint32_t &c0, uint32_t &c1, uint32_t &c2,
                                               uint32_t &c3, uint32_t k0, uint32_t k1) {
-#pragma unroll
-    for (int round = 0; round < 10; ++round) {
+    {
         const uint64_t pa = mul_wide(0xD2511F53u, c0);
         const uint64_t pb = mul_wide(0xCD9E8D57u, c2);
         const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
@@ -39,8 +44,19 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &c0, uint32_t &c1, uint32
         c3 = (uint32_t)pa;
         c0 = n0;
         c2 = n2;
+    }
+#pragma unroll
+    for (int round = 1; round < 10; ++round) {
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
+        const uint64_t pa = mul_wide(0xD2511F53u, c0);
+        const uint64_t pb = mul_wide(0xCD9E8D57u, c2);
+        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
+        c1 = (uint32_t)pb;
+        c3 = (uint32_t)pa;
+        c0 = n0;
+        c2 = n2;
     }
 }
 
@@ -53,8 +69,11 @@ __device__ __forceinline__ uint4 noise_words(const Key &key, uint32_t q, uint32_
 }
 
 __device__ __forceinline__ float uniform01(uint32_t w) {
-    // (m + 1/2) * 2^-23 with m < 2^23: exact, in [2^-24, 1 - 2^-24].
-    return __builtin_fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+    // (m + 1/2) * 2^-23 with m = w >> 9 < 2^23, exact, in [2^-24, 1 - 2^-24]. One funnel shift
+    // builds the fp32 bit pattern of 1 + m 2^-23 (exponent field 0x7F above the 23 mantissa
+    // bits), and subtracting 1 - 2^-24 leaves (2m + 1) 2^-24, which fp32 holds exactly.
+    const float one_plus = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u));
+    return one_plus - 0x1.fffffep-1f;
 }
 
 // One Box-Muller pair: radius from wa, angle (in revolutions) from wb.

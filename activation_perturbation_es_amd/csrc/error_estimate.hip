@@ -20,7 +20,9 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
     const float *__restrict__ r, float *__restrict__ g, uint16_t *__restrict__ gt, uint32_t K,
     uint32_t T, uint32_t d, uint32_t q0, float scale, Key key, uint32_t draw0, uint32_t tok0,
     int accumulate, uint32_t n_ctiles) {
-    const uint32_t w = blockIdx.x * 4u + wave_in_block();
+    // Consecutive logical waves share g_hat^T lines (neighbouring token tiles) and reward rows
+    // (the channel tiles of one token tile), so they are kept on one XCD.
+    const uint32_t w = xcd_logical_block(blockIdx.x, gridDim.x) * 4u + wave_in_block();
     const uint32_t ttile = w / n_ctiles;
     const uint32_t ctile = w % n_ctiles;
     const uint32_t t0 = ttile * TPW;
@@ -55,25 +57,27 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
     const uint32_t nch = min(4u, d - j0);
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
-        if (tt >= (int)ntok) break;
-        float *gr = g + (uint64_t)(t0 + tt) * d + j0;
-        if (VEC) {
-            float4 v = make_float4(scale * acc[tt][0], scale * acc[tt][1], scale * acc[tt][2],
-                                   scale * acc[tt][3]);
-            if (accumulate) {
-                const float4 o = *(const float4 *)gr;
-                v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
-            }
-            *(float4 *)gr = v;
-            acc[tt][0] = v.x; acc[tt][1] = v.y; acc[tt][2] = v.z; acc[tt][3] = v.w;
-        } else {
+        if (tt < (int)ntok) {
+            float *gr = g + (uint64_t)(t0 + tt) * d + j0;
+            if constexpr (VEC) {
+                float4 v = make_float4(scale * acc[tt][0], scale * acc[tt][1], scale * acc[tt][2],
+                                       scale * acc[tt][3]);
+                if (accumulate) {
+                    const float4 o = *(const float4 *)gr;
+                    v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+                }
+                *(float4 *)gr = v;
+                acc[tt][0] = v.x; acc[tt][1] = v.y; acc[tt][2] = v.z; acc[tt][3] = v.w;
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (e >= (int)nch) break;
-                float v = scale * acc[tt][e];
-                if (accumulate) v += gr[e];
-                gr[e] = v;
-                acc[tt][e] = v;
+                for (int e = 0; e < 4; ++e) {
+                    if (e < (int)nch) {
+                        float v = scale * acc[tt][e];
+                        if (accumulate) v += gr[e];
+                        gr[e] = v;
+                        acc[tt][e] = v;
+                    }
+                }
             }
         }
     }
@@ -82,23 +86,22 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
     const bool gt_vec = VEC && (ntok == TPW) && ((T % 8u) == 0u) && ((TPW % 8) == 0);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        if (e >= (int)nch) break;
-        uint16_t *row = gt + (uint64_t)(j0 + e) * T + t0;
-        if (gt_vec) {
+        if (e < (int)nch) {
+            uint16_t *row = gt + (uint64_t)(j0 + e) * T + t0;
+            if (gt_vec) {
 #pragma unroll
-            for (int h = 0; h < TPW / 8; ++h) {
-                uint4 v;
-                v.x = (uint32_t)f32_to_bf16(acc[8 * h + 0][e]) | ((uint32_t)f32_to_bf16(acc[8 * h + 1][e]) << 16);
-                v.y = (uint32_t)f32_to_bf16(acc[8 * h + 2][e]) | ((uint32_t)f32_to_bf16(acc[8 * h + 3][e]) << 16);
-                v.z = (uint32_t)f32_to_bf16(acc[8 * h + 4][e]) | ((uint32_t)f32_to_bf16(acc[8 * h + 5][e]) << 16);
-                v.w = (uint32_t)f32_to_bf16(acc[8 * h + 6][e]) | ((uint32_t)f32_to_bf16(acc[8 * h + 7][e]) << 16);
-                *(uint4 *)(row + 8 * h) = v;
-            }
-        } else {
+                for (int h = 0; h < TPW / 8; ++h) {
+                    uint4 v;
+                    v.x = pack_bf16x2(acc[8 * h + 0][e], acc[8 * h + 1][e]);
+                    v.y = pack_bf16x2(acc[8 * h + 2][e], acc[8 * h + 3][e]);
+                    v.z = pack_bf16x2(acc[8 * h + 4][e], acc[8 * h + 5][e]);
+                    v.w = pack_bf16x2(acc[8 * h + 6][e], acc[8 * h + 7][e]);
+                    *(uint4 *)(row + 8 * h) = v;
+                }
+            } else {
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) {
-                if (tt >= (int)ntok) break;
-                row[tt] = f32_to_bf16(acc[tt][e]);
+                for (int tt = 0; tt < TPW; ++tt)
+                    if (tt < (int)ntok) row[tt] = f32_to_bf16(acc[tt][e]);
             }
         }
     }
@@ -128,8 +131,9 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
     const float scale = (float)(-1.0 / ((double)K_total * (double)sigma));
     const uint32_t n_ctiles = (uint32_t)((d + 255) / 256);
     const bool vec = (d % 4 == 0) && aligned16(g) && (gt == nullptr || aligned16(gt));
-    // Largest token tile that still gives every SIMD several waves.
-    int tpw = 16;
+    // Largest token tile (8 or 4) that still gives every SIMD several waves. A 16-token tile
+    // would need more than the registers the compiler keeps the accumulators in.
+    int tpw = 8;
     while (tpw > 4 && ((T + tpw - 1) / tpw) * (int64_t)n_ctiles < 8192) tpw /= 2;
     const uint64_t waves = (uint64_t)((T + tpw - 1) / tpw) * n_ctiles;
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
@@ -139,9 +143,9 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
                                                         (uint32_t)d, q0, scale, key, draw0,    \
                                                         tok0, accumulate ? 1 : 0, n_ctiles)
     if (vec) {
-        if (tpw == 16) DUST_EE(16, true); else if (tpw == 8) DUST_EE(8, true); else DUST_EE(4, true);
+        if (tpw == 8) DUST_EE(8, true); else DUST_EE(4, true);
     } else {
-        if (tpw == 16) DUST_EE(16, false); else if (tpw == 8) DUST_EE(8, false); else DUST_EE(4, false);
+        if (tpw == 8) DUST_EE(8, false); else DUST_EE(4, false);
     }
 #undef DUST_EE
     return hipGetLastError();

@@ -97,10 +97,7 @@ __global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_
         if constexpr (BF16) {
             uint16_t *out = (uint16_t *)yp_ + off;
             if constexpr (VEC) {
-                uint2 v;
-                v.x = (uint32_t)f32_to_bf16(o0) | ((uint32_t)f32_to_bf16(o1) << 16);
-                v.y = (uint32_t)f32_to_bf16(o2) | ((uint32_t)f32_to_bf16(o3) << 16);
-                *(uint2 *)out = v;
+                *(uint2 *)out = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
             } else {
                 const float o[4] = {o0, o1, o2, o3};
 #pragma unroll

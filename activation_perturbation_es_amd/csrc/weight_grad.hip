@@ -10,7 +10,7 @@
 // which wants 8 consecutive k per lane; each thread therefore loads a 4 (k) x 8 (n) block of x
 // and transposes it in registers before writing it to LDS as [n][k].
 // Tiling: 128 x 128 output tile per 256-thread block, 2 x 2 waves of 64 x 64, k-step 64 staged
-// through LDS with the next tile's global loads in flight during the MFMAs. The token axis is
+// through two LDS buffers, with the next step's global loads in flight during the MFMAs. The token axis is
 // split across blocks so that small outputs still fill the 256 CUs; the split partial sums go to
 // a workspace and are added in split order by a second kernel, so results are deterministic.
 #include "dust_internal.hpp"
@@ -46,17 +46,23 @@ SplitPlan plan_split(int64_t T, int64_t M, int64_t N) {
     return p;
 }
 
+// Block -> (split, m-tile, n-tile) in the logical order (split, m, n), n fastest, dealt out to
+// the XCDs in contiguous eighths (xcd_logical_block): the n-tiles that share an A row-block run
+// side by side on one XCD, and with 8 splits each XCD owns exactly one split, whose slice of x
+// all of its blocks read.
 __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B,
                                                          float *__restrict__ out, uint32_t M,
                                                          uint32_t N, uint32_t K, SplitPlan p,
                                                          uint64_t split_stride) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[BM * LDS_PITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * LDS_PITCH];
+    // two LDS stages: the next k-step is written while the current one feeds the MFMAs
+    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * LDS_PITCH];
+    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * LDS_PITCH];
 
     const uint32_t ntile_all = p.mtiles * p.ntiles;
-    const uint32_t split = blockIdx.x / ntile_all;
-    const uint32_t tile = blockIdx.x % ntile_all;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const uint32_t split = lb / ntile_all;
+    const uint32_t tile = lb % ntile_all;
     const uint32_t m0 = (tile / p.ntiles) * BM;
     const uint32_t n0 = (tile % p.ntiles) * BN;
     const uint32_t kbeg = split * p.kchunk;
@@ -78,29 +84,37 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
     // A: 128 rows x 8 pieces of 16 B; thread takes pieces tid, tid+256, tid+512, tid+768.
     // B: 16 x 16 blocks of 4 k-rows x 8 n-columns; thread takes block (kb, nb).
     const uint32_t kb = tid & 15u, nb = tid >> 4;
-    uint4 ra[4], rb[4];
-    const uint4 zero4 = make_uint4(0, 0, 0, 0);
+    // native clang vectors: a select on HIP's struct vector types goes through scratch
+    u32x4 ra[4], rb[4];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
+    // Out-of-range pieces read a clamped in-range address and are zeroed by a value select (a
+    // select between a global pointer and a private zero would put the zero in scratch).
+    // K, kend and N are multiples of 8, so a piece is either wholly inside or wholly outside.
     auto gload = [&](uint32_t k0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t piece = tid + 256u * j;
             const uint32_t row = piece >> 3, kc = piece & 7u;
             const uint32_t gm = m0 + row, gk = k0 + 8u * kc;
-            ra[j] = (gm < M && gk < kend) ? *(const uint4 *)(A + (uint64_t)gm * K + gk) : zero4;
+            const bool in = gm < M && gk < kend;
+            const u32x4 v = *(const u32x4 *)(A + (uint64_t)min(gm, M - 1u) * K + min(gk, kend - 8u));
+            ra[j] = in ? v : zero4;
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const uint32_t gk = k0 + 4u * kb + r, gn = n0 + 8u * nb;
-            rb[r] = (gk < kend && gn < N) ? *(const uint4 *)(B + (uint64_t)gk * N + gn) : zero4;
+            const bool in = gk < kend && gn < N;
+            const u32x4 v = *(const u32x4 *)(B + (uint64_t)min(gk, kend - 1u) * N + min(gn, N - 8u));
+            rb[r] = in ? v : zero4;
         }
     };
-    auto lstore = [&]() {
+    auto lstore = [&](int st) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t piece = tid + 256u * j;
             const uint32_t row = piece >> 3, kc = piece & 7u;
-            *(uint4 *)(As + row * LDS_PITCH + 8u * kc) = ra[j];
+            *(u32x4 *)(As[st] + row * LDS_PITCH + 8u * kc) = ra[j];
         }
         // rb[r] holds x[k = 4kb + r][n = 8nb .. 8nb+7]; dword h packs columns 2h (low half)
         // and 2h+1 (high half). Column n gets its four k values as two dwords.
@@ -115,33 +129,39 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
             lo.y = (w2[h] & 0xFFFFu) | (w3[h] << 16);
             hi.x = (w0[h] >> 16) | (w1[h] & 0xFFFF0000u);
             hi.y = (w2[h] >> 16) | (w3[h] & 0xFFFF0000u);
-            *(uint2 *)(Bs + (8u * nb + 2u * h) * LDS_PITCH + 4u * kb) = lo;
-            *(uint2 *)(Bs + (8u * nb + 2u * h + 1u) * LDS_PITCH + 4u * kb) = hi;
+            *(uint2 *)(Bs[st] + (8u * nb + 2u * h) * LDS_PITCH + 4u * kb) = lo;
+            *(uint2 *)(Bs[st] + (8u * nb + 2u * h + 1u) * LDS_PITCH + 4u * kb) = hi;
         }
     };
 
-    if (kbeg < kend) gload(kbeg);
+    if (kbeg < kend) {
+        gload(kbeg);
+        lstore(0);
+    }
+    __syncthreads();
+    int st = 0;
     for (uint32_t k0 = kbeg; k0 < kend; k0 += BK) {
-        lstore();
-        __syncthreads();
-        if (k0 + BK < kend) gload(k0 + BK);
+        const bool more = k0 + BK < kend;
+        if (more) gload(k0 + BK);       // in flight during the MFMAs below
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const uint32_t koff = kk * 16u + 8u * (lane >> 5);
             bf16x8 a[2], b[2];
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-                a[i] = *(const bf16x8 *)(As + (wm * 64u + i * 32u + (lane & 31u)) * LDS_PITCH + koff);
+                a[i] = *(const bf16x8 *)(As[st] + (wm * 64u + i * 32u + (lane & 31u)) * LDS_PITCH + koff);
 #pragma unroll
             for (int j = 0; j < 2; ++j)
-                b[j] = *(const bf16x8 *)(Bs + (wn * 64u + j * 32u + (lane & 31u)) * LDS_PITCH + koff);
+                b[j] = *(const bf16x8 *)(Bs[st] + (wn * 64u + j * 32u + (lane & 31u)) * LDS_PITCH + koff);
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
+        if (more) lstore(st ^ 1);
         __syncthreads();
+        st ^= 1;
     }
 
     // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32.

@@ -74,6 +74,7 @@ def _load():
     lib.dust_or_head_ce_at.argtypes = [_d, ctypes.POINTER(ctypes.c_int32), _i64, _i64, _i64, _i64,
                                        ctypes.c_double, _u64, _u32, _u32, _u32, _pi64, _pi64, _i64,
                                        _d]
+    lib.dust_or_threads.restype = ctypes.c_int
     lib.dust_or_round_bf16.argtypes = [ctypes.c_double]
     lib.dust_or_round_bf16.restype = ctypes.c_double
     _lib = lib
@@ -86,6 +87,11 @@ def _f64(a) -> np.ndarray:
 
 def _p(a: np.ndarray):
     return a.ctypes.data_as(_d)
+
+
+def threads() -> int:
+    """Threads the oracle's OpenMP loops use."""
+    return int(_load().dust_or_threads())
 
 
 # ------------------------------------------------------------------------------ generator

@@ -31,10 +31,23 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 #ifndef M_PI
 #define M_PI 3.14159265358979323846
 #endif
+
+/* Number of threads the OpenMP loops below use. */
+int dust_or_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* ---------------------------------------------------------------------------------------- */
 /* Philox4x32-10 (SC'11). One round maps (x0, x1, x2, x3) under key (k0, k1) to
