@@ -1,22 +1,24 @@
 #!/usr/bin/env python3
 """Throughput of the Dust estimator chain on one MI355X.
 
-One step = one whole estimate for the MLP up-projection 512 -> 2048 of the 8-layer width-512
-GPT (T = 16 x 1024 tokens, K = 64 draws, gamma = 0, sigma = 0.01), with every input resident in
-HBM before the timed region:
+One step = one whole estimate, with every input resident in HBM before the timed region. The
+default workload is the MLP up-projection 512 -> 2048 of the 8-layer width-512 GPT
+(T = 16 x 1024 tokens, K = 64 draws, gamma = 0, sigma = 0.01):
     dust_noise_inject   x 8 (8-draw blocks into a rotating perturbed-output buffer)
     dust_loss_delta     (loss mode, [64, 16384])
     dust_reward_scan    (gamma = 0, sequences of 1024)
     dust_error_estimate (g_hat [16384, 2048] fp32 + its bf16 transpose)
     dust_weight_grad    (G_W [2048, 512], bf16 matrix cores)
-The perturbed forward of the rest of the model that sits between the perturbation and the loss
-change is not part of the estimator; its per-token losses are synthetic inputs here.
+The perturbed forward of the rest of the model, between the perturbation and the loss change,
+is not part of the estimator; its per-token losses are synthetic inputs here.
+--workload 3 / 4 / 5 time the LM-head chunk, the attention k/v inner-product and the 240M-shape
+chains the same way (for the report; the default line is workload 2).
 
-Metric: draws x tokens per second (K * T / step time). Prints one JSON line; with the per-kernel
-HIP-event durations measured inside the timed region it adds the roofline of the dominant
-kernel, and the CPU oracle's throughput on a bounded sample of the same workload.
+Metric: draws x tokens per second (K * T / step time). Prints one JSON line with the per-kernel
+HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
+the CPU oracle's throughput on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--cpu-tokens 8192 | --no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -36,7 +38,6 @@ import synth  # noqa: E402
 
 METRIC = "Dust estimator draws·tokens/sec on 1 GPU + % of HBM/MFMA roofline"
 UNIT = "draws·tokens/s"
-CFG_ID = 2
 
 # MI355X published peaks
 HBM_PEAK_GBS = 8000.0
@@ -54,6 +55,7 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 OPS_PER_NORMAL = 8.5 + 5.5
 OPS_INJECT_EXTRA = 1.5    # fma with y, and half of a packed fp32 -> bf16 conversion
 OPS_EE_EXTRA = 1.0        # fma of reward x normal into the accumulator
+OPS_HEAD_EXTRA = 3.0      # scale, exp2, fma into the perturbed partition sum
 
 
 def parse():
@@ -61,35 +63,278 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-tokens", type=int, default=8192,
-                    help="tokens (whole sequences) of the CPU oracle's sample")
+    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--cpu-scale", type=float, default=1.0,
+                    help="scale of the CPU oracle's sample (1.0 = about 10-30 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
     return ap.parse_args()
 
 
-def cpu_baseline(c, ybits, xbits, lc, lp, tokens: int) -> dict:
-    """The oracle's chain (as it stands) on the first `tokens` tokens with all K draws."""
-    import oracle
-    T_s = min(tokens, c["T"])
-    T_s -= T_s % c["seg_len"]
-    K, KB, d_out, sigma = c["K"], c["inject_block"], c["d_out"], c["sigma"]
-    seed, tag = synth.noise_seed(CFG_ID), synth.NOISE_TAG
-    y = synth.bf16_bits_to_f32(ybits[:T_s]).astype(np.float64)
-    x = synth.bf16_bits_to_f32(xbits[:T_s]).astype(np.float64)
-    oracle.threads()   # load before timing
-    t0 = time.perf_counter()
-    for b in range(K // KB):
-        oracle.noise_inject(y, sigma, KB, seed, tag, draw0=b * KB)
-    r = oracle.reward_scan(oracle.loss_delta_loss(lc[:T_s], lp[:, :T_s]), c["seg_len"], c["gamma"])
-    g = oracle.error_estimate(r, d_out, sigma, seed, tag)
-    oracle.weight_grad(g, x)
-    dt = time.perf_counter() - t0
-    return {"value": K * T_s / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
-            "sample": "all %d draws x first %d of %d tokens (%d whole sequences), whole chain "
-                      "incl. the full G_W contraction over those tokens; %.1f s"
-                      % (K, T_s, c["T"], T_s // c["seg_len"], dt)}
+def _alu(normals, extra):
+    return ("alu", normals * (OPS_PER_NORMAL + extra), 1e12, VALU_PEAK_TOPS, "Tops/s")
+
+
+def _hbm(nbytes):
+    return ("hbm", float(nbytes), 1e9, HBM_PEAK_GBS, "GB/s")
+
+
+def _mfma(flops):
+    return ("mfma", float(flops), 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s")
+
+
+class Chain:
+    """Device buffers, one step of the estimator, the work model per kernel, and the oracle
+    sample of one workload."""
+
+    def __init__(self, cfg_id, dust, torch, dev):
+        self.cfg_id, self.dust, self.torch, self.dev = cfg_id, dust, torch, dev
+        self.c = synth.CONFIGS[cfg_id]
+        self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
+
+    def bf(self, bits):
+        return self.torch.from_numpy(bits.view(np.int16)).to(self.dev).view(self.torch.bfloat16)
+
+    def f32(self, a):
+        return self.torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(self.dev)
+
+    def empty(self, shape, dtype):
+        return self.torch.empty(shape, dtype=dtype, device=self.dev)
+
+
+class LinearChain(Chain):
+    """Workloads 2 and 5: perturb a linear layer's output, score by the loss change."""
+
+    def setup(self):
+        c, t = self.c, self.torch
+        self.T, self.d_in, self.d_out, self.K = c["T"], c["d_in"], c["d_out"], c["K"]
+        self.KB, self.S, self.gamma, self.sigma = c["inject_block"], c["seg_len"], c["gamma"], c["sigma"]
+        g = synth.rng(self.cfg_id, 1)
+        self.ybits = synth.normal_bf16(g, (self.T, self.d_out))
+        self.xbits = synth.normal_bf16(g, (self.T, self.d_in))
+        self.lc_h, self.lp_h = synth.losses(synth.rng(self.cfg_id, 2), self.K, self.T)
+        self.y, self.x = self.bf(self.ybits), self.bf(self.xbits)
+        self.lc, self.lp = self.f32(self.lc_h), self.f32(self.lp_h)
+        self.ybuf = self.empty((self.KB, self.T, self.d_out), t.bfloat16)
+        self.cbuf = self.empty((self.K, self.T), t.float32)
+        self.rbuf = self.empty((self.K, self.T), t.float32)
+        self.gh = self.empty((self.T, self.d_out), t.float32)
+        self.ght = self.empty((self.d_out, self.T), t.bfloat16)
+        self.G = self.empty((self.d_out, self.d_in), t.float32)
+        self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d_out, self.d_in)
+        self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
+
+    def step(self, run, sh):
+        d, T, K, KB = self.dust, self.T, self.K, self.KB
+        for blk in range(K // KB):
+            run("dust_noise_inject", d.dust_noise_inject, self.y, self.ybuf, d.DUST_BF16, T, self.d_out,
+                self.d_out, 0, KB, self.sigma, self.seed, self.tag, blk * KB, 0, sh)
+        run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None, None,
+            d.DUST_F32, self.cbuf, K, T, 0, sh)
+        run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.rbuf, K, T, self.S, self.gamma, sh)
+        run("dust_error_estimate", d.dust_error_estimate, self.rbuf, self.gh, self.ght, K, K, T,
+            self.d_out, 0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
+        run("dust_weight_grad", d.dust_weight_grad, self.ght, self.x, self.G, T, self.d_out, self.d_in,
+            self.ws, self.ws_bytes, sh)
+
+    def draws_tokens(self):
+        return self.K * self.T
+
+    def model(self):
+        T, K, do = self.T, self.K, self.d_out
+        return {
+            "dust_noise_inject": _alu(self.KB * T * do, OPS_INJECT_EXTRA),
+            "dust_loss_delta": _hbm((8.0 + 4.0 / K) * K * T),
+            "dust_reward_scan": _hbm(8.0 * K * T),
+            "dust_error_estimate": _alu(K * T * do, OPS_EE_EXTRA),
+            "dust_weight_grad": _mfma(2.0 * T * do * self.d_in),
+        }
+
+    def config(self):
+        return {"workload": self.c["name"], "d_in": self.d_in, "d_out": self.d_out, "tokens": self.T,
+                "seq_len": self.S, "draws": self.K, "gamma": self.gamma, "sigma": self.sigma,
+                "inject_block": self.KB, "storage": "bf16 activations, fp32 rewards/g_hat/G_W"}
+
+    def cpu_baseline(self, scale):
+        """The oracle's chain (as it stands) on whole sequences with all K draws (workload 2) or
+        on a draw subset (workload 5)."""
+        import oracle
+        S = self.S
+        if self.cfg_id == 2:
+            K_s, T_s = self.K, min(self.T, max(S, int(16 * S * scale) // S * S))
+        else:
+            K_s, T_s = max(4, int(512 * scale) // 4 * 4), S
+        KB = min(self.KB, K_s)
+        y = synth.bf16_bits_to_f32(self.ybits[:T_s]).astype(np.float64)
+        x = synth.bf16_bits_to_f32(self.xbits[:T_s]).astype(np.float64)
+        oracle.threads()
+        t0 = time.perf_counter()
+        for b in range(K_s // KB):
+            oracle.noise_inject(y, self.sigma, KB, self.seed, self.tag, draw0=b * KB)
+        r = oracle.reward_scan(oracle.loss_delta_loss(self.lc_h[:T_s], self.lp_h[:K_s, :T_s]), S, self.gamma)
+        g = oracle.error_estimate(r, self.d_out, self.sigma, self.seed, self.tag, K_total=self.K)
+        oracle.weight_grad(g, x)
+        dt = time.perf_counter() - t0
+        return {"value": K_s * T_s / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
+                "sample": "%d of %d draws x first %d of %d tokens (%d whole sequences), whole chain "
+                          "incl. the full G_W contraction over those tokens; %.1f s"
+                          % (K_s, self.K, T_s, self.T, T_s // S, dt)}
+
+
+class HeadChain(Chain):
+    """Workload 3: LM head perturbed on cached logits, one vocabulary chunk."""
+
+    def setup(self):
+        c, t = self.c, self.torch
+        self.T, self.V, self.v0, self.C, self.K = c["T"], c["V"], c["v0"], c["C"], c["K"]
+        self.H, self.S, self.gamma, self.sigma = c["hidden"], c["seg_len"], c["gamma"], c["sigma"]
+        g = synth.rng(self.cfg_id, 1)
+        self.z_h = synth.normal_f32(g, (self.T, self.V), np.sqrt(2.0))
+        self.tgt_h = synth.targets(g, self.T, self.V)
+        self.hbits = synth.normal_bf16(g, (self.T, self.H))
+        self.z, self.h = self.f32(self.z_h), self.bf(self.hbits)
+        self.tgt = self.torch.from_numpy(self.tgt_h).to(self.dev)
+        self.lp = self.empty((self.K, self.T), t.float32)
+        self.lc = self.empty((self.T,), t.float32)
+        self.cbuf = self.empty((self.K, self.T), t.float32)
+        self.gh = self.empty((self.T, self.C), t.float32)
+        self.ght = self.empty((self.C, self.T), t.bfloat16)
+        self.G = self.empty((self.C, self.H), t.float32)
+        self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.C, self.H)
+        self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
+
+    def step(self, run, sh):
+        d, T, K = self.dust, self.T, self.K
+        run("dust_head_ce_chunk", d.dust_head_ce_chunk, self.z, self.tgt, self.lp, self.lc, T, self.V,
+            self.v0, self.C, K, self.sigma, self.seed, self.tag, 0, 0, sh)
+        run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None, None,
+            d.DUST_F32, self.cbuf, K, T, 0, sh)
+        run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S, self.gamma, sh)
+        run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K, T, self.C,
+            self.v0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
+        run("dust_weight_grad", d.dust_weight_grad, self.ght, self.h, self.G, T, self.C, self.H,
+            self.ws, self.ws_bytes, sh)
+
+    def draws_tokens(self):
+        return self.K * self.T
+
+    def model(self):
+        T, K, C = self.T, self.K, self.C
+        return {
+            "dust_head_ce_chunk": _alu(K * T * C, OPS_HEAD_EXTRA),
+            "dust_loss_delta": _hbm((8.0 + 4.0 / K) * K * T),
+            "dust_reward_scan": _hbm(8.0 * K * T),
+            "dust_error_estimate": _alu(K * T * C, OPS_EE_EXTRA),
+            "dust_weight_grad": _mfma(2.0 * T * C * self.H),
+        }
+
+    def config(self):
+        return {"workload": self.c["name"], "vocab": self.V, "chunk": [self.v0, self.v0 + self.C],
+                "hidden": self.H, "tokens": self.T, "draws": self.K, "gamma": self.gamma,
+                "sigma": self.sigma, "storage": "fp32 logits, bf16 hidden"}
+
+    def cpu_baseline(self, scale):
+        import oracle
+        K_s, T_s = self.K, max(2, int(2048 * scale))
+        oracle.threads()
+        t0 = time.perf_counter()
+        lp, lc = oracle.head_ce_chunk(self.z_h[:T_s], self.tgt_h[:T_s], self.v0, self.C, K_s,
+                                      self.sigma, self.seed, self.tag)
+        r = oracle.reward_scan(oracle.loss_delta_loss(lc, lp), T_s, self.gamma)
+        g = oracle.error_estimate(r, self.C, self.sigma, self.seed, self.tag, chan0=self.v0)
+        oracle.weight_grad(g, synth.bf16_bits_to_f32(self.hbits[:T_s]).astype(np.float64))
+        dt = time.perf_counter() - t0
+        return {"value": K_s * T_s / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
+                "sample": "all %d draws x first %d of %d tokens, whole chain; %.1f s"
+                          % (K_s, T_s, self.T, dt)}
+
+
+class InnerChain(Chain):
+    """Workload 4: attention k/v projection scored by inner products, gamma = 0.99."""
+
+    def setup(self):
+        c, t = self.c, self.torch
+        self.T, self.d, self.K, self.KB = c["T"], c["d"], c["K"], c["draw_block"]
+        self.S, self.gamma, self.sigma, self.std = c["seg_len"], c["gamma"], c["sigma"], c["delta_o_std"]
+        g = synth.rng(self.cfg_id, 1)
+        self.gobits = synth.normal_bf16(g, (self.T, self.d))
+        self.xbits = synth.normal_bf16(g, (self.T, self.d))
+        self.go, self.x = self.bf(self.gobits), self.bf(self.xbits)
+        # One 512-draw block of the synthetic attention-output change, drawn on the device before
+        # timing; every block of the timed step streams this buffer (the kernel's work does not
+        # depend on the values).
+        zero = self.torch.zeros((self.T, self.d), dtype=t.bfloat16, device=self.dev)
+        self.do = self.empty((self.KB, self.T, self.d), t.bfloat16)
+        self.dust.dust_noise_inject(zero, self.do, self.dust.DUST_BF16, self.T, self.d, self.d, 0,
+                                    self.KB, self.std, self.seed, synth.DELTA_O_TAG, 0, 0)
+        del zero
+        self.cbuf = self.empty((self.K, self.T), t.float32)
+        self.gh = self.empty((self.T, self.d), t.float32)
+        self.ght = self.empty((self.d, self.T), t.bfloat16)
+        self.G = self.empty((self.d, self.d), t.float32)
+        self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d, self.d)
+        self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
+
+    def step(self, run, sh):
+        d, T, K, KB = self.dust, self.T, self.K, self.KB
+        for blk in range(K // KB):
+            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do, self.go,
+                d.DUST_BF16, self.cbuf[blk * KB:(blk + 1) * KB], KB, T, self.d, sh)
+        run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S, self.gamma, sh)
+        run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K, T, self.d,
+            0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
+        run("dust_weight_grad", d.dust_weight_grad, self.ght, self.x, self.G, T, self.d, self.d,
+            self.ws, self.ws_bytes, sh)
+
+    def draws_tokens(self):
+        return self.K * self.T
+
+    def model(self):
+        T, K, d = self.T, self.K, self.d
+        return {
+            "dust_loss_delta": _hbm(self.KB * T * (2.0 * d + 4.0) + 2.0 * T * d),
+            "dust_reward_scan": _hbm(8.0 * K * T),
+            "dust_error_estimate": _alu(K * T * d, OPS_EE_EXTRA),
+            "dust_weight_grad": _mfma(2.0 * T * d * d),
+        }
+
+    def config(self):
+        return {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
+                "draws": self.K, "draw_block": self.KB, "gamma": self.gamma, "sigma": self.sigma,
+                "storage": "bf16 delta_o / g_o / x, fp32 scores, rewards, g_hat, G_W"}
+
+    def cpu_baseline(self, scale):
+        import oracle
+        S, d = self.S, self.d
+        K_s, T_s = max(8, int(8192 * scale) // 8 * 8), S
+        oracle.threads()
+        go = synth.bf16_bits_to_f32(self.gobits[:T_s]).astype(np.float64)
+        c = np.empty((K_s, T_s))
+        t_gen = t_inner = 0.0
+        for k0 in range(0, K_s, 1024):   # blocks of draws bound the host memory
+            kb = min(1024, K_s - k0)
+            t1 = time.perf_counter()
+            do = self.std * oracle.normals(self.seed, synth.DELTA_O_TAG, k0, 0, 0, kb, T_s, d)
+            t2 = time.perf_counter()
+            c[k0:k0 + kb] = oracle.loss_delta_inner(do, go)
+            t3 = time.perf_counter()
+            t_gen += t2 - t1
+            t_inner += t3 - t2
+            del do
+        t0 = time.perf_counter()
+        r = oracle.reward_scan(c, S, self.gamma)
+        g = oracle.error_estimate(r, d, self.sigma, self.seed, self.tag, K_total=self.K)
+        oracle.weight_grad(g, synth.bf16_bits_to_f32(self.xbits[:T_s]).astype(np.float64))
+        dt = t_inner + time.perf_counter() - t0
+        return {"value": K_s * T_s / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
+                "sample": "%d of %d draws x first %d tokens (one sequence): inner-product scores, "
+                          "scan, error estimate, G_W; the attention-output change is drawn "
+                          "untimed (%.1f s), as on the device; %.1f s"
+                          % (K_s, self.K, T_s, t_gen, dt)}
+
+
+CHAINS = {2: LinearChain, 3: HeadChain, 4: InnerChain, 5: LinearChain}
 
 
 def main() -> int:
@@ -104,12 +349,7 @@ def main() -> int:
     import torch
     import activation_perturbation_es_amd as dust
 
-    c = synth.CONFIGS[CFG_ID]
-    T, d_in, d_out, K, KB = c["T"], c["d_in"], c["d_out"], c["K"], c["inject_block"]
-    S, gamma, sigma = c["seg_len"], c["gamma"], c["sigma"]
-    seed, tag = synth.noise_seed(CFG_ID), synth.NOISE_TAG
     dev = "cuda:0"
-
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)
@@ -117,119 +357,73 @@ def main() -> int:
         torch.cuda.synchronize()
         del a, b
 
-    # ---- inputs, resident in HBM before timing
-    g = synth.rng(CFG_ID, 1)
-    ybits = synth.normal_bf16(g, (T, d_out))
-    xbits = synth.normal_bf16(g, (T, d_in))
-    lc_h, lp_h = synth.losses(synth.rng(CFG_ID, 2), K, T)
-
-    def bf(bits):
-        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    y, x = bf(ybits), bf(xbits)
-    lc, lp = torch.from_numpy(lc_h).to(dev), torch.from_numpy(lp_h).to(dev)
-    ybuf = torch.empty((KB, T, d_out), dtype=torch.bfloat16, device=dev)
-    cbuf = torch.empty((K, T), dtype=torch.float32, device=dev)
-    rbuf = torch.empty((K, T), dtype=torch.float32, device=dev)
-    gh = torch.empty((T, d_out), dtype=torch.float32, device=dev)
-    ght = torch.empty((d_out, T), dtype=torch.bfloat16, device=dev)
-    G = torch.empty((d_out, d_in), dtype=torch.float32, device=dev)
-    ws_bytes = dust.dust_weight_grad_workspace(T, d_out, d_in)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    chain = CHAINS[args.workload](args.workload, dust, torch, dev)
+    chain.setup()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
-
     events = []   # (kernel, start event, end event) inside the timed region
 
-    def timed(name, fn, *a, record):
-        if record:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn(*a)
-            e1.record(stream)
-            events.append((name, e0, e1))
-        else:
-            fn(*a)
+    def plain(name, fn, *a):
+        fn(*a)
 
-    def step(record=False):
-        for blk in range(K // KB):
-            timed("dust_noise_inject", dust.dust_noise_inject, y, ybuf, dust.DUST_BF16, T, d_out,
-                  d_out, 0, KB, sigma, seed, tag, blk * KB, 0, sh, record=record)
-        timed("dust_loss_delta", dust.dust_loss_delta, dust.DUST_DELTA_LOSS, lc, lp, None, None,
-              dust.DUST_F32, cbuf, K, T, 0, sh, record=record)
-        timed("dust_reward_scan", dust.dust_reward_scan, cbuf, rbuf, K, T, S, gamma, sh, record=record)
-        timed("dust_error_estimate", dust.dust_error_estimate, rbuf, gh, ght, K, K, T, d_out, 0,
-              sigma, seed, tag, 0, 0, 0, sh, record=record)
-        timed("dust_weight_grad", dust.dust_weight_grad, ght, x, G, T, d_out, d_in, ws, ws_bytes, sh,
-              record=record)
+    def recorded(name, fn, *a):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        events.append((name, e0, e1))
 
     for _ in range(args.warmup):
-        step()
+        chain.step(plain, sh)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(record=True)
+        chain.step(recorded, sh)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
-    value = K * T / (elapsed / args.steps)
+    value = chain.draws_tokens() / (elapsed / args.steps)
 
     # ---- per-kernel durations (HIP events on the launch stream)
     per = {}
     for name, e0, e1 in events:
         per.setdefault(name, []).append(e0.elapsed_time(e1))
-    steps = args.steps
-    normals_inject = KB * T * d_out
-    normals_ee = K * T * d_out
-    model = {
-        # name: (bound, algorithmic work per launch, unit scale, peak, unit)
-        "dust_noise_inject": ("alu", normals_inject * (OPS_PER_NORMAL + OPS_INJECT_EXTRA), 1e12,
-                              VALU_PEAK_TOPS, "Tops/s"),
-        "dust_error_estimate": ("alu", normals_ee * (OPS_PER_NORMAL + OPS_EE_EXTRA), 1e12,
-                                VALU_PEAK_TOPS, "Tops/s"),
-        "dust_loss_delta": ("hbm", (8.0 + 4.0 / K) * K * T, 1e9, HBM_PEAK_GBS, "GB/s"),
-        "dust_reward_scan": ("hbm", 8.0 * K * T, 1e9, HBM_PEAK_GBS, "GB/s"),
-        "dust_weight_grad": ("mfma", 2.0 * T * d_out * d_in, 1e12, BF16_MFMA_PEAK_TFLOPS, "TFLOP/s"),
-    }
+    model = chain.model()
     kernels = {}
     for name, ms in per.items():
         bound, work, scale, peak, unit = model[name]
         avg_ms = float(np.mean(ms))
         ach = work / (avg_ms * 1e-3) / scale
-        kernels[name] = {"launches_per_step": len(ms) // steps, "avg_ms": round(avg_ms, 5),
-                         "ms_per_step": round(sum(ms) / steps, 5), "bound": bound,
+        kernels[name] = {"launches_per_step": len(ms) // args.steps, "avg_ms": round(avg_ms, 5),
+                         "ms_per_step": round(sum(ms) / args.steps, 5), "bound": bound,
                          "achieved": round(ach, 3), "peak": peak, "unit": unit,
                          "frac": round(ach / peak, 4)}
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": dk["achieved"],
-                "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
-                "traffic": None}
+                "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"], "traffic": None}
     # HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE,
-    # scaled by the copy-kernel calibration (see profiles/); null when not measured for the
-    # current kernel build.
+    # scaled by the copy-kernel calibration (profiles/); null unless they were taken for this
+    # workload, this kernel and the current kernel sources.
     traffic_file = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(traffic_file):
         with open(traffic_file) as f:
             tr = json.load(f)
-        if tr.get("kernel") == dominant and tr.get("build") == _kernel_build_id():
+        if (tr.get("kernel") == dominant and tr.get("workload") == chain.c["name"]
+                and tr.get("build") == _kernel_build_id()):
             roofline["traffic"] = tr.get("bytes_per_launch")
 
+    cfg = chain.config()
+    cfg["parallelism"] = "single GPU"
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
-        "data": "synthetic",
-        "config": {"workload": c["name"], "d_in": d_in, "d_out": d_out, "tokens": T,
-                   "seq_len": S, "draws": K, "gamma": gamma, "sigma": sigma,
-                   "inject_block": KB, "storage": "bf16 activations, fp32 rewards/g_hat/G_W",
-                   "parallelism": "single GPU"},
-        "roofline": roofline,
-        "kernels": kernels,
+        "data": "synthetic", "config": cfg, "roofline": roofline, "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(c, ybits, xbits, lc_h, lp_h, args.cpu_tokens)
+        line["cpu_baseline"] = chain.cpu_baseline(args.cpu_scale)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -1,0 +1,165 @@
+"""The C ABI without a GPU: the library loads, exports every entry point include/dust.h declares,
+and validates arguments on the host (no call below reaches a HIP API: each is rejected, or is
+a zero-size call that returns before any launch)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dust.h")
+
+import activation_perturbation_es_amd as dust  # noqa: E402
+
+FAKE = 0x100000        # a 16-byte-aligned address that is never dereferenced
+FAKE2 = 0x900000000    # far from FAKE, so ranges do not overlap
+
+
+@pytest.fixture(scope="module", autouse=True)
+def built_library():
+    if not os.path.exists(dust.LIB_PATH):
+        from activation_perturbation_es_amd import build
+        build.build(force=True)
+    return dust.library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char \*)\s*(dust_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_six_estimator_calls():
+    names = _declared()
+    for n in ("dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_error_estimate",
+              "dust_weight_grad", "dust_head_ce_chunk", "dust_weight_grad_workspace",
+              "dust_status_string", "dust_last_error", "dust_noise_words"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(dust.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", dust.LIB_PATH], capture_output=True,
+                        text=True, check=True).stdout
+    exported = set(re.findall(r" T (dust_\w+)$", nm, re.M))
+    assert set(_declared()) <= exported
+    # the binding mirrors exactly the declared set
+    assert sorted(dust.EXPORTED_SYMBOLS) == _declared()
+
+
+def test_status_strings():
+    assert dust.dust_status_string(0) == "DUST_OK"
+    assert dust.dust_status_string(1) == "DUST_ERR_INVALID"
+    assert dust.dust_status_string(2) == "DUST_ERR_UNSUPPORTED"
+    assert dust.dust_status_string(3) == "DUST_ERR_WORKSPACE"
+    assert dust.dust_status_string(4) == "DUST_ERR_HIP"
+    assert dust.dust_status_string(99) == "DUST_ERR_UNKNOWN"
+
+
+def _rc(name, *args):
+    return getattr(dust.library(), name)(*args)
+
+
+# (entry point, arguments, expected status, fragment of the message)
+INVALID = [
+    ("dust_noise_inject", (FAKE, FAKE2, 7, 4, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "dtype"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, -1, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "negative"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, 4, 8, 7, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "ld_y"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, 4, 8, 8, 2, 2, 0.1, 1, 1, 0, 0, None), 1, "chan0"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, 4, 8, 8, 0, 2, float("nan"), 1, 1, 0, 0, None), 1, "sigma"),
+    ("dust_noise_inject", (None, FAKE2, 0, 4, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "null"),
+    ("dust_noise_inject", (FAKE + 1, FAKE2, 1, 4, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "aligned"),
+    ("dust_noise_inject", (FAKE, FAKE, 0, 4, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None), 1, "overlap"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, 4, 8, 8, 0, 2, 0.1, 1, 1, 0xFFFFFFFF, 0, None), 1, "draw0"),
+    ("dust_noise_inject", (FAKE, FAKE2, 0, 4, 8, 8, 0, 2, 0.1, 1, 1, 0, 0xFFFFFFFE, None), 1, "tok0"),
+    ("dust_loss_delta", (5, FAKE, FAKE2, None, None, 0, FAKE2 + 4096, 2, 8, 0, None), 1, "mode"),
+    ("dust_loss_delta", (0, None, FAKE2, None, None, 0, FAKE2 + 4096, 2, 8, 0, None), 1, "null"),
+    ("dust_loss_delta", (0, FAKE, FAKE2, None, None, 0, FAKE, 2, 8, 0, None), 1, "overlap"),
+    ("dust_loss_delta", (1, None, None, FAKE, FAKE2, 3, FAKE2 + 4096, 2, 8, 4, None), 1, "io_dtype"),
+    ("dust_loss_delta", (1, None, None, FAKE, FAKE2, 1, FAKE2 + 4096, 2, 8, 0, None), 1, "d >= 1"),
+    ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 3, 0.5, None), 1, "multiple"),
+    ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 0, 0.5, None), 1, "seg_len"),
+    ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 5, 1.5, None), 1, "gamma"),
+    ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 5, -0.1, None), 1, "gamma"),
+    ("dust_reward_scan", (FAKE, FAKE + 4, 2, 10, 5, 0.5, None), 1, "overlap"),
+    ("dust_error_estimate", (FAKE, FAKE2, None, 4, 3, 8, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "K_total"),
+    ("dust_error_estimate", (FAKE, FAKE2, None, 4, 4, 8, 8, 0, 0.0, 1, 1, 0, 0, 0, None), 1, "sigma"),
+    ("dust_error_estimate", (FAKE, FAKE2, None, 4, 4, 8, 8, 6, 0.1, 1, 1, 0, 0, 0, None), 1, "chan0"),
+    ("dust_error_estimate", (None, FAKE2, None, 4, 4, 8, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "null"),
+    ("dust_error_estimate", (FAKE, FAKE, None, 4, 4, 8, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "overlap"),
+    ("dust_weight_grad", (FAKE, FAKE2, FAKE2 + (1 << 30), 4096, 256, 256, None, 0, None), 3, "workspace"),
+    ("dust_weight_grad", (FAKE, FAKE2, FAKE2 + (1 << 30), 4096, 256, 256, FAKE2 + (2 << 30), 16, None), 3, "workspace"),
+    ("dust_weight_grad", (None, FAKE2, FAKE2 + (1 << 30), 64, 8, 8, None, 0, None), 1, "null"),
+    ("dust_weight_grad", (FAKE, FAKE2, FAKE, 64, 8, 8, None, 0, None), 1, "overlap"),
+    ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 96, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "chunk"),
+    ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 2, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "chan0"),
+    ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 9000, 0, 5000, 2, 0.1, 1, 1, 0, 0, None), 2, "4096"),
+    ("dust_head_ce_chunk", (None, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "null"),
+    ("dust_noise_words", (FAKE + 8, 1, 1, 1, 0, 1, 1, 0, 0, None), 1, "16-byte"),
+    ("dust_noise_words", (FAKE, 1, 1, 2, 0xFFFFFFFF, 1, 1, 0, 0, None), 1, "2^32"),
+]
+
+
+@pytest.mark.parametrize("name,args,status,fragment", INVALID,
+                         ids=["%s-%d" % (c[0], i) for i, c in enumerate(INVALID)])
+def test_invalid_arguments_are_rejected_on_the_host(name, args, status, fragment):
+    rc = _rc(name, *args)
+    assert rc == status, (rc, dust.dust_last_error())
+    assert fragment in dust.dust_last_error()
+
+
+ZERO_SIZE = [
+    ("dust_noise_inject", (None, None, 0, 0, 8, 8, 0, 2, 0.1, 1, 1, 0, 0, None)),
+    ("dust_noise_inject", (None, None, 1, 4, 8, 8, 0, 0, 0.1, 1, 1, 0, 0, None)),
+    ("dust_loss_delta", (0, None, None, None, None, 0, None, 0, 8, 0, None)),
+    ("dust_loss_delta", (1, None, None, None, None, 1, None, 3, 0, 16, None)),
+    ("dust_reward_scan", (None, None, 0, 10, 5, 0.5, None)),
+    ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
+    ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),
+    ("dust_head_ce_chunk", (None, None, None, None, 0, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None)),
+    ("dust_noise_words", (None, 0, 4, 4, 0, 1, 1, 0, 0, None)),
+]
+
+
+@pytest.mark.parametrize("name,args", ZERO_SIZE, ids=["%s-%d" % (c[0], i) for i, c in enumerate(ZERO_SIZE)])
+def test_zero_sizes_return_ok_without_launching(name, args):
+    assert _rc(name, *args) == dust.DUST_OK
+    assert dust.dust_last_error() == ""
+
+
+def test_binding_raises_dust_error_with_message():
+    with pytest.raises(dust.DustError) as e:
+        dust.dust_reward_scan(FAKE, FAKE2, 2, 10, 3, 0.5, stream=0)
+    assert e.value.status == dust.DUST_ERR_INVALID
+    assert "multiple" in str(e.value)
+
+
+def test_weight_grad_workspace_sizes():
+    # tiled path with a split over tokens: splits x d_out x d_in x 4 bytes
+    assert dust.dust_weight_grad_workspace(16384, 2048, 512) == 8 * 2048 * 512 * 4
+    assert dust.dust_weight_grad_workspace(16384, 4096, 1024) == 2 * 4096 * 1024 * 4
+    # one split, or the plain path, or an empty problem: no workspace
+    assert dust.dust_weight_grad_workspace(512, 128, 128) == 0
+    assert dust.dust_weight_grad_workspace(1001, 33, 17) == 0
+    assert dust.dust_weight_grad_workspace(0, 64, 64) == 0
+    assert dust.dust_weight_grad_workspace(-1, 64, 64) == 0
+
+
+def test_product_path_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "activation_perturbation_es_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f), errors="ignore").read()
+                assert "import oracle" not in text and "dust_oracle" not in text, f
+                assert "libdust_oracle" not in text, f
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

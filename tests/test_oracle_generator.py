@@ -149,3 +149,18 @@ def test_global_indices_make_noise_split_invariant():
     full = oracle.normals(77, 5, 0, 0, 0, 6, 20, 40)
     part = oracle.normals(77, 5, 2, 3, 8, 3, 10, 20)   # draws 2..4, tokens 3..12, channels 8..27
     assert np.array_equal(part, full[2:5, 3:13, 8:28])
+
+
+def test_golden_fixture_unchanged():
+    """Regression pin: the oracle still produces the words and normals stored by
+    tests/golden/make_golden.py."""
+    path = os.path.join(HERE, "golden", "oracle_noise.txt")
+    for line in open(path):
+        if line.startswith("#"):
+            continue
+        head, words, norms = line.split("|")
+        seed, tag, draw, token, q = (int(v) for v in head.split())
+        assert [int(v) for v in words.split()] == list(oracle.noise_words(seed, tag, draw, token, q))
+        ref = [float(v) for v in norms.split()]
+        got = [oracle.normal(seed, tag, draw, token, 4 * q + e) for e in range(4)]
+        assert np.allclose(got, ref, rtol=1e-15, atol=1e-15)
