@@ -133,6 +133,107 @@ __global__ __launch_bounds__(256) void loss_delta_inner_kernel(const void *__res
     }
 }
 
+// Tile version for rows of at most 64 pieces (bf16 d <= 512, fp32 d <= 256, 16-byte aligned):
+// one wave per 4 consecutive tokens and one slice of the draws. Per draw the wave reads the 4
+// rows dO[i][s0 .. s0+3] -- one contiguous span of 4 rows -- DRAWS draws at a time (4 x DRAWS
+// loads in flight per lane). The 4 x 2 row partials of a lane are summed across the wave with a
+// transposed butterfly: after the 32- and 16-lane exchanges each lane carries one row's partial
+// (row = 2 * bit5 + bit4 of the lane), and four in-row DPP steps finish the sums, so 4 rows
+// cost 3 LDS-crossbar shuffles and 4 DPP adds instead of 24 shuffles.
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
+
+// Sum over the 16 lanes of each DPP row; every lane of the row receives the row's sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // xor 1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // xor 2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // half-row mirror
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
+    return x;
+}
+
+template <bool BF16, int DRAWS>
+__global__ __launch_bounds__(256) void loss_delta_inner_tile_kernel(const void *__restrict__ dO_,
+                                                                    const void *__restrict__ gO_,
+                                                                    float *__restrict__ c,
+                                                                    uint32_t Kc, uint32_t T,
+                                                                    uint32_t d, uint32_t nsplit) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    const uint32_t w = blockIdx.x * 4u + wave_in_block();
+    const uint32_t tile = w / nsplit, part = w % nsplit;
+    const uint32_t s0 = tile * 4u;
+    if (s0 >= T) return;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t e0 = lane * EPV;
+    const bool lane_in = e0 < d;
+    const uint32_t i_beg = (uint32_t)(((uint64_t)Kc * part) / nsplit);
+    const uint32_t i_end = (uint32_t)(((uint64_t)Kc * (part + 1)) / nsplit);
+
+    float gv[4][EPV];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint32_t s = s0 + r;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) gv[r][e] = 0.f;
+        if (lane_in && s < T) {
+            if constexpr (BF16) {
+                const u32x4 v = *(const u32x4 *)((const uint16_t *)gO_ + (uint64_t)s * d + e0);
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    gv[r][2 * h] = __uint_as_float(v[h] << 16);
+                    gv[r][2 * h + 1] = __uint_as_float(v[h] & 0xFFFF0000u);
+                }
+            } else {
+                const f32x4 v = *(const f32x4 *)((const float *)gO_ + (uint64_t)s * d + e0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) gv[r][e] = v[e];
+            }
+        }
+    }
+    const uint64_t draw_stride = (uint64_t)T * d;
+    const bool b5 = (lane & 32u) != 0, b4 = (lane & 16u) != 0;
+    const uint32_t myrow = (b5 ? 2u : 0u) + (b4 ? 1u : 0u);
+    const bool writer = (lane & 15u) == 0 && s0 + myrow < T;
+
+    for (uint32_t i = i_beg; i < i_end; i += DRAWS) {
+        float p[DRAWS][4];
+#pragma unroll
+        for (int u = 0; u < DRAWS; ++u) {
+            const bool draw_ok = i + u < i_end;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[u][r] = 0.f;
+                const uint32_t s = s0 + r;
+                if (!(draw_ok && lane_in && s < T)) continue;
+                const uint64_t off = (uint64_t)(i + u) * draw_stride + (uint64_t)s * d + e0;
+                if constexpr (BF16) {
+                    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)dO_ + off));
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        p[u][r] = __builtin_fmaf(__uint_as_float(v[h] << 16), gv[r][2 * h], p[u][r]);
+                        p[u][r] = __builtin_fmaf(__uint_as_float(v[h] & 0xFFFF0000u), gv[r][2 * h + 1], p[u][r]);
+                    }
+                } else {
+                    const f32x4 v = __builtin_nontemporal_load((const f32x4 *)((const float *)dO_ + off));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) p[u][r] = __builtin_fmaf(v[e], gv[r][e], p[u][r]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < DRAWS; ++u) {
+            // 32-lane exchange: keep rows {0,1} (bit5 = 0) or {2,3} (bit5 = 1), send the others
+            const float k0 = sel(b5, p[u][2], p[u][0]), s0v = sel(b5, p[u][0], p[u][2]);
+            const float k1 = sel(b5, p[u][3], p[u][1]), s1v = sel(b5, p[u][1], p[u][3]);
+            const float q0 = k0 + __shfl_xor(s0v, 32);
+            const float q1 = k1 + __shfl_xor(s1v, 32);
+            // 16-lane exchange: keep row (bit4) of the pair, send the other
+            const float kk = sel(b4, q1, q0), ss = sel(b4, q0, q1);
+            const float t = row16_sum(kk + __shfl_xor(ss, 16));
+            if (writer && i + u < i_end) c[(uint64_t)(i + u) * T + s0 + myrow] = -t;
+        }
+    }
+}
+
 // Same as above for rows too long to keep g_o in registers: g_o is re-read per draw (L1/L2).
 template <bool BF16>
 __global__ __launch_bounds__(256) void loss_delta_inner_long_kernel(const void *__restrict__ dO_,
@@ -262,9 +363,26 @@ hipError_t launch_loss_delta_loss(const float *lc, const float *lp, float *c, in
 
 hipError_t launch_loss_delta_inner(const void *delta_o, const void *g_o, bool bf16, float *c,
                                    int64_t Kc, int64_t T, int64_t d, hipStream_t s) {
-    const uint32_t blocks = (uint32_t)((T + 3) / 4);
     const int epv = bf16 ? 8 : 4;
     const bool vec = (d % epv == 0) && aligned16(delta_o) && aligned16(g_o);
+    if (vec && d <= 64 * epv) {
+        // tiles of 4 tokens; split the draws until there are >= 32768 waves (four rounds of
+        // 8 waves per SIMD: shorter work units keep the concurrently read rows closer together)
+        const int64_t tiles = (T + 3) / 4;
+        int64_t nsplit = 1;
+        while (tiles * nsplit < 32768 && nsplit * 16 <= Kc) nsplit *= 2;
+        const uint32_t blocks = (uint32_t)((tiles * nsplit + 3) / 4);
+        if (bf16)
+            loss_delta_inner_tile_kernel<true, 2><<<blocks, 256, 0, s>>>(delta_o, g_o, c, (uint32_t)Kc,
+                                                                      (uint32_t)T, (uint32_t)d,
+                                                                      (uint32_t)nsplit);
+        else
+            loss_delta_inner_tile_kernel<false, 2><<<blocks, 256, 0, s>>>(delta_o, g_o, c, (uint32_t)Kc,
+                                                                       (uint32_t)T, (uint32_t)d,
+                                                                       (uint32_t)nsplit);
+        return hipGetLastError();
+    }
+    const uint32_t blocks = (uint32_t)((T + 3) / 4);
     const int64_t piece = vec ? 64 * epv : 64;
     const int64_t nchunk = (d + piece - 1) / piece;
 #define DUST_INNER(B, V, M)                                                                    \

@@ -49,18 +49,13 @@ static RowMap make_rowmap(int64_t ngroups, int64_t T, uint32_t &blocks) {
     return m;
 }
 
+// All draws of one (token, 4-channel group): y is read once, then each draw's four normals come
+// from one Philox call and the four perturbed values are written.
 template <bool BF16, bool VEC>
-__global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_,
-                                                     void *__restrict__ yp_, uint32_t T,
-                                                     uint32_t d, uint64_t ld_y, uint32_t q0,
-                                                     uint32_t Kc, float sigma, Key key,
-                                                     uint32_t draw0, uint32_t tok0, RowMap m) {
-    uint32_t t, g;
-    if (!map_thread(m, T, t, g)) return;
-    const uint32_t j0 = 4u * g;
-    const uint32_t token = tok0 + t;
-    const uint32_t q = q0 + g;
-
+__device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__restrict__ yp_,
+                                           uint32_t t, uint32_t T, uint32_t d, uint64_t ld_y,
+                                           uint32_t j0, uint32_t q, uint32_t Kc, float sigma,
+                                           const Key &key, uint32_t draw0, uint32_t token) {
     float yv[4];
     if constexpr (BF16) {
         const uint16_t *y = (const uint16_t *)y_ + (uint64_t)t * ld_y + j0;
@@ -118,6 +113,24 @@ __global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_
     }
 }
 
+// One thread per (token slot, 4-channel group). With few draws per call a thread's life would
+// be short; a token slot then covers `nseq` adjacent tokens, handled one after the other.
+template <bool BF16, bool VEC>
+__global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_,
+                                                     void *__restrict__ yp_, uint32_t T,
+                                                     uint32_t d, uint64_t ld_y, uint32_t q0,
+                                                     uint32_t Kc, float sigma, Key key,
+                                                     uint32_t draw0, uint32_t tok0, RowMap m,
+                                                     uint32_t nseq) {
+    uint32_t ts, g;
+    if (!map_thread(m, (T + nseq - 1) / nseq, ts, g)) return;
+    const uint32_t t_end = min(T, (ts + 1) * nseq);
+#pragma unroll 1
+    for (uint32_t t = ts * nseq; t < t_end; ++t)
+        inject_one<BF16, VEC>(y_, yp_, t, T, d, ld_y, 4u * g, q0 + g, Kc, sigma, key, draw0,
+                              tok0 + t);
+}
+
 __global__ __launch_bounds__(256) void words_kernel(uint4 *__restrict__ words, uint32_t T,
                                                     uint32_t Kc, uint32_t group0, Key key,
                                                     uint32_t draw0, uint32_t tok0, RowMap m) {
@@ -135,14 +148,17 @@ hipError_t launch_noise_inject(const void *y, void *y_pert, bool bf16, int64_t T
                                int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, Key key,
                                uint32_t draw0, uint32_t tok0, hipStream_t s) {
     const int64_t ngroups = (d + 3) / 4;
+    // walk 4 adjacent tokens per thread when a call carries at most 4 draws and there are
+    // still >= 64k threads
+    const int64_t nseq = (Kc <= 4 && ((T + 3) / 4) * ngroups >= 65536) ? 4 : 1;
     uint32_t blocks = 0;
-    const RowMap m = make_rowmap(ngroups, T, blocks);
+    const RowMap m = make_rowmap(ngroups, (T + nseq - 1) / nseq, blocks);
     const bool vec = (d % 4 == 0) && (ld_y % 4 == 0) && aligned16(y) && aligned16(y_pert);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
 #define DUST_INJECT(B, V)                                                                      \
     inject_kernel<B, V><<<blocks, 256, 0, s>>>(y, y_pert, (uint32_t)T, (uint32_t)d,            \
                                                (uint64_t)ld_y, q0, (uint32_t)Kc, sigma, key,   \
-                                               draw0, tok0, m)
+                                               draw0, tok0, m, (uint32_t)nseq)
     if (bf16) {
         if (vec) DUST_INJECT(true, true); else DUST_INJECT(true, false);
     } else {

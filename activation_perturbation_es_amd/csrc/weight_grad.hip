@@ -10,7 +10,7 @@
 // which wants 8 consecutive k per lane; each thread therefore loads a 4 (k) x 8 (n) block of x
 // and transposes it in registers before writing it to LDS as [n][k].
 // Tiling: 128 x 128 output tile per 256-thread block, 2 x 2 waves of 64 x 64, k-step 64 staged
-// through two LDS buffers, with the next step's global loads in flight during the MFMAs. The token axis is
+// through two LDS buffers, with global loads issued two k-steps ahead of the MFMAs. The token axis is
 // split across blocks so that small outputs still fill the 256 CUs; the split partial sums go to
 // a workspace and are added in split order by a second kernel, so results are deterministic.
 #include "dust_internal.hpp"
@@ -50,7 +50,7 @@ SplitPlan plan_split(int64_t T, int64_t M, int64_t N) {
 // the XCDs in contiguous eighths (xcd_logical_block): the n-tiles that share an A row-block run
 // side by side on one XCD, and with 8 splits each XCD owns exactly one split, whose slice of x
 // all of its blocks read.
-__global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restrict__ A,
+__global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const uint16_t *__restrict__ A,
                                                          const uint16_t *__restrict__ B,
                                                          float *__restrict__ out, uint32_t M,
                                                          uint32_t N, uint32_t K, SplitPlan p,
@@ -85,13 +85,14 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
     // B: 16 x 16 blocks of 4 k-rows x 8 n-columns; thread takes block (kb, nb).
     const uint32_t kb = tid & 15u, nb = tid >> 4;
     // native clang vectors: a select on HIP's struct vector types goes through scratch
-    u32x4 ra[4], rb[4];
+    typedef u32x4 piece4[4];
+    u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
     const u32x4 zero4 = {0u, 0u, 0u, 0u};
 
     // Out-of-range pieces read a clamped in-range address and are zeroed by a value select (a
     // select between a global pointer and a private zero would put the zero in scratch).
     // K, kend and N are multiples of 8, so a piece is either wholly inside or wholly outside.
-    auto gload = [&](uint32_t k0) {
+    auto gload = [&](uint32_t k0, piece4 &ra, piece4 &rb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t piece = tid + 256u * j;
@@ -109,7 +110,7 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
             rb[r] = in ? v : zero4;
         }
     };
-    auto lstore = [&](int st) {
+    auto lstore = [&](int st, const piece4 &ra, const piece4 &rb) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const uint32_t piece = tid + 256u * j;
@@ -118,31 +119,18 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
         }
         // rb[r] holds x[k = 4kb + r][n = 8nb .. 8nb+7]; dword h packs columns 2h (low half)
         // and 2h+1 (high half). Column n gets its four k values as two dwords.
-        const uint32_t w0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-        const uint32_t w1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
-        const uint32_t w2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
-        const uint32_t w3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
             uint2 lo, hi;
-            lo.x = (w0[h] & 0xFFFFu) | (w1[h] << 16);
-            lo.y = (w2[h] & 0xFFFFu) | (w3[h] << 16);
-            hi.x = (w0[h] >> 16) | (w1[h] & 0xFFFF0000u);
-            hi.y = (w2[h] >> 16) | (w3[h] & 0xFFFF0000u);
+            lo.x = (rb[0][h] & 0xFFFFu) | (rb[1][h] << 16);
+            lo.y = (rb[2][h] & 0xFFFFu) | (rb[3][h] << 16);
+            hi.x = (rb[0][h] >> 16) | (rb[1][h] & 0xFFFF0000u);
+            hi.y = (rb[2][h] >> 16) | (rb[3][h] & 0xFFFF0000u);
             *(uint2 *)(Bs[st] + (8u * nb + 2u * h) * LDS_PITCH + 4u * kb) = lo;
             *(uint2 *)(Bs[st] + (8u * nb + 2u * h + 1u) * LDS_PITCH + 4u * kb) = hi;
         }
     };
-
-    if (kbeg < kend) {
-        gload(kbeg);
-        lstore(0);
-    }
-    __syncthreads();
-    int st = 0;
-    for (uint32_t k0 = kbeg; k0 < kend; k0 += BK) {
-        const bool more = k0 + BK < kend;
-        if (more) gload(k0 + BK);       // in flight during the MFMAs below
+    auto mfma_step = [&](int st) {
 #pragma unroll
         for (int kk = 0; kk < BK / 16; ++kk) {
             const uint32_t koff = kk * 16u + 8u * (lane >> 5);
@@ -159,9 +147,31 @@ __global__ __launch_bounds__(256) void wgrad_mfma_kernel(const uint16_t *__restr
                 for (int j = 0; j < 2; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
         }
-        if (more) lstore(st ^ 1);
+    };
+
+    // Global loads run two k-steps ahead of the MFMAs: step s is loaded into register set s % 2
+    // during step s - 2, written to LDS stage s % 2 at the end of step s - 1, and multiplied in
+    // step s. The loop body covers two steps so that the register sets stay static.
+    const uint32_t nsteps = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+    if (nsteps > 0) {
+        gload(kbeg, ra0, rb0);
+        if (nsteps > 1) gload(kbeg + BK, ra1, rb1);
+        lstore(0, ra0, rb0);
+    }
+    __syncthreads();
+    for (uint32_t s = 0; s < nsteps; s += 2) {
+        // step s: stage 0, registers of step s + 1 in set 1
+        if (s + 2 < nsteps) gload(kbeg + (s + 2) * BK, ra0, rb0);
+        mfma_step(0);
+        if (s + 1 < nsteps) lstore(1, ra1, rb1);
         __syncthreads();
-        st ^= 1;
+        // step s + 1: stage 1, registers of step s + 2 in set 0
+        if (s + 1 < nsteps) {
+            if (s + 3 < nsteps) gload(kbeg + (s + 3) * BK, ra1, rb1);
+            mfma_step(1);
+            if (s + 2 < nsteps) lstore(0, ra0, rb0);
+        }
+        __syncthreads();
     }
 
     // D layout of the 32x32 MFMA: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32.

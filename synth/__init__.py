@@ -18,8 +18,9 @@ CONFIGS = {
     1: dict(name="tiny_linear_64x64_head256", d_in=64, d_out=64, V=256, T=128, seg_len=128,
             K=16, sigma=0.01, gammas=(0.0, 0.9)),
     # MLP up-projection 512 -> 2048 of the 8-layer width-512 GPT, 16 x 1024 tokens, 64 draws.
+    # The whole population is perturbed in one call (a 4.3 GB perturbed-output buffer).
     2: dict(name="mlp_up_512x2048_T16384_K64", d_in=512, d_out=2048, V=4096, T=16384,
-            seg_len=1024, K=64, gamma=0.0, sigma=0.01, inject_block=8),
+            seg_len=1024, K=64, gamma=0.0, sigma=0.01, inject_block=64),
     # LM head on cached logits: vocabulary 4096, chunk [0, 1024), hidden 512, 1024 draws.
     3: dict(name="lm_head_chunk1024_V4096_T16384_K1024", hidden=512, V=4096, v0=0, C=1024,
             T=16384, seg_len=1024, K=1024, gamma=0.0, sigma=0.01),
@@ -27,9 +28,10 @@ CONFIGS = {
     # output error, gamma = 0.99 over 16 x 1024 tokens, 16384 draws in blocks of 512.
     4: dict(name="attn_kv_inner_512_T16384_K16384", d=512, T=16384, seg_len=1024, K=16384,
             draw_block=512, gamma=0.99, sigma=0.01, delta_o_std=0.01),
-    # ~240M-parameter GPT (width 1024): MLP up-projection 1024 -> 4096, 1024 draws.
+    # ~240M-parameter GPT (width 1024): MLP up-projection 1024 -> 4096, 1024 draws, perturbed
+    # in blocks of 32 draws (a 4.3 GB perturbed-output buffer).
     5: dict(name="mlp_up_1024x4096_T16384_K1024", d_in=1024, d_out=4096, V=4096, T=16384,
-            seg_len=1024, K=1024, gamma=0.0, sigma=0.01, inject_block=4),
+            seg_len=1024, K=1024, gamma=0.0, sigma=0.01, inject_block=32),
 }
 
 NOISE_TAG = 1          # Philox tag of the estimator's noise

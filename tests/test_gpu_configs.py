@@ -19,6 +19,12 @@ pytestmark = pytest.mark.gpu
 NS = 20000   # sampled elements per check
 
 
+def _gather_bits(t: torch.Tensor, *idx) -> np.ndarray:
+    """bf16 bit patterns of the sampled elements, gathered on the device."""
+    ii = tuple(torch.from_numpy(np.asarray(i, dtype=np.int64)).to(DEV) for i in idx)
+    return host_bf16_bits(t[ii].contiguous())
+
+
 def _check_inject_block(cfg, d_key):
     c = synth.CONFIGS[cfg]
     T, d, sigma, Kb = c["T"], c[d_key], c["sigma"], c["inject_block"]
@@ -27,13 +33,14 @@ def _check_inject_block(cfg, d_key):
     ybits = synth.normal_bf16(synth.rng(cfg, 1), (T, d))
     out = torch.empty((Kb, T, d), dtype=torch.bfloat16, device=DEV)
     dust.dust_noise_inject(bf16(ybits), out, dust.DUST_BF16, T, d, d, 0, Kb, sigma, seed, tag, draw0, 0)
-    got = host_bf16_bits(out)
     g = np.random.default_rng(100 + cfg)
     k, t, j = g.integers(0, Kb, NS), g.integers(0, T, NS), g.integers(0, d, NS)
     k[:2], t[:2], j[:2] = [0, Kb - 1], [0, T - 1], [0, d - 1]
+    got = _gather_bits(out, k, t, j)
+    del out
     n = oracle.normals_at(seed, tag, k, t, j, draw0=draw0)
     ref = oracle.round_bf16(bits_to_f64(ybits[t, j]) + sigma * n)
-    gv = bits_to_f64(got[k, t, j])
+    gv = bits_to_f64(got)
     assert np.all(np.abs(gv - ref) <= bf16_ulp(ref))
     assert np.mean(gv != ref) < 0.01
 
@@ -148,12 +155,12 @@ def test_w4_delta_o_block_generation():
     do = torch.empty((Kb, T, d), dtype=torch.bfloat16, device=DEV)
     draw0 = c["K"] - Kb
     dust.dust_noise_inject(zero, do, dust.DUST_BF16, T, d, d, 0, Kb, std, seed, synth.DELTA_O_TAG, draw0, 0)
-    got = host_bf16_bits(do)
-    del do
     g = np.random.default_rng(404)
     k, t, j = g.integers(0, Kb, NS), g.integers(0, T, NS), g.integers(0, d, NS)
+    got = _gather_bits(do, k, t, j)
+    del do
     ref = oracle.round_bf16(std * oracle.normals_at(seed, synth.DELTA_O_TAG, k, t, j, draw0=draw0))
-    gv = bits_to_f64(got[k, t, j])
+    gv = bits_to_f64(got)
     assert np.all(np.abs(gv - ref) <= bf16_ulp(ref))
 
 

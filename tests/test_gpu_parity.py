@@ -57,7 +57,12 @@ def test_normals_through_f32_inject(T, d, ld, chan0, Kc, draw0, tok0):
     assert np.abs(got - ref).max() <= 2.5e-6
 
 
-@pytest.mark.parametrize("T,d,ld,chan0,Kc", [(33, 72, 72, 8, 4), (17, 70, 80, 0, 3), (5, 1, 1, 0, 2)])
+@pytest.mark.parametrize("T,d,ld,chan0,Kc", [
+    (33, 72, 72, 8, 4), (17, 70, 80, 0, 3), (5, 1, 1, 0, 2),
+    # <= 4 draws with many threads: each thread walks 4 adjacent tokens (ragged last slot),
+    # with several tokens per block (d = 256) and several blocks per token (d = 4096)
+    (4099, 256, 256, 0, 3), (301, 4096, 4096, 16, 2),
+])
 def test_inject_f32_and_bf16(T, d, ld, chan0, Kc):
     announce("inject f32/bf16 %s" % ((T, d, ld, chan0, Kc),))
     g = np.random.default_rng(20)
@@ -105,6 +110,9 @@ def test_loss_delta_loss_bit_exact(Kc, T, inplace):
 @pytest.mark.parametrize("dt,Kc,T,d", [
     ("bf16", 9, 37, 512), ("bf16", 6, 21, 1000), ("bf16", 5, 13, 100), ("bf16", 3, 9, 5000),
     ("f32", 9, 37, 512), ("f32", 7, 11, 6), ("f32", 2, 5, 3000),
+    # 4-token tiles: ragged last tile, fp32 rows, short rows, one token, draws split over waves
+    ("f32", 5, 23, 256), ("bf16", 33, 7, 64), ("bf16", 1, 1, 8), ("bf16", 64, 37, 512),
+    ("bf16", 100, 6, 504),
 ])
 def test_loss_delta_inner(dt, Kc, T, d):
     announce("loss_delta INNER %s" % ((dt, Kc, T, d),))
