@@ -13,6 +13,8 @@ namespace dust {
 namespace {
 
 // ---------------------------------------------------------------- loss mode: c = l_clean - l_pert
+// VEC: each thread handles 4 float4 pieces of one draw row, strided by the block width, so four
+// loads per thread are in flight at once.
 template <bool VEC>
 __global__ __launch_bounds__(256) void loss_delta_loss_kernel(const float *__restrict__ lc,
                                                               const float *__restrict__ lp,
@@ -22,11 +24,20 @@ __global__ __launch_bounds__(256) void loss_delta_loss_kernel(const float *__res
     const uint32_t tb = blockIdx.x % nb_row;
     const uint64_t row = (uint64_t)i * T;
     if constexpr (VEC) {
-        const uint32_t t = (tb * 256u + threadIdx.x) * 4u;
-        if (t >= T) return;
-        const float4 l = *(const float4 *)(lp + row + t);
-        const float4 k = *(const float4 *)(lc + t);
-        *(float4 *)(c + row + t) = make_float4(k.x - l.x, k.y - l.y, k.z - l.z, k.w - l.w);
+        f32x4 l[4], k[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t t = (tb * 1024u + u * 256u + threadIdx.x) * 4u;
+            if (t < T) {
+                l[u] = __builtin_nontemporal_load((const f32x4 *)(lp + row + t));
+                k[u] = *(const f32x4 *)(lc + t);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t t = (tb * 1024u + u * 256u + threadIdx.x) * 4u;
+            if (t < T) *(f32x4 *)(c + row + t) = k[u] - l[u];
+        }
     } else {
         const uint32_t t = tb * 256u + threadIdx.x;
         if (t >= T) return;
@@ -301,17 +312,46 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
     }
 
     constexpr uint32_t CH = 64u * VEC;
+    // Sequences of up to PRE chunks are loaded up front (all loads in flight at once); longer
+    // ones stream chunk by chunk.
+    constexpr uint32_t PRE = 4;
+    float pre[PRE][VEC];
+    const bool preload = seg_len <= PRE * CH;
+    if (preload) {
+#pragma unroll
+        for (uint32_t ch = 0; ch < PRE; ++ch) {
+            const int64_t pos = (int64_t)seg_len - (int64_t)(ch + 1) * CH + (int64_t)lane * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) pre[ch][e] = 0.f;
+            if (ch * CH < seg_len && pos >= 0) {
+                if constexpr (VEC == 4) {
+                    const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) pre[ch][e] = x[e];
+                } else {
+                    pre[ch][0] = c[seg_base + pos];
+                }
+            }
+        }
+    }
     float carry = 0.f;  // r at the first element after the current chunk (0 past the end)
-    for (uint32_t done = 0; done < seg_len; done += CH) {
+    for (uint32_t done = 0, ch = 0; done < seg_len; done += CH, ++ch) {
         // chunk covers sequence positions [seg_len - done - CH, seg_len - done)
         const int64_t start = (int64_t)seg_len - (int64_t)done - (int64_t)CH;
         const int64_t pos = start + (int64_t)lane * VEC;   // first element of this lane
         float v[VEC];
         const bool in = pos >= 0;    // with VEC > 1, seg_len % VEC == 0, so a lane is all in or out
-        if constexpr (VEC == 4) {
+        if (preload) {
+#pragma unroll
+            for (uint32_t q = 0; q < PRE; ++q)
+                if (q == ch) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[e] = pre[q][e];
+                }
+        } else if constexpr (VEC == 4) {
             if (in) {
-                const float4 x = *(const float4 *)(c + seg_base + pos);
-                v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+                const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
+                v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
             } else {
                 v[0] = v[1] = v[2] = v[3] = 0.f;
             }
@@ -337,7 +377,8 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
         for (int e = 0; e < VEC; ++e) v[e] = __builtin_fmaf(gpow[VEC - e], after, v[e]);
         if (in) {
             if constexpr (VEC == 4) {
-                *(float4 *)(r + seg_base + pos) = make_float4(v[0], v[1], v[2], v[3]);
+                const f32x4 o = {v[0], v[1], v[2], v[3]};
+                *(f32x4 *)(r + seg_base + pos) = o;
             } else {
                 r[seg_base + pos] = v[0];
             }
@@ -351,7 +392,7 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
 hipError_t launch_loss_delta_loss(const float *lc, const float *lp, float *c, int64_t Kc,
                                   int64_t T, hipStream_t s) {
     const bool vec = (T % 4 == 0) && aligned16(lc) && aligned16(lp) && aligned16(c);
-    const int64_t per_block = vec ? 1024 : 256;
+    const int64_t per_block = vec ? 4096 : 256;
     const uint32_t nb_row = (uint32_t)((T + per_block - 1) / per_block);
     const uint32_t blocks = (uint32_t)(nb_row * Kc);
     if (vec)
