@@ -42,12 +42,8 @@ def build(force: bool = False) -> str:
     return _LIB_PATH
 
 
-def _load():
-    global _lib
-    if _lib is not None:
-        return _lib
-    build()
-    lib = ctypes.CDLL(_LIB_PATH)
+def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Declare the C signatures on a loaded oracle library."""
     lib.dust_or_philox4x32_10.argtypes = [ctypes.POINTER(_u32), ctypes.POINTER(_u32),
                                           ctypes.POINTER(_u32)]
     lib.dust_or_noise_words.argtypes = [_u64, _u32, _u32, _u32, _u32, ctypes.POINTER(_u32)]
@@ -77,8 +73,16 @@ def _load():
     lib.dust_or_threads.restype = ctypes.c_int
     lib.dust_or_round_bf16.argtypes = [ctypes.c_double]
     lib.dust_or_round_bf16.restype = ctypes.c_double
-    _lib = lib
     return lib
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    _lib = _configure(ctypes.CDLL(_LIB_PATH))
+    return _lib
 
 
 def _f64(a) -> np.ndarray:

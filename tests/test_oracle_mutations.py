@@ -1,0 +1,131 @@
+"""Mutation check of the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in a copy of oracle/dust_oracle.c (a wrong Philox
+constant, a dropped key advance, swapped counter words, a wrong Box-Muller radius, a flipped
+sign, a missing sigma, a scan that leaks across sequences, an off-by-one chunk, ...), builds it,
+swaps it in for the oracle's library, and requires that at least one of the pins the other
+oracle tests use rejects it. The real oracle passes all of them (tests/test_oracle_*.py).
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import test_oracle_steps as steps
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(os.path.dirname(HERE), "oracle", "dust_oracle.c")
+
+
+@pytest.fixture(scope="module")
+def rocrand_exe(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc) or not os.path.exists("/opt/rocm/include/rocrand/rocrand_philox4x32_10.h"):
+        return None
+    exe = str(tmp_path_factory.mktemp("xcheck_mut") / "xcheck")
+    subprocess.check_call([hipcc, "-O1", "-o", exe, os.path.join(HERE, "rocrand_philox_xcheck.cpp")])
+    return exe
+
+
+def _pin_rocrand(exe):
+    def pin():
+        if exe is None:
+            return
+        g = np.random.default_rng(3)
+        cases = [(int(g.integers(0, 2**62)), int(g.integers(0, 2**32)), int(g.integers(0, 2**32)),
+                  int(g.integers(0, 2**30)), int(g.integers(0, 2**32))) for _ in range(64)]
+        lines = ["%d %d %d" % (s, dr | (tg << 32), 4 * (q | (tk << 32))) for s, tg, dr, tk, q in cases]
+        out = subprocess.run([exe], input="\n".join(lines) + "\n", capture_output=True, text=True,
+                             check=True).stdout.split()
+        ref = np.array([int(v) for v in out], dtype=np.uint64).reshape(-1, 4)
+        got = np.array([oracle.noise_words(*c) for c in cases], dtype=np.uint64)
+        assert np.array_equal(got, ref)
+    return pin
+
+
+def _pin_normal_moments():
+    n = oracle.normals(0xBEEF, 1, 0, 0, 0, 4, 256, 256).ravel()
+    N = n.size
+    assert np.all(np.isfinite(n))
+    assert abs(n.mean()) < 5 / np.sqrt(N) and abs(n.var() - 1) < 5 * np.sqrt(2 / N)
+
+
+PINS_STEPS = [
+    steps.test_inject_sigma_zero_is_identity,
+    steps.test_inject_leading_dimension_and_offsets,
+    steps.test_loss_delta_loss_is_clean_minus_perturbed,
+    steps.test_loss_delta_inner_matches_einsum,
+    steps.test_scan_gamma_zero_keeps_own_token,
+    steps.test_scan_impulse_response,
+    steps.test_scan_constant_input_geometric_series,
+    lambda: steps.test_scan_brute_force(0.9),
+    steps.test_error_estimate_brute_force_tiny,
+    steps.test_error_estimate_chunked_population_equals_one_pass,
+    lambda: steps.test_error_estimate_recovers_linear_loss_gradient(0.0),
+    lambda: steps.test_error_estimate_recovers_linear_loss_gradient(0.9),
+    lambda: steps.test_head_ce_matches_torch_cross_entropy(64, 12, 20),
+    lambda: steps.test_head_ce_matches_torch_cross_entropy(97, 88, 9),
+    steps.test_head_ce_sigma_zero_and_large_logits,
+]
+
+# (id, text in dust_oracle.c, replacement)
+MUTATIONS = [
+    ("philox multiplier", "(uint64_t)0xD2511F53u * (uint64_t)x0", "(uint64_t)0xD2511F57u * (uint64_t)x0"),
+    ("philox low/high swap", "uint32_t y1 = (uint32_t)pb;", "uint32_t y1 = (uint32_t)(pb >> 32);"),
+    ("philox no key advance", "k0 += 0x9E3779B9u;", "k0 += 0u;"),
+    ("philox nine rounds", "round < 10; ++round", "round < 9; ++round"),
+    ("counter token/draw swapped", "uint32_t ctr[4] = {q, token, draw, tag};", "uint32_t ctr[4] = {q, draw, token, tag};"),
+    ("box-muller radius", "double rho = sqrt(-2.0 * log(ua));", "double rho = sqrt(-log(ua));"),
+    ("uniform bit width", "return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);",
+     "return ((double)(w >> 8) + 0.5) * (1.0 / 8388608.0);"),
+    ("inject sign", "y[t * ld_y + j] +\n                    sigma", "y[t * ld_y + j] -\n                    sigma"),
+    ("inject channel offset dropped",
+     "(uint32_t)(draw0 + k), (uint32_t)(tok0 + t),\n                                           (uint64_t)(chan0 + j));",
+     "(uint32_t)(draw0 + k), (uint32_t)(tok0 + t),\n                                           (uint64_t)(j));"),
+    ("bulk normals ignore token offset", "(uint32_t)(tok0 + t),\n                                                          (uint64_t)(chan0 + j));",
+     "(uint32_t)(t),\n                                                          (uint64_t)(chan0 + j));"),
+    ("loss change sign", "c[i * T + t] = loss_clean[t] - loss_pert[i * T + t];",
+     "c[i * T + t] = loss_pert[i * T + t] - loss_clean[t];"),
+    ("inner score sign", "c[i * T + s] = -acc;", "c[i * T + s] = acc;"),
+    ("scan off by one", "r[i * T + t] = c[i * T + t] + gamma * r[i * T + t + 1];",
+     "r[i * T + t] = gamma * (c[i * T + t] + r[i * T + t + 1]);"),
+    ("scan leaks across sequences", "r[i * T + last] = c[i * T + last];",
+     "r[i * T + last] = c[i * T + last] + (last + 1 < T ? gamma * c[i * T + last + 1] : 0.0);"),
+    ("estimate without sigma", "double scale = -1.0 / ((double)K_total * sigma);\n    #pragma omp parallel for collapse(2)",
+     "double scale = -1.0 / ((double)K_total);\n    #pragma omp parallel for collapse(2)"),
+    ("estimate sign", "double scale = -1.0 / ((double)K_total * sigma);\n    #pragma omp parallel for collapse(2)",
+     "double scale = 1.0 / ((double)K_total * sigma);\n    #pragma omp parallel for collapse(2)"),
+    ("estimate ignores draw0", "acc += r[i * T + t] * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),",
+     "acc += r[i * T + t] * dust_or_normal(seed, tag, (uint32_t)(i),"),
+    ("head target not perturbed", "if (j == y) zy = zj;", "if (j == y) zy = z[j];"),
+    ("head chunk off by one", "if (j >= v0 && j < v0 + C)\n                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),\n                                                 (uint32_t)(tok0 + t), (uint64_t)j);\n                if (zj > m)",
+     "if (j >= v0 && j <= v0 + C)\n                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),\n                                                 (uint32_t)(tok0 + t), (uint64_t)j);\n                if (zj > m)"),
+    ("head clean loss drops max", "loss_clean[t] = m + log(s) - z[y];", "loss_clean[t] = log(s) - z[y];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_reject_planted_mistake(name, old, new, tmp_path, rocrand_exe):
+    src = open(SRC).read()
+    assert src.count(old) >= 1, "mutation anchor not found: %s" % name
+    mutant_src = tmp_path / "mutant.c"
+    mutant_src.write_text(src.replace(old, new, 1))
+    lib_path = str(tmp_path / "libmutant.so")
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-o", lib_path,
+                           str(mutant_src), "-lm"])
+    saved = oracle._load()
+    oracle._lib = oracle._configure(ctypes.CDLL(lib_path))
+    failed = []
+    try:
+        for pin in [_pin_rocrand(rocrand_exe), _pin_normal_moments] + PINS_STEPS:
+            try:
+                pin()
+            except (AssertionError, ValueError, FloatingPointError):
+                failed.append(getattr(pin, "__name__", "pin"))
+    finally:
+        oracle._lib = saved
+    assert failed, "no pin rejected the planted mistake '%s'" % name
