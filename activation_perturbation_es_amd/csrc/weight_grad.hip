@@ -7,12 +7,17 @@
 //
 // Operands: A = g_hat^T [M = d_out][K = T] is K-contiguous (the error-estimate kernel writes it
 // that way). B = x [K][N = d_in] is N-contiguous, the wrong way round for an MFMA B operand,
-// which wants 8 consecutive k per lane; each thread therefore loads a 4 (k) x 8 (n) block of x
-// and transposes it in registers before writing it to LDS as [n][k].
-// Tiling: 128 x 128 output tile per 256-thread block, 2 x 2 waves of 64 x 64, k-step 64 staged
-// through two LDS buffers, with global loads issued two k-steps ahead of the MFMAs. The token axis is
-// split across blocks so that small outputs still fill the 256 CUs; the split partial sums go to
-// a workspace and are added in split order by a second kernel, so results are deterministic.
+// which wants 8 consecutive k per lane.
+//
+// Two tilings. Outputs of at least 2^19 elements with T a multiple of 32 take the large-tile
+// kernel: 256 x 256 output tile per 256-thread block (one block per CU), 2 x 2 waves of 128 x 128,
+// both operands moved by direct-to-LDS loads through four stages of 32 tokens, A fragments read
+// with ds_read_b128 and B fragments with the transposing ds_read_b64_tr_b16, so x needs no
+// register transpose. Other shapes take the small-tile kernel: 128 x 128 output tile, 2 x 2 waves
+// of 64 x 64, k-step 64 staged through two LDS buffers, global loads two k-steps ahead, x
+// transposed 4 x 8 in registers. Both split the token axis across blocks so that the 256 CUs fill;
+// the split partial sums go to a workspace and are added in split order by a second kernel, so
+// results are deterministic.
 #include "dust_internal.hpp"
 
 namespace dust {
@@ -190,6 +195,244 @@ __global__ __launch_bounds__(256, 2) void wgrad_mfma_kernel(const uint16_t *__re
         }
 }
 
+// ------------------------------------------------------------------------------------------
+// Large-tile kernel.
+namespace big {
+
+constexpr uint32_t BM = 256, BN = 256, BK = 32, NST = 4;
+constexpr uint32_t STAGE = 256u * BK * 2u;   // bytes per operand stage (16 KB)
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define DUST_LDS __attribute__((address_space(3)))
+
+struct Plan {
+    uint32_t mtiles, ntiles, splits, kchunk;
+};
+
+// Aim for one block per CU (256 blocks), each split at least 256 tokens long.
+Plan plan_split(int64_t T, int64_t M, int64_t N) {
+    Plan p;
+    p.mtiles = (uint32_t)((M + BM - 1) / BM);
+    p.ntiles = (uint32_t)((N + BN - 1) / BN);
+    const int64_t tiles = (int64_t)p.mtiles * p.ntiles;
+    int64_t splits = (256 + tiles - 1) / tiles;
+    const int64_t max_by_k = (T + 255) / 256;
+    if (splits > max_by_k) splits = max_by_k;
+    if (splits < 1) splits = 1;
+    int64_t kchunk = (T + splits - 1) / splits;
+    kchunk = (kchunk + BK - 1) / BK * BK;
+    splits = (T + kchunk - 1) / kchunk;
+    p.splits = (uint32_t)splits;
+    p.kchunk = (uint32_t)kchunk;
+    return p;
+}
+
+// LDS layouts, chosen so that the fragment reads hit all 64 banks (measured free of bank
+// conflicts on gfx950). A stage: row m holds 32 k = four 16-byte chunks; rows 4L..4L+3 share a
+// 256-byte line and chunk c of row r sits in slot 4 (r & 3) + (c ^ ((r >> 2) & 3)), so that 16
+// lanes reading one chunk of 16 consecutive rows hit 16 different slots.
+__device__ __forceinline__ uint32_t a_byte(uint32_t r, uint32_t c) {
+    return (r >> 2) * 256u + (4u * (r & 3u) + (c ^ ((r >> 2) & 3u))) * 16u;
+}
+// B stage: row k holds 256 n (sixteen 32-byte pieces); piece p of row k sits at
+// (p & ~7) | ((p & 7) ^ 2 (k & 3)), so that the 32 lanes of one transposing read (four rows x two
+// adjacent pieces) hit eight different pieces of a 256-byte line.
+__device__ __forceinline__ uint32_t b_byte(uint32_t k, uint32_t n) {
+    const uint32_t p = n >> 4;
+    const uint32_t ps = (p & ~7u) | ((p & 7u) ^ ((k & 3u) << 1));
+    return k * 512u + ps * 32u + (n & 15u) * 2u;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t *p) {
+    return (uint32_t)(uintptr_t)(DUST_LDS const void *)p;
+}
+
+// One direct-to-LDS load: lane l's 16 bytes at sbase + voff land at LDS byte m0 + 16 l. Written
+// as inline asm so that the compiler, which would otherwise wait for every pending direct load
+// before each LDS read, leaves the waiting to the kernel (explicit vmcnt before each barrier).
+__device__ __forceinline__ void dma16(const void *sbase, uint32_t voff, uint32_t m0) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
+}
+
+// Requires T % 32 == 0 (every split is a whole number of 32-token steps), N % 8 == 0, 16-byte
+// aligned operands, 256 * T * 2 < 2^32 and 32 * N * 2 < 2^32 (32-bit lane offsets).
+__global__ __launch_bounds__(256, 1) void wgrad_mfma256_kernel(const uint16_t *__restrict__ A,
+                                                               const uint16_t *__restrict__ B,
+                                                               float *__restrict__ out, uint32_t M,
+                                                               uint32_t N, uint32_t K, Plan p,
+                                                               uint64_t split_stride) {
+    __shared__ __attribute__((aligned(1024))) uint8_t As[NST][STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t Bs[NST][STAGE];
+
+    // logical block order (split, m-tile, n-tile), dealt to the XCDs in contiguous eighths:
+    // the blocks of one split share an XCD and its L2
+    const uint32_t tiles = p.mtiles * p.ntiles;
+    const uint32_t lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const uint32_t split = lb / tiles, tile = lb % tiles;
+    const uint32_t m0 = (tile / p.ntiles) * BM;
+    const uint32_t n0 = (tile % p.ntiles) * BN;
+    const uint32_t kbeg = split * p.kchunk;
+    const uint32_t kend = min(K, kbeg + p.kchunk);
+    const uint32_t nsteps = (kend - kbeg) / BK;   // >= 1
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t wave = wave_in_block();
+    const uint32_t wm = wave >> 1, wn = wave & 1u;
+    const uint32_t g16 = lane >> 4, i16 = lane & 15u;
+
+    // Each wave moves 4 KB of each operand's 16 KB stage per step as four 1 KB direct loads.
+    // Per-lane byte offsets are fixed for the block; rows past M and columns past N read clamped
+    // in-range data that only feeds output elements that are never stored.
+    uint32_t offa[4], offb[4];
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) {
+        const uint32_t inst = 4u * j + wave;
+        // A: 16-byte unit P of the stage -> (row, chunk), inverting a_byte
+        const uint32_t P = inst * 64u + lane;
+        const uint32_t L = P >> 4, sl = P & 15u;
+        const uint32_t r = 4u * L + (sl >> 2), ch = (sl & 3u) ^ (L & 3u);
+        offa[j] = (min(m0 + r, M - 1u) - m0) * K * 2u + ch * 16u;
+        // B: the instruction covers rows 2 inst, 2 inst + 1; lane -> row, stored 16-byte chunk,
+        // logical column (the piece swizzle is its own inverse)
+        const uint32_t k = 2u * inst + (lane >> 5);
+        const uint32_t cs = lane & 31u;
+        const uint32_t ps = cs >> 1;
+        const uint32_t pl = (ps & ~7u) | ((ps & 7u) ^ ((k & 3u) << 1));
+        const uint32_t n = pl * 16u + (cs & 1u) * 8u;
+        offb[j] = k * N * 2u + (min(n0 + n, N - 8u) - n0) * 2u;
+    }
+    const uint16_t *abase = A + (uint64_t)m0 * K + kbeg;
+    const uint16_t *bbase = B + (uint64_t)kbeg * N + n0;
+
+    // Loads of step s go to stage s % 4. Steps past the split's end reload its last step into a
+    // stage that is never read, so that every step issues the same number of loads.
+    auto dma_one = [&](uint32_t s, uint32_t q) {   // q = 0..7: A (even) or B (odd), part q / 2
+        const uint32_t sc = min(s, nsteps - 1u);
+        const uint32_t j = q >> 1, inst = 4u * j + wave;
+        if (q & 1u)
+            dma16(bbase + (uint64_t)sc * BK * N, offb[j], lds_addr(Bs[s % NST] + inst * 1024u));
+        else
+            dma16(abase + sc * BK, offa[j], lds_addr(As[s % NST] + inst * 1024u));
+    };
+    // MFMA 32x32x16 operands: lane l holds row (A) or column (B) l % 32, k = 8 (l / 32) .. + 7.
+    auto read_a = [&](const uint8_t *as, uint32_t kk, uint32_t i) {
+        const uint32_t ch = 2u * kk + (lane >> 5);
+        return *(const bf16x8 *)(as + a_byte(128u * wm + 32u * i + (lane & 31u), ch));
+    };
+    // ds_read_b64_tr_b16: in each group of 16 lanes, lane 4 r + c names 4 columns of row r; lane
+    // i receives column i of the 4 rows. Two reads give a lane its 8 consecutive k.
+    auto read_b = [&](const uint8_t *bs, uint32_t kk, uint32_t j) {
+        const uint32_t kb = 16u * kk + 8u * (g16 >> 1) + (i16 >> 2);
+        const uint32_t n = 128u * wn + 32u * j + 16u * (g16 & 1u) + 4u * (i16 & 3u);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (DUST_LDS i16x4 *)(DUST_LDS void *)(bs + b_byte(kb, n)));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (DUST_LDS i16x4 *)(DUST_LDS void *)(bs + b_byte(kb + 4u, n)));
+        const i16x8 both = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, both);
+    };
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    for (uint32_t q = 0; q < 8; ++q) dma_one(0, q);
+    for (uint32_t q = 0; q < 8; ++q) dma_one(1, q);
+    for (uint32_t q = 0; q < 8; ++q) dma_one(2, q);
+    asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");   // stage 0 complete
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+#pragma unroll
+    for (uint32_t i = 0; i < 4; ++i) a0[i] = read_a(As[0], 0, i);
+#pragma unroll
+    for (uint32_t j = 0; j < 4; ++j) b0[j] = read_b(Bs[0], 0, j);
+    // No scalar load may be pending in the loop: with one in flight the compiler could wait for
+    // LDS results only with lgkmcnt(0).
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+
+    // Software pipeline, scheduled by hand (sched_barrier pins the order): each half step issues
+    // its 16 multiplies one by one and slips the other work between them, so that the wave never
+    // stalls on a full load queue while the matrix core idles. First half of step st: multiplies
+    // of k slice 0 (read during the previous half), reads of slice 1, direct loads of step st + 3
+    // into the stage read last in step st - 1. Barrier: stage st + 1 complete in every wave.
+    // Second half: multiplies of slice 1, reads of slice 0 of step st + 1.
+#define DUST_MMA(Q, A_, B_)                                                                     \
+    acc[(Q) >> 2][(Q) & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(A_[(Q) >> 2], B_[(Q) & 3],  \
+                                                                     acc[(Q) >> 2][(Q) & 3], 0, 0, 0)
+#define DUST_SB __builtin_amdgcn_sched_barrier(0)
+    for (uint32_t st = 0; st < nsteps; ++st) {
+        const uint8_t *as = As[st % NST], *bs = Bs[st % NST];
+        DUST_MMA(0, a0, b0); a1[0] = read_a(as, 1, 0); a1[1] = read_a(as, 1, 1); DUST_SB;
+        DUST_MMA(1, a0, b0); a1[2] = read_a(as, 1, 2); a1[3] = read_a(as, 1, 3); DUST_SB;
+        DUST_MMA(2, a0, b0); b1[0] = read_b(bs, 1, 0); DUST_SB;
+        DUST_MMA(3, a0, b0); b1[1] = read_b(bs, 1, 1); DUST_SB;
+        DUST_MMA(4, a0, b0); b1[2] = read_b(bs, 1, 2); DUST_SB;
+        DUST_MMA(5, a0, b0); b1[3] = read_b(bs, 1, 3); DUST_SB;
+        DUST_MMA(6, a0, b0); dma_one(st + 3u, 0); DUST_SB;
+        DUST_MMA(7, a0, b0); dma_one(st + 3u, 1); DUST_SB;
+        DUST_MMA(8, a0, b0); dma_one(st + 3u, 2); DUST_SB;
+        DUST_MMA(9, a0, b0); dma_one(st + 3u, 3); DUST_SB;
+        DUST_MMA(10, a0, b0); dma_one(st + 3u, 4); DUST_SB;
+        DUST_MMA(11, a0, b0); dma_one(st + 3u, 5); DUST_SB;
+        DUST_MMA(12, a0, b0); dma_one(st + 3u, 6); DUST_SB;
+        DUST_MMA(13, a0, b0); dma_one(st + 3u, 7); DUST_SB;
+        DUST_MMA(14, a0, b0); DUST_SB;
+        DUST_MMA(15, a0, b0); DUST_SB;
+        // This wave's loads of step st + 1 are complete once at most those of steps st + 2 and
+        // st + 3 (16 instructions; loads complete in issue order) are in flight; its reads of
+        // slice 1 are complete, so after the barrier stage st % 4 may be overwritten. After the
+        // last step the barrier and the reads below are redundant but harmless; keeping them
+        // unconditional keeps the compiler's wait counts exact.
+        __builtin_amdgcn_s_waitcnt(0x4070);   // vmcnt(16) lgkmcnt(0)
+        asm volatile("s_barrier" ::: "memory");
+        const uint8_t *an = As[(st + 1u) % NST], *bn = Bs[(st + 1u) % NST];
+        DUST_MMA(0, a1, b1); a0[0] = read_a(an, 0, 0); a0[1] = read_a(an, 0, 1); DUST_SB;
+        DUST_MMA(1, a1, b1); a0[2] = read_a(an, 0, 2); a0[3] = read_a(an, 0, 3); DUST_SB;
+        DUST_MMA(2, a1, b1); b0[0] = read_b(bn, 0, 0); DUST_SB;
+        DUST_MMA(3, a1, b1); b0[1] = read_b(bn, 0, 1); DUST_SB;
+        DUST_MMA(4, a1, b1); b0[2] = read_b(bn, 0, 2); DUST_SB;
+        DUST_MMA(5, a1, b1); b0[3] = read_b(bn, 0, 3); DUST_SB;
+        DUST_MMA(6, a1, b1); DUST_SB;
+        DUST_MMA(7, a1, b1); DUST_SB;
+        DUST_MMA(8, a1, b1); DUST_SB;
+        DUST_MMA(9, a1, b1); DUST_SB;
+        DUST_MMA(10, a1, b1); DUST_SB;
+        DUST_MMA(11, a1, b1); DUST_SB;
+        DUST_MMA(12, a1, b1); DUST_SB;
+        DUST_MMA(13, a1, b1); DUST_SB;
+        DUST_MMA(14, a1, b1); DUST_SB;
+        DUST_MMA(15, a1, b1); DUST_SB;
+    }
+#undef DUST_MMA
+#undef DUST_SB
+    // no direct load may still be writing LDS when the block ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+    float *o = out + (uint64_t)split * split_stride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t col = n0 + wn * 128u + j * 32u + (lane & 31u);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const uint32_t row = m0 + wm * 128u + i * 32u + 8u * (r >> 2) + 4u * (lane >> 5) + (r & 3);
+                if (row < M && col < N) o[(uint64_t)row * N + col] = acc[i][j][r];
+            }
+        }
+}
+#undef DUST_LDS
+
+bool usable(int64_t T, int64_t M, int64_t N) {
+    return T % 32 == 0 && N % 8 == 0 && M * N >= (int64_t)1 << 19 && T < ((int64_t)1 << 23) &&
+           N < ((int64_t)1 << 26);
+}
+
+}  // namespace big
+
 // Sum of the split partial sums in split order.
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float *__restrict__ ws,
                                                             float *__restrict__ G, uint64_t n4,
@@ -230,6 +473,10 @@ bool tiled_ok(int64_t T, int64_t d_in) { return (T % 8 == 0) && (d_in % 8 == 0);
 
 size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in) {
     if (T <= 0 || d_out <= 0 || d_in <= 0 || !tiled_ok(T, d_in)) return 0;
+    if (big::usable(T, d_out, d_in)) {
+        const big::Plan q = big::plan_split(T, d_out, d_in);
+        return q.splits <= 1 ? 0 : (size_t)q.splits * (size_t)d_out * (size_t)d_in * sizeof(float);
+    }
     const SplitPlan p = plan_split(T, d_out, d_in);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)d_out * (size_t)d_in * sizeof(float);
@@ -247,16 +494,25 @@ hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, i
                                                                       (uint32_t)d_in, (uint32_t)T);
         return hipGetLastError();
     }
-    const SplitPlan p = plan_split(T, d_out, d_in);
-    const uint32_t blocks = p.mtiles * p.ntiles * p.splits;
-    float *dst = p.splits > 1 ? (float *)workspace : G;
-    wgrad_mfma_kernel<<<blocks, 256, 0, s>>>(gt, x, dst, (uint32_t)d_out, (uint32_t)d_in,
-                                             (uint32_t)T, p, (uint64_t)n);
+    uint32_t splits;
+    if (big::usable(T, d_out, d_in)) {
+        const big::Plan q = big::plan_split(T, d_out, d_in);
+        splits = q.splits;
+        float *dst = splits > 1 ? (float *)workspace : G;
+        big::wgrad_mfma256_kernel<<<q.mtiles * q.ntiles * q.splits, 256, 0, s>>>(
+            gt, x, dst, (uint32_t)d_out, (uint32_t)d_in, (uint32_t)T, q, (uint64_t)n);
+    } else {
+        const SplitPlan p = plan_split(T, d_out, d_in);
+        splits = p.splits;
+        float *dst = splits > 1 ? (float *)workspace : G;
+        wgrad_mfma_kernel<<<p.mtiles * p.ntiles * p.splits, 256, 0, s>>>(
+            gt, x, dst, (uint32_t)d_out, (uint32_t)d_in, (uint32_t)T, p, (uint64_t)n);
+    }
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.splits <= 1) return e;
+    if (e != hipSuccess || splits <= 1) return e;
     const uint64_t n4 = n / 4;   // d_in % 8 == 0, so n is a multiple of 4
     splitk_reduce_kernel<<<(uint32_t)((n4 + 255) / 256), 256, 0, s>>>((const float *)workspace, G,
-                                                                      n4, p.splits);
+                                                                      n4, splits);
     return hipGetLastError();
 }
 

@@ -139,9 +139,14 @@ def test_binding_raises_dust_error_with_message():
 
 
 def test_weight_grad_workspace_sizes():
-    # tiled path with a split over tokens: splits x d_out x d_in x 4 bytes
-    assert dust.dust_weight_grad_workspace(16384, 2048, 512) == 8 * 2048 * 512 * 4
-    assert dust.dust_weight_grad_workspace(16384, 4096, 1024) == 2 * 4096 * 1024 * 4
+    # split over tokens: splits x d_out x d_in x 4 bytes. Large-tile path (256 x 256 tiles,
+    # about 256 blocks, >= 256 tokens per split): 16 and 4 splits.
+    assert dust.dust_weight_grad_workspace(16384, 2048, 512) == 16 * 2048 * 512 * 4
+    assert dust.dust_weight_grad_workspace(16384, 4096, 1024) == 4 * 4096 * 1024 * 4
+    # small-tile path (128 x 128 tiles, about 512 blocks, >= 512 tokens per split): outputs
+    # below 2^19 elements, or T not a multiple of 32
+    assert dust.dust_weight_grad_workspace(16384, 512, 512) == 32 * 512 * 512 * 4
+    assert dust.dust_weight_grad_workspace(16376, 2048, 512) == 8 * 2048 * 512 * 4
     # one split, or the plain path, or an empty problem: no workspace
     assert dust.dust_weight_grad_workspace(512, 128, 128) == 0
     assert dust.dust_weight_grad_workspace(1001, 33, 17) == 0

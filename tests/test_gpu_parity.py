@@ -231,6 +231,10 @@ def test_error_estimate_zero_draws_writes_zero():
     (1000, 64, 64),      # T not a multiple of the 64-token step
     (1001, 33, 17),      # plain path (T, d_in not multiples of 8)
     (64, 1, 8),
+    (1024, 1024, 512),   # large-tile path, whole tiles, 4 splits
+    (1056, 1040, 520),   # large-tile path, ragged row and column tiles, last split shorter
+    (32, 2048, 512),     # large-tile path, one 32-token step, one split
+    (4096, 520, 1016),   # large-tile path, N not a multiple of 16
 ])
 def test_weight_grad(T, d_out, d_in):
     announce("weight_grad %s" % ((T, d_out, d_in),))
