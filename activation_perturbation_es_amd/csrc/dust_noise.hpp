@@ -5,10 +5,15 @@
 // K x T x d values; instead every kernel that needs a^{(i)}_{t, ch} regenerates it from a
 // counter-based generator:
 //   Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) of counter (ch/4, token, draw, tag) under
-//   key (seed lo, seed hi) -> four 32-bit words -> two Box-Muller pairs -> channels 4q..4q+3.
-// Uniform: u(w) = (floor(w / 2^9) + 1/2) * 2^-23, exact in fp32.
+//   key (seed lo, seed hi) -> four 32-bit words -> two Box-Muller pairs -> channels 4q..4q+3:
+//   channel 4q+0 = rho(w0) cos(2 pi v(w1)), 4q+1 = rho(w0) sin(2 pi v(w1)), likewise (w2, w3),
+//   rho(w) = sqrt(-2 ln u(w)), radius uniform u(w) = (floor(w / 2^9) + 1/2) 2^-23 in (0, 1),
+//   angle uniform v(w) = floor(w / 2^9) 2^-23 in [0, 1) (turns). Both are exact in fp32.
 // Box-Muller uses the hardware transcendentals: v_log_f32 (log2), v_sqrt_f32, and
-// v_sin_f32 / v_cos_f32, whose argument is in revolutions, so sin(2 pi u) costs one op.
+// v_sin_f32 / v_cos_f32, whose argument is in turns, so sin(2 pi v) costs one op; the angle
+// needs no subtraction (see box_muller). The generator returns the normals divided by
+// kNormalScale = sqrt(2 ln 2), since sqrt(-2 ln u) = sqrt(2 ln 2) sqrt(-log2 u); every caller
+// folds the constant into a coefficient it applies anyway, saving one multiply per pair.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -31,15 +36,20 @@ __device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
     return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
 }
 
-// Ten Philox rounds on (c0, c1, c2, c3) under (k0, k1); results in place. The first round keeps
-// plain XORs so that wave-uniform counter words (draw, tag, often token) stay on the scalar unit.
+// Ten Philox rounds on (c0, c1, c2, c3) under (k0, k1); results in place. Round r maps
+//   (c0, c1, c2, c3) -> (hi(M1 c2) ^ c1 ^ k0_r, lo(M1 c2), hi(M0 c0) ^ c3 ^ k1_r, lo(M0 c0)).
+// UNIFORM: the caller's token and draw are the same across the wave. Then the first rounds see
+// scalar operands, and the XORs are grouped so that two scalar operands are combined on the
+// scalar unit first (a VALU instruction reads at most one scalar); otherwise, and from round 3 on,
+// one three-input XOR does each pair.
+template <bool UNIFORM>
 __device__ __forceinline__ void philox4x32_10(uint32_t &c0, uint32_t &c1, uint32_t &c2,
                                               uint32_t &c3, uint32_t k0, uint32_t k1) {
-    {
+    {   // round 0: plain XORs keep wave-uniform words on the scalar unit
         const uint64_t pa = mul_wide(0xD2511F53u, c0);
         const uint64_t pb = mul_wide(0xCD9E8D57u, c2);
-        const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = ((uint32_t)(pb >> 32) ^ k0) ^ c1;
+        const uint32_t n2 = (uint32_t)(pa >> 32) ^ (c3 ^ k1);
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;
@@ -51,8 +61,19 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &c0, uint32_t &c1, uint32
         k1 += 0xBB67AE85u;
         const uint64_t pa = mul_wide(0xD2511F53u, c0);
         const uint64_t pb = mul_wide(0xCD9E8D57u, c2);
-        const uint32_t n0 = xor3((uint32_t)(pb >> 32), c1, k0);
-        const uint32_t n2 = xor3((uint32_t)(pa >> 32), c3, k1);
+        uint32_t n0, n2;
+        if (UNIFORM && round == 1) {
+            // c1 = lo(M1 draw) and hi(M0 c0) (c0 from the uniform token and draw) are scalar
+            n0 = (uint32_t)(pb >> 32) ^ (c1 ^ k0);
+            n2 = c3 ^ ((uint32_t)(pa >> 32) ^ k1);
+        } else if (UNIFORM && round == 2) {
+            // c3 = lo(M0 c0) of round 1 is scalar
+            n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+            n2 = (uint32_t)(pa >> 32) ^ (c3 ^ k1);
+        } else {
+            n0 = xor3((uint32_t)(pb >> 32), c1, k0);
+            n2 = xor3((uint32_t)(pa >> 32), c3, k1);
+        }
         c1 = (uint32_t)pb;
         c3 = (uint32_t)pa;
         c0 = n0;
@@ -60,13 +81,17 @@ __device__ __forceinline__ void philox4x32_10(uint32_t &c0, uint32_t &c1, uint32
     }
 }
 
-// Words of channel group q (channels 4q..4q+3) for (draw, token).
+// Words of channel group q (channels 4q..4q+3) for (draw, token). UNIFORM: see philox4x32_10.
+template <bool UNIFORM = false>
 __device__ __forceinline__ uint4 noise_words(const Key &key, uint32_t q, uint32_t token,
                                              uint32_t draw) {
     uint32_t c0 = q, c1 = token, c2 = draw, c3 = key.tag;
-    philox4x32_10(c0, c1, c2, c3, key.k0, key.k1);
+    philox4x32_10<UNIFORM>(c0, c1, c2, c3, key.k0, key.k1);
     return make_uint4(c0, c1, c2, c3);
 }
+
+// sqrt(2 ln 2): the normals below are a / kNormalScale.
+constexpr double kNormalScale = 1.17741002251547469101;
 
 __device__ __forceinline__ float uniform01(uint32_t w) {
     // (m + 1/2) * 2^-23 with m = w >> 9 < 2^23, exact, in [2^-24, 1 - 2^-24]. One funnel shift
@@ -76,23 +101,28 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
     return one_plus - 0x1.fffffep-1f;
 }
 
-// One Box-Muller pair: radius from wa, angle (in revolutions) from wb.
-__device__ __forceinline__ void box_muller(uint32_t wa, uint32_t wb, float &n_cos, float &n_sin) {
+// One Box-Muller pair divided by kNormalScale: radius from wa, angle from wb. The angle is
+// passed as 1 + v(wb) (the funnel shift alone); v_sin / v_cos take turns and reduce their
+// argument modulo 1 exactly, so the whole turn costs nothing.
+__device__ __forceinline__ void box_muller_unit(uint32_t wa, uint32_t wb, float &n_cos,
+                                                float &n_sin) {
     const float ua = uniform01(wa);
-    const float ub = uniform01(wb);
-    // -2 ln u = -2 ln(2) log2(u)
-    const float rho = __builtin_amdgcn_sqrtf(-1.38629436111989061883f * __builtin_amdgcn_logf(ua));
-    n_cos = rho * __builtin_amdgcn_cosf(ub);
-    n_sin = rho * __builtin_amdgcn_sinf(ub);
+    const float turns = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, wb, 9u));
+    const float rho = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(ua));   // sqrt(-log2 u)
+    n_cos = rho * __builtin_amdgcn_cosf(turns);
+    n_sin = rho * __builtin_amdgcn_sinf(turns);
 }
 
-// The four standard normals of channels 4q..4q+3 of (draw, token).
-__device__ __forceinline__ float4 noise4(const Key &key, uint32_t q, uint32_t token,
-                                         uint32_t draw) {
-    const uint4 w = noise_words(key, q, token, draw);
+// The four standard normals of channels 4q..4q+3 of (draw, token), divided by kNormalScale.
+// UNIFORM: token and draw are the same across the wave (see philox4x32_10); the result does not
+// depend on it.
+template <bool UNIFORM = false>
+__device__ __forceinline__ float4 unit_noise4(const Key &key, uint32_t q, uint32_t token,
+                                              uint32_t draw) {
+    const uint4 w = noise_words<UNIFORM>(key, q, token, draw);
     float4 n;
-    box_muller(w.x, w.y, n.x, n.y);
-    box_muller(w.z, w.w, n.z, n.w);
+    box_muller_unit(w.x, w.y, n.x, n.y);
+    box_muller_unit(w.z, w.w, n.z, n.w);
     return n;
 }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const float rv = (tt < (int)ntok) ? rp[tt] : 0.f;
-            const float4 n = noise4(key, q, tok0 + t0 + tt, draw);
+            const float4 n = unit_noise4<true>(key, q, tok0 + t0 + tt, draw);
             acc[tt][0] = __builtin_fmaf(rv, n.x, acc[tt][0]);
             acc[tt][1] = __builtin_fmaf(rv, n.y, acc[tt][1]);
             acc[tt][2] = __builtin_fmaf(rv, n.z, acc[tt][2]);
@@ -128,7 +128,8 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
         zero_estimate_kernel<<<(uint32_t)((n + 255) / 256), 256, 0, s>>>(g, gt, n);
         return hipGetLastError();
     }
-    const float scale = (float)(-1.0 / ((double)K_total * (double)sigma));
+    // the generator's normals come divided by kNormalScale
+    const float scale = (float)(-kNormalScale / ((double)K_total * (double)sigma));
     const uint32_t n_ctiles = (uint32_t)((d + 255) / 256);
     const bool vec = (d % 4 == 0) && aligned16(g) && (gt == nullptr || aligned16(gt));
     // Largest token tile (8 or 4) that still gives every SIMD several waves. A 16-token tile

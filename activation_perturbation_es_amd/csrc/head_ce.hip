@@ -27,7 +27,7 @@ template <int GPL>  // channel groups (of 4) per lane: chunk size C <= 256 * GPL
 __global__ __launch_bounds__(256) void head_ce_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ targets,
     float *__restrict__ lp, float *__restrict__ lc, uint32_t T, uint32_t V, uint32_t v0,
-    uint32_t C, uint32_t Kc, float sigma, float sigma_log2e, Key key, uint32_t draw0,
+    uint32_t C, uint32_t Kc, float sigma_c, float sigma_log2e, Key key, uint32_t draw0,
     uint32_t tok0) {
     const uint32_t t = blockIdx.x * 4u + wave_in_block();
     if (t >= T) return;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
         for (int m = 0; m < GPL; ++m) {
             const uint32_t grp = lane + 64u * m;
             if (4u * grp >= C) continue;
-            const float4 n = noise4(key, q0 + grp, token, draw);
+            const float4 n = unit_noise4<true>(key, q0 + grp, token, draw);
             s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(sigma_log2e * n.x), s);
             s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(sigma_log2e * n.y), s);
             s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(sigma_log2e * n.z), s);
@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
         float ny = 0.f;
         if (y_in) ny = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ysel), owner));
         if (lane == 0)
-            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(sigma, ny, zy);
+            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(sigma_c, ny, zy);
     }
 }
 
@@ -112,11 +112,13 @@ hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, flo
                                 int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                 hipStream_t s) {
     const uint32_t blocks = (uint32_t)((T + 3) / 4);
-    const float sl2e = sigma * LOG2E;
+    // the generator's normals come divided by kNormalScale: both coefficients carry it
+    const float sl2e = (float)((double)sigma * 1.44269504088896340736 * kNormalScale);
+    const float sig = (float)((double)sigma * kNormalScale);
 #define DUST_HEAD(G)                                                                           \
     head_ce_kernel<G><<<blocks, 256, 0, s>>>(logits, targets, loss_pert, loss_clean,           \
                                              (uint32_t)T, (uint32_t)V, (uint32_t)v0,           \
-                                             (uint32_t)C, (uint32_t)Kc, sigma, sl2e, key,      \
+                                             (uint32_t)C, (uint32_t)Kc, sig, sl2e, key,        \
                                              draw0, tok0)
     if (C <= 256) DUST_HEAD(1);
     else if (C <= 512) DUST_HEAD(2);

@@ -51,7 +51,7 @@ static RowMap make_rowmap(int64_t ngroups, int64_t T, uint32_t &blocks) {
 
 // All draws of one (token, 4-channel group): y is read once, then each draw's four normals come
 // from one Philox call and the four perturbed values are written.
-template <bool BF16, bool VEC>
+template <bool BF16, bool VEC, bool UNIFORM>
 __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__restrict__ yp_,
                                            uint32_t t, uint32_t T, uint32_t d, uint64_t ld_y,
                                            uint32_t j0, uint32_t q, uint32_t Kc, float sigma,
@@ -83,7 +83,7 @@ __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__
     const uint64_t draw_stride = (uint64_t)T * d;
     const uint64_t base = (uint64_t)t * d + j0;
     for (uint32_t k = 0; k < Kc; ++k) {
-        const float4 n = noise4(key, q, token, draw0 + k);
+        const float4 n = unit_noise4<UNIFORM>(key, q, token, draw0 + k);
         const float o0 = __builtin_fmaf(sigma, n.x, yv[0]);
         const float o1 = __builtin_fmaf(sigma, n.y, yv[1]);
         const float o2 = __builtin_fmaf(sigma, n.z, yv[2]);
@@ -115,7 +115,10 @@ __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__
 
 // One thread per (token slot, 4-channel group). With few draws per call a thread's life would
 // be short; a token slot then covers `nseq` adjacent tokens, handled one after the other.
-template <bool BF16, bool VEC>
+// WIDE (rows of at least 256 groups): a block lies inside one row, so the token is uniform across
+// the block and the compiler keeps it, and the Philox words that depend only on the token and
+// the draw, on the scalar unit.
+template <bool BF16, bool VEC, bool WIDE>
 __global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_,
                                                      void *__restrict__ yp_, uint32_t T,
                                                      uint32_t d, uint64_t ld_y, uint32_t q0,
@@ -123,11 +126,17 @@ __global__ __launch_bounds__(256) void inject_kernel(const void *__restrict__ y_
                                                      uint32_t draw0, uint32_t tok0, RowMap m,
                                                      uint32_t nseq) {
     uint32_t ts, g;
-    if (!map_thread(m, (T + nseq - 1) / nseq, ts, g)) return;
+    if constexpr (WIDE) {
+        ts = blockIdx.x / m.nblk_g;
+        g = (blockIdx.x % m.nblk_g) * 256u + threadIdx.x;
+        if (ts * nseq >= T || g >= m.ngroups) return;
+    } else {
+        if (!map_thread(m, (T + nseq - 1) / nseq, ts, g)) return;
+    }
     const uint32_t t_end = min(T, (ts + 1) * nseq);
 #pragma unroll 1
     for (uint32_t t = ts * nseq; t < t_end; ++t)
-        inject_one<BF16, VEC>(y_, yp_, t, T, d, ld_y, 4u * g, q0 + g, Kc, sigma, key, draw0,
+        inject_one<BF16, VEC, WIDE>(y_, yp_, t, T, d, ld_y, 4u * g, q0 + g, Kc, sigma, key, draw0,
                               tok0 + t);
 }
 
@@ -155,14 +164,25 @@ hipError_t launch_noise_inject(const void *y, void *y_pert, bool bf16, int64_t T
     const RowMap m = make_rowmap(ngroups, (T + nseq - 1) / nseq, blocks);
     const bool vec = (d % 4 == 0) && (ld_y % 4 == 0) && aligned16(y) && aligned16(y_pert);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-#define DUST_INJECT(B, V)                                                                      \
-    inject_kernel<B, V><<<blocks, 256, 0, s>>>(y, y_pert, (uint32_t)T, (uint32_t)d,            \
-                                               (uint64_t)ld_y, q0, (uint32_t)Kc, sigma, key,   \
-                                               draw0, tok0, m, (uint32_t)nseq)
+    // the generator's normals come divided by kNormalScale
+    const float sig = (float)((double)sigma * kNormalScale);
+#define DUST_INJECT(B, V, W)                                                                   \
+    inject_kernel<B, V, W><<<blocks, 256, 0, s>>>(y, y_pert, (uint32_t)T, (uint32_t)d,         \
+                                                  (uint64_t)ld_y, q0, (uint32_t)Kc, sig, key,   \
+                                                  draw0, tok0, m, (uint32_t)nseq)
+    const bool wide = m.tpr_log2 == 8;
     if (bf16) {
-        if (vec) DUST_INJECT(true, true); else DUST_INJECT(true, false);
+        if (vec) {
+            if (wide) DUST_INJECT(true, true, true); else DUST_INJECT(true, true, false);
+        } else {
+            DUST_INJECT(true, false, false);
+        }
     } else {
-        if (vec) DUST_INJECT(false, true); else DUST_INJECT(false, false);
+        if (vec) {
+            if (wide) DUST_INJECT(false, true, true); else DUST_INJECT(false, true, false);
+        } else {
+            DUST_INJECT(false, false, false);
+        }
     }
 #undef DUST_INJECT
     return hipGetLastError();

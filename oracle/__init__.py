@@ -49,6 +49,10 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.dust_or_noise_words.argtypes = [_u64, _u32, _u32, _u32, _u32, ctypes.POINTER(_u32)]
     lib.dust_or_uniform.argtypes = [_u32]
     lib.dust_or_uniform.restype = ctypes.c_double
+    lib.dust_or_angle.argtypes = [_u32]
+    lib.dust_or_angle.restype = ctypes.c_double
+    lib.dust_or_box_muller.argtypes = [_u32, _u32, ctypes.c_int]
+    lib.dust_or_box_muller.restype = ctypes.c_double
     lib.dust_or_normal.argtypes = [_u64, _u32, _u32, _u32, _u64]
     lib.dust_or_normal.restype = ctypes.c_double
     lib.dust_or_normals.argtypes = [_u64, _u32, _u32, _u32, _i64, _i64, _i64, _i64, _d]
@@ -118,7 +122,18 @@ def noise_words(seed: int, tag: int, draw: int, token: int, q: int) -> np.ndarra
 
 
 def uniform(w: int) -> float:
+    """Radius uniform u(w) in (0, 1)."""
     return _load().dust_or_uniform(int(w) & 0xFFFFFFFF)
+
+
+def angle(w: int) -> float:
+    """Angle uniform v(w) in [0, 1), in turns."""
+    return _load().dust_or_angle(int(w) & 0xFFFFFFFF)
+
+
+def box_muller(wa: int, wb: int, sine: bool) -> float:
+    """One normal of the word pair (wa, wb): rho(wa) sin or cos (2 pi v(wb))."""
+    return _load().dust_or_box_muller(int(wa) & 0xFFFFFFFF, int(wb) & 0xFFFFFFFF, int(bool(sine)))
 
 
 def normal(seed: int, tag: int, draw: int, token: int, ch: int) -> float:

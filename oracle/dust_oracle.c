@@ -20,10 +20,13 @@
  * pages fix neither the generator nor the index layout; the readings used here are:
  *   key     = (seed mod 2^32, seed >> 32)
  *   counter = (floor(ch / 4), token, draw, tag)      ch = global channel (vocab id for the head)
- *   u(w)    = (floor(w / 2^9) + 1/2) * 2^-23          exact in fp32 and fp64, in (0, 1)
- *   channel 4q+0 = rho(w0) cos(2 pi u(w1)), 4q+1 = rho(w0) sin(2 pi u(w1)),
- *   channel 4q+2 = rho(w2) cos(2 pi u(w3)), 4q+3 = rho(w2) sin(2 pi u(w3)),
+ *   u(w)    = (floor(w / 2^9) + 1/2) * 2^-23          radius uniform, exact, in (0, 1)
+ *   v(w)    =  floor(w / 2^9) * 2^-23                 angle uniform (turns), exact, in [0, 1)
+ *   channel 4q+0 = rho(w0) cos(2 pi v(w1)), 4q+1 = rho(w0) sin(2 pi v(w1)),
+ *   channel 4q+2 = rho(w2) cos(2 pi v(w3)), 4q+3 = rho(w2) sin(2 pi v(w3)),
  *   rho(w) = sqrt(-2 ln u(w)).
+ * The radius uniform must exclude 0 (log), the angle uniform need not, so the angle takes the
+ * left end of each of the 2^23 bins.
  *
  * Every loop below is the definition written out: no blocking, fusion or reordering of any
  * sum. OpenMP splits only independent output elements across threads.
@@ -83,10 +86,25 @@ void dust_or_noise_words(uint64_t seed, uint32_t tag, uint32_t draw, uint32_t to
     dust_or_philox4x32_10(ctr, key, out);
 }
 
-/* Uniform in (0, 1) from the top 23 bits of a word, centred in its bin. */
+/* Radius uniform in (0, 1) from the top 23 bits of a word, centred in its bin. */
 double dust_or_uniform(uint32_t w)
 {
     return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);
+}
+
+/* Angle uniform in [0, 1) (turns) from the top 23 bits of a word, left end of its bin. */
+double dust_or_angle(uint32_t w)
+{
+    return (double)(w >> 9) * (1.0 / 8388608.0);
+}
+
+/* Box-Muller (1958): one of the two normals of the word pair (wa, wb); sine != 0 selects
+ * rho sin(theta), else rho cos(theta). */
+double dust_or_box_muller(uint32_t wa, uint32_t wb, int sine)
+{
+    double rho = sqrt(-2.0 * log(dust_or_uniform(wa)));
+    double theta = 2.0 * M_PI * dust_or_angle(wb);
+    return sine ? rho * sin(theta) : rho * cos(theta);
 }
 
 /* Standard normal a^{(draw)}_{token, ch}: explainer, "Credit assignment", a_t ~ N(0, I). */
@@ -95,11 +113,7 @@ double dust_or_normal(uint64_t seed, uint32_t tag, uint32_t draw, uint32_t token
     uint32_t w[4];
     dust_or_noise_words(seed, tag, draw, token, (uint32_t)(ch / 4), w);
     unsigned pair = (unsigned)((ch % 4) / 2);       /* words (0,1) or (2,3) */
-    double ua = dust_or_uniform(w[2 * pair]);
-    double ub = dust_or_uniform(w[2 * pair + 1]);
-    double rho = sqrt(-2.0 * log(ua));
-    double theta = 2.0 * M_PI * ub;
-    return (ch % 2 == 0) ? rho * cos(theta) : rho * sin(theta);
+    return dust_or_box_muller(w[2 * pair], w[2 * pair + 1], (int)(ch % 2));
 }
 
 /* Bulk normals for (draw0 + k, token0 + t, chan0 + j): out[k][t][j], k < K, t < T, j < d. */

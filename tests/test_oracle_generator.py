@@ -95,6 +95,33 @@ def test_uniform_map_is_exact_and_inside_unit_interval():
         assert float(np.float32(u)) == u
 
 
+def test_angle_map_is_exact_left_bin_edge():
+    assert oracle.angle(0) == 0.0
+    assert oracle.angle(511) == 0.0                    # same 23-bit bin as 0
+    assert oracle.angle(512) == 2.0 ** -23
+    assert oracle.angle(0xFFFFFFFF) == 1.0 - 2.0 ** -23
+    for w in (0, 12345678, 0xFFFFFFFF, 0x80000000):
+        v = oracle.angle(w)
+        assert float(np.float32(v)) == v and 0.0 <= v < 1.0
+
+
+def test_box_muller_at_special_angles():
+    """Angles 0, 1/4, 1/2 and 3/4 turn put the pair on the axes: one normal of the pair is
+    exactly 0 (angle 0) or |.| <= 1e-15 rho, the other is +-rho; rho^2 + 0 = the pair's squared
+    norm, the same for every angle."""
+    wa = 0x5A5A5A5A
+    quarter = 1 << 30             # top 23 bits = 2^21 -> v = 1/4
+    rho_c = oracle.box_muller(wa, 0, False)
+    assert rho_c > 0 and oracle.box_muller(wa, 0, True) == 0.0
+    assert abs(oracle.box_muller(wa, quarter, False)) <= 1e-15 * rho_c
+    assert oracle.box_muller(wa, quarter, True) == pytest.approx(rho_c, rel=1e-15)
+    assert oracle.box_muller(wa, 2 * quarter, False) == pytest.approx(-rho_c, rel=1e-15)
+    assert oracle.box_muller(wa, 3 * quarter, True) == pytest.approx(-rho_c, rel=1e-15)
+    for wb in (1 << 9, 12345 << 9, 0xFFFFFFFF):
+        c, s = oracle.box_muller(wa, wb, False), oracle.box_muller(wa, wb, True)
+        assert c * c + s * s == pytest.approx(rho_c * rho_c, rel=1e-14)
+
+
 @pytest.fixture(scope="module")
 def big_normals():
     return oracle.normals(0xBEEF, 1, 0, 0, 0, 8, 1024, 512)   # 4.2M normals [K, T, d]

@@ -15,6 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_generator as gen
 import test_oracle_steps as steps
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -70,6 +71,7 @@ PINS_STEPS = [
     lambda: steps.test_head_ce_matches_torch_cross_entropy(64, 12, 20),
     lambda: steps.test_head_ce_matches_torch_cross_entropy(97, 88, 9),
     steps.test_head_ce_sigma_zero_and_large_logits,
+    gen.test_box_muller_at_special_angles,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -79,7 +81,12 @@ MUTATIONS = [
     ("philox no key advance", "k0 += 0x9E3779B9u;", "k0 += 0u;"),
     ("philox nine rounds", "round < 10; ++round", "round < 9; ++round"),
     ("counter token/draw swapped", "uint32_t ctr[4] = {q, token, draw, tag};", "uint32_t ctr[4] = {q, draw, token, tag};"),
-    ("box-muller radius", "double rho = sqrt(-2.0 * log(ua));", "double rho = sqrt(-log(ua));"),
+    ("box-muller radius", "double rho = sqrt(-2.0 * log(dust_or_uniform(wa)));",
+     "double rho = sqrt(-log(dust_or_uniform(wa)));"),
+    ("angle centred in its bin", "return (double)(w >> 9) * (1.0 / 8388608.0);",
+     "return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);"),
+    ("cos and sin swapped", "return sine ? rho * sin(theta) : rho * cos(theta);",
+     "return sine ? rho * cos(theta) : rho * sin(theta);"),
     ("uniform bit width", "return ((double)(w >> 9) + 0.5) * (1.0 / 8388608.0);",
      "return ((double)(w >> 8) + 0.5) * (1.0 / 8388608.0);"),
     ("inject sign", "y[t * ld_y + j] +\n                    sigma", "y[t * ld_y + j] -\n                    sigma"),
