@@ -25,7 +25,9 @@ HEADERS = [os.path.join(CSRC, h) for h in ("dust_noise.hpp", "dust_internal.hpp"
           [os.path.join(INCLUDE, "dust.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-# Packed fp32 instructions are disabled for all device code.
+# Packed fp32 instructions (v_pk_add/mul/fma_f32), which the compiler would otherwise form from
+# scalar or float2 code, are disabled for all device code; the host pass warns that it does not
+# know the feature, which is harmless.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-Wno-unused-function"]

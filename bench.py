@@ -45,14 +45,16 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 # Vector ALU issue rate: 256 CUs x 64 lanes x 2.4 GHz = 39.32e12 lane-operations per second.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 
-# Algorithmic vector operations per generated standard normal (one issue slot each; derivation
-# in the design doc). Philox4x32-10: a round is 2 32x32->64 multiplies (v_mad_u64_u32) + 2 three-input
-# XORs (v_bitop3_b32). Of the counter (channel group, token, draw, tag), the channel group and
-# tag are fixed per lane and draw is uniform across the wave, so the first round and the
-# multiplies of the second run once per lane or on the scalar unit, not per draw: 2 + 8 x 4 = 34
-# operations per 4 words -> 8.5 per normal. Box-Muller per pair: 2 x 2 for the uniforms
-# (funnel shift, subtract), log2, scale, sqrt, cos, sin, 2 multiplies = 11 -> 5.5 per normal.
-OPS_PER_NORMAL = 8.5 + 5.5
+# Algorithmic vector operations per generated standard normal (one issue slot each).
+# Philox4x32-10: a round is 2 32x32->64 multiplies (v_mad_u64_u32) + 2 three-input XORs
+# (v_bitop3_b32). Of the counter (channel group, token, draw, tag), the channel group and tag
+# are fixed per lane and token and draw are uniform across the wave, so the first round and half
+# of the second run once per lane or on the scalar unit, not per draw: 2 + 8 x 4 = 34 operations
+# per 4 words -> 8.5 per normal. Box-Muller per pair: funnel shift + subtract for the radius
+# uniform, one funnel shift for the angle (in turns, the whole turn is free), log2, sqrt of the
+# negated log, cos, sin, 2 multiplies = 9 -> 4.5 per normal; the constant sqrt(2 ln 2) is folded
+# into a coefficient the consumer applies anyway.
+OPS_PER_NORMAL = 8.5 + 4.5
 OPS_INJECT_EXTRA = 1.5    # fma with y, and half of a packed fp32 -> bf16 conversion
 OPS_EE_EXTRA = 1.0        # fma of reward x normal into the accumulator
 OPS_HEAD_EXTRA = 3.0      # scale, exp2, fma into the perturbed partition sum
@@ -342,7 +344,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the estimator runs on a single MI355X here "
-              "(multi-GPU sharding is described in DESIGN.md, not built). Use --gpus 1.",
+              "(the path shards by sequences across GPUs, but only the one-GPU case is built). "
+              "Use --gpus 1.",
               file=sys.stderr)
         return 2
 
