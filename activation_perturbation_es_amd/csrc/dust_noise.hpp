@@ -11,9 +11,10 @@
 //   angle uniform v(w) = floor(w / 2^9) 2^-23 in [0, 1) (turns). Both are exact in fp32.
 // Box-Muller uses the hardware transcendentals: v_log_f32 (log2), v_sqrt_f32, and
 // v_sin_f32 / v_cos_f32, whose argument is in turns, so sin(2 pi v) costs one op; the angle
-// needs no subtraction (see box_muller). The generator returns the normals divided by
-// kNormalScale = sqrt(2 ln 2), since sqrt(-2 ln u) = sqrt(2 ln 2) sqrt(-log2 u); every caller
-// folds the constant into a coefficient it applies anyway, saving one multiply per pair.
+// needs no subtraction (see box_muller_polar). The generator returns each pair in polar form,
+// rho = sqrt(-log2 u) and (cos, sin) of the angle, since sqrt(-2 ln u) = kNormalScale
+// sqrt(-log2 u) with kNormalScale = sqrt(2 ln 2): every caller folds the constant into a
+// coefficient it applies anyway and multiplies rho by it once per pair.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -90,7 +91,7 @@ __device__ __forceinline__ uint4 noise_words(const Key &key, uint32_t q, uint32_
     return make_uint4(c0, c1, c2, c3);
 }
 
-// sqrt(2 ln 2): the normals below are a / kNormalScale.
+// sqrt(2 ln 2): a normal is kNormalScale * rho * (cos or sin) of its pair's polar form.
 constexpr double kNormalScale = 1.17741002251547469101;
 
 __device__ __forceinline__ float uniform01(uint32_t w) {
@@ -101,29 +102,34 @@ __device__ __forceinline__ float uniform01(uint32_t w) {
     return one_plus - 0x1.fffffep-1f;
 }
 
-// One Box-Muller pair divided by kNormalScale: radius from wa, angle from wb. The angle is
-// passed as 1 + v(wb) (the funnel shift alone); v_sin / v_cos take turns and reduce their
-// argument modulo 1 exactly, so the whole turn costs nothing.
-__device__ __forceinline__ void box_muller_unit(uint32_t wa, uint32_t wb, float &n_cos,
-                                                float &n_sin) {
+// Polar form of one Box-Muller pair: the pair is kNormalScale * rho * (cos, sin), with
+// rho = sqrt(-log2 u(wa)). The angle is passed as 1 + v(wb) (the funnel shift alone);
+// v_sin / v_cos take turns and reduce their argument modulo 1 exactly, so the whole turn costs
+// nothing. Callers multiply rho by their own coefficient once and apply it to both trig values.
+struct Polar {
+    float rho, c, s;
+};
+
+__device__ __forceinline__ Polar box_muller_polar(uint32_t wa, uint32_t wb) {
     const float ua = uniform01(wa);
     const float turns = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, wb, 9u));
-    const float rho = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(ua));   // sqrt(-log2 u)
-    n_cos = rho * __builtin_amdgcn_cosf(turns);
-    n_sin = rho * __builtin_amdgcn_sinf(turns);
+    Polar p;
+    p.rho = __builtin_amdgcn_sqrtf(-__builtin_amdgcn_logf(ua));   // sqrt(-log2 u)
+    p.c = __builtin_amdgcn_cosf(turns);
+    p.s = __builtin_amdgcn_sinf(turns);
+    return p;
 }
 
-// The four standard normals of channels 4q..4q+3 of (draw, token), divided by kNormalScale.
+// Channels 4q..4q+3 of (draw, token) in polar form: pair 0 (channels 4q, 4q+1) and pair 1
+// (4q+2, 4q+3); a^{(draw)}_{token, 4q+1} = kNormalScale * p[0].rho * p[0].s, and so on.
 // UNIFORM: token and draw are the same across the wave (see philox4x32_10); the result does not
 // depend on it.
 template <bool UNIFORM = false>
-__device__ __forceinline__ float4 unit_noise4(const Key &key, uint32_t q, uint32_t token,
-                                              uint32_t draw) {
+__device__ __forceinline__ void noise4_polar(const Key &key, uint32_t q, uint32_t token,
+                                             uint32_t draw, Polar (&p)[2]) {
     const uint4 w = noise_words<UNIFORM>(key, q, token, draw);
-    float4 n;
-    box_muller_unit(w.x, w.y, n.x, n.y);
-    box_muller_unit(w.z, w.w, n.z, n.w);
-    return n;
+    p[0] = box_muller_polar(w.x, w.y);
+    p[1] = box_muller_polar(w.z, w.w);
 }
 
 }  // namespace dust

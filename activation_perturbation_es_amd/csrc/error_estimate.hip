@@ -45,11 +45,14 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
             const float rv = (tt < (int)ntok) ? rp[tt] : 0.f;
-            const float4 n = unit_noise4<true>(key, q, tok0 + t0 + tt, draw);
-            acc[tt][0] = __builtin_fmaf(rv, n.x, acc[tt][0]);
-            acc[tt][1] = __builtin_fmaf(rv, n.y, acc[tt][1]);
-            acc[tt][2] = __builtin_fmaf(rv, n.z, acc[tt][2]);
-            acc[tt][3] = __builtin_fmaf(rv, n.w, acc[tt][3]);
+            Polar p[2];
+            noise4_polar<true>(key, q, tok0 + t0 + tt, draw, p);
+            // r a = kNormalScale (r rho) (cos, sin); kNormalScale is folded into the final scale
+            const float k0 = rv * p[0].rho, k1 = rv * p[1].rho;
+            acc[tt][0] = __builtin_fmaf(k0, p[0].c, acc[tt][0]);
+            acc[tt][1] = __builtin_fmaf(k0, p[0].s, acc[tt][1]);
+            acc[tt][2] = __builtin_fmaf(k1, p[1].c, acc[tt][2]);
+            acc[tt][3] = __builtin_fmaf(k1, p[1].s, acc[tt][3]);
         }
     }
 

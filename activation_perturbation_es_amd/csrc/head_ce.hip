@@ -27,7 +27,7 @@ template <int GPL>  // channel groups (of 4) per lane: chunk size C <= 256 * GPL
 __global__ __launch_bounds__(256) void head_ce_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ targets,
     float *__restrict__ lp, float *__restrict__ lc, uint32_t T, uint32_t V, uint32_t v0,
-    uint32_t C, uint32_t Kc, float sigma_c, float sigma_log2e, Key key, uint32_t draw0,
+    uint32_t C, uint32_t Kc, float sigma_log2e, Key key, uint32_t draw0,
     uint32_t tok0) {
     const uint32_t t = blockIdx.x * 4u + wave_in_block();
     if (t >= T) return;
@@ -89,19 +89,24 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
         for (int m = 0; m < GPL; ++m) {
             const uint32_t grp = lane + 64u * m;
             if (4u * grp >= C) continue;
-            const float4 n = unit_noise4<true>(key, q0 + grp, token, draw);
-            s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(sigma_log2e * n.x), s);
-            s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(sigma_log2e * n.y), s);
-            s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(sigma_log2e * n.z), s);
-            s = __builtin_fmaf(q[m][3], __builtin_amdgcn_exp2f(sigma_log2e * n.w), s);
+            Polar p[2];
+            noise4_polar<true>(key, q0 + grp, token, draw, p);
+            // x_j = sigma log2(e) a_j: the exponent of e^{sigma a_j} in base 2
+            const float k0 = sigma_log2e * p[0].rho, k1 = sigma_log2e * p[1].rho;
+            const float x0 = k0 * p[0].c, x1 = k0 * p[0].s, x2 = k1 * p[1].c, x3 = k1 * p[1].s;
+            s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(x0), s);
+            s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(x1), s);
+            s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(x2), s);
+            s = __builtin_fmaf(q[m][3], __builtin_amdgcn_exp2f(x3), s);
             if (y_in && (uint32_t)m == my)
-                ysel = ey == 0 ? n.x : (ey == 1 ? n.y : (ey == 2 ? n.z : n.w));
+                ysel = ey == 0 ? x0 : (ey == 1 ? x1 : (ey == 2 ? x2 : x3));
         }
         const float tot = wave_sum(s);
-        float ny = 0.f;
-        if (y_in) ny = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ysel), owner));
+        float xy = 0.f;
+        if (y_in) xy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ysel), owner));
+        // the perturbed target logit is z_y + sigma a_y = z_y + ln(2) x_y
         if (lane == 0)
-            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(sigma_c, ny, zy);
+            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(LN2, xy, zy);
     }
 }
 
@@ -112,13 +117,12 @@ hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, flo
                                 int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                 hipStream_t s) {
     const uint32_t blocks = (uint32_t)((T + 3) / 4);
-    // the generator's normals come divided by kNormalScale: both coefficients carry it
+    // the generator's polar form leaves out kNormalScale: the coefficient carries it
     const float sl2e = (float)((double)sigma * 1.44269504088896340736 * kNormalScale);
-    const float sig = (float)((double)sigma * kNormalScale);
 #define DUST_HEAD(G)                                                                           \
     head_ce_kernel<G><<<blocks, 256, 0, s>>>(logits, targets, loss_pert, loss_clean,           \
                                              (uint32_t)T, (uint32_t)V, (uint32_t)v0,           \
-                                             (uint32_t)C, (uint32_t)Kc, sig, sl2e, key,        \
+                                             (uint32_t)C, (uint32_t)Kc, sl2e, key,             \
                                              draw0, tok0)
     if (C <= 256) DUST_HEAD(1);
     else if (C <= 512) DUST_HEAD(2);

@@ -83,11 +83,13 @@ __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__
     const uint64_t draw_stride = (uint64_t)T * d;
     const uint64_t base = (uint64_t)t * d + j0;
     for (uint32_t k = 0; k < Kc; ++k) {
-        const float4 n = unit_noise4<UNIFORM>(key, q, token, draw0 + k);
-        const float o0 = __builtin_fmaf(sigma, n.x, yv[0]);
-        const float o1 = __builtin_fmaf(sigma, n.y, yv[1]);
-        const float o2 = __builtin_fmaf(sigma, n.z, yv[2]);
-        const float o3 = __builtin_fmaf(sigma, n.w, yv[3]);
+        Polar p[2];
+        noise4_polar<UNIFORM>(key, q, token, draw0 + k, p);
+        const float k0 = sigma * p[0].rho, k1 = sigma * p[1].rho;   // sigma carries kNormalScale
+        const float o0 = __builtin_fmaf(k0, p[0].c, yv[0]);
+        const float o1 = __builtin_fmaf(k0, p[0].s, yv[1]);
+        const float o2 = __builtin_fmaf(k1, p[1].c, yv[2]);
+        const float o3 = __builtin_fmaf(k1, p[1].s, yv[3]);
         const uint64_t off = (uint64_t)k * draw_stride + base;
         if constexpr (BF16) {
             uint16_t *out = (uint16_t *)yp_ + off;

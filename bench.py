@@ -50,14 +50,14 @@ VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
 # (v_bitop3_b32). Of the counter (channel group, token, draw, tag), the channel group and tag
 # are fixed per lane and token and draw are uniform across the wave, so the first round and half
 # of the second run once per lane or on the scalar unit, not per draw: 2 + 8 x 4 = 34 operations
-# per 4 words -> 8.5 per normal. Box-Muller per pair: funnel shift + subtract for the radius
-# uniform, one funnel shift for the angle (in turns, the whole turn is free), log2, sqrt of the
-# negated log, cos, sin, 2 multiplies = 9 -> 4.5 per normal; the constant sqrt(2 ln 2) is folded
-# into a coefficient the consumer applies anyway.
-OPS_PER_NORMAL = 8.5 + 4.5
-OPS_INJECT_EXTRA = 1.5    # fma with y, and half of a packed fp32 -> bf16 conversion
-OPS_EE_EXTRA = 1.0        # fma of reward x normal into the accumulator
-OPS_HEAD_EXTRA = 3.0      # scale, exp2, fma into the perturbed partition sum
+# per 4 words -> 8.5 per normal. Box-Muller per pair, in polar form: funnel shift + subtract for
+# the radius uniform, one funnel shift for the angle (in turns, the whole turn is free), log2,
+# sqrt of the negated log, cos, sin = 7 -> 3.5 per normal. The consumer multiplies the radius by
+# its own coefficient (which carries sqrt(2 ln 2)) once per pair and applies it to cos and sin.
+OPS_PER_NORMAL = 8.5 + 3.5
+OPS_INJECT_EXTRA = 2.0    # half the coefficient x radius multiply, fma with y, half a bf16 pack
+OPS_EE_EXTRA = 1.5        # half the reward x radius multiply, fma into the accumulator
+OPS_HEAD_EXTRA = 3.5      # half the coefficient x radius multiply, multiply, exp2, fma
 
 
 def parse():
