@@ -170,7 +170,11 @@ __global__ __launch_bounds__(256) void loss_delta_inner_tile_kernel(const void *
                                                                     uint32_t d, uint32_t nsplit) {
     constexpr int EPV = BF16 ? 8 : 4;
     const uint32_t w = blockIdx.x * 4u + wave_in_block();
-    const uint32_t tile = w / nsplit, part = w % nsplit;
+    // draw slice major, token tile minor: the waves resident at one time walk the same draws over
+    // adjacent tokens, so the chip reads each draw plane as one long sequential sweep
+    const uint32_t ntiles = (T + 3u) / 4u;
+    const uint32_t tile = w % ntiles, part = w / ntiles;
+    if (part >= nsplit) return;
     const uint32_t s0 = tile * 4u;
     if (s0 >= T) return;
     const uint32_t lane = threadIdx.x & 63u;
