@@ -32,10 +32,11 @@
  *     key      = (seed mod 2^32, seed >> 32)
  *     counter  = (floor(ch / 4), token, draw, tag)         -- Philox4x32-10 (Salmon et al.,
  *                                                             SC'11) -> words w0..w3
- *     u(w)     = (floor(w / 2^9) + 1/2) * 2^-23            -- uniform in (0, 1)
+ *     u(w)     = (floor(w / 2^9) + 1/2) * 2^-23            -- radius uniform in (0, 1)
+ *     v(w)     =  floor(w / 2^9) * 2^-23                   -- angle uniform in [0, 1) turns
  *     rho(w)   = sqrt(-2 ln u(w))                          -- Box-Muller radius
- *     a[ch=4q+0] = rho(w0) cos(2 pi u(w1))   a[ch=4q+1] = rho(w0) sin(2 pi u(w1))
- *     a[ch=4q+2] = rho(w2) cos(2 pi u(w3))   a[ch=4q+3] = rho(w2) sin(2 pi u(w3))
+ *     a[ch=4q+0] = rho(w0) cos(2 pi v(w1))   a[ch=4q+1] = rho(w0) sin(2 pi v(w1))
+ *     a[ch=4q+2] = rho(w2) cos(2 pi v(w3))   a[ch=4q+3] = rho(w2) sin(2 pi v(w3))
  *   `ch` is the GLOBAL channel (chan0 + local channel; the vocabulary id for the head), `token`
  *   is tok0 + local token and `draw` is draw0 + local draw, so the noise of an element does not
  *   depend on how tokens, draws or channels are split across calls. `tag` separates
