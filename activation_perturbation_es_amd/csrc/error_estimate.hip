@@ -39,20 +39,38 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[tt][e] = 0.f;
 
-    const float *rp = r + t0;
-    for (uint32_t i = 0; i < K; ++i, rp += T) {
-        const uint32_t draw = draw0 + i;
+    // one draw: r a = kNormalScale (r rho) (cos, sin); kNormalScale is folded into the final scale
+    auto accumulate_draw = [&](uint32_t draw, const float (&rv)[TPW]) {
 #pragma unroll
         for (int tt = 0; tt < TPW; ++tt) {
-            const float rv = (tt < (int)ntok) ? rp[tt] : 0.f;
             Polar p[2];
             noise4_polar<true>(key, q, tok0 + t0 + tt, draw, p);
-            // r a = kNormalScale (r rho) (cos, sin); kNormalScale is folded into the final scale
-            const float k0 = rv * p[0].rho, k1 = rv * p[1].rho;
+            const float k0 = rv[tt] * p[0].rho, k1 = rv[tt] * p[1].rho;
             acc[tt][0] = __builtin_fmaf(k0, p[0].c, acc[tt][0]);
             acc[tt][1] = __builtin_fmaf(k0, p[0].s, acc[tt][1]);
             acc[tt][2] = __builtin_fmaf(k1, p[1].c, acc[tt][2]);
             acc[tt][3] = __builtin_fmaf(k1, p[1].s, acc[tt][3]);
+        }
+    };
+    const float *rp = r + t0;
+    if (ntok == TPW) {
+        // whole tile: a draw's TPW rewards are one contiguous row piece, fetched by one scalar
+        // load one draw ahead of their use
+        typedef float f32xT __attribute__((ext_vector_type(TPW)));
+        f32xT next = K > 0 ? *(const f32xT *)rp : f32xT{};
+        for (uint32_t i = 0; i < K; ++i) {
+            float rv[TPW];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) rv[tt] = next[tt];
+            if (i + 1 < K) next = *(const f32xT *)(rp + (uint64_t)(i + 1) * T);
+            accumulate_draw(draw0 + i, rv);
+        }
+    } else {
+        for (uint32_t i = 0; i < K; ++i, rp += T) {
+            float rv[TPW];
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) rv[tt] = (tt < (int)ntok) ? rp[tt] : 0.f;
+            accumulate_draw(draw0 + i, rv);
         }
     }
 
