@@ -153,15 +153,6 @@ __global__ __launch_bounds__(256) void loss_delta_inner_kernel(const void *__res
 // cost 3 LDS-crossbar shuffles and 4 DPP adds instead of 24 shuffles.
 __device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
-// Sum over the 16 lanes of each DPP row; every lane of the row receives the row's sum.
-__device__ __forceinline__ float row16_sum(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // xor 1
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // xor 2
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // half-row mirror
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
-    return x;
-}
-
 template <bool BF16, int DRAWS>
 __global__ __launch_bounds__(256) void loss_delta_inner_tile_kernel(const void *__restrict__ dO_,
                                                                     const void *__restrict__ gO_,

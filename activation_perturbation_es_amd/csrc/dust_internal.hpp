@@ -71,6 +71,16 @@ __device__ __forceinline__ float wave_sum(float x) {
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
     return x;
 }
+// Sum over the 16 lanes of each DPP row (lanes 16k .. 16k+15); every lane of the row receives
+// the row's sum. No LDS traffic: four DPP steps (swap neighbours, swap pairs, mirror halves,
+// mirror the row).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false));
+    return x;
+}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
