@@ -242,6 +242,10 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
         return fail(DUST_ERR_INVALID, "%s: G overlaps an input", fn);
     if (need > 0 && ranges_overlap(G, (size_t)(d_out * d_in) * 4, workspace, need))
         return fail(DUST_ERR_INVALID, "%s: G overlaps the workspace", fn);
+    if (need > 0 && T > 0 &&
+        (ranges_overlap(workspace, need, g_hat_t_bf16, (size_t)(d_out * T) * 2) ||
+         ranges_overlap(workspace, need, x_bf16, (size_t)(T * d_in) * 2)))
+        return fail(DUST_ERR_INVALID, "%s: the workspace overlaps an input", fn);
     return hip_status(dust::launch_weight_grad((const uint16_t *)g_hat_t_bf16,
                                                (const uint16_t *)x_bf16, G, T, d_out, d_in,
                                                workspace, (hipStream_t)stream),

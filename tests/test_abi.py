@@ -95,6 +95,7 @@ INVALID = [
     ("dust_weight_grad", (FAKE, FAKE2, FAKE2 + (1 << 30), 4096, 256, 256, FAKE2 + (2 << 30), 16, None), 3, "workspace"),
     ("dust_weight_grad", (None, FAKE2, FAKE2 + (1 << 30), 64, 8, 8, None, 0, None), 1, "null"),
     ("dust_weight_grad", (FAKE, FAKE2, FAKE, 64, 8, 8, None, 0, None), 1, "overlap"),
+    ("dust_weight_grad", (FAKE, FAKE2, FAKE2 + (1 << 30), 4096, 256, 256, FAKE2, 1 << 30, None), 1, "workspace overlaps"),
     ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 96, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "chunk"),
     ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 2, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "chan0"),
     ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 9000, 0, 5000, 2, 0.1, 1, 1, 0, 0, None), 2, "4096"),
