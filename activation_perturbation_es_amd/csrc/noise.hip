@@ -82,6 +82,7 @@ __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__
 
     const uint64_t draw_stride = (uint64_t)T * d;
     const uint64_t base = (uint64_t)t * d + j0;
+    uint32_t lane_off = j0 * 2u;   // byte offset of this lane's group in a bf16 row
     for (uint32_t k = 0; k < Kc; ++k) {
         Polar p[2];
         noise4_polar<UNIFORM>(key, q, token, draw0 + k, p);
@@ -91,7 +92,14 @@ __device__ __forceinline__ void inject_one(const void *__restrict__ y_, void *__
         const float o2 = __builtin_fmaf(k1, p[1].c, yv[2]);
         const float o3 = __builtin_fmaf(k1, p[1].s, yv[3]);
         const uint64_t off = (uint64_t)k * draw_stride + base;
-        if constexpr (BF16) {
+        if constexpr (BF16 && VEC && UNIFORM) {
+            // the token is wave-uniform, so the row start stays on the scalar unit and each lane
+            // adds a 32-bit byte offset (no 64-bit vector address arithmetic per draw)
+            char *row = (char *)((uint16_t *)yp_ + (uint64_t)k * draw_stride + (uint64_t)t * d);
+            asm volatile("" : "+v"(lane_off));   // keeps the per-draw step off the lane offset
+            *(uint2 *)(row + lane_off) =
+                make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
+        } else if constexpr (BF16) {
             uint16_t *out = (uint16_t *)yp_ + off;
             if constexpr (VEC) {
                 *(uint2 *)out = make_uint2(pack_bf16x2(o0, o1), pack_bf16x2(o2, o3));
