@@ -23,12 +23,19 @@ constexpr float LN2 = 0.69314718055994530942f;
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * LOG2E); }
 __device__ __forceinline__ float fast_log(float x) { return __builtin_amdgcn_logf(x) * LN2; }
 
+// Draws per batch: one per lane of a 16-lane quarter of the wave. A partial-sum row holds the
+// 64 lanes plus 4 words of padding, so the 16 lanes of a quarter read 16 different bank groups.
+constexpr int kBatch = 16;
+constexpr int kRow = 68;
+
 template <int GPL>  // channel groups (of 4) per lane: chunk size C <= 256 * GPL
 __global__ __launch_bounds__(256) void head_ce_kernel(
     const float *__restrict__ logits, const int32_t *__restrict__ targets,
     float *__restrict__ lp, float *__restrict__ lc, uint32_t T, uint32_t V, uint32_t v0,
     uint32_t C, uint32_t Kc, float sigma_log2e, Key key, uint32_t draw0,
     uint32_t tok0) {
+    __shared__ __align__(16) float part_lds[4][kBatch][kRow];
+    __shared__ float xsel_lds[4][kBatch];
     const uint32_t t = blockIdx.x * 4u + wave_in_block();
     if (t >= T) return;
     const uint32_t lane = threadIdx.x & 63u;
@@ -82,31 +89,55 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
 
     const uint32_t token = tok0 + t;
     const uint32_t q0 = v0 / 4u;
-    for (uint32_t i = 0; i < Kc; ++i) {
-        const uint32_t draw = draw0 + i;
-        float s = 0.f, ysel = 0.f;
+    // Draws go in batches of kBatch. Per draw each lane leaves its partial sum in LDS (no VALU
+    // work), and the lane owning the target channel leaves x_y there; after the batch the wave
+    // sums the partials transposed (lane l: draw l % kBatch, a quarter of the lanes) and lanes
+    // 0 .. kBatch-1 finish one draw's loss each, so the log and the store run once per batch.
+    float(&part)[kBatch][kRow] = part_lds[wave_in_block()];
+    float(&xsel)[kBatch] = xsel_lds[wave_in_block()];
+    const float base = M;                        // l' = M + ln(s_rest + tot) - z_y - ln2 x_y
+    for (uint32_t ib = 0; ib < Kc; ib += kBatch) {
+        const uint32_t nb = __builtin_amdgcn_readfirstlane(min((uint32_t)kBatch, Kc - ib));
+        for (uint32_t b = 0; b < nb; ++b) {
+            const uint32_t draw = draw0 + ib + b;
+            float s = 0.f;
 #pragma unroll
-        for (int m = 0; m < GPL; ++m) {
-            const uint32_t grp = lane + 64u * m;
-            if (4u * grp >= C) continue;
-            Polar p[2];
-            noise4_polar<true>(key, q0 + grp, token, draw, p);
-            // x_j = sigma log2(e) a_j: the exponent of e^{sigma a_j} in base 2
-            const float k0 = sigma_log2e * p[0].rho, k1 = sigma_log2e * p[1].rho;
-            const float x0 = k0 * p[0].c, x1 = k0 * p[0].s, x2 = k1 * p[1].c, x3 = k1 * p[1].s;
-            s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(x0), s);
-            s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(x1), s);
-            s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(x2), s);
-            s = __builtin_fmaf(q[m][3], __builtin_amdgcn_exp2f(x3), s);
-            if (y_in && (uint32_t)m == my)
-                ysel = ey == 0 ? x0 : (ey == 1 ? x1 : (ey == 2 ? x2 : x3));
+            for (int m = 0; m < GPL; ++m) {
+                const uint32_t grp = lane + 64u * m;
+                if (4u * grp >= C) continue;
+                Polar p[2];
+                noise4_polar<true>(key, q0 + grp, token, draw, p);
+                // x_j = sigma log2(e) a_j: the exponent of e^{sigma a_j} in base 2
+                const float k0 = sigma_log2e * p[0].rho, k1 = sigma_log2e * p[1].rho;
+                const float x0 = k0 * p[0].c, x1 = k0 * p[0].s, x2 = k1 * p[1].c,
+                            x3 = k1 * p[1].s;
+                s = __builtin_fmaf(q[m][0], __builtin_amdgcn_exp2f(x0), s);
+                s = __builtin_fmaf(q[m][1], __builtin_amdgcn_exp2f(x1), s);
+                s = __builtin_fmaf(q[m][2], __builtin_amdgcn_exp2f(x2), s);
+                s = __builtin_fmaf(q[m][3], __builtin_amdgcn_exp2f(x3), s);
+                if (y_in && (uint32_t)m == my && lane == owner)   // wave-uniform but for lane
+                    xsel[b] = ey == 0 ? x0 : (ey == 1 ? x1 : (ey == 2 ? x2 : x3));
+            }
+            part[b][lane] = s;
         }
-        const float tot = wave_sum(s);
-        float xy = 0.f;
-        if (y_in) xy = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ysel), owner));
-        // the perturbed target logit is z_y + sigma a_y = z_y + ln(2) x_y
-        if (lane == 0)
-            lp[(uint64_t)i * T + t] = M + fast_log(s_rest + tot) - __builtin_fmaf(LN2, xy, zy);
+        __builtin_amdgcn_wave_barrier();
+        // lane l adds the partials of draw l % kBatch from lanes 16 (l / 16) .. 16 (l / 16) + 15
+        const uint32_t bl = lane % kBatch, quarter = lane / 16u;
+        float tot = 0.f;
+#pragma unroll
+        for (int k = 0; k < 16; k += 4) {
+            const float4 v = *(const float4 *)&part[bl][16u * quarter + k];
+            tot += (v.x + v.y) + (v.z + v.w);
+        }
+        tot += __shfl_xor(tot, 16);
+        tot += __shfl_xor(tot, 32);
+        if (lane < nb) {
+            const float xy = y_in ? xsel[lane] : 0.f;
+            // the perturbed target logit is z_y + sigma a_y = z_y + ln(2) x_y
+            lp[(uint64_t)(ib + lane) * T + t] =
+                base + fast_log(s_rest + tot) - __builtin_fmaf(LN2, xy, zy);
+        }
+        __builtin_amdgcn_wave_barrier();
     }
 }
 

@@ -416,7 +416,7 @@ def main() -> int:
         with open(traffic_file) as f:
             tr = json.load(f)
         if (tr.get("kernel") == dominant and tr.get("workload") == chain.c["name"]
-                and tr.get("build") == _kernel_build_id()):
+                and tr.get("build") == _kernel_build_id(dominant)):
             roofline["traffic"] = tr.get("bytes_per_launch")
 
     cfg = chain.config()
@@ -433,14 +433,25 @@ def main() -> int:
     return 0
 
 
-def _kernel_build_id() -> str:
-    """Hash of the HIP sources, so recorded counter traffic is tied to the kernels it measured."""
+# HIP translation unit of each entry point's kernels; every unit also includes the two shared
+# device headers, and build.py fixes the compile flags.
+KERNEL_SOURCES = {
+    "dust_noise_inject": "noise.hip", "dust_loss_delta": "delta_scan.hip",
+    "dust_reward_scan": "delta_scan.hip", "dust_error_estimate": "error_estimate.hip",
+    "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
+}
+
+
+def _kernel_build_id(kernel: str) -> str:
+    """Hash of the sources one entry point's kernels are compiled from, so recorded counter
+    traffic is tied to the kernels it measured and goes stale when any of them changes."""
     import hashlib
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "activation_perturbation_es_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+    pkg = os.path.join(ROOT, "activation_perturbation_es_amd")
+    for rel in (os.path.join("csrc", KERNEL_SOURCES[kernel]), os.path.join("csrc", "dust_internal.hpp"),
+                os.path.join("csrc", "dust_noise.hpp"), "build.py"):
+        with open(os.path.join(pkg, rel), "rb") as f:
+            h.update(rel.encode() + f.read())
     return h.hexdigest()[:16]
 
 

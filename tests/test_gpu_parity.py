@@ -279,6 +279,8 @@ def test_weight_grad_zero_tokens_writes_zero():
     (9, 64, 60, 4, 4),
     (5, 5000, 0, 4096, 2),
     (11, 300, 100, 130, 3),    # ragged last channel group
+    (13, 700, 64, 256, 37),    # draws in batches of 16: two whole batches and a ragged one
+    (6, 512, 0, 512, 16),      # exactly one whole batch
 ])
 def test_head_ce_chunk(T, V, v0, C, Kc):
     announce("head_ce_chunk %s" % ((T, V, v0, C, Kc),))
