@@ -8,10 +8,12 @@
 // One wave per token. Pass 1 (once per token) reads the logit row: an online log-sum-exp over
 // the entries outside the chunk (running max and rescaled sum per lane, then merged across
 // lanes) and the chunk entries kept in registers as q_j = e^{z_j - M}. Pass 2 loops over the
-// draws: each lane regenerates the noise of its chunk channels (four per Philox call), forms
-// sum_j q_j 2^{sigma log2(e) a_j}, and the wave sums it. The target's perturbation is read from
-// the lane that owns the target channel. The loop is bound by the generator's ALU work; the
-// logits are read once per token.
+// draws: each lane regenerates the noise of its chunk channels (four per Philox call) and forms
+// its part of sum_j q_j 2^{sigma log2(e) a_j}. The parts, and the target's perturbation from
+// the lane that owns the target channel, go to LDS; every 16 draws the wave sums them transposed
+// and 16 lanes finish one draw's loss each, so neither the cross-lane sum nor the log and store
+// cost vector instructions per draw. The loop is bound by the generator's ALU work; the logits
+// are read once per token.
 #include "dust_internal.hpp"
 
 namespace dust {
