@@ -220,3 +220,29 @@ def test_w5_weight_grad():
     announce("w5 weight grad")
     c = synth.CONFIGS[5]
     _check_weight_grad(5, c["T"], c["d_out"], c["d_in"], 128)
+
+
+# ------------------------------------------------------------------------------ maximum sizes
+@pytest.mark.parametrize("Kc,T,d", [
+    (80, 16384, 4096),    # rows inside one block each: 5.4e9 output elements, 10.7 GB
+    (1100, 16384, 256),   # several rows per block: 4.6e9 output elements, 9.2 GB
+])
+def test_inject_beyond_32_bit_element_offsets(Kc, T, d):
+    """One call whose output has more than 2^32 elements, so element offsets, and not only byte
+    offsets, leave 32 bits; sampled outputs include the very last element."""
+    assert Kc * T * d > 1 << 32
+    announce("inject beyond 32-bit offsets %s" % ((Kc, T, d),))
+    seed, tag, sigma, draw0 = 0x1234_5678_9ABC, 9, 0.01, 7
+    ybits = synth.normal_bf16(np.random.default_rng(31), (T, d))
+    out = torch.empty((Kc, T, d), dtype=torch.bfloat16, device=DEV)
+    dust.dust_noise_inject(bf16(ybits), out, dust.DUST_BF16, T, d, d, 0, Kc, sigma, seed, tag, draw0, 0)
+    g = np.random.default_rng(32)
+    k, t, j = g.integers(0, Kc, NS), g.integers(0, T, NS), g.integers(0, d, NS)
+    k[:3], t[:3], j[:3] = [0, Kc - 1, Kc - 1], [0, T - 1, T - 1], [0, d - 1, 0]
+    got = _gather_bits(out, k, t, j)
+    del out
+    n = oracle.normals_at(seed, tag, k, t, j, draw0=draw0)
+    ref = oracle.round_bf16(bits_to_f64(ybits[t, j]) + sigma * n)
+    gv = bits_to_f64(got)
+    assert np.all(np.abs(gv - ref) <= bf16_ulp(ref))
+    assert np.mean(gv != ref) < 0.01
