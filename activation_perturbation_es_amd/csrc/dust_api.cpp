@@ -59,6 +59,13 @@ int check_noise_ranges(const char *fn, int64_t T, int64_t d, int64_t chan0, int6
     return DUST_OK;
 }
 
+// Bytes of an n0 x n1 x n2 array of es-byte elements, or -1 when that exceeds 2^62: no device
+// holds such an array, and the product could overflow 64-bit size arithmetic.
+int64_t span(int64_t n0, int64_t n1, int64_t n2, int64_t es) {
+    const __int128 p = (__int128)n0 * n1 * n2 * es;
+    return p > ((__int128)1 << 62) ? -1 : (int64_t)p;
+}
+
 bool ranges_overlap(const void *a, size_t abytes, const void *b, size_t bbytes) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + bbytes && b0 < a0 + abytes;
@@ -103,7 +110,11 @@ int dust_noise_inject(const void *y, void *y_pert, int dtype, int64_t T, int64_t
         return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
     if ((d + 3) / 4 >= 256 && ((d + 3) / 4 + 255) / 256 * T > kMaxIdx)
         return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
-    if (ranges_overlap(y, (size_t)((T - 1) * ld_y + d) * es, y_pert, (size_t)(Kc * T * d) * es))
+    const int64_t y_bytes = span(T - 1, ld_y, 1, es) + span(d, 1, 1, es);
+    const int64_t out_bytes = span(Kc, T, d, es);
+    if (out_bytes < 0 || y_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (ranges_overlap(y, (size_t)y_bytes, y_pert, (size_t)out_bytes))
         return fail(DUST_ERR_INVALID, "%s: y and y_pert overlap", fn);
     return hip_status(dust::launch_noise_inject(y, y_pert, dtype == DUST_BF16, T, d, ld_y, chan0,
                                                 Kc, sigma, make_key(seed, tag), draw0, tok0,
@@ -130,9 +141,11 @@ int dust_loss_delta(int mode, const float *loss_clean, const float *loss_pert,
             return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
         if (((T + 255) / 256) * Kc > kMaxIdx)
             return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
-        if (ranges_overlap(loss_clean, (size_t)T * 4, c, (size_t)(Kc * T) * 4))
+        const int64_t c_bytes = span(Kc, T, 1, 4);
+        if (c_bytes < 0) return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+        if (ranges_overlap(loss_clean, (size_t)T * 4, c, (size_t)c_bytes))
             return fail(DUST_ERR_INVALID, "%s: loss_clean and c overlap", fn);
-        if (loss_pert != c && ranges_overlap(loss_pert, (size_t)(Kc * T) * 4, c, (size_t)(Kc * T) * 4))
+        if (loss_pert != c && ranges_overlap(loss_pert, (size_t)c_bytes, c, (size_t)c_bytes))
             return fail(DUST_ERR_INVALID, "%s: loss_pert and c partially overlap", fn);
         return hip_status(dust::launch_loss_delta_loss(loss_clean, loss_pert, c, Kc, T,
                                                        (hipStream_t)stream),
@@ -149,8 +162,12 @@ int dust_loss_delta(int mode, const float *loss_clean, const float *loss_pert,
     const size_t es = io_dtype == DUST_BF16 ? 2 : 4;
     if (!elem_aligned(delta_o, es) || !elem_aligned(g_o, es) || !elem_aligned(c, 4))
         return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
-    if (ranges_overlap(delta_o, (size_t)(Kc * T * d) * es, c, (size_t)(Kc * T) * 4) ||
-        ranges_overlap(g_o, (size_t)(T * d) * es, c, (size_t)(Kc * T) * 4))
+    const int64_t do_bytes = span(Kc, T, d, es), go_bytes = span(T, d, 1, es);
+    const int64_t c_bytes = span(Kc, T, 1, 4);
+    if (do_bytes < 0 || go_bytes < 0 || c_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (ranges_overlap(delta_o, (size_t)do_bytes, c, (size_t)c_bytes) ||
+        ranges_overlap(g_o, (size_t)go_bytes, c, (size_t)c_bytes))
         return fail(DUST_ERR_INVALID, "%s: inputs and c overlap", fn);
     return hip_status(dust::launch_loss_delta_inner(delta_o, g_o, io_dtype == DUST_BF16, c, Kc, T,
                                                     d, (hipStream_t)stream),
@@ -175,7 +192,9 @@ int dust_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg
         return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
     if (K > kMaxIdx || T > kMaxIdx || K * (T / seg_len) > 4 * kMaxIdx)
         return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
-    if (c != r && ranges_overlap(c, (size_t)(K * T) * 4, r, (size_t)(K * T) * 4))
+    const int64_t c_bytes = span(K, T, 1, 4);
+    if (c_bytes < 0) return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (c != r && ranges_overlap(c, (size_t)c_bytes, r, (size_t)c_bytes))
         return fail(DUST_ERR_INVALID, "%s: c and r partially overlap", fn);
     return hip_status(dust::launch_reward_scan(c, r, K, T, seg_len, gamma, (hipStream_t)stream), fn);
 }
@@ -203,9 +222,12 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
         return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
     if ((T / 4 + 1) * ((d + 255) / 256) > kMaxIdx)
         return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
-    if (r && ranges_overlap(r, (size_t)(K * T) * 4, g_hat, (size_t)(T * d) * 4))
+    const int64_t r_bytes = span(K, T, 1, 4), g_bytes = span(T, d, 1, 4);
+    if (r_bytes < 0 || g_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (r && ranges_overlap(r, (size_t)r_bytes, g_hat, (size_t)g_bytes))
         return fail(DUST_ERR_INVALID, "%s: r and g_hat overlap", fn);
-    if (g_hat_t_bf16 && ranges_overlap(g_hat_t_bf16, (size_t)(T * d) * 2, g_hat, (size_t)(T * d) * 4))
+    if (g_hat_t_bf16 && ranges_overlap(g_hat_t_bf16, (size_t)g_bytes / 2, g_hat, (size_t)g_bytes))
         return fail(DUST_ERR_INVALID, "%s: g_hat_t_bf16 and g_hat overlap", fn);
     return hip_status(dust::launch_error_estimate(r, g_hat, (uint16_t *)g_hat_t_bf16, K, K_total, T,
                                                   d, chan0, sigma, make_key(seed, tag), draw0,
@@ -214,6 +236,10 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
 }
 
 size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in) {
+    // sizes dust_weight_grad rejects need no workspace
+    if (T < 0 || d_out < 0 || d_in < 0 || T > kMaxIdx || d_out > kMaxIdx || d_in > kMaxIdx ||
+        d_out * d_in > 256 * kMaxIdx)
+        return 0;
     return dust::weight_grad_workspace_bytes(T, d_out, d_in);
 }
 
@@ -237,14 +263,18 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
                     workspace ? ws_bytes : (size_t)0);
     if (need > 0 && ((uintptr_t)workspace & 15u))
         return fail(DUST_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
-    if (T > 0 && (ranges_overlap(G, (size_t)(d_out * d_in) * 4, g_hat_t_bf16, (size_t)(d_out * T) * 2) ||
-                  ranges_overlap(G, (size_t)(d_out * d_in) * 4, x_bf16, (size_t)(T * d_in) * 2)))
+    const int64_t G_bytes = span(d_out, d_in, 1, 4);
+    const int64_t a_bytes = span(d_out, T, 1, 2), b_bytes = span(T, d_in, 1, 2);
+    if (G_bytes < 0 || a_bytes < 0 || b_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (T > 0 && (ranges_overlap(G, (size_t)G_bytes, g_hat_t_bf16, (size_t)a_bytes) ||
+                  ranges_overlap(G, (size_t)G_bytes, x_bf16, (size_t)b_bytes)))
         return fail(DUST_ERR_INVALID, "%s: G overlaps an input", fn);
-    if (need > 0 && ranges_overlap(G, (size_t)(d_out * d_in) * 4, workspace, need))
+    if (need > 0 && ranges_overlap(G, (size_t)G_bytes, workspace, need))
         return fail(DUST_ERR_INVALID, "%s: G overlaps the workspace", fn);
     if (need > 0 && T > 0 &&
-        (ranges_overlap(workspace, need, g_hat_t_bf16, (size_t)(d_out * T) * 2) ||
-         ranges_overlap(workspace, need, x_bf16, (size_t)(T * d_in) * 2)))
+        (ranges_overlap(workspace, need, g_hat_t_bf16, (size_t)a_bytes) ||
+         ranges_overlap(workspace, need, x_bf16, (size_t)b_bytes)))
         return fail(DUST_ERR_INVALID, "%s: the workspace overlaps an input", fn);
     return hip_status(dust::launch_weight_grad((const uint16_t *)g_hat_t_bf16,
                                                (const uint16_t *)x_bf16, G, T, d_out, d_in,
@@ -275,7 +305,10 @@ int dust_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_
         (loss_pert && !elem_aligned(loss_pert, 4)) || (loss_clean && !elem_aligned(loss_clean, 4)))
         return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
     if (Kc == 0 && loss_clean == nullptr) return ok();
-    if (Kc > 0 && ranges_overlap(loss_pert, (size_t)(Kc * T) * 4, logits, (size_t)(T * V) * 4))
+    const int64_t lp_bytes = span(Kc, T, 1, 4), z_bytes = span(T, V, 1, 4);
+    if (lp_bytes < 0 || z_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (Kc > 0 && ranges_overlap(loss_pert, (size_t)lp_bytes, logits, (size_t)z_bytes))
         return fail(DUST_ERR_INVALID, "%s: loss_pert overlaps logits", fn);
     return hip_status(dust::launch_head_ce_chunk(logits, targets, loss_pert, loss_clean, T, V, v0, C,
                                                  Kc, sigma, make_key(seed, tag), draw0, tok0,

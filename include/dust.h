@@ -21,7 +21,8 @@
  *     left untouched, except where an entry point states otherwise).
  *   - All arguments are validated on the host before any HIP call. Invalid arguments return
  *     DUST_ERR_INVALID; shapes that are valid but outside what the kernels implement return
- *     DUST_ERR_UNSUPPORTED; a short workspace returns DUST_ERR_WORKSPACE; a failed launch
+ *     DUST_ERR_UNSUPPORTED (among them any array of more than 2^62 bytes); a short workspace
+ *     returns DUST_ERR_WORKSPACE; a failed launch
  *     returns DUST_ERR_HIP. dust_last_error() then holds a one-line description for the
  *     calling thread. Nothing is enqueued when a call fails validation.
  *   - Entry points are re-entrant and keep no state between calls.
@@ -135,7 +136,7 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
 
 /*
  * dust_weight_grad_workspace -- bytes of device workspace dust_weight_grad needs for this
- * shape (0 when none). Host-only; never fails.
+ * shape (0 when none, and for shapes dust_weight_grad rejects). Host-only; never fails.
  */
 size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in);
 

@@ -100,6 +100,9 @@ INVALID = [
     ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 2, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "chan0"),
     ("dust_head_ce_chunk", (FAKE, FAKE2, FAKE2 + (1 << 30), None, 8, 9000, 0, 5000, 2, 0.1, 1, 1, 0, 0, None), 2, "4096"),
     ("dust_head_ce_chunk", (None, FAKE2, FAKE2 + (1 << 30), None, 8, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None), 1, "null"),
+    # arrays whose byte size would overflow the size arithmetic
+    ("dust_noise_inject", (FAKE, FAKE2, 1, (1 << 31) - 1, 4, 4, 0, (1 << 31) - 1, 0.1, 1, 1, 0, 0, None), 2, "2^62"),
+    ("dust_loss_delta", (1, None, None, FAKE, FAKE2, 1, FAKE2 + 4096, (1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1, None), 2, "2^62"),
     ("dust_noise_words", (FAKE + 8, 1, 1, 1, 0, 1, 1, 0, 0, None), 1, "16-byte"),
     ("dust_noise_words", (FAKE, 1, 1, 2, 0xFFFFFFFF, 1, 1, 0, 0, None), 1, "2^32"),
 ]
@@ -153,6 +156,9 @@ def test_weight_grad_workspace_sizes():
     assert dust.dust_weight_grad_workspace(1001, 33, 17) == 0
     assert dust.dust_weight_grad_workspace(0, 64, 64) == 0
     assert dust.dust_weight_grad_workspace(-1, 64, 64) == 0
+    # sizes dust_weight_grad rejects as unsupported
+    assert dust.dust_weight_grad_workspace(1 << 40, 4096, 4096) == 0
+    assert dust.dust_weight_grad_workspace(16384, 1 << 30, 1 << 30) == 0
 
 
 def test_product_path_never_touches_the_oracle():
