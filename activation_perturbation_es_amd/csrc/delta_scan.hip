@@ -277,10 +277,13 @@ __global__ __launch_bounds__(256) void loss_delta_inner_long_kernel(const void *
 // (the block of lane l+off contributes gamma^(VEC*off) times its running sum), and the value at
 // the chunk's first element is carried into the next chunk. gamma powers come from repeated
 // squaring: gp[b] = gamma^(VEC * 2^b).
-template <int VEC>
-__global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float *r, uint32_t K,
-                                                          uint32_t T, uint32_t seg_len,
-                                                          float gamma) {
+// LOSSES: the scores are not read but formed on load from the losses, c = l_clean - l_pert
+// (c then points at l_pert [K, T] and lc at l_clean [T]); the same fp32 subtraction as the
+// loss-change kernel, so the fused rewards equal the two-kernel ones bit for bit.
+template <int VEC, bool LOSSES>
+__global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, const float *lc,
+                                                          float *r, uint32_t K, uint32_t T,
+                                                          uint32_t seg_len, float gamma) {
     const uint32_t nseg = T / seg_len;
     const uint64_t w = (uint64_t)blockIdx.x * 4u + wave_in_block();
     if (w >= (uint64_t)K * nseg) return;
@@ -288,6 +291,23 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
     const uint32_t b = (uint32_t)(w % nseg);
     const uint32_t lane = threadIdx.x & 63u;
     const uint64_t seg_base = (uint64_t)i * T + (uint64_t)b * seg_len;
+    const float *lseg = lc + (uint64_t)b * seg_len;   // l_clean of this sequence (LOSSES)
+    // the VEC scores of sequence positions pos .. pos+VEC-1
+    auto load = [&](int64_t pos, float (&v)[VEC]) {
+        if constexpr (VEC == 4) {
+            const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
+            if constexpr (LOSSES) {
+                const f32x4 l = *(const f32x4 *)(lseg + pos);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = l[e] - x[e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = x[e];
+            }
+        } else {
+            v[0] = LOSSES ? lseg[pos] - c[seg_base + pos] : c[seg_base + pos];
+        }
+    };
 
     float gpow[VEC + 1];  // gamma^0 .. gamma^VEC
     gpow[0] = 1.f;
@@ -318,15 +338,7 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
             const int64_t pos = (int64_t)seg_len - (int64_t)(ch + 1) * CH + (int64_t)lane * VEC;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) pre[ch][e] = 0.f;
-            if (ch * CH < seg_len && pos >= 0) {
-                if constexpr (VEC == 4) {
-                    const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) pre[ch][e] = x[e];
-                } else {
-                    pre[ch][0] = c[seg_base + pos];
-                }
-            }
+            if (ch * CH < seg_len && pos >= 0) load(pos, pre[ch]);
         }
     }
     float carry = 0.f;  // r at the first element after the current chunk (0 past the end)
@@ -343,15 +355,11 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, float 
 #pragma unroll
                     for (int e = 0; e < VEC; ++e) v[e] = pre[q][e];
                 }
-        } else if constexpr (VEC == 4) {
-            if (in) {
-                const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
-                v[0] = x[0]; v[1] = x[1]; v[2] = x[2]; v[3] = x[3];
-            } else {
-                v[0] = v[1] = v[2] = v[3] = 0.f;
-            }
+        } else if (in) {
+            load(pos, v);
         } else {
-            v[0] = in ? c[seg_base + pos] : 0.f;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = 0.f;
         }
         // local suffix sums inside the lane
 #pragma unroll
@@ -450,15 +458,24 @@ hipError_t launch_loss_delta_inner(const void *delta_o, const void *g_o, bool bf
 
 hipError_t launch_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
                               float gamma, hipStream_t s) {
+    return launch_loss_reward(nullptr, c, r, K, T, seg_len, gamma, s);
+}
+
+hipError_t launch_loss_reward(const float *lc, const float *c, float *r, int64_t K, int64_t T,
+                              int64_t seg_len, float gamma, hipStream_t s) {
     const int64_t waves = K * (T / seg_len);
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
-    const bool vec = (seg_len % 4 == 0) && aligned16(c) && aligned16(r);
-    if (vec)
-        reward_scan_kernel<4><<<blocks, 256, 0, s>>>(c, r, (uint32_t)K, (uint32_t)T,
-                                                     (uint32_t)seg_len, gamma);
-    else
-        reward_scan_kernel<1><<<blocks, 256, 0, s>>>(c, r, (uint32_t)K, (uint32_t)T,
-                                                     (uint32_t)seg_len, gamma);
+    const bool vec = (seg_len % 4 == 0) && aligned16(c) && aligned16(r) &&
+                     (lc == nullptr || aligned16(lc));
+#define DUST_SCAN(V, L)                                                                        \
+    reward_scan_kernel<V, L><<<blocks, 256, 0, s>>>(c, lc, r, (uint32_t)K, (uint32_t)T,        \
+                                                    (uint32_t)seg_len, gamma)
+    if (lc != nullptr) {
+        if (vec) DUST_SCAN(4, true); else DUST_SCAN(1, true);
+    } else {
+        if (vec) DUST_SCAN(4, false); else DUST_SCAN(1, false);
+    }
+#undef DUST_SCAN
     return hipGetLastError();
 }
 

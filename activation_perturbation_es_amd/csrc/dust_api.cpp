@@ -199,6 +199,35 @@ int dust_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg
     return hip_status(dust::launch_reward_scan(c, r, K, T, seg_len, gamma, (hipStream_t)stream), fn);
 }
 
+int dust_loss_reward(const float *loss_clean, const float *loss_pert, float *r, int64_t K,
+                     int64_t T, int64_t seg_len, float gamma, void *stream) {
+    const char *fn = "dust_loss_reward";
+    if (K < 0 || T < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size (K=%lld T=%lld)", fn, (long long)K,
+                    (long long)T);
+    if (seg_len < 1) return fail(DUST_ERR_INVALID, "%s: seg_len=%lld < 1", fn, (long long)seg_len);
+    if (T % seg_len != 0)
+        return fail(DUST_ERR_INVALID, "%s: T=%lld is not a multiple of seg_len=%lld", fn,
+                    (long long)T, (long long)seg_len);
+    if (!(gamma >= 0.f && gamma <= 1.f))
+        return fail(DUST_ERR_INVALID, "%s: gamma=%g outside [0, 1]", fn, (double)gamma);
+    if (K == 0 || T == 0) return ok();
+    if (!loss_clean || !loss_pert || !r) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(loss_clean, 4) || !elem_aligned(loss_pert, 4) || !elem_aligned(r, 4))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+    if (K > kMaxIdx || T > kMaxIdx || K * (T / seg_len) > 4 * kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    const int64_t r_bytes = span(K, T, 1, 4);
+    if (r_bytes < 0) return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (ranges_overlap(loss_clean, (size_t)T * 4, r, (size_t)r_bytes))
+        return fail(DUST_ERR_INVALID, "%s: loss_clean and r overlap", fn);
+    if (loss_pert != r && ranges_overlap(loss_pert, (size_t)r_bytes, r, (size_t)r_bytes))
+        return fail(DUST_ERR_INVALID, "%s: loss_pert and r partially overlap", fn);
+    return hip_status(dust::launch_loss_reward(loss_clean, loss_pert, r, K, T, seg_len, gamma,
+                                               (hipStream_t)stream),
+                      fn);
+}
+
 int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_t K,
                         int64_t K_total, int64_t T, int64_t d, int64_t chan0, float sigma,
                         uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,

@@ -48,6 +48,11 @@ hipError_t launch_loss_delta_inner(const void *delta_o, const void *g_o, bool bf
 hipError_t launch_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg_len,
                               float gamma, hipStream_t s);
 
+// The scan with its scores formed on load as lc[t] - lp[i][t]; lc == nullptr reads c = lp as
+// the scores themselves (launch_reward_scan).
+hipError_t launch_loss_reward(const float *lc, const float *lp, float *r, int64_t K, int64_t T,
+                              int64_t seg_len, float gamma, hipStream_t s);
+
 hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t K,
                                  int64_t K_total, int64_t T, int64_t d, int64_t chan0,
                                  float sigma, Key key, uint32_t draw0, uint32_t tok0,

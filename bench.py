@@ -4,9 +4,9 @@
 One step = one whole estimate, with every input resident in HBM before the timed region. The
 default workload is the MLP up-projection 512 -> 2048 of the 8-layer width-512 GPT
 (T = 16 x 1024 tokens, K = 64 draws, gamma = 0, sigma = 0.01):
-    dust_noise_inject   x 8 (8-draw blocks into a rotating perturbed-output buffer)
-    dust_loss_delta     (loss mode, [64, 16384])
-    dust_reward_scan    (gamma = 0, sequences of 1024)
+    dust_noise_inject   (all 64 draws in one call, [64, 16384, 2048] bf16 perturbed outputs)
+    dust_loss_reward    (loss change and reward scan in one pass, [64, 16384]; --unfused runs
+                         dust_loss_delta and dust_reward_scan instead)
     dust_error_estimate (g_hat [16384, 2048] fp32 + its bf16 transpose)
     dust_weight_grad    (G_W [2048, 512], bf16 matrix cores)
 The perturbed forward of the rest of the model, between the perturbation and the loss change,
@@ -18,7 +18,7 @@ Metric: draws x tokens per second (K * T / step time). Prints one JSON line with
 HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
 the CPU oracle's throughput on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--workload 2] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--unfused", action="store_true",
+                    help="loss mode: run the loss change and the reward scan as two kernels "
+                         "instead of dust_loss_reward")
     return ap.parse_args()
 
 
@@ -96,6 +99,7 @@ class Chain:
         self.cfg_id, self.dust, self.torch, self.dev = cfg_id, dust, torch, dev
         self.c = synth.CONFIGS[cfg_id]
         self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
+        self.fused = True   # loss mode: scores and rewards in one pass (dust_loss_reward)
 
     def bf(self, bits):
         return self.torch.from_numpy(bits.view(np.int16)).to(self.dev).view(self.torch.bfloat16)
@@ -134,9 +138,14 @@ class LinearChain(Chain):
         for blk in range(K // KB):
             run("dust_noise_inject", d.dust_noise_inject, self.y, self.ybuf, d.DUST_BF16, T, self.d_out,
                 self.d_out, 0, KB, self.sigma, self.seed, self.tag, blk * KB, 0, sh)
-        run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None, None,
-            d.DUST_F32, self.cbuf, K, T, 0, sh)
-        run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.rbuf, K, T, self.S, self.gamma, sh)
+        if self.fused:
+            run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.rbuf, K, T, self.S,
+                self.gamma, sh)
+        else:
+            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None,
+                None, d.DUST_F32, self.cbuf, K, T, 0, sh)
+            run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.rbuf, K, T, self.S,
+                self.gamma, sh)
         run("dust_error_estimate", d.dust_error_estimate, self.rbuf, self.gh, self.ght, K, K, T,
             self.d_out, 0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
         run("dust_weight_grad", d.dust_weight_grad, self.ght, self.x, self.G, T, self.d_out, self.d_in,
@@ -151,6 +160,7 @@ class LinearChain(Chain):
             "dust_noise_inject": _alu(self.KB * T * do, OPS_INJECT_EXTRA),
             "dust_loss_delta": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_reward_scan": _hbm(8.0 * K * T),
+            "dust_loss_reward": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_error_estimate": _alu(K * T * do, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * do * self.d_in),
         }
@@ -212,9 +222,14 @@ class HeadChain(Chain):
         d, T, K = self.dust, self.T, self.K
         run("dust_head_ce_chunk", d.dust_head_ce_chunk, self.z, self.tgt, self.lp, self.lc, T, self.V,
             self.v0, self.C, K, self.sigma, self.seed, self.tag, 0, 0, sh)
-        run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None, None,
-            d.DUST_F32, self.cbuf, K, T, 0, sh)
-        run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S, self.gamma, sh)
+        if self.fused:
+            run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.cbuf, K, T, self.S,
+                self.gamma, sh)
+        else:
+            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None,
+                None, d.DUST_F32, self.cbuf, K, T, 0, sh)
+            run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S,
+                self.gamma, sh)
         run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K, T, self.C,
             self.v0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
         run("dust_weight_grad", d.dust_weight_grad, self.ght, self.h, self.G, T, self.C, self.H,
@@ -229,6 +244,7 @@ class HeadChain(Chain):
             "dust_head_ce_chunk": _alu(K * T * C, OPS_HEAD_EXTRA),
             "dust_loss_delta": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_reward_scan": _hbm(8.0 * K * T),
+            "dust_loss_reward": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_error_estimate": _alu(K * T * C, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * C * self.H),
         }
@@ -363,6 +379,7 @@ def main() -> int:
         del a, b
 
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
+    chain.fused = not args.unfused
     chain.setup()
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -421,6 +438,8 @@ def main() -> int:
 
     cfg = chain.config()
     cfg["parallelism"] = "single GPU"
+    if args.workload != 4:
+        cfg["loss_to_reward"] = "one kernel" if chain.fused else "two kernels"
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -437,7 +456,7 @@ def main() -> int:
 # device headers, and build.py fixes the compile flags.
 KERNEL_SOURCES = {
     "dust_noise_inject": "noise.hip", "dust_loss_delta": "delta_scan.hip",
-    "dust_reward_scan": "delta_scan.hip", "dust_error_estimate": "error_estimate.hip",
+    "dust_reward_scan": "delta_scan.hip", "dust_loss_reward": "delta_scan.hip", "dust_error_estimate": "error_estimate.hip",
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
 }
 

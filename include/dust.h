@@ -118,6 +118,22 @@ int dust_reward_scan(const float *c, float *r, int64_t K, int64_t T, int64_t seg
                      float gamma, void *stream);
 
 /*
+ * dust_loss_reward -- dust_loss_delta (loss mode) and dust_reward_scan in one pass:
+ *     r[i][t] = sum_{s >= t, s in t's sequence} gamma^(s-t) (loss_clean[s] - loss_pert[i][s])
+ * (explainer, "Credit assignment": the loss reduction c of each draw and token, then its
+ * discounted reward). The scores c are formed on load and never stored, so the K x T scores
+ * make no round trip through memory; the result equals dust_loss_delta followed by
+ * dust_reward_scan bit for bit.
+ *   loss_clean  [T] fp32                                                             (in)
+ *   loss_pert   [K, T] fp32                                                          (in)
+ *   r           [K, T] fp32; r == loss_pert (in place) is allowed                    (out)
+ * Requires seg_len >= 1, T % seg_len == 0, 0 <= gamma <= 1; r must not overlap loss_clean,
+ * nor loss_pert other than exactly.
+ */
+int dust_loss_reward(const float *loss_clean, const float *loss_pert, float *r, int64_t K,
+                     int64_t T, int64_t seg_len, float gamma, void *stream);
+
+/*
  * dust_error_estimate -- output-error estimate g_hat [T, d] fp32 (out, or in/out).
  * Explainer, "Credit assignment":
  *     g_hat[t][j] = -(1 / (K_total * sigma)) * sum_{i < K} r[i][t] * a^{(draw0+i)}_{t, chan0+j}

@@ -86,6 +86,11 @@ INVALID = [
     ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 5, 1.5, None), 1, "gamma"),
     ("dust_reward_scan", (FAKE, FAKE2, 2, 10, 5, -0.1, None), 1, "gamma"),
     ("dust_reward_scan", (FAKE, FAKE + 4, 2, 10, 5, 0.5, None), 1, "overlap"),
+    ("dust_loss_reward", (FAKE, FAKE2, FAKE2 + 4096, 2, 10, 3, 0.5, None), 1, "multiple"),
+    ("dust_loss_reward", (FAKE, FAKE2, FAKE2 + 4096, 2, 10, 5, 1.5, None), 1, "gamma"),
+    ("dust_loss_reward", (None, FAKE2, FAKE2 + 4096, 2, 10, 5, 0.5, None), 1, "null"),
+    ("dust_loss_reward", (FAKE, FAKE2, FAKE, 2, 10, 5, 0.5, None), 1, "loss_clean and r overlap"),
+    ("dust_loss_reward", (FAKE, FAKE2, FAKE2 + 4, 2, 10, 5, 0.5, None), 1, "partially overlap"),
     ("dust_error_estimate", (FAKE, FAKE2, None, 4, 3, 8, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "K_total"),
     ("dust_error_estimate", (FAKE, FAKE2, None, 4, 4, 8, 8, 0, 0.0, 1, 1, 0, 0, 0, None), 1, "sigma"),
     ("dust_error_estimate", (FAKE, FAKE2, None, 4, 4, 8, 8, 6, 0.1, 1, 1, 0, 0, 0, None), 1, "chan0"),
@@ -122,6 +127,7 @@ ZERO_SIZE = [
     ("dust_loss_delta", (0, None, None, None, None, 0, None, 0, 8, 0, None)),
     ("dust_loss_delta", (1, None, None, None, None, 1, None, 3, 0, 16, None)),
     ("dust_reward_scan", (None, None, 0, 10, 5, 0.5, None)),
+    ("dust_loss_reward", (None, None, None, 0, 10, 5, 0.5, None)),
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),
     ("dust_head_ce_chunk", (None, None, None, None, 0, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None)),

@@ -95,6 +95,9 @@ def test_w2_loss_delta_and_scan():
     rd = torch.empty_like(cd)
     dust.dust_reward_scan(cd, rd, K, T, S, c["gamma"])
     assert np.array_equal(host_f32(rd), host_f32(cd))    # gamma = 0
+    rf = torch.empty_like(cd)                             # the fused call the benchmark times
+    dust.dust_loss_reward(f32(lc), f32(lp), rf, K, T, S, c["gamma"])
+    assert np.array_equal(host_f32(rf), host_f32(rd))
 
 
 def test_w2_error_estimate():
@@ -208,6 +211,16 @@ def test_w4_weight_grad():
 def test_w5_inject_block():
     announce("w5 inject block")
     _check_inject_block(5, "d_out")
+
+
+def test_w5_loss_reward():
+    announce("w5 loss -> reward")
+    c = synth.CONFIGS[5]
+    K, T, S = c["K"], c["T"], c["seg_len"]
+    lc, lp = synth.losses(synth.rng(5, 2), K, T)
+    rf = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_reward(f32(lc), f32(lp), rf, K, T, S, c["gamma"])
+    assert np.array_equal(host_f32(rf), oracle.loss_delta_loss(lc, lp).astype(np.float32))
 
 
 def test_w5_error_estimate():

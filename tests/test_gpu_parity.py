@@ -164,6 +164,48 @@ def test_reward_scan_in_place():
     assert frob_rel(host_f32(buf), oracle.reward_scan(c, S, gamma)) <= 1e-5
 
 
+# ------------------------------------------------------------------------------ fused loss -> reward
+@pytest.mark.parametrize("K,T,S", SCAN_CASES)
+@pytest.mark.parametrize("gamma", [0.0, 0.9, 1.0])
+def test_loss_reward(K, T, S, gamma):
+    announce("loss_reward %s" % ((K, T, S, gamma),))
+    g = np.random.default_rng(25)
+    lc = g.standard_normal(T).astype(np.float32)
+    lp = (lc + 0.01 * g.standard_normal((K, T))).astype(np.float32)
+    r = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_reward(f32(lc), f32(lp), r, K, T, S, gamma)
+    got = host_f32(r)
+    c = oracle.loss_delta_loss(lc, lp)
+    ref = oracle.reward_scan(c, S, gamma)
+    assert frob_rel(got, ref) <= 1e-5
+    bound = oracle.reward_scan(np.abs(c), S, gamma)
+    assert np.all(np.abs(got - ref) <= 1e-5 * bound + 1e-30)
+    # the two-kernel path gives the same bits
+    c2 = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    r2 = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_delta(dust.DUST_DELTA_LOSS, f32(lc), f32(lp), None, None, dust.DUST_F32, c2, K, T, 0)
+    dust.dust_reward_scan(c2, r2, K, T, S, gamma)
+    assert np.array_equal(got, host_f32(r2))
+
+
+def test_loss_reward_in_place_and_unaligned():
+    announce("loss_reward in place / unaligned")
+    K, T, S, gamma = 3, 2048, 1024, 0.99
+    g = np.random.default_rng(26)
+    lc = g.standard_normal(T).astype(np.float32)
+    lp = g.standard_normal((K, T)).astype(np.float32)
+    ref = oracle.reward_scan(oracle.loss_delta_loss(lc, lp), S, gamma)
+    buf = f32(lp)
+    dust.dust_loss_reward(f32(lc), buf, buf, K, T, S, gamma)
+    assert frob_rel(host_f32(buf), ref) <= 1e-5
+    # loss_clean one element off a 16-byte boundary: the scalar path
+    lcs = torch.zeros(T + 1, dtype=torch.float32, device=DEV)
+    lcs[1:] = f32(lc)
+    r = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_reward(lcs[1:], f32(lp), r, K, T, S, gamma)
+    assert frob_rel(host_f32(r), ref) <= 1e-5
+
+
 # ------------------------------------------------------------------------------ error estimate
 @pytest.mark.parametrize("K,K_total,T,d,chan0,draw0,tok0", [
     (37, 100, 50, 300, 16, 7, 3),     # ragged token tile and channel tile, vector path
