@@ -1,0 +1,81 @@
+"""The estimator chain captured into a HIP graph (torch.cuda.CUDAGraph) replays exactly like the
+eager calls (MI355X only).
+
+The library allocates nothing and clears nothing with memset, so a caller may capture a whole
+estimate (inject -> loss and reward -> output error -> weight gradient, with a preallocated
+weight-gradient workspace) and replay it. Each replay here follows eager work of the program's
+own and a synchronisation, and every output is poisoned before the replay and compared with the
+eager result bit for bit afterwards.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_helpers import DEV, announce, bf16, dust, f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _chain(buf, stream):
+    T, d_out, d_in, K, S, gamma, sigma, seed, tag = buf["shape"]
+    dust.dust_noise_inject(buf["y"], buf["yp"], dust.DUST_BF16, T, d_out, d_out, 0, K, sigma, seed,
+                           tag, 0, 0, stream)
+    dust.dust_loss_reward(buf["lc"], buf["lp"], buf["r"], K, T, S, gamma, stream)
+    dust.dust_error_estimate(buf["r"], buf["gh"], buf["ght"], K, K, T, d_out, 0, sigma, seed, tag,
+                             0, 0, 0, stream)
+    dust.dust_weight_grad(buf["ght"], buf["x"], buf["G"], T, d_out, d_in, buf["ws"],
+                          buf["ws_bytes"], stream)
+
+
+def _buffers(T, d_out, d_in, K, S, gamma, sigma):
+    g = np.random.default_rng(41)
+    lc, lp = synth.losses(g, K, T)
+    ws_bytes = dust.dust_weight_grad_workspace(T, d_out, d_in)
+    return {
+        "shape": (T, d_out, d_in, K, S, gamma, sigma, 0xC0FFEE, 5),
+        "y": bf16(synth.normal_bf16(g, (T, d_out))), "x": bf16(synth.normal_bf16(g, (T, d_in))),
+        "lc": f32(lc), "lp": f32(lp),
+        "yp": torch.empty((K, T, d_out), dtype=torch.bfloat16, device=DEV),
+        "r": torch.empty((K, T), dtype=torch.float32, device=DEV),
+        "gh": torch.empty((T, d_out), dtype=torch.float32, device=DEV),
+        "ght": torch.empty((d_out, T), dtype=torch.bfloat16, device=DEV),
+        "G": torch.empty((d_out, d_in), dtype=torch.float32, device=DEV),
+        "ws": torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV), "ws_bytes": ws_bytes,
+    }
+
+
+OUTS = ("yp", "r", "gh", "ght", "G")
+
+
+@pytest.mark.parametrize("T,d_out,d_in,K,S,gamma", [
+    (2048, 256, 128, 16, 512, 0.9),     # small-tile contraction with split partials
+    (4096, 1024, 512, 8, 1024, 0.0),    # large-tile contraction with split partials
+])
+def test_captured_chain_replays_like_eager(T, d_out, d_in, K, S, gamma):
+    announce("graph replay %s" % ((T, d_out, d_in, K, S, gamma),))
+    buf = _buffers(T, d_out, d_in, K, S, gamma, 0.01)
+    assert buf["ws_bytes"] > 0      # the split-K path, whose partials live in the workspace
+    _chain(buf, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = {k: buf[k].clone() for k in OUTS}
+
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        _chain(buf, side.cuda_stream)     # warm-up on the capture stream
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            _chain(buf, side.cuda_stream)
+    torch.cuda.synchronize()
+
+    other = _buffers(T, d_out, d_in, K, S, gamma, 0.02)
+    for rep in range(3):
+        for k in OUTS:
+            buf[k].view(torch.uint8).fill_(0xFF)          # NaN in every float format
+        _chain(other, torch.cuda.current_stream().cuda_stream)   # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in OUTS:
+            assert torch.equal(buf[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
