@@ -46,6 +46,9 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     """Declare the C signatures on a loaded oracle library."""
     lib.dust_or_philox4x32_10.argtypes = [ctypes.POINTER(_u32), ctypes.POINTER(_u32),
                                           ctypes.POINTER(_u32)]
+    lib.dust_or_sgd_momentum.argtypes = [_d, _d, _d, _i64, ctypes.c_double, ctypes.c_double]
+    lib.dust_or_adam.argtypes = [_d, _d, _d, _d, _i64, ctypes.c_double, ctypes.c_double,
+                                 ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64]
     lib.dust_or_noise_words.argtypes = [_u64, _u32, _u32, _u32, _u32, ctypes.POINTER(_u32)]
     lib.dust_or_uniform.argtypes = [_u32]
     lib.dust_or_uniform.restype = ctypes.c_double
@@ -296,3 +299,23 @@ def tiny_analytic_grad(W, H, x, targets):
     p[np.arange(len(targets)), np.asarray(targets)] -= 1.0
     g = p @ _f64(H)
     return g, g.T @ x
+
+
+# ------------------------------------------------------------------------------ optimizer steps
+def sgd_momentum(w, g, buf, lr: float, momentum: float):
+    """One SGD-with-momentum step (dust_oracle.c states the formula): returns new (w, buf)."""
+    w, buf = _f64(w).copy(), _f64(buf).copy()
+    gg = _f64(g)
+    _load().dust_or_sgd_momentum(_p(w), _p(gg), _p(buf), w.size, lr, momentum)
+    return w, buf
+
+
+def adam(w, g, m, v, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+         step: int):
+    """One Adam step with decoupled weight decay at step t = step >= 1 (dust_oracle.c states
+    the formula): returns new (w, m, v)."""
+    w, m, v = _f64(w).copy(), _f64(m).copy(), _f64(v).copy()
+    gg = _f64(g)
+    _load().dust_or_adam(_p(w), _p(gg), _p(m), _p(v), w.size, lr, beta1, beta2, eps,
+                         weight_decay, step)
+    return w, m, v

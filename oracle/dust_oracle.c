@@ -322,6 +322,39 @@ void dust_or_head_ce_at(const double *logits, const int32_t *targets, int64_t T,
 }
 
 /* ---------------------------------------------------------------------------------------- */
+/* Optimizer steps that turn the estimate G into a weight update. The explainer names the two
+ * used with Dust -- SGD with momentum at a constant learning rate (the ladders of the main
+ * comparison) and Adam (the rerun of the 1M-token ladders, section "Gradients grow") -- and
+ * prints neither formula, so these are the textbook ones, state updated in place:
+ *   SGD with momentum (heavy ball, no dampening, as torch.optim.SGD):
+ *       buf <- mu buf + g;  w <- w - lr buf
+ *   Adam (Kingma & Ba, ICLR 2015) with decoupled weight decay wd (Loshchilov & Hutter,
+ *   ICLR 2019; wd = 0 is plain Adam), step t >= 1:
+ *       w <- w (1 - lr wd)
+ *       m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2
+ *       w <- w - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)                       */
+void dust_or_sgd_momentum(double *w, const double *g, double *buf, int64_t n, double lr,
+                          double mu)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        buf[i] = mu * buf[i] + g[i];
+        w[i] = w[i] - lr * buf[i];
+    }
+}
+
+void dust_or_adam(double *w, const double *g, double *m, double *v, int64_t n, double lr,
+                  double b1, double b2, double eps, double wd, int64_t t)
+{
+    const double bc1 = 1.0 - pow(b1, (double)t), bc2 = 1.0 - pow(b2, (double)t);
+    for (int64_t i = 0; i < n; ++i) {
+        w[i] = w[i] * (1.0 - lr * wd);
+        m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+        v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+        w[i] = w[i] - lr * (m[i] / bc1) / (sqrt(v[i] / bc2) + eps);
+    }
+}
+
+/* ---------------------------------------------------------------------------------------- */
 /* Round a double to the nearest bfloat16 value (8 significant bits, fp32 exponent range),
  * ties to even, returned as a double. Used to state what a bf16 output must hold. */
 double dust_or_round_bf16(double x)

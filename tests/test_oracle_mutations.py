@@ -2,7 +2,8 @@
 
 Each case plants one plausible mistake in a copy of oracle/dust_oracle.c (a wrong Philox
 constant, a dropped key advance, swapped counter words, a wrong Box-Muller radius, a flipped
-sign, a missing sigma, a scan that leaks across sequences, an off-by-one chunk, ...), builds it,
+sign, a missing sigma, a scan that leaks across sequences, an off-by-one chunk, an optimizer
+step without bias correction, ...), builds it,
 swaps it in for the oracle's library, and requires that at least one of the pins the other
 oracle tests use rejects it. The real oracle passes all of them (tests/test_oracle_*.py).
 """
@@ -16,6 +17,7 @@ import pytest
 
 import oracle
 import test_oracle_generator as gen
+import test_oracle_optim as optim
 import test_oracle_steps as steps
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +74,9 @@ PINS_STEPS = [
     lambda: steps.test_head_ce_matches_torch_cross_entropy(97, 88, 9),
     steps.test_head_ce_sigma_zero_and_large_logits,
     gen.test_box_muller_at_special_angles,
+    lambda: optim.test_sgd_momentum_matches_torch(0.05, 0.9),
+    lambda: optim.test_adam_matches_torch(1e-2, 0.9, 0.999, 1e-8, 0.1),
+    optim.test_adam_first_step_and_weight_decay_closed_forms,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -112,6 +117,12 @@ MUTATIONS = [
     ("head chunk off by one", "if (j >= v0 && j < v0 + C)\n                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),\n                                                 (uint32_t)(tok0 + t), (uint64_t)j);\n                if (zj > m)",
      "if (j >= v0 && j <= v0 + C)\n                    zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + i),\n                                                 (uint32_t)(tok0 + t), (uint64_t)j);\n                if (zj > m)"),
     ("head clean loss drops max", "loss_clean[t] = m + log(s) - z[y];", "loss_clean[t] = log(s) - z[y];"),
+    ("sgd momentum dampened", "buf[i] = mu * buf[i] + g[i];", "buf[i] = mu * buf[i] + (1.0 - mu) * g[i];"),
+    ("adam without bias correction", "w[i] = w[i] - lr * (m[i] / bc1) / (sqrt(v[i] / bc2) + eps);",
+     "w[i] = w[i] - lr * m[i] / (sqrt(v[i]) + eps);"),
+    ("adam decay coupled to the gradient", "w[i] = w[i] * (1.0 - lr * wd);\n        m[i] = b1 * m[i] + (1.0 - b1) * g[i];",
+     "m[i] = b1 * m[i] + (1.0 - b1) * (g[i] + wd * w[i]);"),
+    ("adam eps inside the root", "(sqrt(v[i] / bc2) + eps)", "sqrt(v[i] / bc2 + eps)"),
 ]
 
 
