@@ -323,8 +323,8 @@ void dust_or_head_ce_at(const double *logits, const int32_t *targets, int64_t T,
 
 /* ---------------------------------------------------------------------------------------- */
 /* Optimizer steps that turn the estimate G into a weight update. The explainer names the two
- * used with Dust -- SGD with momentum at a constant learning rate (the ladders of the main
- * comparison) and Adam (the rerun of the 1M-token ladders, section "Gradients grow") -- and
+ * used with Dust in its section "Results" -- SGD with momentum at a constant learning rate
+ * (the ladders of the main comparison) and Adam (the rerun of the 1M-token ladders) -- and
  * prints neither formula, so these are the textbook ones, state updated in place:
  *   SGD with momentum (heavy ball, no dampening, as torch.optim.SGD):
  *       buf <- mu buf + g;  w <- w - lr buf

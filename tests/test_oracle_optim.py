@@ -1,7 +1,8 @@
 """Pins of the oracle's optimizer steps (CPU only).
 
-The explainer names the optimizers Dust's estimate was used with (SGD with momentum at a
-constant learning rate; Adam) without printing formulas, so the oracle states the textbook ones.
+The explainer's section "Results" names the optimizers Dust's estimate was used with (SGD with
+momentum at a constant learning rate; Adam) without printing formulas, so the oracle states the
+textbook ones.
 They are pinned here to torch.optim's implementations run in fp64 on the CPU (a library routine
 doing the same step), and to closed forms: with zero momentum SGD is w - lr g; Adam's first step
 from zero moments moves every weight by lr g / (|g| + eps), i.e. by about lr against the sign
