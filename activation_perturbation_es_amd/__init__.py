@@ -18,7 +18,7 @@ __all__ = [
     "DUST_OK", "DUST_ERR_INVALID", "DUST_ERR_UNSUPPORTED", "DUST_ERR_WORKSPACE", "DUST_ERR_HIP",
     "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DustError",
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
-    "dust_error_estimate", "dust_weight_grad_workspace", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
+    "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
     "dust_status_string", "dust_last_error", "library", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -44,6 +44,8 @@ _SIGNATURES = {
     "dust_loss_delta": (_int, [_int, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _vp]),
     "dust_reward_scan": (_int, [_vp, _vp, _i64, _i64, _i64, _f32, _vp]),
     "dust_loss_reward": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp]),
+    "dust_sgd_momentum": (_int, [_vp, _vp, _vp, _i64, _f32, _f32, _vp]),
+    "dust_adam": (_int, [_vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "dust_error_estimate": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                    _u32, _u32, _int, _vp]),
     "dust_weight_grad_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
@@ -125,6 +127,15 @@ def dust_loss_delta(mode, loss_clean, loss_pert, delta_o, g_o, io_dtype, c, Kc, 
 
 def dust_reward_scan(c, r, K, T, seg_len, gamma, stream=None):
     return _call("dust_reward_scan", _ptr(c), _ptr(r), K, T, seg_len, gamma, _stream(stream))
+
+
+def dust_sgd_momentum(w, g, buf, n, lr, momentum, stream=None):
+    return _call("dust_sgd_momentum", _ptr(w), _ptr(g), _ptr(buf), n, lr, momentum, _stream(stream))
+
+
+def dust_adam(w, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step, stream=None):
+    return _call("dust_adam", _ptr(w), _ptr(g), _ptr(m), _ptr(v), n, lr, beta1, beta2, eps,
+                 weight_decay, step, _stream(stream))
 
 
 def dust_loss_reward(loss_clean, loss_pert, r, K, T, seg_len, gamma, stream=None):

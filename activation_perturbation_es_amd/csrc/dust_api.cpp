@@ -311,6 +311,50 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
                       fn);
 }
 
+int dust_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr, float momentum,
+                      void *stream) {
+    const char *fn = "dust_sgd_momentum";
+    if (n < 0) return fail(DUST_ERR_INVALID, "%s: negative size n=%lld", fn, (long long)n);
+    if (!std::isfinite(lr) || !std::isfinite(momentum) || momentum < 0.f)
+        return fail(DUST_ERR_INVALID, "%s: lr and momentum must be finite, momentum >= 0", fn);
+    if (n == 0) return ok();
+    if (!w || !g || !buf) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(w, 4) || !elem_aligned(g, 4) || !elem_aligned(buf, 4))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+    if (n > ((int64_t)1 << 39)) return fail(DUST_ERR_UNSUPPORTED, "%s: n beyond 2^39", fn);
+    const size_t b = (size_t)n * 4;
+    if (ranges_overlap(w, b, g, b) || ranges_overlap(w, b, buf, b) || ranges_overlap(g, b, buf, b))
+        return fail(DUST_ERR_INVALID, "%s: w, g and buf overlap", fn);
+    return hip_status(dust::launch_sgd_momentum(w, g, buf, n, lr, momentum, (hipStream_t)stream),
+                      fn);
+}
+
+int dust_adam(float *w, const float *g, float *m, float *v, int64_t n, float lr, float beta1,
+              float beta2, float eps, float weight_decay, int64_t step, void *stream) {
+    const char *fn = "dust_adam";
+    if (n < 0) return fail(DUST_ERR_INVALID, "%s: negative size n=%lld", fn, (long long)n);
+    if (!(beta1 >= 0.f && beta1 < 1.f) || !(beta2 >= 0.f && beta2 < 1.f))
+        return fail(DUST_ERR_INVALID, "%s: betas must lie in [0, 1)", fn);
+    if (!(eps > 0.f) || !std::isfinite(eps) || !std::isfinite(lr) ||
+        !(weight_decay >= 0.f) || !std::isfinite(weight_decay))
+        return fail(DUST_ERR_INVALID, "%s: eps > 0, lr finite and weight_decay >= 0 required", fn);
+    if (step < 1) return fail(DUST_ERR_INVALID, "%s: step=%lld < 1", fn, (long long)step);
+    if (n == 0) return ok();
+    if (!w || !g || !m || !v) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(w, 4) || !elem_aligned(g, 4) || !elem_aligned(m, 4) || !elem_aligned(v, 4))
+        return fail(DUST_ERR_INVALID, "%s: pointers must be 4-byte aligned", fn);
+    if (n > ((int64_t)1 << 39)) return fail(DUST_ERR_UNSUPPORTED, "%s: n beyond 2^39", fn);
+    const size_t b = (size_t)n * 4;
+    const void *p[4] = {w, g, m, v};
+    for (int a = 0; a < 4; ++a)
+        for (int c = a + 1; c < 4; ++c)
+            if (ranges_overlap(p[a], b, p[c], b))
+                return fail(DUST_ERR_INVALID, "%s: w, g, m and v overlap", fn);
+    return hip_status(dust::launch_adam(w, g, m, v, n, lr, beta1, beta2, eps, weight_decay, step,
+                                        (hipStream_t)stream),
+                      fn);
+}
+
 int dust_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
                        float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
                        int64_t Kc, float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,

@@ -60,6 +60,13 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
 
 size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in);
 
+hipError_t launch_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr,
+                               float momentum, hipStream_t s);
+
+hipError_t launch_adam(float *w, const float *g, float *m, float *v, int64_t n, float lr,
+                       float beta1, float beta2, float eps, float weight_decay, int64_t step,
+                       hipStream_t s);
+
 hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, int64_t T,
                               int64_t d_out, int64_t d_in, void *workspace, hipStream_t s);
 

@@ -73,6 +73,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--optimizer", choices=("none", "sgd", "adam"), default="none",
+                    help="also apply the estimate to synthetic fp32 weights each step: SGD with "
+                         "momentum or Adam (not part of the estimate; off by default)")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -100,6 +103,31 @@ class Chain:
         self.c = synth.CONFIGS[cfg_id]
         self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
         self.fused = True   # loss mode: scores and rewards in one pass (dust_loss_reward)
+
+    # ---- optional optimizer step on the estimate (dust_sgd_momentum / dust_adam)
+    optimizer = "none"
+
+    def opt_setup(self):
+        if self.optimizer == "none":
+            return
+        n = self.G.numel()
+        self.W = self.f32(synth.normal_f32(synth.rng(self.cfg_id, 7), (n,), 0.02))
+        self.s1 = self.torch.zeros(n, dtype=self.torch.float32, device=self.dev)
+        self.s2 = self.torch.zeros(n, dtype=self.torch.float32, device=self.dev)
+        self.opt_t = 0
+
+    def opt_step(self, run, sh):
+        d, n = self.dust, self.G.numel()
+        if self.optimizer == "sgd":
+            run("dust_sgd_momentum", d.dust_sgd_momentum, self.W, self.G, self.s1, n, 0.01, 0.9, sh)
+        elif self.optimizer == "adam":
+            self.opt_t += 1
+            run("dust_adam", d.dust_adam, self.W, self.G, self.s1, self.s2, n, 1e-3, 0.9, 0.999,
+                1e-8, 0.0, self.opt_t, sh)
+
+    def opt_model(self):
+        n = self.G.numel()
+        return {"dust_sgd_momentum": _hbm(20.0 * n), "dust_adam": _hbm(28.0 * n)}
 
     def bf(self, bits):
         return self.torch.from_numpy(bits.view(np.int16)).to(self.dev).view(self.torch.bfloat16)
@@ -380,7 +408,15 @@ def main() -> int:
 
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
+    chain.optimizer = args.optimizer
     chain.setup()
+    chain.opt_setup()
+
+    def full_step(run):
+        chain.step(run, sh)
+        if chain.optimizer != "none":
+            chain.opt_step(run, sh)
+
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     events = []   # (kernel, start event, end event) inside the timed region
@@ -397,11 +433,11 @@ def main() -> int:
         events.append((name, e0, e1))
 
     for _ in range(args.warmup):
-        chain.step(plain, sh)
+        full_step(plain)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        chain.step(recorded, sh)
+        full_step(recorded)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
@@ -412,6 +448,7 @@ def main() -> int:
     for name, e0, e1 in events:
         per.setdefault(name, []).append(e0.elapsed_time(e1))
     model = chain.model()
+    model.update(chain.opt_model())
     kernels = {}
     for name, ms in per.items():
         bound, work, scale, peak, unit = model[name]
@@ -440,6 +477,8 @@ def main() -> int:
     cfg["parallelism"] = "single GPU"
     if args.workload != 4:
         cfg["loss_to_reward"] = "one kernel" if chain.fused else "two kernels"
+    if chain.optimizer != "none":
+        cfg["optimizer"] = chain.optimizer
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -456,8 +495,10 @@ def main() -> int:
 # device headers, and build.py fixes the compile flags.
 KERNEL_SOURCES = {
     "dust_noise_inject": "noise.hip", "dust_loss_delta": "delta_scan.hip",
-    "dust_reward_scan": "delta_scan.hip", "dust_loss_reward": "delta_scan.hip", "dust_error_estimate": "error_estimate.hip",
+    "dust_reward_scan": "delta_scan.hip", "dust_loss_reward": "delta_scan.hip",
+    "dust_error_estimate": "error_estimate.hip",
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
+    "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
 }
 
 

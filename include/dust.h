@@ -173,6 +173,33 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
                      void *stream);
 
 /*
+ * dust_sgd_momentum -- one SGD-with-momentum step on n fp32 weights, in place.
+ * The explainer's section "Results" trains with the estimate through SGD with momentum at a
+ * constant learning rate; the step is the textbook heavy ball without dampening:
+ *     buf <- momentum * buf + g;   w <- w - lr * buf
+ *   w    [n] fp32 weights                                                       (in/out)
+ *   g    [n] fp32 gradient estimate, e.g. dust_weight_grad's G                  (in)
+ *   buf  [n] fp32 momentum buffer, zero before the first step                   (in/out)
+ * lr and momentum finite, momentum >= 0. w, g and buf must not overlap. fp32 arithmetic.
+ */
+int dust_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr, float momentum,
+                      void *stream);
+
+/*
+ * dust_adam -- one Adam step (Kingma & Ba, ICLR 2015) with decoupled weight decay
+ * (Loshchilov & Hutter, ICLR 2019; weight_decay = 0 is plain Adam) on n fp32 weights, in place.
+ * The explainer's section "Results" reruns a comparison of Dust with Adam. At step t >= 1:
+ *     w <- w (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *     w <- w - lr (m / (1 - b1^t)) / (sqrt(v / (1 - b2^t)) + eps)
+ *   w, g, m, v  [n] fp32: weights (in/out), gradient estimate (in), first and second moments
+ *               (in/out; zero before step 1)
+ * 0 <= beta1, beta2 < 1; eps > 0; lr, weight_decay finite, weight_decay >= 0; step >= 1.
+ * No two arrays may overlap. fp32 arithmetic with the bias corrections formed in fp64.
+ */
+int dust_adam(float *w, const float *g, float *m, float *v, int64_t n, float lr, float beta1,
+              float beta2, float eps, float weight_decay, int64_t step, void *stream);
+
+/*
  * dust_head_ce_chunk -- perturbed per-token cross-entropy of the LM head for one vocabulary
  * chunk. Explainer, "The real work": the head is perturbed directly on cached logits and only
  * the cross-entropy involving one chunk of the vocabulary is recomputed. For draw i and token t

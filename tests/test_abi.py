@@ -108,6 +108,14 @@ INVALID = [
     # arrays whose byte size would overflow the size arithmetic
     ("dust_noise_inject", (FAKE, FAKE2, 1, (1 << 31) - 1, 4, 4, 0, (1 << 31) - 1, 0.1, 1, 1, 0, 0, None), 2, "2^62"),
     ("dust_loss_delta", (1, None, None, FAKE, FAKE2, 1, FAKE2 + 4096, (1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1, None), 2, "2^62"),
+    ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, 0.1, -0.5, None), 1, "momentum"),
+    ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, float("inf"), 0.9, None), 1, "finite"),
+    ("dust_sgd_momentum", (FAKE, FAKE, FAKE2 + 4096, 16, 0.1, 0.9, None), 1, "overlap"),
+    ("dust_sgd_momentum", (FAKE, FAKE2, None, 16, 0.1, 0.9, None), 1, "null"),
+    ("dust_adam", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, 16, 0.1, 1.0, 0.999, 1e-8, 0.0, 1, None), 1, "betas"),
+    ("dust_adam", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, 16, 0.1, 0.9, 0.999, 0.0, 0.0, 1, None), 1, "eps"),
+    ("dust_adam", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, 16, 0.1, 0.9, 0.999, 1e-8, 0.0, 0, None), 1, "step"),
+    ("dust_adam", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 4100, 16, 0.1, 0.9, 0.999, 1e-8, 0.0, 1, None), 1, "overlap"),
     ("dust_noise_words", (FAKE + 8, 1, 1, 1, 0, 1, 1, 0, 0, None), 1, "16-byte"),
     ("dust_noise_words", (FAKE, 1, 1, 2, 0xFFFFFFFF, 1, 1, 0, 0, None), 1, "2^32"),
 ]
@@ -128,6 +136,8 @@ ZERO_SIZE = [
     ("dust_loss_delta", (1, None, None, None, None, 1, None, 3, 0, 16, None)),
     ("dust_reward_scan", (None, None, 0, 10, 5, 0.5, None)),
     ("dust_loss_reward", (None, None, None, 0, 10, 5, 0.5, None)),
+    ("dust_sgd_momentum", (None, None, None, 0, 0.1, 0.9, None)),
+    ("dust_adam", (None, None, None, None, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, 1, None)),
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),
     ("dust_head_ce_chunk", (None, None, None, None, 0, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None)),
