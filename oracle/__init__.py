@@ -46,6 +46,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     """Declare the C signatures on a loaded oracle library."""
     lib.dust_or_philox4x32_10.argtypes = [ctypes.POINTER(_u32), ctypes.POINTER(_u32),
                                           ctypes.POINTER(_u32)]
+    lib.dust_or_attn_value_scores.argtypes = [_d, _d, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
+                                              _u64, _u32, _u32, _u32, _i64, _d]
     lib.dust_or_sgd_momentum.argtypes = [_d, _d, _d, _i64, ctypes.c_double, ctypes.c_double]
     lib.dust_or_adam.argtypes = [_d, _d, _d, _d, _i64, ctypes.c_double, ctypes.c_double,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64]
@@ -195,6 +197,20 @@ def loss_delta_inner(delta_o, g_o) -> np.ndarray:
     K, T, d = do.shape
     c = np.empty((K, T), dtype=np.float64)
     _load().dust_or_loss_delta_inner(_p(do), _p(go), K, T, d, _p(c))
+    return c
+
+
+def attn_value_scores(P, g_o, K: int, sigma: float, seed: int, tag: int, draw0: int = 0,
+                      tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """Scores c [K, T] of K draws perturbing an attention value projection (dust_oracle.c
+    states the formula): P [B, H, S, S] attention weights (query rows), g_o [T, H*dh]."""
+    Pd, gd = _f64(P), _f64(g_o)
+    B, H, S, _ = Pd.shape
+    T = B * S
+    dh = gd.shape[1] // H
+    c = np.empty((K, T), dtype=np.float64)
+    _load().dust_or_attn_value_scores(_p(Pd), _p(gd), K, B, H, S, dh, sigma, seed, tag, draw0,
+                                      tok0, chan0, _p(c))
     return c
 
 

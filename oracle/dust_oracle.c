@@ -186,6 +186,43 @@ void dust_or_loss_delta_inner(const double *delta_o, const double *g_o, int64_t 
 }
 
 /* ---------------------------------------------------------------------------------------- */
+/* Inner-product scores of a perturbed attention VALUE projection (explainer, "The real work":
+ * attention internals are scored through the attention output, by the inner product of the
+ * output's change with the output's estimated error). Perturbing the value projection's output,
+ * v'_s = v_s + sigma a_s, leaves the attention weights P of the clean forward unchanged (they
+ * come from queries and keys), so re-running head h's attention changes its output at query t
+ * by Delta o_t = sigma sum_{s <= t, same sequence} P^h_ts a^h_s, and the score is
+ *     c_t = -<Delta o_t, g_t>
+ *         = -sigma sum_h sum_{s <= t} P^h_ts sum_j a_{s, h dh + j} g_{t, h dh + j}.
+ * P [B, H, S, S] holds head h's weights of query row t over keys s (only s <= t is read),
+ * g [T, H dh] with T = B S; the noise of (token s, head h, column j) is channel chan0 + h dh + j
+ * of token tok0 + s in draw draw0 + i. */
+void dust_or_attn_value_scores(const double *P, const double *g, int64_t K, int64_t B, int64_t H,
+                               int64_t S, int64_t dh, double sigma, uint64_t seed, uint32_t tag,
+                               uint32_t draw0, uint32_t tok0, int64_t chan0, double *c)
+{
+    const int64_t T = B * S, d = H * dh;
+    #pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int64_t i = 0; i < K; ++i)
+        for (int64_t t = 0; t < T; ++t) {
+            const int64_t b = t / S, tl = t % S;
+            double acc = 0.0;
+            for (int64_t h = 0; h < H; ++h)
+                for (int64_t sl = 0; sl <= tl; ++sl) {
+                    const double p = P[((b * H + h) * S + tl) * S + sl];
+                    double dot = 0.0;
+                    for (int64_t j = 0; j < dh; ++j)
+                        dot += dust_or_normal(seed, tag, (uint32_t)(draw0 + i),
+                                              (uint32_t)(tok0 + b * S + sl),
+                                              (uint64_t)(chan0 + h * dh + j)) *
+                               g[t * d + h * dh + j];
+                    acc += p * dot;
+                }
+            c[i * T + t] = -sigma * acc;
+        }
+}
+
+/* ---------------------------------------------------------------------------------------- */
 /* Discounted reward r_t = sum_{s >= t, s in t's sequence} gamma^(s - t) c_s (explainer,
  * "Credit assignment"). Tokens are T = B * seg_len, sequence b owns [b*seg_len, (b+1)*seg_len).
  * Written as the backward recursion r_t = c_t + gamma r_{t+1}, r_last = c_last. */

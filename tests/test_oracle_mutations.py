@@ -16,6 +16,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_attn as attn
 import test_oracle_generator as gen
 import test_oracle_optim as optim
 import test_oracle_steps as steps
@@ -77,6 +78,10 @@ PINS_STEPS = [
     lambda: optim.test_sgd_momentum_matches_torch(0.05, 0.9),
     lambda: optim.test_adam_matches_torch(1e-2, 0.9, 0.999, 1e-8, 0.1),
     optim.test_adam_first_step_and_weight_decay_closed_forms,
+    lambda: attn.test_scores_equal_an_explicit_attention_rerun(2, 2, 16, 8, 3, 0, 0, 0),
+    lambda: attn.test_scores_equal_an_explicit_attention_rerun(1, 3, 24, 4, 2, 64, 5, 100),
+    attn.test_identity_attention_is_the_own_token_inner_product,
+    attn.test_linear_in_sigma_and_blind_above_the_diagonal,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -123,6 +128,11 @@ MUTATIONS = [
     ("adam decay coupled to the gradient", "w[i] = w[i] * (1.0 - lr * wd);\n        m[i] = b1 * m[i] + (1.0 - b1) * g[i];",
      "m[i] = b1 * m[i] + (1.0 - b1) * (g[i] + wd * w[i]);"),
     ("adam eps inside the root", "(sqrt(v[i] / bc2) + eps)", "sqrt(v[i] / bc2 + eps)"),
+    ("attention scores not causal", "for (int64_t sl = 0; sl <= tl; ++sl) {\n                    const double p = P[((b * H + h) * S + tl) * S + sl];",
+     "for (int64_t sl = 0; sl < S; ++sl) {\n                    const double p = P[((b * H + h) * S + tl) * S + sl];"),
+    ("attention noise at the query token", "(uint32_t)(tok0 + b * S + sl),\n                                              (uint64_t)(chan0 + h * dh + j))",
+     "(uint32_t)(tok0 + t),\n                                              (uint64_t)(chan0 + h * dh + j))"),
+    ("attention head offset dropped", "(uint64_t)(chan0 + h * dh + j)) *", "(uint64_t)(chan0 + j)) *"),
 ]
 
 
