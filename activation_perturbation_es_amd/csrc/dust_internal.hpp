@@ -60,6 +60,11 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
 
 size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in);
 
+hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float *c, int64_t Kc,
+                                    int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
+                                    float sigma, Key key, uint32_t draw0, uint32_t tok0,
+                                    hipStream_t s);
+
 hipError_t launch_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr,
                                float momentum, hipStream_t s);
 

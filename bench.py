@@ -499,6 +499,7 @@ KERNEL_SOURCES = {
     "dust_error_estimate": "error_estimate.hip",
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
+    "dust_attn_value_scores": "attn_scores.hip",
 }
 
 

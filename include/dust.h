@@ -173,6 +173,32 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
                      void *stream);
 
 /*
+ * dust_attn_value_scores -- loss change of K draws that perturb an attention VALUE projection,
+ * scored through the attention output (explainer, "The real work: suppressing interference":
+ * the inner product of the output's change with the output's estimated error):
+ *     c[i][t] = -<Delta o^{(i)}_t, g_o[t]>,  Delta o^{(i)}_t = sigma sum_{s <= t} P^h_ts a^h_s
+ * per head h. With v'_s = v_s + sigma a_s and the attention weights unchanged (they come from
+ * queries and keys), Delta o is exactly the change of the attention output a re-run with the
+ * perturbed values gives; the call computes the scores without forming Delta o. Use them as
+ * dust_loss_delta's inner-mode scores (dust_reward_scan, then dust_error_estimate with the
+ * same seed, tag, draw0, tok0 and chan0 and d = H * dh).
+ *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
+ *           keys s; only s <= t is read                                                 (in)
+ *   g_o     [B*S, H*dh] bf16 estimated error of the attention output, head h in columns
+ *           h*dh .. h*dh+dh-1                                                           (in)
+ *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
+ * The noise a of (token s, head h, column j) is channel chan0 + h*dh + j of token tok0 + s
+ * (the value projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
+ * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P 8-byte
+ * and g_o 16-byte aligned; sigma finite. c must not overlap P or g_o. fp32 accumulation; the
+ * noise enters the bf16 matrix cores as a high part plus a remainder (16 significant bits).
+ */
+int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc, int64_t B,
+                           int64_t H, int64_t S, int64_t dh, int64_t chan0, float sigma,
+                           uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                           void *stream);
+
+/*
  * dust_sgd_momentum -- one SGD-with-momentum step on n fp32 weights, in place.
  * The explainer's section "Results" trains with the estimate through SGD with momentum at a
  * constant learning rate; the step is the textbook heavy ball without dampening:

@@ -108,6 +108,12 @@ INVALID = [
     # arrays whose byte size would overflow the size arithmetic
     ("dust_noise_inject", (FAKE, FAKE2, 1, (1 << 31) - 1, 4, 4, 0, (1 << 31) - 1, 0.1, 1, 1, 0, 0, None), 2, "2^62"),
     ("dust_loss_delta", (1, None, None, FAKE, FAKE2, 1, FAKE2 + 4096, (1 << 31) - 1, (1 << 31) - 1, (1 << 31) - 1, None), 2, "2^62"),
+    ("dust_attn_value_scores", (FAKE, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 48, 16, 0, 0.01, 1, 1, 0, 0, None), 2, "multiple of 32"),
+    ("dust_attn_value_scores", (FAKE, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 24, 0, 0.01, 1, 1, 0, 0, None), 2, "multiple of 16"),
+    ("dust_attn_value_scores", (FAKE, FAKE2 + 8, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "aligned"),
+    ("dust_attn_value_scores", (FAKE, FAKE2, FAKE, 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "overlap"),
+    ("dust_attn_value_scores", (None, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "null"),
+    ("dust_attn_value_scores", (FAKE, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 2, 0.01, 1, 1, 0, 0, None), 1, "chan0"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, 0.1, -0.5, None), 1, "momentum"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, float("inf"), 0.9, None), 1, "finite"),
     ("dust_sgd_momentum", (FAKE, FAKE, FAKE2 + 4096, 16, 0.1, 0.9, None), 1, "overlap"),
@@ -137,6 +143,7 @@ ZERO_SIZE = [
     ("dust_reward_scan", (None, None, 0, 10, 5, 0.5, None)),
     ("dust_loss_reward", (None, None, None, 0, 10, 5, 0.5, None)),
     ("dust_sgd_momentum", (None, None, None, 0, 0.1, 0.9, None)),
+    ("dust_attn_value_scores", (None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None)),
     ("dust_adam", (None, None, None, None, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, 1, None)),
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),

@@ -1,0 +1,76 @@
+"""GPU parity of dust_attn_value_scores with the oracle (MI355X only).
+
+The scores c = -<Delta o, g_o> of a perturbed attention value projection, computed on the
+device without forming Delta o, are compared with the oracle's fp64 sum element by element at
+sizes the oracle finishes in seconds: several 32-key and 32-query tiles, several heads, all
+supported head widths' layouts (dh = 16 .. 128), ragged draw groups (the device runs four
+draws per block), channel, draw and token offsets, and weights above the diagonal that must be
+ignored. Tolerance: relative Frobenius 1e-5, the bar of the inner-mode scores (the noise enters
+the bf16 matrix cores as a high part plus a bf16 remainder, about 2^-17 relative). With
+identity attention the call must agree with the inner-mode loss change of sigma a computed by
+two other entry points (dust_noise_inject into zeros, then dust_loss_delta).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DEV, announce, bf16, bits_to_f64, dust, f32, frob_rel, host_f32, rne_bf16_bits_of_f32
+
+pytestmark = pytest.mark.gpu
+
+
+def _causal_weights(g, B, H, S, garbage_above=False):
+    z = g.standard_normal((B, H, S, S)) * 2.0
+    mask = np.tril(np.ones((S, S), dtype=bool))
+    p = np.exp(np.where(mask, z, -np.inf) - np.where(mask, z, -np.inf).max(-1, keepdims=True))
+    p = p / p.sum(-1, keepdims=True)
+    if garbage_above:
+        p = p + np.triu(np.abs(g.standard_normal((S, S))), 1)[None, None]
+    return p
+
+
+@pytest.mark.parametrize("B,H,S,dh,Kc,chan0,draw0,tok0,garbage", [
+    (2, 2, 32, 16, 5, 0, 3, 7, False),       # one tile, ragged draw group
+    (1, 3, 64, 32, 6, 64, 0, 0, True),       # channel offset, weights above the diagonal
+    (2, 2, 128, 64, 3, 0, 11, 1000, False),  # 4 x 4 tiles, the workload's head width
+    (1, 1, 96, 128, 9, 8, 2, 5, True),       # widest heads, three groups of draws
+    (1, 4, 64, 48, 4, 4, 0, 0, False),       # three k-slices
+])
+def test_attn_value_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage):
+    announce("attn value scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage),))
+    g = np.random.default_rng(70)
+    T, d, sigma, seed, tag = B * S, H * dh, 0.02, 0xA77E, 6
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
+    gbits = rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32))
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_value_scores(bf16(Pbits), bf16(gbits), c, Kc, B, H, S, dh, chan0, sigma, seed, tag,
+                                draw0, tok0)
+    ref = oracle.attn_value_scores(bits_to_f64(Pbits), bits_to_f64(gbits), Kc, sigma, seed, tag,
+                                   draw0, tok0, chan0)
+    assert frob_rel(host_f32(c), ref) <= 1e-5
+
+
+def test_identity_attention_equals_inner_mode_of_injected_noise():
+    announce("attn value scores vs inject + inner mode")
+    B, H, S, dh, Kc, sigma, seed, tag = 2, 4, 64, 32, 6, 0.05, 77, 9
+    T, d = B * S, H * dh
+    g = np.random.default_rng(71)
+    P = np.broadcast_to(np.eye(S, dtype=np.float32), (B, H, S, S)).copy()
+    gbits = rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32))
+    c = torch.empty((Kc, T), dtype=torch.float32, device=DEV)
+    dust.dust_attn_value_scores(bf16(rne_bf16_bits_of_f32(P)), bf16(gbits), c, Kc, B, H, S, dh, 0,
+                                sigma, seed, tag, 0, 0)
+    zeros = torch.zeros((T, d), dtype=torch.float32, device=DEV)
+    do = torch.empty((Kc, T, d), dtype=torch.float32, device=DEV)      # sigma a
+    dust.dust_noise_inject(zeros, do, dust.DUST_F32, T, d, d, 0, Kc, sigma, seed, tag, 0, 0)
+    c2 = torch.empty((Kc, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_delta(dust.DUST_DELTA_INNER, None, None, do, f32(bits_to_f64(gbits)), dust.DUST_F32,
+                         c2, Kc, T, d)
+    assert frob_rel(host_f32(c), host_f32(c2).astype(np.float64)) <= 1e-5
+
+
+def test_attn_value_scores_zero_draws_touch_nothing():
+    c = torch.full((2, 64), 5.0, device=DEV)
+    dust.dust_attn_value_scores(None, None, c, 0, 2, 2, 32, 16, 0, 0.01, 1, 1, 0, 0)
+    assert torch.all(c == 5.0)
