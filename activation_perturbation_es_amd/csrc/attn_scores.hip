@@ -33,86 +33,166 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// LDS row pitches (bytes): 32 keys of P plus 8 bytes and DH columns of g plus 16 bytes, so that
+// the fragment reads of 32 consecutive rows fall into distinct banks.
+constexpr uint32_t kPPitch = 72;
+__host__ __device__ constexpr uint32_t g_pitch(int KS) { return 32u * KS + 16u; }
+__host__ __device__ constexpr uint32_t stage_bytes(int KS) { return 32u * (kPPitch + g_pitch(KS)); }
+
 // KS k-slices of 16 head columns: head width dh = 16 KS.
 template <int KS>
 __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ g, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t chan0, float scale, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
-    extern __shared__ float c_lds[];   // [4][S] running scores, one row per wave
+    // LDS: two stages of one step's operands (P tile [32 queries][32 keys], g tile
+    // [32 queries][DH]), then per wave two rows of S running scores (lanes 0-31 and 32-63 hold
+    // different key rows of a tile, so each half keeps its own partial sums).
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr uint32_t DH = 16u * KS;
+    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS);
+    const uint32_t tid = threadIdx.x;
     const uint32_t wave = wave_in_block();
-    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
     const uint32_t i = (blockIdx.x % ndg) * 4u + wave;   // this wave's draw (local index)
-    if (i >= Kc) return;
-    float *cw = c_lds + (uint64_t)wave * S;
-    for (uint32_t t = lane; t < S; t += 64u) cw[t] = 0.f;
-
-    constexpr uint32_t DH = 16u * KS;
-    const uint32_t d = H * DH;
+    // a wave past the last draw still loads and synchronises with the others; it writes nothing
+    const bool active = i < Kc;
+    const uint32_t draw = draw0 + (active ? i : Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
-    const uint32_t draw = draw0 + i;
+    float *cw = (float *)(lds + 2u * SB) + (uint64_t)wave * 2u * S;
+    for (uint32_t t = lane; t < 2u * S; t += 64u) cw[t] = 0.f;
+    float *cwh = cw + half * S;
+
+    const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
-    for (uint32_t h = 0; h < H; ++h) {
-        const uint16_t *Ph = P + ((uint64_t)b * H + h) * S * S;
-        for (uint32_t kt = 0; kt < nt; ++kt) {
-            // A operand: the noise of key 32 kt + col at head columns 16 ks + 8 half .. + 7,
-            // as a bf16 high part and a bf16 remainder (scaled by kNormalScale in the end)
-            bf16x8 ahi[KS], alo[KS];
-            const uint32_t token = tok0 + b * S + kt * 32u + col;
+
+    // Global -> registers -> LDS staging of one step's tiles, coalesced: P rows are 64 bytes
+    // (4 pieces of 16), g rows DH * 2 bytes (2 KS pieces).
+    constexpr uint32_t NPC = 128u + 64u * KS;            // 16-byte pieces per step
+    constexpr uint32_t PPT = (NPC + 255u) / 256u;        // pieces per thread
+    u32x4 stg[PPT];
+    auto gload = [&](uint32_t h, uint32_t kt, uint32_t ct) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint32_t q = (chan0 + h * DH + 16u * ks + 8u * half) / 4u;
-                Polar pa[2], pb[2];   // channels 4q .. 4q+3 and 4q+4 .. 4q+7
-                noise4_polar<false>(key, q, token, draw, pa);
-                noise4_polar<false>(key, q + 1u, token, draw, pb);
-                const Polar *pp[4] = {&pa[0], &pa[1], &pb[0], &pb[1]};
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float x0 = pp[e]->rho * pp[e]->c, x1 = pp[e]->rho * pp[e]->s;
-                    hw[e] = pack_bf16x2(x0, x1);
-                    lw[e] = pack_bf16x2(x0 - __uint_as_float(hw[e] << 16),
-                                        x1 - __uint_as_float(hw[e] & 0xFFFF0000u));
-                }
-                ahi[ks] = as_bf16x8(hw);
-                alo[ks] = as_bf16x8(lw);
-            }
-            for (uint32_t ct = kt; ct < nt; ++ct) {
-                const uint32_t t = ct * 32u + col;   // this lane's query (within the sequence)
-                // B operand: g of query t at the same head columns
-                const uint16_t *grow = g + ((uint64_t)b * S + t) * d + h * DH + 8u * half;
-                f32x16 e = {};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 gb = *(const bf16x8 *)(grow + 16u * ks);
-                    e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], gb, e, 0, 0, 0);
-                    e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], gb, e, 0, 0, 0);
-                }
-                // e[4 q + r] is key row 8 q + 4 half + r of the tile; weight by P and sum
-                const uint16_t *prow = Ph + (uint64_t)t * S + kt * 32u + 4u * half;
-                float part = 0.f;
-#pragma unroll
-                for (int qd = 0; qd < 4; ++qd) {
-                    const uint2 pw = *(const uint2 *)(prow + 8u * qd);
-                    const float pv[4] = {__uint_as_float(pw.x << 16),
-                                         __uint_as_float(pw.x & 0xFFFF0000u),
-                                         __uint_as_float(pw.y << 16),
-                                         __uint_as_float(pw.y & 0xFFFF0000u)};
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const uint32_t krow = 8u * qd + 4u * half + r;
-                        const float wgt = (ct == kt && krow > col) ? 0.f : pv[r];   // keys after t
-                        part = __builtin_fmaf(wgt, e[4 * qd + r], part);
-                    }
-                }
-                part += __shfl_xor(part, 32);
-                if (half == 0) cw[t] += part;
+        for (uint32_t j = 0; j < PPT; ++j) {
+            const uint32_t pc = tid + 256u * j;
+            if (pc < 128u) {
+                const uint32_t row = pc >> 2, seg = pc & 3u;
+                stg[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + ct * 32u + row) * S +
+                                          kt * 32u + 8u * seg);
+            } else if (pc < NPC) {
+                const uint32_t q = pc - 128u, row = q / (2u * KS), seg = q % (2u * KS);
+                stg[j] = *(const u32x4 *)(g + ((uint64_t)b * S + ct * 32u + row) * d + h * DH +
+                                          8u * seg);
             }
         }
+    };
+    auto lstore = [&](uint32_t st) {
+        unsigned char *base = lds + st * SB;
+#pragma unroll
+        for (uint32_t j = 0; j < PPT; ++j) {
+            const uint32_t pc = tid + 256u * j;
+            if (pc < 128u) {
+                const uint32_t row = pc >> 2, seg = pc & 3u;
+                uint2 *dst = (uint2 *)(base + row * kPPitch + 16u * seg);   // 8-byte aligned
+                dst[0] = make_uint2(stg[j][0], stg[j][1]);
+                dst[1] = make_uint2(stg[j][2], stg[j][3]);
+            } else if (pc < NPC) {
+                const uint32_t q = pc - 128u, row = q / (2u * KS), seg = q % (2u * KS);
+                *(u32x4 *)(base + 32u * kPPitch + row * GP + 16u * seg) = stg[j];
+            }
+        }
+    };
+
+    // A operand: the noise of key 32 kt + col at head columns 16 ks + 8 half .. + 7, as a bf16
+    // high part and a bf16 remainder (kNormalScale is applied to the final score)
+    bf16x8 ahi[KS], alo[KS];
+    auto noise = [&](uint32_t h, uint32_t kt) {
+        const uint32_t token = tok0 + b * S + kt * 32u + col;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint32_t q = (chan0 + h * DH + 16u * ks + 8u * half) / 4u;
+            Polar pa[2], pb[2];   // channels 4q .. 4q+3 and 4q+4 .. 4q+7
+            noise4_polar<false>(key, q, token, draw, pa);
+            noise4_polar<false>(key, q + 1u, token, draw, pb);
+            const Polar *pp[4] = {&pa[0], &pa[1], &pb[0], &pb[1]};
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float x0 = pp[e]->rho * pp[e]->c, x1 = pp[e]->rho * pp[e]->s;
+                hw[e] = pack_bf16x2(x0, x1);
+                lw[e] = pack_bf16x2(x0 - __uint_as_float(hw[e] << 16),
+                                    x1 - __uint_as_float(hw[e] & 0xFFFF0000u));
+            }
+            ahi[ks] = as_bf16x8(hw);
+            alo[ks] = as_bf16x8(lw);
+        }
+    };
+
+    // Steps in the order head, key tile, query tile >= key tile. Step n's tiles are in LDS
+    // stage n % 2; step n + 1's are fetched into registers at the start of step n and stored
+    // to the other stage at its end, before the one barrier per step.
+    uint32_t h = 0, kt = 0, ct = 0;
+    gload(0, 0, 0);
+    lstore(0);
+    noise(0, 0);
+    __syncthreads();
+    for (uint32_t st = 0;; st ^= 1u) {
+        uint32_t nh = h, nk = kt, nc = ct + 1u;
+        if (nc == nt) {
+            nk = kt + 1u;
+            nc = nk;
+            if (nk == nt) { nh = h + 1u; nk = 0; nc = 0; }
+        }
+        const bool more = nh < H;   // uniform across the block
+        if (more) gload(nh, nk, nc);
+
+        const unsigned char *base = lds + st * SB;
+        const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
+        f32x16 e = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 gb = *(const bf16x8 *)(grow + 32u * ks);
+            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], gb, e, 0, 0, 0);
+            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], gb, e, 0, 0, 0);
+        }
+        // e[4 qd + r] is key row 8 qd + 4 half + r of the tile: weight by P and sum
+        const unsigned char *prow = base + col * kPPitch + 8u * half;
+        float part = 0.f;
+        if (ct != kt) {
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const uint2 w = *(const uint2 *)(prow + 16u * qd);
+                part = __builtin_fmaf(__uint_as_float(w.x << 16), e[4 * qd + 0], part);
+                part = __builtin_fmaf(__uint_as_float(w.x & 0xFFFF0000u), e[4 * qd + 1], part);
+                part = __builtin_fmaf(__uint_as_float(w.y << 16), e[4 * qd + 2], part);
+                part = __builtin_fmaf(__uint_as_float(w.y & 0xFFFF0000u), e[4 * qd + 3], part);
+            }
+        } else {   // diagonal tile: keys after the lane's query do not count
+#pragma unroll
+            for (int qd = 0; qd < 4; ++qd) {
+                const uint2 w = *(const uint2 *)(prow + 16u * qd);
+                const float pv[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
+                                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t krow = 8u * qd + 4u * half + r;
+                    part = __builtin_fmaf(krow <= col ? pv[r] : 0.f, e[4 * qd + r], part);
+                }
+            }
+        }
+        cwh[ct * 32u + col] += part;
+        if (!more) break;
+        lstore(st ^ 1u);
+        if (nk != kt || nh != h) noise(nh, nk);
+        __syncthreads();
+        h = nh;
+        kt = nk;
+        ct = nc;
     }
+    if (!active) return;
     float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
-    for (uint32_t t = lane; t < S; t += 64u) cr[t] = scale * cw[t];
+    for (uint32_t t = lane; t < S; t += 64u) cr[t] = scale * (cw[t] + cw[S + t]);
 }
 
 }  // namespace
@@ -123,11 +203,11 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
                                     hipStream_t s) {
     const uint32_t ndg = (uint32_t)((Kc + 3) / 4);
     const uint32_t blocks = (uint32_t)(B * ndg);
-    const size_t lds = (size_t)4 * S * sizeof(float);
+    const size_t cbytes = (size_t)8 * S * sizeof(float);
     // the noise comes divided by kNormalScale; the score carries -sigma
     const float scale = (float)(-(double)sigma * kNormalScale);
 #define DUST_AVS(KS)                                                                           \
-    attn_value_scores_kernel<KS><<<blocks, 256, lds, s>>>(                                     \
+    attn_value_scores_kernel<KS><<<blocks, 256, 2 * stage_bytes(KS) + cbytes, s>>>(           \
         P, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, (uint32_t)chan0,   \
         scale, key, draw0, tok0, ndg)
     switch (dh / 16) {

@@ -36,6 +36,7 @@ def _causal_weights(g, B, H, S, garbage_above=False):
     (2, 2, 128, 64, 3, 0, 11, 1000, False),  # 4 x 4 tiles, the workload's head width
     (1, 1, 96, 128, 9, 8, 2, 5, True),       # widest heads, three groups of draws
     (1, 4, 64, 48, 4, 4, 0, 0, False),       # three k-slices
+    (1, 1, 2048, 16, 2, 0, 0, 0, False),     # long sequence: more than 64 KB of LDS per block
 ])
 def test_attn_value_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage):
     announce("attn value scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage),))
