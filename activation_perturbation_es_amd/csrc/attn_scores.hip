@@ -33,9 +33,9 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS row pitches (bytes): 32 keys of P plus 8 bytes and DH columns of g plus 16 bytes, so that
-// the fragment reads of 32 consecutive rows fall into distinct banks.
-constexpr uint32_t kPPitch = 72;
+// LDS row pitches (bytes): 32 keys of P as fp32 plus 16 bytes and DH bf16 columns of g plus
+// 16 bytes, so that the 16-byte fragment reads of 16 consecutive rows fall into distinct banks.
+constexpr uint32_t kPPitch = 144;
 __host__ __device__ constexpr uint32_t g_pitch(int KS) { return 32u * KS + 16u; }
 __host__ __device__ constexpr uint32_t stage_bytes(int KS) { return 32u * (kPPitch + g_pitch(KS)); }
 
@@ -92,11 +92,14 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 #pragma unroll
         for (uint32_t j = 0; j < PPT; ++j) {
             const uint32_t pc = tid + 256u * j;
-            if (pc < 128u) {
+            if (pc < 128u) {   // 8 weights, widened to fp32 once here for all four draws
                 const uint32_t row = pc >> 2, seg = pc & 3u;
-                uint2 *dst = (uint2 *)(base + row * kPPitch + 16u * seg);   // 8-byte aligned
-                dst[0] = make_uint2(stg[j][0], stg[j][1]);
-                dst[1] = make_uint2(stg[j][2], stg[j][3]);
+                f32x4 *dst = (f32x4 *)(base + row * kPPitch + 32u * seg);
+                const u32x4 w = stg[j];
+                dst[0] = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                               __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+                dst[1] = f32x4{__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                               __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u)};
             } else if (pc < NPC) {
                 const uint32_t q = pc - 128u, row = q / (2u * KS), seg = q % (2u * KS);
                 *(u32x4 *)(base + 32u * kPPitch + row * GP + 16u * seg) = stg[j];
@@ -157,27 +160,23 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
             e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], gb, e, 0, 0, 0);
         }
         // e[4 qd + r] is key row 8 qd + 4 half + r of the tile: weight by P and sum
-        const unsigned char *prow = base + col * kPPitch + 8u * half;
+        const unsigned char *prow = base + col * kPPitch + 16u * half;
         float part = 0.f;
         if (ct != kt) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const uint2 w = *(const uint2 *)(prow + 16u * qd);
-                part = __builtin_fmaf(__uint_as_float(w.x << 16), e[4 * qd + 0], part);
-                part = __builtin_fmaf(__uint_as_float(w.x & 0xFFFF0000u), e[4 * qd + 1], part);
-                part = __builtin_fmaf(__uint_as_float(w.y << 16), e[4 * qd + 2], part);
-                part = __builtin_fmaf(__uint_as_float(w.y & 0xFFFF0000u), e[4 * qd + 3], part);
+                const f32x4 w = *(const f32x4 *)(prow + 32u * qd);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) part = __builtin_fmaf(w[r], e[4 * qd + r], part);
             }
         } else {   // diagonal tile: keys after the lane's query do not count
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
-                const uint2 w = *(const uint2 *)(prow + 16u * qd);
-                const float pv[4] = {__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xFFFF0000u),
-                                     __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xFFFF0000u)};
+                const f32x4 w = *(const f32x4 *)(prow + 32u * qd);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t krow = 8u * qd + 4u * half + r;
-                    part = __builtin_fmaf(krow <= col ? pv[r] : 0.f, e[4 * qd + r], part);
+                    part = __builtin_fmaf(krow <= col ? w[r] : 0.f, e[4 * qd + r], part);
                 }
             }
         }
