@@ -55,11 +55,12 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    const uint32_t i = (blockIdx.x % ndg) * 4u + wave;   // this wave's draw (local index)
-    // a wave past the last draw still loads and synchronises with the others; it writes nothing
-    const bool active = i < Kc;
-    const uint32_t draw = draw0 + (active ? i : Kc - 1u);
+    // this wave's two draws (local indices i0, i0 + 1); a draw past the last one is computed
+    // with the last draw's noise and not written, so every wave loads and synchronises
+    const uint32_t i0 = (blockIdx.x % ndg) * 8u + wave * 2u;
+    const uint32_t drawA = draw0 + min(i0, Kc - 1u), drawB = draw0 + min(i0 + 1u, Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
+    // running scores of the two draws: lanes 0-31 add draw i0's, lanes 32-63 draw i0 + 1's
     float *cw = (float *)(lds + 2u * SB) + (uint64_t)wave * 2u * S;
     for (uint32_t t = lane; t < 2u * S; t += 64u) cw[t] = 0.f;
     float *cwh = cw + half * S;
@@ -109,8 +110,9 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 
     // A operand: the noise of key 32 kt + col at head columns 16 ks + 8 half .. + 7, as a bf16
     // high part and a bf16 remainder (kNormalScale is applied to the final score)
-    bf16x8 ahi[KS], alo[KS];
-    auto noise = [&](uint32_t h, uint32_t kt) {
+    bf16x8 ahiA[KS], aloA[KS], ahiB[KS], aloB[KS];
+    auto noise = [&](uint32_t h, uint32_t kt, uint32_t draw, bf16x8 (&ahi)[KS],
+                     bf16x8 (&alo)[KS]) {
         const uint32_t token = tok0 + b * S + kt * 32u + col;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -138,7 +140,8 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     uint32_t h = 0, kt = 0, ct = 0;
     gload(0, 0, 0);
     lstore(0);
-    noise(0, 0);
+    noise(0, 0, drawA, ahiA, aloA);
+    noise(0, 0, drawB, ahiB, aloB);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         uint32_t nh = h, nk = kt, nc = ct + 1u;
@@ -152,22 +155,30 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
-        f32x16 e = {};
+        bf16x8 gb[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) gb[ks] = *(const bf16x8 *)(grow + 32u * ks);
+        // two independent accumulation chains, one per draw
+        f32x16 eA = {}, eB = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 gb = *(const bf16x8 *)(grow + 32u * ks);
-            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], gb, e, 0, 0, 0);
-            e = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], gb, e, 0, 0, 0);
+            eA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahiA[ks], gb[ks], eA, 0, 0, 0);
+            eB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahiB[ks], gb[ks], eB, 0, 0, 0);
+            eA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aloA[ks], gb[ks], eA, 0, 0, 0);
+            eB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aloB[ks], gb[ks], eB, 0, 0, 0);
         }
         // e[4 qd + r] is key row 8 qd + 4 half + r of the tile: weight by P and sum
         const unsigned char *prow = base + col * kPPitch + 16u * half;
-        float part = 0.f;
+        float partA = 0.f, partB = 0.f;
         if (ct != kt) {
 #pragma unroll
             for (int qd = 0; qd < 4; ++qd) {
                 const f32x4 w = *(const f32x4 *)(prow + 32u * qd);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) part = __builtin_fmaf(w[r], e[4 * qd + r], part);
+                for (int r = 0; r < 4; ++r) {
+                    partA = __builtin_fmaf(w[r], eA[4 * qd + r], partA);
+                    partB = __builtin_fmaf(w[r], eB[4 * qd + r], partB);
+                }
             }
         } else {   // diagonal tile: keys after the lane's query do not count
 #pragma unroll
@@ -176,22 +187,34 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const uint32_t krow = 8u * qd + 4u * half + r;
-                    part = __builtin_fmaf(krow <= col ? w[r] : 0.f, e[4 * qd + r], part);
+                    const float wr = krow <= col ? w[r] : 0.f;
+                    partA = __builtin_fmaf(wr, eA[4 * qd + r], partA);
+                    partB = __builtin_fmaf(wr, eB[4 * qd + r], partB);
                 }
             }
         }
-        cwh[ct * 32u + col] += part;
+        // Swap the upper half of partA with the lower half of partB: afterwards lanes 0-31
+        // hold both halves of draw A's key rows, lanes 32-63 both halves of draw B's.
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(partA),
+                                                         __float_as_uint(partB), false, false);
+        cwh[ct * 32u + col] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (!more) break;
         lstore(st ^ 1u);
-        if (nk != kt || nh != h) noise(nh, nk);
+        if (nk != kt || nh != h) {
+            noise(nh, nk, drawA, ahiA, aloA);
+            noise(nh, nk, drawB, ahiB, aloB);
+        }
         __syncthreads();
         h = nh;
         kt = nk;
         ct = nc;
     }
-    if (!active) return;
-    float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
-    for (uint32_t t = lane; t < S; t += 64u) cr[t] = scale * (cw[t] + cw[S + t]);
+#pragma unroll
+    for (uint32_t k = 0; k < 2u; ++k) {
+        if (i0 + k >= Kc) break;
+        float *cr = c + (uint64_t)(i0 + k) * T + (uint64_t)b * S;
+        for (uint32_t t = lane; t < S; t += 64u) cr[t] = scale * cw[k * S + t];
+    }
 }
 
 }  // namespace
@@ -200,9 +223,9 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
                                     int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
                                     float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s) {
-    const uint32_t ndg = (uint32_t)((Kc + 3) / 4);
+    const uint32_t ndg = (uint32_t)((Kc + 7) / 8);   // blocks of 8 draws, 2 per wave
     const uint32_t blocks = (uint32_t)(B * ndg);
-    const size_t cbytes = (size_t)8 * S * sizeof(float);
+    const size_t cbytes = (size_t)8 * S * sizeof(float);   // 4 waves x 2 draws x S scores
     // the noise comes divided by kNormalScale; the score carries -sigma
     const float scale = (float)(-(double)sigma * kNormalScale);
 #define DUST_AVS(KS)                                                                           \
