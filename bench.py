@@ -76,6 +76,10 @@ def parse():
     ap.add_argument("--optimizer", choices=("none", "sgd", "adam"), default="none",
                     help="also apply the estimate to synthetic fp32 weights each step: SGD with "
                          "momentum or Adam (not part of the estimate; off by default)")
+    ap.add_argument("--attention-values", action="store_true",
+                    help="workload 4: score by re-running the attention with perturbed values "
+                         "(dust_attn_value_scores on synthetic attention weights, 8 heads of 64) "
+                         "instead of streaming a synthetic attention-output change")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -309,14 +313,24 @@ class InnerChain(Chain):
         self.gobits = synth.normal_bf16(g, (self.T, self.d))
         self.xbits = synth.normal_bf16(g, (self.T, self.d))
         self.go, self.x = self.bf(self.gobits), self.bf(self.xbits)
-        # One 512-draw block of the synthetic attention-output change, drawn on the device before
-        # timing; every block of the timed step streams this buffer (the kernel's work does not
-        # depend on the values).
-        zero = self.torch.zeros((self.T, self.d), dtype=t.bfloat16, device=self.dev)
-        self.do = self.empty((self.KB, self.T, self.d), t.bfloat16)
-        self.dust.dust_noise_inject(zero, self.do, self.dust.DUST_BF16, self.T, self.d, self.d, 0,
-                                    self.KB, self.std, self.seed, synth.DELTA_O_TAG, 0, 0)
-        del zero
+        if self.attn_values:
+            # attention weights of the clean forward: a causal softmax of N(0, 1) scores per
+            # head and sequence, drawn on the device from a seeded generator before timing
+            B, S, H = self.T // self.S, self.S, self.HEADS
+            gen = t.Generator(device=self.dev).manual_seed(7000 + self.cfg_id)
+            z = t.randn((B, H, S, S), generator=gen, device=self.dev)
+            z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
+            self.P = t.softmax(z, -1).to(t.bfloat16)
+            del z
+        else:
+            # One 512-draw block of the synthetic attention-output change, drawn on the device
+            # before timing; every block of the timed step streams this buffer (the kernel's work
+            # does not depend on the values).
+            zero = self.torch.zeros((self.T, self.d), dtype=t.bfloat16, device=self.dev)
+            self.do = self.empty((self.KB, self.T, self.d), t.bfloat16)
+            self.dust.dust_noise_inject(zero, self.do, self.dust.DUST_BF16, self.T, self.d, self.d,
+                                        0, self.KB, self.std, self.seed, synth.DELTA_O_TAG, 0, 0)
+            del zero
         self.cbuf = self.empty((self.K, self.T), t.float32)
         self.gh = self.empty((self.T, self.d), t.float32)
         self.ght = self.empty((self.d, self.T), t.bfloat16)
@@ -324,11 +338,19 @@ class InnerChain(Chain):
         self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d, self.d)
         self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
 
+    attn_values = False
+    HEADS = 8
+
     def step(self, run, sh):
         d, T, K, KB = self.dust, self.T, self.K, self.KB
-        for blk in range(K // KB):
-            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do, self.go,
-                d.DUST_BF16, self.cbuf[blk * KB:(blk + 1) * KB], KB, T, self.d, sh)
+        if self.attn_values:
+            run("dust_attn_value_scores", d.dust_attn_value_scores, self.P, self.go, self.cbuf, K,
+                T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma, self.seed,
+                self.tag, 0, 0, sh)
+        else:
+            for blk in range(K // KB):
+                run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do,
+                    self.go, d.DUST_BF16, self.cbuf[blk * KB:(blk + 1) * KB], KB, T, self.d, sh)
         run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S, self.gamma, sh)
         run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K, T, self.d,
             0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
@@ -340,20 +362,33 @@ class InnerChain(Chain):
 
     def model(self):
         T, K, d = self.T, self.K, self.d
+        S, H = self.S, self.HEADS
         return {
             "dust_loss_delta": _hbm(self.KB * T * (2.0 * d + 4.0) + 2.0 * T * d),
+            # the key-query inner products over the causal triangle: 2 (S (S + 1) / 2) dh flops
+            # per draw, head and sequence
+            "dust_attn_value_scores": _mfma(2.0 * K * (T // S) * H * (S * (S + 1) / 2) * (d // H)),
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_error_estimate": _alu(K * T * d, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * d * d),
         }
 
     def config(self):
-        return {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
-                "draws": self.K, "draw_block": self.KB, "gamma": self.gamma, "sigma": self.sigma,
-                "storage": "bf16 delta_o / g_o / x, fp32 scores, rewards, g_hat, G_W"}
+        cfg = {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
+               "draws": self.K, "draw_block": self.KB, "gamma": self.gamma, "sigma": self.sigma,
+               "storage": "bf16 delta_o / g_o / x, fp32 scores, rewards, g_hat, G_W"}
+        if self.attn_values:
+            cfg.update({"workload": self.c["name"] + "_attention_values", "heads": self.HEADS,
+                        "head_dim": self.d // self.HEADS, "draw_block": self.K,
+                        "delta_o": "attention re-run with perturbed values (synthetic weights)",
+                        "storage": "bf16 attention weights / g_o / x, fp32 scores, rewards, "
+                                   "g_hat, G_W"})
+        return cfg
 
     def cpu_baseline(self, scale):
         import oracle
+        if self.attn_values:
+            return self._cpu_baseline_attention(scale)
         S, d = self.S, self.d
         K_s, T_s = max(8, int(8192 * scale) // 8 * 8), S
         oracle.threads()
@@ -380,6 +415,24 @@ class InnerChain(Chain):
                           "scan, error estimate, G_W; the attention-output change is drawn "
                           "untimed (%.1f s), as on the device; %.1f s"
                           % (K_s, self.K, T_s, t_gen, dt)}
+
+
+    def _cpu_baseline_attention(self, scale):
+        import oracle
+        S, d, H = self.S, self.d, self.HEADS
+        K_s = max(1, int(4 * scale))
+        P = self.P[:1].float().cpu().numpy().astype(np.float64)          # the first sequence
+        go = synth.bf16_bits_to_f32(self.gobits[:S]).astype(np.float64)
+        t0 = time.perf_counter()
+        c = oracle.attn_value_scores(P, go, K_s, self.sigma, self.seed, self.tag)
+        r = oracle.reward_scan(c, S, self.gamma)
+        g = oracle.error_estimate(r, d, self.sigma, self.seed, self.tag, K_total=self.K)
+        oracle.weight_grad(g, synth.bf16_bits_to_f32(self.xbits[:S]).astype(np.float64))
+        dt = time.perf_counter() - t0
+        return {"value": K_s * S / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
+                "sample": "%d of %d draws x first %d tokens (one sequence, %d heads): attention "
+                          "value scores, scan, error estimate, G_W; %.1f s"
+                          % (K_s, self.K, S, H, dt)}
 
 
 CHAINS = {2: LinearChain, 3: HeadChain, 4: InnerChain, 5: LinearChain}
@@ -409,6 +462,11 @@ def main() -> int:
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
     chain.optimizer = args.optimizer
+    if args.attention_values:
+        if args.workload != 4:
+            print("--attention-values applies to workload 4 only", file=sys.stderr)
+            return 2
+        chain.attn_values = True
     chain.setup()
     chain.opt_setup()
 
