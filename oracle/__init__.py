@@ -48,6 +48,10 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
                                           ctypes.POINTER(_u32)]
     lib.dust_or_attn_value_scores.argtypes = [_d, _d, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
                                               _u64, _u32, _u32, _u32, _i64, _d]
+    lib.dust_or_attn_value_scores_at.argtypes = [_d, _d, _i64, _i64, _i64, _i64, ctypes.c_double,
+                                                 _u64, _u32, _u32, _u32, _i64,
+                                                 ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
+                                                 _d]
     lib.dust_or_sgd_momentum.argtypes = [_d, _d, _d, _i64, ctypes.c_double, ctypes.c_double]
     lib.dust_or_adam.argtypes = [_d, _d, _d, _d, _i64, ctypes.c_double, ctypes.c_double,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64]
@@ -212,6 +216,19 @@ def attn_value_scores(P, g_o, K: int, sigma: float, seed: int, tag: int, draw0: 
     _load().dust_or_attn_value_scores(_p(Pd), _p(gd), K, B, H, S, dh, sigma, seed, tag, draw0,
                                       tok0, chan0, _p(c))
     return c
+
+
+def attn_value_scores_at(P, g_o, k, t, sigma: float, seed: int, tag: int, draw0: int = 0,
+                         tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """attn_value_scores at chosen local (draw, token) pairs."""
+    Pd, gd = _f64(P), _f64(g_o)
+    B, H, S, _ = Pd.shape
+    dh = gd.shape[1] // H
+    k, t = _idx(k), _idx(t)
+    out = np.empty(len(k), dtype=np.float64)
+    _load().dust_or_attn_value_scores_at(_p(Pd), _p(gd), B, H, S, dh, sigma, seed, tag, draw0,
+                                         tok0, chan0, _pidx(k), _pidx(t), len(k), _p(out))
+    return out
 
 
 def reward_scan(c, seg_len: int, gamma: float) -> np.ndarray:

@@ -222,6 +222,33 @@ void dust_or_attn_value_scores(const double *P, const double *g, int64_t K, int6
         }
 }
 
+/* The same scores at n chosen (draw, token) pairs: out[m] = c[k[m]][t[m]]. */
+void dust_or_attn_value_scores_at(const double *P, const double *g, int64_t B, int64_t H,
+                                  int64_t S, int64_t dh, double sigma, uint64_t seed,
+                                  uint32_t tag, uint32_t draw0, uint32_t tok0, int64_t chan0,
+                                  const int64_t *k, const int64_t *t, int64_t n, double *out)
+{
+    const int64_t d = H * dh;
+    (void)B;
+    #pragma omp parallel for schedule(dynamic)
+    for (int64_t m = 0; m < n; ++m) {
+        const int64_t b = t[m] / S, tl = t[m] % S;
+        double acc = 0.0;
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t sl = 0; sl <= tl; ++sl) {
+                const double p = P[((b * H + h) * S + tl) * S + sl];
+                double dot = 0.0;
+                for (int64_t j = 0; j < dh; ++j)
+                    dot += dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),
+                                          (uint32_t)(tok0 + b * S + sl),
+                                          (uint64_t)(chan0 + h * dh + j)) *
+                           g[t[m] * d + h * dh + j];
+                acc += p * dot;
+            }
+        out[m] = -sigma * acc;
+    }
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Discounted reward r_t = sum_{s >= t, s in t's sequence} gamma^(s - t) c_s (explainer,
  * "Credit assignment"). Tokens are T = B * seg_len, sequence b owns [b*seg_len, (b+1)*seg_len).

@@ -207,6 +207,33 @@ def test_w4_weight_grad():
     _check_weight_grad(4, c["T"], c["d"], c["d"], 512)
 
 
+def test_w4_attention_value_scores():
+    """The attention workload scored through a re-run of the attention with perturbed values
+    (8 heads of 64, bench.py --attention-values), at full size: all 16384 draws in one call as
+    the benchmark times it, sampled outputs against the oracle."""
+    announce("w4 attention value scores")
+    c = synth.CONFIGS[4]
+    T, d, S, K, sigma = c["T"], c["d"], c["seg_len"], c["K"], c["sigma"]
+    B, H = T // S, 8
+    seed, tag = synth.noise_seed(4), synth.NOISE_TAG
+    g = np.random.default_rng(404)
+    z = g.standard_normal((B, H, S, S)).astype(np.float32)
+    z[:, :, np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] = -np.inf
+    z = np.exp(z - z.max(-1, keepdims=True))
+    Pbits = rne_bf16_bits_of_f32((z / z.sum(-1, keepdims=True)).astype(np.float32))
+    del z
+    gbits = synth.normal_bf16(synth.rng(4, 1), (T, d))
+    cd = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_attn_value_scores(bf16(Pbits), bf16(gbits), cd, K, B, H, S, d // H, 0, sigma, seed,
+                                tag, 0, 0)
+    got = host_f32(cd)
+    s = np.random.default_rng(405)
+    k, t = s.integers(0, K, 120), s.integers(0, T, 120)
+    k[:3], t[:3] = [0, K - 1, K - 1], [0, T - 1, S - 1]
+    ref = oracle.attn_value_scores_at(bits_to_f64(Pbits), bits_to_f64(gbits), k, t, sigma, seed, tag)
+    assert frob_rel(got[k, t], ref) <= 1e-5
+
+
 # ------------------------------------------------------------------------------ workload 5
 def test_w5_inject_block():
     announce("w5 inject block")

@@ -71,3 +71,14 @@ def test_linear_in_sigma_and_blind_above_the_diagonal():
     assert np.all(oracle.attn_value_scores(P, go, K, 0.0, 9, 2) == 0.0)
     Pj = P + np.triu(g.standard_normal((S, S)), 1)[None, None]
     assert np.array_equal(oracle.attn_value_scores(Pj, go, K, 0.01, 9, 2), c1)
+
+
+def test_sampled_scores_equal_the_full_array():
+    g = np.random.default_rng(63)
+    B, H, S, dh, K = 2, 2, 16, 8, 3
+    P = _causal_weights(g, B, H, S)
+    go = g.standard_normal((B * S, H * dh))
+    full = oracle.attn_value_scores(P, go, K, 0.03, 11, 5, 2, 7, 16)
+    k, t = np.array([0, 2, 1, 2]), np.array([0, 31, 17, 16])
+    np.testing.assert_array_equal(oracle.attn_value_scores_at(P, go, k, t, 0.03, 11, 5, 2, 7, 16),
+                                  full[k, t])
