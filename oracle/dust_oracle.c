@@ -34,6 +34,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 #ifdef _OPENMP
 #include <omp.h>
 #endif
@@ -246,6 +247,87 @@ void dust_or_attn_value_scores_at(const double *P, const double *g, int64_t B, i
                 acc += p * dot;
             }
         out[m] = -sigma * acc;
+    }
+}
+
+/* ---------------------------------------------------------------------------------------- */
+/* Scores of draws that perturb an attention KEY projection, scored through the attention output
+ * (explainer, "The real work": the inner product of the output's change with its estimated
+ * error). With k'_s = k_s + sigma a_s, head h's logit of query t on key s moves by
+ * delta_ts = sigma tau <q_t, a_s> (tau the softmax scale), so the re-run weights are the softmax
+ * of the moved logits, P'_ts = P_ts e^{delta_ts} / sum_{s' <= t} P_ts' e^{delta_ts'}, the given
+ * weights standing in for the clean softmax. The clean output is taken with the given weights
+ * normalised per row, Pbar_ts = P_ts / sum_{s' <= t} P_ts', so that sigma = 0 changes nothing:
+ *     Delta o_t = sum_{s <= t} (P'_ts - Pbar_ts) v_s,   c_t = -sum_h <Delta o^h_t, g^h_t>.
+ * A row whose weights sum to zero adds nothing. q, v and g are [T, H dh]; the noise of
+ * (token s, head h, column j) is channel chan0 + h dh + j of token tok0 + s in draw draw0 + i. */
+static double key_score_one(const double *P, const double *q, const double *v, const double *g,
+                            int64_t H, int64_t S, int64_t dh, double sigma, double tau,
+                            uint64_t seed, uint32_t tag, uint32_t draw, uint32_t tok0,
+                            int64_t chan0, int64_t t, double *dl)
+{
+    const int64_t b = t / S, tl = t % S, d = H * dh;
+    double acc = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+        const double *prow = P + ((b * H + h) * S + tl) * S;
+        double Z = 0.0, mx = -INFINITY;
+        for (int64_t sl = 0; sl <= tl; ++sl) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < dh; ++j)
+                dot += q[t * d + h * dh + j] *
+                       dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + b * S + sl),
+                                      (uint64_t)(chan0 + h * dh + j));
+            dl[sl] = sigma * tau * dot;
+            Z += prow[sl];
+            if (dl[sl] > mx) mx = dl[sl];
+        }
+        if (Z == 0.0) continue;
+        double den = 0.0;
+        for (int64_t sl = 0; sl <= tl; ++sl) den += prow[sl] * exp(dl[sl] - mx);
+        for (int64_t j = 0; j < dh; ++j) {
+            double dO = 0.0;
+            for (int64_t sl = 0; sl <= tl; ++sl)
+                dO += (prow[sl] * exp(dl[sl] - mx) / den - prow[sl] / Z) *
+                      v[(b * S + sl) * d + h * dh + j];
+            acc += dO * g[t * d + h * dh + j];
+        }
+    }
+    return -acc;
+}
+
+void dust_or_attn_key_scores(const double *P, const double *q, const double *v, const double *g,
+                             int64_t K, int64_t B, int64_t H, int64_t S, int64_t dh, double sigma,
+                             double tau, uint64_t seed, uint32_t tag, uint32_t draw0,
+                             uint32_t tok0, int64_t chan0, double *c)
+{
+    const int64_t T = B * S;
+    #pragma omp parallel
+    {
+        double *dl = malloc((size_t)S * sizeof(double));
+        #pragma omp for collapse(2) schedule(dynamic)
+        for (int64_t i = 0; i < K; ++i)
+            for (int64_t t = 0; t < T; ++t)
+                c[i * T + t] = key_score_one(P, q, v, g, H, S, dh, sigma, tau, seed, tag,
+                                             (uint32_t)(draw0 + i), tok0, chan0, t, dl);
+        free(dl);
+    }
+}
+
+/* The same scores at n chosen (draw, token) pairs: out[m] = c[k[m]][t[m]]. */
+void dust_or_attn_key_scores_at(const double *P, const double *q, const double *v,
+                                const double *g, int64_t H, int64_t S, int64_t dh, double sigma,
+                                double tau, uint64_t seed, uint32_t tag, uint32_t draw0,
+                                uint32_t tok0, int64_t chan0, const int64_t *k, const int64_t *t,
+                                int64_t n, double *out)
+{
+    #pragma omp parallel
+    {
+        double *dl = malloc((size_t)S * sizeof(double));
+        #pragma omp for schedule(dynamic)
+        for (int64_t m = 0; m < n; ++m)
+            out[m] = key_score_one(P, q, v, g, H, S, dh, sigma, tau, seed, tag,
+                                   (uint32_t)(draw0 + k[m]), tok0, chan0, t[m], dl);
+        free(dl);
     }
 }
 

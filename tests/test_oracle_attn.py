@@ -1,12 +1,21 @@
-"""Pins of the oracle's attention value-projection scores (CPU only).
+"""Pins of the oracle's attention scores (CPU only).
 
 The scores are the inner-mode loss change of the explainer's "The real work" for a perturbed
-value projection: c = -<Delta o, g> with Delta o the change of the attention output when the
-values move by sigma a. The oracle uses that the attention weights do not depend on the values.
-The pins do not: they re-run a causal attention with numpy on explicit values v and v + sigma a
-(noise taken from the oracle's generator, itself pinned in test_oracle_generator.py) and take
-numpy's inner product; with identity attention every token sees only itself and the score is
+attention projection: c = -<Delta o, g> with Delta o the change of the attention output when
+the values (or the keys) move by sigma a.
+
+Values: the oracle uses that the attention weights do not depend on the values. The pins do
+not: they re-run a causal attention with numpy on explicit values v and v + sigma a (noise
+taken from the oracle's generator, itself pinned in test_oracle_generator.py) and take numpy's
+inner product; with identity attention every token sees only itself and the score is
 -sigma <a_t, g_t>; the score is linear in sigma; weights above the diagonal are never read.
+
+Keys: the oracle re-runs the softmax from the given weights with the logits moved by
+sigma tau <q_t, a_s>. The pins build explicit queries and keys, take the causal softmax of
+tau q k^T and of tau q (k + sigma a)^T with numpy, and compare the output change's inner
+product; the first-order term is the textbook softmax Jacobian P_s (delta_sr - P_r); a row's
+weights count only relative to their sum, so rescaling rows changes nothing; sigma = 0 and a
+query that attends only to itself give exactly zero; weights above the diagonal are ignored.
 """
 import numpy as np
 import pytest
@@ -82,3 +91,93 @@ def test_sampled_scores_equal_the_full_array():
     k, t = np.array([0, 2, 1, 2]), np.array([0, 31, 17, 16])
     np.testing.assert_array_equal(oracle.attn_value_scores_at(P, go, k, t, 0.03, 11, 5, 2, 7, 16),
                                   full[k, t])
+
+
+def _softmax_causal(z):
+    S = z.shape[-1]
+    z = np.where(np.tril(np.ones((S, S), dtype=bool)), z, -np.inf)
+    z = np.exp(z - z.max(-1, keepdims=True))
+    return z / z.sum(-1, keepdims=True)
+
+
+def _heads(x, B, S, H):
+    """[B*S, H*dh] -> [B, H, S, dh]."""
+    return x.reshape(B, S, H, -1).transpose(0, 2, 1, 3)
+
+
+@pytest.mark.parametrize("B,H,S,dh,K,chan0,draw0,tok0", [
+    (2, 2, 12, 8, 3, 0, 0, 0),
+    (1, 3, 20, 4, 2, 64, 5, 100),
+])
+def test_key_scores_equal_an_explicit_attention_rerun(B, H, S, dh, K, chan0, draw0, tok0):
+    g = np.random.default_rng(64)
+    T, d, sigma, tau, seed, tag = B * S, H * dh, 0.3, 1.0 / np.sqrt(dh), 0x5EED, 4
+    q, k, v, go = (g.standard_normal((T, d)) for _ in range(4))
+    P = _softmax_causal(tau * _heads(q, B, S, H) @ _heads(k, B, S, H).transpose(0, 1, 3, 2))
+    o = np.einsum("bhts,bhsj->bhtj", P, _heads(v, B, S, H))
+    a = oracle.normals(seed, tag, draw0, tok0, chan0, K, T, d)
+    ref = np.empty((K, T))
+    for i in range(K):
+        kp = _heads(k + sigma * a[i], B, S, H)
+        Pp = _softmax_causal(tau * _heads(q, B, S, H) @ kp.transpose(0, 1, 3, 2))
+        do = np.einsum("bhts,bhsj->bhtj", Pp, _heads(v, B, S, H)) - o       # [B, H, S, dh]
+        ref[i] = -np.einsum("bhtj,bhtj->bt", do, _heads(go, B, S, H)).reshape(T)
+    got = oracle.attn_key_scores(P, q, v, go, K, sigma, tau, seed, tag, draw0, tok0, chan0)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
+
+
+def test_key_scores_first_order_is_the_softmax_jacobian():
+    g = np.random.default_rng(65)
+    B, H, S, dh, K, tau = 1, 2, 16, 8, 2, 0.4
+    T, d = B * S, H * dh
+    q, v, go = (g.standard_normal((T, d)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    a = oracle.normals(3, 7, 0, 0, 0, K, T, d)
+    qh, vh, gh = _heads(q, B, S, H), _heads(v, B, S, H), _heads(go, B, S, H)
+    u = gh @ vh.transpose(0, 1, 3, 2)                        # u[b,h,t,s] = <g_t, v_s>
+    lin = np.empty((K, T))
+    for i in range(K):
+        D = tau * qh @ _heads(a[i], B, S, H).transpose(0, 1, 3, 2)     # d logit_ts / d sigma
+        # d o_t / d sigma = sum_s P_ts (D_ts - sum_r P_tr D_tr) v_s
+        dP = P * (D - (P * D).sum(-1, keepdims=True))
+        lin[i] = -(dP * u).sum(-1).sum(1).reshape(T)
+    for sigma in (1e-5, 1e-6):
+        got = oracle.attn_key_scores(P, q, v, go, K, sigma, tau, 3, 7) / sigma
+        np.testing.assert_allclose(got, lin, rtol=3 * sigma * 1e2, atol=1e-9)
+
+
+def test_key_scores_invariant_to_row_scale_and_blind_above_the_diagonal():
+    g = np.random.default_rng(66)
+    B, H, S, dh, K, sigma, tau = 2, 2, 12, 4, 2, 0.2, 0.5
+    T, d = B * S, H * dh
+    q, v, go = (g.standard_normal((T, d)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    c = oracle.attn_key_scores(P, q, v, go, K, sigma, tau, 9, 2)
+    scaled = P * np.exp(g.standard_normal((B, H, S, 1)))
+    np.testing.assert_allclose(oracle.attn_key_scores(scaled, q, v, go, K, sigma, tau, 9, 2), c,
+                               rtol=1e-10, atol=1e-13)
+    junk = P + np.triu(np.abs(g.standard_normal((S, S))), 1)[None, None]
+    assert np.array_equal(oracle.attn_key_scores(junk, q, v, go, K, sigma, tau, 9, 2), c)
+
+
+def test_key_scores_vanish_at_sigma_zero_and_for_self_attention():
+    g = np.random.default_rng(67)
+    B, H, S, dh, K = 1, 2, 10, 4, 3
+    T, d = B * S, H * dh
+    q, v, go = (g.standard_normal((T, d)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    assert np.all(oracle.attn_key_scores(P, q, v, go, K, 0.0, 0.5, 1, 1) == 0.0)
+    eye = np.broadcast_to(np.eye(S), (B, H, S, S)).copy()
+    assert np.all(oracle.attn_key_scores(eye, q, v, go, K, 0.7, 0.5, 1, 1) == 0.0)
+    assert np.any(oracle.attn_key_scores(P, q, v, go, K, 0.7, 0.5, 1, 1) != 0.0)
+
+
+def test_sampled_key_scores_equal_the_full_array():
+    g = np.random.default_rng(68)
+    B, H, S, dh, K = 2, 2, 16, 8, 3
+    q, v, go = (g.standard_normal((B * S, H * dh)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    full = oracle.attn_key_scores(P, q, v, go, K, 0.03, 0.35, 11, 5, 2, 7, 16)
+    k, t = np.array([0, 2, 1, 2]), np.array([0, 31, 17, 16])
+    np.testing.assert_array_equal(
+        oracle.attn_key_scores_at(P, q, v, go, k, t, 0.03, 0.35, 11, 5, 2, 7, 16), full[k, t])

@@ -3,7 +3,7 @@
 Each case plants one plausible mistake in a copy of oracle/dust_oracle.c (a wrong Philox
 constant, a dropped key advance, swapped counter words, a wrong Box-Muller radius, a flipped
 sign, a missing sigma, a scan that leaks across sequences, an off-by-one chunk, an optimizer
-step without bias correction, ...), builds it,
+step without bias correction, a softmax re-run against unnormalised weights, ...), builds it,
 swaps it in for the oracle's library, and requires that at least one of the pins the other
 oracle tests use rejects it. The real oracle passes all of them (tests/test_oracle_*.py).
 """
@@ -82,6 +82,11 @@ PINS_STEPS = [
     lambda: attn.test_scores_equal_an_explicit_attention_rerun(1, 3, 24, 4, 2, 64, 5, 100),
     attn.test_identity_attention_is_the_own_token_inner_product,
     attn.test_linear_in_sigma_and_blind_above_the_diagonal,
+    lambda: attn.test_key_scores_equal_an_explicit_attention_rerun(2, 2, 12, 8, 3, 0, 0, 0),
+    lambda: attn.test_key_scores_equal_an_explicit_attention_rerun(1, 3, 20, 4, 2, 64, 5, 100),
+    attn.test_key_scores_first_order_is_the_softmax_jacobian,
+    attn.test_key_scores_invariant_to_row_scale_and_blind_above_the_diagonal,
+    attn.test_key_scores_vanish_at_sigma_zero_and_for_self_attention,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -133,6 +138,17 @@ MUTATIONS = [
     ("attention noise at the query token", "(uint32_t)(tok0 + b * S + sl),\n                                              (uint64_t)(chan0 + h * dh + j))",
      "(uint32_t)(tok0 + t),\n                                              (uint64_t)(chan0 + h * dh + j))"),
     ("attention head offset dropped", "(uint64_t)(chan0 + h * dh + j)) *", "(uint64_t)(chan0 + j)) *"),
+    ("key scores against unnormalised weights", "/ den - prow[sl] / Z)", "/ den - prow[sl])"),
+    ("key logit shift without the softmax scale", "dl[sl] = sigma * tau * dot;", "dl[sl] = sigma * dot;"),
+    ("key score sign", "    return -acc;\n}", "    return acc;\n}"),
+    ("key noise at the query token", "dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + b * S + sl),",
+     "dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + t),"),
+    ("key logit uses the key token's query", "dot += q[t * d + h * dh + j] *",
+     "dot += q[(b * S + sl) * d + h * dh + j] *"),
+    ("key scores not causal", "for (int64_t sl = 0; sl <= tl; ++sl) {\n            double dot = 0.0;",
+     "for (int64_t sl = 0; sl < S; ++sl) {\n            double dot = 0.0;"),
+    ("key output change drops the value", "* exp(dl[sl] - mx) / den - prow[sl] / Z) *\n                      v[(b * S + sl) * d + h * dh + j];",
+     "* exp(dl[sl] - mx) / den - prow[sl] / Z) *\n                      v[t * d + h * dh + j];"),
 ]
 
 
