@@ -199,6 +199,39 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
                            void *stream);
 
 /*
+ * dust_attn_key_scores -- loss change of K draws that perturb an attention KEY projection,
+ * scored through the attention output (explainer, "The real work: suppressing interference":
+ * the inner product of the output's change with the output's estimated error). With
+ * k'_s = k_s + sigma a_s, head h's logit of query t on key s moves by
+ * delta_ts = sigma * softmax_scale * <q^h_t, a^h_s>, and the re-run attention weights are the
+ * softmax of the moved logits, taken relative to the given weights:
+ *     P'_ts = P_ts e^{delta_ts} / sum_{s' <= t} P_ts' e^{delta_ts'},
+ *     c[i][t] = -sum_h <sum_{s <= t} (P'_ts - P_ts / Z_t) v^h_s, g^h_t>,  Z_t = sum_{s <= t} P_ts
+ * (each row is normalised, so bf16 weights that do not sum to one exactly still give 0 at
+ * sigma = 0; a row whose weights sum to zero adds nothing). The call computes the scores
+ * without forming the perturbed outputs. Use them as dust_loss_delta's inner-mode scores
+ * (dust_reward_scan, then dust_error_estimate with the same seed, tag, draw0, tok0 and chan0
+ * and d = H * dh).
+ *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
+ *           keys s; entries above the diagonal are ignored                              (in)
+ *   q       [B*S, H*dh] bf16 queries, head h in columns h*dh .. h*dh+dh-1                (in)
+ *   v       [B*S, H*dh] bf16 values                                                      (in)
+ *   g_o     [B*S, H*dh] bf16 estimated error of the attention output                     (in)
+ *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
+ * The noise a of (token s, head h, column j) is channel chan0 + h*dh + j of token tok0 + s
+ * (the key projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
+ * Supported: S a multiple of 32 and at most 1024, dh a multiple of 16 in [16, 128]; P, q, v and
+ * g_o 16-byte aligned; sigma and softmax_scale finite with |sigma * softmax_scale| <= 2^20.
+ * c must not overlap the inputs. fp32 accumulation; the noise enters the bf16 matrix cores as
+ * a high part plus a remainder (16 significant bits). Logit shifts beyond about 80 overflow
+ * e^delta and give non-finite scores.
+ */
+int dust_attn_key_scores(const void *P, const void *q, const void *v, const void *g_o, float *c,
+                         int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
+                         float sigma, float softmax_scale, uint64_t seed, uint32_t tag,
+                         uint32_t draw0, uint32_t tok0, void *stream);
+
+/*
  * dust_sgd_momentum -- one SGD-with-momentum step on n fp32 weights, in place.
  * The explainer's section "Results" trains with the estimate through SGD with momentum at a
  * constant learning rate; the step is the textbook heavy ball without dampening:

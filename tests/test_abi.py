@@ -114,6 +114,15 @@ INVALID = [
     ("dust_attn_value_scores", (FAKE, FAKE2, FAKE, 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "overlap"),
     ("dust_attn_value_scores", (None, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "null"),
     ("dust_attn_value_scores", (FAKE, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 2, 0.01, 1, 1, 0, 0, None), 1, "chan0"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 2048, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 2, "up to 1024"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 144, 0, 0.01, 0.25, 1, 1, 0, 0, None), 2, "multiple of 16"),
+    ("dust_attn_key_scores", (FAKE + 8, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "aligned"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4104, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "aligned"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + 8192, 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "overlap"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, None, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "null"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, float("nan"), 1, 1, 0, 0, None), 1, "finite"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 3e3, 1e3, 1, 1, 0, 0, None), 2, "2^20"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 6, 0.01, 0.25, 1, 1, 0, 0, None), 1, "chan0"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, 0.1, -0.5, None), 1, "momentum"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, float("inf"), 0.9, None), 1, "finite"),
     ("dust_sgd_momentum", (FAKE, FAKE, FAKE2 + 4096, 16, 0.1, 0.9, None), 1, "overlap"),
@@ -144,6 +153,7 @@ ZERO_SIZE = [
     ("dust_loss_reward", (None, None, None, 0, 10, 5, 0.5, None)),
     ("dust_sgd_momentum", (None, None, None, 0, 0.1, 0.9, None)),
     ("dust_attn_value_scores", (None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None)),
+    ("dust_attn_key_scores", (None, None, None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None)),
     ("dust_adam", (None, None, None, None, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, 1, None)),
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),

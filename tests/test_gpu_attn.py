@@ -1,4 +1,4 @@
-"""GPU parity of dust_attn_value_scores with the oracle (MI355X only).
+"""GPU parity of dust_attn_value_scores and dust_attn_key_scores with the oracle (MI355X only).
 
 The scores c = -<Delta o, g_o> of a perturbed attention value projection, computed on the
 device without forming Delta o, are compared with the oracle's fp64 sum element by element at
@@ -9,6 +9,11 @@ ignored. Tolerance: relative Frobenius 1e-5, the bar of the inner-mode scores (t
 the bf16 matrix cores as a high part plus a bf16 remainder, about 2^-17 relative). With
 identity attention the call must agree with the inner-mode loss change of sigma a computed by
 two other entry points (dust_noise_inject into zeros, then dust_loss_delta).
+
+The key scores (a softmax re-run with the logits moved by sigma tau <q_t, a_s>) are compared the
+same way, at the same bar, over the same layouts, with logit shifts both inside and beyond the
+range where the kernel takes e^x - 1 from a polynomial (|x| <= 0.2), and on tiles that mix the
+two; sigma = 0 must give exactly zero and attention to the own token only (nearly) zero.
 """
 import numpy as np
 import pytest
@@ -75,3 +80,70 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     c = torch.full((2, 64), 5.0, device=DEV)
     dust.dust_attn_value_scores(None, None, c, 0, 2, 2, 32, 16, 0, 0.01, 1, 1, 0, 0)
     assert torch.all(c == 5.0)
+
+
+@pytest.mark.parametrize("B,H,S,dh,Kc,chan0,draw0,tok0,garbage,sigma,tau", [
+    (2, 2, 32, 16, 5, 0, 3, 7, False, 0.05, 0.25),       # one tile, ragged draw group
+    (1, 3, 64, 32, 6, 64, 0, 0, True, 0.05, 0.18),       # channel offset, weights above the diagonal
+    (2, 2, 128, 64, 3, 0, 11, 1000, False, 0.01, 0.125), # 4 x 4 tiles, the workload's head width
+    (1, 1, 96, 128, 9, 8, 2, 5, True, 0.02, 0.09),       # widest heads, three groups of draws
+    (1, 4, 64, 48, 4, 4, 0, 0, False, 0.05, 0.144),      # three k-slices
+    (1, 2, 1024, 16, 2, 0, 0, 0, False, 0.05, 0.25),     # longest sequence
+    (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
+    (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
+])
+def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
+    announce("attn key scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
+    g = np.random.default_rng(72)
+    T, d, seed, tag = B * S, H * dh, 0xA77F, 7
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
+    qb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh, chan0,
+                              sigma, tau, seed, tag, draw0, tok0)
+    ref = oracle.attn_key_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
+                                 bits_to_f64(gb), Kc, sigma, tau, seed, tag, draw0, tok0, chan0)
+    err = frob_rel(host_f32(c), ref)
+    print("key scores rel. Frobenius error %.2e" % err)
+    assert err <= 1e-5
+
+
+def test_attn_key_scores_vanish_at_sigma_zero_and_for_self_attention():
+    announce("attn key scores sigma = 0, self attention")
+    B, H, S, dh, Kc = 1, 2, 64, 32, 4
+    T, d = B * S, H * dh
+    g = np.random.default_rng(73)
+    qb, vb, gb = (bf16(rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)))
+                  for _ in range(3))
+    P = bf16(rne_bf16_bits_of_f32(_causal_weights(g, B, H, S).astype(np.float32)))
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_key_scores(P, qb, vb, gb, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
+    assert torch.all(c == 0)
+    eye = bf16(rne_bf16_bits_of_f32(np.broadcast_to(np.eye(S, dtype=np.float32), (B, H, S, S)).copy()))
+    dust.dust_attn_key_scores(eye, qb, vb, gb, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
+    assert float(c.abs().max()) <= 1e-6
+
+
+def test_attn_key_scores_zero_draws_touch_nothing():
+    c = torch.full((2, 64), 5.0, device=DEV)
+    dust.dust_attn_key_scores(None, None, None, None, c, 0, 2, 2, 32, 16, 0, 0.01, 0.25, 1, 1, 0, 0)
+    assert torch.all(c == 5.0)
+
+
+def test_attn_scores_channels_beyond_32_bits():
+    """chan0 above 2^32 (the noise's channel index goes to 2^34): the kernels take chan0 / 4."""
+    announce("attn scores chan0 >= 2^32")
+    B, H, S, dh, Kc, sigma, tau, chan0 = 1, 2, 32, 16, 3, 0.05, 0.25, (1 << 32) + 64
+    T, d = B * S, H * dh
+    g = np.random.default_rng(74)
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S).astype(np.float32))
+    qb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
+    c = torch.empty((Kc, T), dtype=torch.float32, device=DEV)
+    dust.dust_attn_value_scores(bf16(Pbits), bf16(gb), c, Kc, B, H, S, dh, chan0, sigma, 3, 1, 0, 0)
+    ref = oracle.attn_value_scores(bits_to_f64(Pbits), bits_to_f64(gb), Kc, sigma, 3, 1, 0, 0, chan0)
+    assert frob_rel(host_f32(c), ref) <= 1e-5
+    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh, chan0,
+                              sigma, tau, 3, 1, 0, 0)
+    ref = oracle.attn_key_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
+                                 bits_to_f64(gb), Kc, sigma, tau, 3, 1, 0, 0, chan0)
+    assert frob_rel(host_f32(c), ref) <= 1e-5
