@@ -62,7 +62,8 @@ __host__ __device__ constexpr uint32_t stage_bytes(int KS, int NQ) {
 template <int KS>
 __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uint32_t half,
                                                 uint32_t token, uint32_t draw, bf16x8 (&ahi)[KS],
-                                                bf16x8 (&alo)[KS]) {
+                                                bf16x8 (&alo)[KS], float *norm2 = nullptr) {
+    float n2 = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         const uint32_t q = q0 + 4u * ks + 2u * half;
@@ -74,6 +75,7 @@ __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float x0 = pp[e]->rho * pp[e]->c, x1 = pp[e]->rho * pp[e]->s;
+            if (norm2) n2 = __builtin_fmaf(x1, x1, __builtin_fmaf(x0, x0, n2));
             hw[e] = pack_bf16x2(x0, x1);
             lw[e] = pack_bf16x2(x0 - __uint_as_float(hw[e] << 16),
                                 x1 - __uint_as_float(hw[e] & 0xFFFF0000u));
@@ -81,51 +83,64 @@ __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uin
         ahi[ks] = as_bf16x8(hw);
         alo[ks] = as_bf16x8(lw);
     }
+    if (norm2) *norm2 = n2;
 }
 
-// Staging of one step: 16-byte pieces, P rows first (4 per query row), then the NQ query-side
-// tiles (2 KS per row each); loads into registers, stores to LDS after the step's compute.
-template <int KS, int NQ>
+// Staging of one step: QT query tiles, each as 16-byte pieces, P rows first (4 per query row),
+// then the NQ query-side tiles (2 KS per row each); loads into registers, stores to LDS after
+// the step's compute. Only the first ntiles query tiles of a step exist.
+template <int KS, int NQ, uint32_t NT = 256, int QT = 1>
 struct Stager {
-    static constexpr uint32_t kPieces = 128u + 64u * KS * NQ;
-    static constexpr uint32_t kPerThread = (kPieces + 255u) / 256u;
+    static constexpr uint32_t kTilePieces = 128u + 64u * KS * NQ;
+    static constexpr uint32_t kPieces = QT * kTilePieces;
+    static constexpr uint32_t kPerThread = (kPieces + NT - 1u) / NT;
+    static constexpr uint32_t kTileBytes = stage_bytes(KS, NQ);
     u32x4 r[kPerThread];
 
-    // P [B, H, S, S]; the query-side arrays [T, H DH], tile ct of sequence b, head h
+    // P [B, H, S, S]; the query-side arrays [T, H DH]; query tiles ct .. ct + ntiles - 1 of
+    // sequence b, head h, key tile kt
     __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P,
                                          const uint16_t *const (&qs)[NQ], uint32_t b, uint32_t H,
                                          uint32_t S, uint32_t d, uint32_t h, uint32_t kt,
-                                         uint32_t ct) {
+                                         uint32_t ct, uint32_t ntiles) {
         constexpr uint32_t DH = 16u * KS;
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
-            const uint32_t pc = tid + 256u * j;
-            if (pc < 128u) {
-                const uint32_t row = pc >> 2, seg = pc & 3u;
-                r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + ct * 32u + row) * S +
+            const uint32_t pc = tid + NT * j;
+            const uint32_t tile = pc / kTilePieces, lp = pc % kTilePieces;
+            if (pc >= kPieces || tile >= ntiles) continue;
+            const uint32_t qt = ct + tile;
+            if (lp < 128u) {
+                const uint32_t row = lp >> 2, seg = lp & 3u;
+                r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + qt * 32u + row) * S +
                                         kt * 32u + 8u * seg);
-            } else if (pc < kPieces) {
-                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
+            } else {
+                const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n)
                     if (m == (uint32_t)n)
-                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + ct * 32u + row) * d +
+                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + qt * 32u + row) * d +
                                                 h * DH + 8u * seg);
             }
         }
     }
 
-    // P widened to fp32 once here for all draws; on a diagonal tile (mask) the keys after the
-    // row's query become 0, so later arithmetic needs no causal test
-    __device__ __forceinline__ void store(uint32_t tid, unsigned char *base, bool mask) const {
+    // P widened to fp32 once here for all draws; on a diagonal tile (the step's first tile when
+    // mask is set) the keys after the row's query become 0, so later arithmetic needs no causal
+    // test
+    __device__ __forceinline__ void store(uint32_t tid, unsigned char *base, bool mask,
+                                          uint32_t ntiles) const {
         constexpr uint32_t GP = g_pitch(KS);
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
-            const uint32_t pc = tid + 256u * j;
-            if (pc < 128u) {
-                const uint32_t row = pc >> 2, seg = pc & 3u;
-                f32x4 *dst = (f32x4 *)(base + row * kPPitch + 32u * seg);
+            const uint32_t pc = tid + NT * j;
+            const uint32_t tile = pc / kTilePieces, lp = pc % kTilePieces;
+            if (pc >= kPieces || tile >= ntiles) continue;
+            unsigned char *tb = base + tile * kTileBytes;
+            if (lp < 128u) {
+                const uint32_t row = lp >> 2, seg = lp & 3u;
+                f32x4 *dst = (f32x4 *)(tb + row * kPPitch + 32u * seg);
                 const u32x4 w = r[j];
                 float f[8];
 #pragma unroll
@@ -133,28 +148,29 @@ struct Stager {
                     f[2 * e] = __uint_as_float(w[e] << 16);
                     f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
-                if (mask) {
+                if (mask && tile == 0) {
 #pragma unroll
                     for (uint32_t e = 0; e < 8u; ++e) f[e] = 8u * seg + e <= row ? f[e] : 0.f;
                 }
                 dst[0] = f32x4{f[0], f[1], f[2], f[3]};
                 dst[1] = f32x4{f[4], f[5], f[6], f[7]};
-            } else if (pc < kPieces) {
-                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
+            } else {
+                const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
-                *(u32x4 *)(base + 32u * kPPitch + (m * 32u + row) * GP + 16u * seg) = r[j];
+                *(u32x4 *)(tb + 32u * kPPitch + (m * 32u + row) * GP + 16u * seg) = r[j];
             }
         }
     }
 };
 
-// Steps in the order head, key tile, query tile >= key tile.
+// Steps in the order head, key tile, query tile >= key tile; a step covers QT query tiles.
+template <uint32_t QT = 1>
 struct StepOrder {
     uint32_t h = 0, kt = 0, ct = 0;
     __device__ __forceinline__ StepOrder next(uint32_t nt) const {
         StepOrder n = *this;
-        n.ct = ct + 1u;
-        if (n.ct == nt) {
+        n.ct = ct + QT;
+        if (n.ct >= nt) {
             n.kt = kt + 1u;
             n.ct = n.kt;
             if (n.kt == nt) { n.h = h + 1u; n.kt = 0; n.ct = 0; }
@@ -202,15 +218,15 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 
     // Step n's tiles are in LDS stage n % 2; step n + 1's are fetched into registers at the
     // start of step n and stored to the other stage at its end, before the one barrier per step.
-    StepOrder cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0);
-    stg.store(tid, lds, true);
+    StepOrder<> cur;
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 1);
+    stg.store(tid, lds, true, 1);
     noise(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;   // uniform across the block
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, 1);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
                                                          __float_as_uint(partB), false, false);
         cwh[cur.ct * 32u + col] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (!more) break;
-        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
+        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct, 1);
         if (nx.kt != cur.kt || nx.h != cur.h) noise(nx.h, nx.kt);
         __syncthreads();
         cur = nx;
@@ -280,99 +296,110 @@ __device__ __forceinline__ float expm1_any(float D, const Expm1Coef &e) {
     return fabsf(x) <= kPolyRange ? expm1_poly(D, e) : expf(x) - 1.f;
 }
 
-template <int KS>
-__global__ __launch_bounds__(256) void attn_key_scores_kernel(
+// Key scores, 8 waves per block (two per SIMD, so that one wave's vector work runs under the
+// other's matrix-core work), one draw per wave, one sequence per block, QT query tiles per step
+// (the tiles' product chains are independent, and the vector work of one overlaps the matrix
+// work of the next).
+template <int KS, int QT>
+__global__ __launch_bounds__(512) void attn_key_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ qm,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
-    // LDS: two stages of one step's operands (P tile [32 queries][32 keys], q and g tiles
-    // [32 queries][DH]); then per wave the head's running sums N1 and N0 of its two draws
-    // ([N1 of A, N1 of B, N0 of A, N0 of B][S]); then per wave the partial row sums Z and base
-    // over the 8 key rows of each tile that the wave owns ([Z, base][S]).
+    // LDS: two stages of one step's operands (per query tile: P tile [32 queries][32 keys], q
+    // and g tiles [32 queries][DH]); per wave the head's running sums of its draw, [N1, N0][S];
+    // per SIMD (waves 0-3) the partial row sums over the 8 key rows of each tile it owns,
+    // [Z, base][S]; the head's query norms |q_t|, [S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
-    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 2);
+    constexpr uint32_t GP = g_pitch(KS), TB = stage_bytes(KS, 2), SB = QT * TB;
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    const uint32_t i0 = (blockIdx.x % ndg) * 8u + wave * 2u;
-    const uint32_t drawA = draw0 + min(i0, Kc - 1u), drawB = draw0 + min(i0 + 1u, Kc - 1u);
+    // this wave's draw; a draw past the last one is computed with the last draw's noise and
+    // not written, so every wave loads and synchronises
+    const uint32_t i = (blockIdx.x % ndg) * 8u + wave;
+    const uint32_t draw = draw0 + min(i, Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
     float *NN = (float *)(lds + 2u * SB);
     float *ZB = NN + 16u * S;
-    float *n1w = NN + (wave * 4u + half) * S, *n0w = NN + (wave * 4u + 2u + half) * S;
-    float *zbw = ZB + (wave * 2u + half) * S;
+    float *QN = ZB + 8u * S;
+    float *nnw = NN + (wave * 2u + half) * S;          // lanes 0-31 keep N1, lanes 32-63 N0
+    float *zbw = ZB + ((wave & 3u) * 2u + half) * S;   // lanes 0-31 keep Z, lanes 32-63 base
 
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
     const uint16_t *const qs[2] = {qm, g};
-    Stager<KS, 2> stg;
+    Stager<KS, 2, 512, QT> stg;
 
-    // key-side operands of the current key tile: both draws' noise and the values
-    bf16x8 ahiA[KS], aloA[KS], ahiB[KS], aloB[KS], vb[KS];
+    // key-side operands of the current key tile: the draw's noise and the values, and the
+    // largest noise norm over the tile's 32 keys (for the range test of e^x - 1)
+    bf16x8 ahi[KS], alo[KS], vb[KS];
+    float amax = 0.f;
     auto key_tile = [&](uint32_t h, uint32_t kt) {
         const uint32_t row = b * S + kt * 32u + col;
         const uint16_t *vrow = v + (uint64_t)row * d + h * DH + 8u * half;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             vb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vrow + 16u * ks));
-        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, drawA, ahiA, aloA);
-        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, drawB, ahiB, aloB);
+        float n2;
+        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
+        n2 += __shfl_xor(n2, 32);
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+    };
+    // |q_t| of head h for every query of the sequence
+    auto query_norms = [&](uint32_t h) {
+        for (uint32_t t = tid; t < S; t += 512u) {
+            const uint16_t *qrow = qm + ((uint64_t)b * S + t) * d + h * DH;
+            float n2 = 0.f;
+#pragma unroll
+            for (uint32_t p = 0; p < 2u * KS; ++p) {
+                const u32x4 w = *(const u32x4 *)(qrow + 8u * p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(w[e] << 16);
+                    const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+                    n2 = __builtin_fmaf(hi, hi, __builtin_fmaf(lo, lo, n2));
+                }
+            }
+            QN[t] = __builtin_sqrtf(n2);
+        }
     };
 
-    // A head is complete: fold its sums into the scores of this wave's draws. The first head
+    // A head is complete: fold its sums into the score of this wave's draw. The first head
     // stores, later heads add; each lane rereads only what it wrote itself.
     auto fold_head = [&](bool first) {
+        if (i >= Kc) return;
+        float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
+        const float *n1 = NN + (wave * 2u) * S, *n0 = n1 + S;
+        for (uint32_t t = lane; t < S; t += 64u) {
+            float Z = 0.f, bs = 0.f;
 #pragma unroll
-        for (uint32_t k = 0; k < 2u; ++k) {
-            if (i0 + k >= Kc) break;
-            float *cr = c + (uint64_t)(i0 + k) * T + (uint64_t)b * S;
-            const float *n1 = NN + (wave * 4u + k) * S, *n0 = NN + (wave * 4u + 2u + k) * S;
-            for (uint32_t t = lane; t < S; t += 64u) {
-                float Z = 0.f, bs = 0.f;
-#pragma unroll
-                for (uint32_t w = 0; w < 4u; ++w) {
-                    Z += ZB[(2u * w) * S + t];
-                    bs += ZB[(2u * w + 1u) * S + t];
-                }
-                const float val = Z > 0.f ? (Z * n1[t] - bs * n0[t]) / (Z * (Z + n0[t])) : 0.f;
-                cr[t] = first ? -val : cr[t] - val;
+            for (uint32_t w = 0; w < 4u; ++w) {
+                Z += ZB[(2u * w) * S + t];
+                bs += ZB[(2u * w + 1u) * S + t];
             }
+            const float val = Z > 0.f ? (Z * n1[t] - bs * n0[t]) / (Z * (Z + n0[t])) : 0.f;
+            cr[t] = first ? -val : cr[t] - val;
         }
     };
 
-    StepOrder cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0);
-    stg.store(tid, lds, true);
-    key_tile(0, 0);
-    __syncthreads();
-    for (uint32_t st = 0;; st ^= 1u) {
-        if (cur.kt == 0 && cur.ct == 0 && cur.h > 0) {   // uniform across the block
-            fold_head(cur.h == 1u);
-            __syncthreads();   // every wave has read Z and base before they are overwritten
-        }
-        const StepOrder nx = cur.next(nt);
-        const bool more = nx.h < H;
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct);
+    // |D| <= lim keeps e^x - 1 on the polynomial. Cauchy-Schwarz bounds |D| by |q_t| amax; the
+    // margin covers the rounding of the norms and of the matrix-core sums.
+    const float lim_cs = ec.lim * 0.999f;
+    const uint32_t lim_bits = __float_as_uint(ec.lim) << 1;   // |x| bits shifted past the sign
 
-        const unsigned char *base = lds + st * SB;
-        const unsigned char *qrow = base + 32u * kPPitch + col * GP + 16u * half;
-        const unsigned char *grow = qrow + 32u * GP;
-        f32x16 dA = {}, dB = {}, u = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
-            const bf16x8 gb = *(const bf16x8 *)(grow + 32u * ks);
-            dA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahiA[ks], qb, dA, 0, 0, 0);
-            dB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahiB[ks], qb, dB, 0, 0, 0);
-            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks], gb, u, 0, 0, 0);
-            dA = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aloA[ks], qb, dA, 0, 0, 0);
-            dB = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aloB[ks], qb, dB, 0, 0, 0);
-        }
+    // One query tile's vector work: e^x - 1 of the products, weighted sums over the tile's keys
+    // into the running sums of query tile qt.
+    auto tile_sums = [&](const f32x16 &dd, const f32x16 &u, const unsigned char *tb, uint32_t qt,
+                         bool first) {
+        const uint32_t tq = qt * 32u + col;
+        const float qn = QN[tq];
         // element 4 qd + r is key row 8 qd + 4 half + r of the tile, query column col
-        const unsigned char *prow = base + col * kPPitch + 16u * half;
+        const unsigned char *prow = tb + col * kPPitch + 16u * half;
         float w[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
@@ -380,65 +407,102 @@ __global__ __launch_bounds__(256) void attn_key_scores_kernel(
 #pragma unroll
             for (int r = 0; r < 4; ++r) w[4 * qd + r] = x[r];
         }
-        float mx = 0.f;
+        bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax <= lim_cs)) == 0;
+        if (!poly) {   // the bound is loose: test the products themselves
+            uint32_t m = 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(fabsf(dA[r]), fabsf(dB[r])));
-        float n1A = 0.f, n0A = 0.f, n1B = 0.f, n0B = 0.f;
-        if (__builtin_amdgcn_ballot_w64(!(mx <= ec.lim)) == 0) {
+            for (int r = 0; r < 16; ++r) m = max(m, __float_as_uint(dd[r]) << 1);
+            poly = __builtin_amdgcn_ballot_w64(!(m <= lim_bits)) == 0;
+        }
+        float n1 = 0.f, n0 = 0.f;
+        if (poly) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pu = w[r] * u[r];
-                const float eA = expm1_poly(dA[r], ec), eB = expm1_poly(dB[r], ec);
-                n1A = __builtin_fmaf(pu, eA, n1A);
-                n0A = __builtin_fmaf(w[r], eA, n0A);
-                n1B = __builtin_fmaf(pu, eB, n1B);
-                n0B = __builtin_fmaf(w[r], eB, n0B);
+                const float e = expm1_poly(dd[r], ec);
+                n1 = __builtin_fmaf(w[r] * u[r], e, n1);
+                n0 = __builtin_fmaf(w[r], e, n0);
             }
         } else {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float pu = w[r] * u[r];
-                const float eA = expm1_any(dA[r], ec), eB = expm1_any(dB[r], ec);
-                n1A = __builtin_fmaf(pu, eA, n1A);
-                n0A = __builtin_fmaf(w[r], eA, n0A);
-                n1B = __builtin_fmaf(pu, eB, n1B);
-                n0B = __builtin_fmaf(w[r], eB, n0B);
+                const float e = expm1_any(dd[r], ec);
+                n1 = __builtin_fmaf(w[r] * u[r], e, n1);
+                n0 = __builtin_fmaf(w[r], e, n0);
             }
         }
-        // the draw-independent row sums: wave w takes key rows 8 w .. 8 w + 7 (its qd = w)
-        float zs = 0.f, bs = 0.f;
-#pragma unroll
-        for (uint32_t qd = 0; qd < 4u; ++qd)
-            if (qd == wave) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    zs += w[4 * qd + r];
-                    bs = __builtin_fmaf(w[4 * qd + r], u[4 * qd + r], bs);
-                }
-            }
-        // lane-half swaps: lanes 0-31 end with draw A's N1 / N0 and Z, lanes 32-63 with draw
-        // B's N1 / N0 and base
-        const auto s1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(n1A),
-                                                         __float_as_uint(n1B), false, false);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(__float_as_uint(n0A),
-                                                         __float_as_uint(n0B), false, false);
-        const auto sz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zs), __float_as_uint(bs),
+        // lane-half swap: lanes 0-31 end with N1 over the tile's 32 keys, lanes 32-63 with N0
+        const auto sn = __builtin_amdgcn_permlane32_swap(__float_as_uint(n1), __float_as_uint(n0),
                                                          false, false);
-        const float n1 = __uint_as_float(s1[0]) + __uint_as_float(s1[1]);
-        const float n0 = __uint_as_float(s0[0]) + __uint_as_float(s0[1]);
-        const float zb = __uint_as_float(sz[0]) + __uint_as_float(sz[1]);
-        const uint32_t tq = cur.ct * 32u + col;
-        if (cur.kt == 0) {   // a query tile's first key tile of the head starts its sums
-            n1w[tq] = n1;
-            n0w[tq] = n0;
-            zbw[tq] = zb;
-        } else {
-            n1w[tq] += n1;
-            n0w[tq] += n0;
-            zbw[tq] += zb;
+        const float nn = __uint_as_float(sn[0]) + __uint_as_float(sn[1]);
+        if (first)   // a query tile's first key tile of the head starts its sums
+            nnw[tq] = nn;
+        else
+            nnw[tq] += nn;
+        if (wave < 4u) {   // the draw-independent row sums, key rows 8 wave .. 8 wave + 7
+            float zs = 0.f, bs = 0.f;
+#pragma unroll
+            for (uint32_t qd = 0; qd < 4u; ++qd)
+                if (qd == wave) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        zs += w[4 * qd + r];
+                        bs = __builtin_fmaf(w[4 * qd + r], u[4 * qd + r], bs);
+                    }
+                }
+            const auto sz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zs),
+                                                             __float_as_uint(bs), false, false);
+            const float zb = __uint_as_float(sz[0]) + __uint_as_float(sz[1]);
+            if (first)
+                zbw[tq] = zb;
+            else
+                zbw[tq] += zb;
         }
+    };
+
+    StepOrder<QT> cur;
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, min((uint32_t)QT, nt));
+    stg.store(tid, lds, true, min((uint32_t)QT, nt));
+    query_norms(0);
+    key_tile(0, 0);
+    __syncthreads();
+    for (uint32_t st = 0;; st ^= 1u) {
+        if (cur.kt == 0 && cur.ct == 0 && cur.h > 0) {   // uniform across the block
+            fold_head(cur.h == 1u);
+            query_norms(cur.h);
+            __syncthreads();   // Z and base read, query norms written, before either is used
+        }
+        const StepOrder<QT> nx = cur.next(nt);
+        const bool more = nx.h < H;
+        const uint32_t ntiles = min((uint32_t)QT, nt - cur.ct);
+        const uint32_t nx_tiles = min((uint32_t)QT, nt - nx.ct);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx_tiles);
+
+        // every tile's products (a tile past the last one computes on stale data, unused)
+        const unsigned char *base = lds + st * SB;
+        f32x16 dd[QT], u[QT];
+#pragma unroll
+        for (int j = 0; j < QT; ++j) {
+            dd[j] = f32x16{};
+            u[j] = f32x16{};
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+            for (int j = 0; j < QT; ++j) {
+                const unsigned char *qrow = base + j * TB + 32u * kPPitch + col * GP + 16u * half;
+                const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
+                const bf16x8 gb = *(const bf16x8 *)(qrow + 32u * GP + 32u * ks);
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd[j], 0, 0, 0);
+                u[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks], gb, u[j], 0, 0, 0);
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd[j], 0, 0, 0);
+            }
+        }
+        tile_sums(dd[0], u[0], base, cur.ct, cur.kt == 0);
+#pragma unroll
+        for (int j = 1; j < QT; ++j)
+            if ((uint32_t)j < ntiles) tile_sums(dd[j], u[j], base + j * TB, cur.ct + j, cur.kt == 0);
         if (!more) break;
-        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
+        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct, nx_tiles);
         if (nx.kt != cur.kt || nx.h != cur.h) key_tile(nx.h, nx.kt);
         __syncthreads();
         cur = nx;
@@ -477,10 +541,13 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
     return hipGetLastError();
 }
 
-size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
-    // two stages, then 4 waves x (4 running sums + 2 row sums) x S floats
-    return 2 * (size_t)stage_bytes((int)(dh / 16), 2) + (size_t)24 * S * sizeof(float);
+// LDS of the key kernel: two stages of QT query tiles, then (8 waves x 2 running sums + 4 x 2
+// row sums + the query norms) x S floats
+size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh, int qt) {
+    return 2 * (size_t)qt * stage_bytes((int)(dh / 16), 2) + (size_t)25 * S * sizeof(float);
 }
+
+constexpr size_t kMaxLds = 160 * 1024;
 
 hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const uint16_t *v,
                                   const uint16_t *g, float *c, int64_t Kc, int64_t B, int64_t H,
@@ -499,22 +566,30 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const ui
     ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
     ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-    const size_t lds = attn_key_scores_lds_bytes(S, dh);
-#define DUST_AKS(KS)                                                                           \
-    attn_key_scores_kernel<KS><<<blocks, 256, lds, s>>>(P, q, v, g, c, (uint32_t)Kc,           \
-                                                        (uint32_t)(B * S), (uint32_t)H,        \
-                                                        (uint32_t)S, q0, ec, key, draw0, tok0, \
-                                                        ndg)
+    // two query tiles per step where their stages fit beside the running sums and their
+    // products fit the registers (dh <= 80)
+    const int qt = dh <= 80 && attn_key_scores_lds_bytes(S, dh, 2) <= kMaxLds ? 2 : 1;
+    const size_t lds = attn_key_scores_lds_bytes(S, dh, qt);
+#define DUST_AKS(KS, QT)                                                                       \
+    attn_key_scores_kernel<KS, QT><<<blocks, 512, lds, s>>>(                                   \
+        P, q, v, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
+        draw0, tok0, ndg)
+#define DUST_AKS2(KS)                                                                          \
+    if (qt == 2)                                                                               \
+        DUST_AKS(KS, 2);                                                                       \
+    else                                                                                       \
+        DUST_AKS(KS, 1)
     switch (dh / 16) {
-        case 1: DUST_AKS(1); break;
-        case 2: DUST_AKS(2); break;
-        case 3: DUST_AKS(3); break;
-        case 4: DUST_AKS(4); break;
-        case 5: DUST_AKS(5); break;
-        case 6: DUST_AKS(6); break;
-        case 7: DUST_AKS(7); break;
-        default: DUST_AKS(8); break;
+        case 1: DUST_AKS2(1); break;
+        case 2: DUST_AKS2(2); break;
+        case 3: DUST_AKS2(3); break;
+        case 4: DUST_AKS2(4); break;
+        case 5: DUST_AKS2(5); break;
+        case 6: DUST_AKS(6, 1); break;
+        case 7: DUST_AKS(7, 1); break;
+        default: DUST_AKS(8, 1); break;
     }
+#undef DUST_AKS2
 #undef DUST_AKS
     return hipGetLastError();
 }

@@ -12,7 +12,10 @@ default workload is the MLP up-projection 512 -> 2048 of the 8-layer width-512 G
 The perturbed forward of the rest of the model, between the perturbation and the loss change,
 is not part of the estimator; its per-token losses are synthetic inputs here.
 --workload 3 / 4 / 5 time the LM-head chunk, the attention k/v inner-product and the 240M-shape
-chains the same way (for the report; the default line is workload 2).
+chains the same way (for the report; the default line is workload 2). With --workload 4,
+--attention-values or --attention-keys scores the draws by re-running the attention with
+perturbed values or keys (dust_attn_value_scores / dust_attn_key_scores) instead of streaming a
+synthetic attention-output change.
 
 Metric: draws x tokens per second (K * T / step time). Prints one JSON line with the per-kernel
 HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
@@ -43,7 +46,13 @@ UNIT = "draws·tokens/s"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 # Vector ALU issue rate: 256 CUs x 64 lanes x 2.4 GHz = 39.32e12 lane-operations per second.
+# This is the roof of the noise generator's instruction mix (64-bit integer multiplies, bit
+# operations, transcendentals), which issues one wave64 instruction per SIMD every 4 cycles.
 VALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12
+# fp32 multiply-adds from two or more waves per SIMD issue twice as fast: the published fp32
+# vector peak, 157.3 TFLOP/s = 78.6e12 fma lane-operations per second. It is the roof of
+# fp32-dominated vector work (the key scores' e^x - 1 and weighted sums).
+FP32_VALU_PEAK_TOPS = 2 * VALU_PEAK_TOPS
 
 # Algorithmic vector operations per generated standard normal (one issue slot each).
 # Philox4x32-10: a round is 2 32x32->64 multiplies (v_mad_u64_u32) + 2 three-input XORs
@@ -58,6 +67,9 @@ OPS_PER_NORMAL = 8.5 + 3.5
 OPS_INJECT_EXTRA = 2.0    # half the coefficient x radius multiply, fma with y, half a bf16 pack
 OPS_EE_EXTRA = 1.5        # half the reward x radius multiply, fma into the accumulator
 OPS_HEAD_EXTRA = 3.5      # half the coefficient x radius multiply, multiply, exp2, fma
+# Key scores, per (draw, head, query, key <= query): e^x - 1 of the logit shift by a degree-5
+# polynomial (4 fma + 1 multiply) and the two weighted sums N1, N0 (2 fma).
+OPS_KEY_SCORE = 7.0
 
 
 def parse():
@@ -80,6 +92,10 @@ def parse():
                     help="workload 4: score by re-running the attention with perturbed values "
                          "(dust_attn_value_scores on synthetic attention weights, 8 heads of 64) "
                          "instead of streaming a synthetic attention-output change")
+    ap.add_argument("--attention-keys", action="store_true",
+                    help="workload 4: score by re-running the softmax with perturbed keys "
+                         "(dust_attn_key_scores on synthetic queries, keys and values, 8 heads of "
+                         "64) instead of streaming a synthetic attention-output change")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -313,12 +329,24 @@ class InnerChain(Chain):
         self.gobits = synth.normal_bf16(g, (self.T, self.d))
         self.xbits = synth.normal_bf16(g, (self.T, self.d))
         self.go, self.x = self.bf(self.gobits), self.bf(self.xbits)
-        if self.attn_values:
+        B, S, H = self.T // self.S, self.S, self.HEADS
+        if self.attn_mode == "values":
             # attention weights of the clean forward: a causal softmax of N(0, 1) scores per
             # head and sequence, drawn on the device from a seeded generator before timing
-            B, S, H = self.T // self.S, self.S, self.HEADS
             gen = t.Generator(device=self.dev).manual_seed(7000 + self.cfg_id)
             z = t.randn((B, H, S, S), generator=gen, device=self.dev)
+            z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
+            self.P = t.softmax(z, -1).to(t.bfloat16)
+            del z
+        elif self.attn_mode == "keys":
+            # queries, keys and values N(0, 1) in bf16; the clean forward's weights are the
+            # causal softmax of tau q k^T per head (fp32 on the device, before timing)
+            self.tau = 1.0 / np.sqrt(self.d // H)
+            self.qbits, kbits, self.vbits = (synth.normal_bf16(synth.rng(self.cfg_id, j),
+                                                               (self.T, self.d)) for j in (3, 4, 5))
+            self.q, self.v = self.bf(self.qbits), self.bf(self.vbits)
+            heads = lambda a: a.float().reshape(B, S, H, -1).permute(0, 2, 1, 3)
+            z = self.tau * heads(self.q) @ heads(self.bf(kbits)).transpose(-1, -2).contiguous()
             z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
             self.P = t.softmax(z, -1).to(t.bfloat16)
             del z
@@ -338,15 +366,19 @@ class InnerChain(Chain):
         self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d, self.d)
         self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
 
-    attn_values = False
+    attn_mode = None   # None, "values" or "keys"
     HEADS = 8
 
     def step(self, run, sh):
         d, T, K, KB = self.dust, self.T, self.K, self.KB
-        if self.attn_values:
+        if self.attn_mode == "values":
             run("dust_attn_value_scores", d.dust_attn_value_scores, self.P, self.go, self.cbuf, K,
                 T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma, self.seed,
                 self.tag, 0, 0, sh)
+        elif self.attn_mode == "keys":
+            run("dust_attn_key_scores", d.dust_attn_key_scores, self.P, self.q, self.v, self.go,
+                self.cbuf, K, T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma,
+                self.tau, self.seed, self.tag, 0, 0, sh)
         else:
             for blk in range(K // KB):
                 run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do,
@@ -368,6 +400,9 @@ class InnerChain(Chain):
             # the key-query inner products over the causal triangle: 2 (S (S + 1) / 2) dh flops
             # per draw, head and sequence
             "dust_attn_value_scores": _mfma(2.0 * K * (T // S) * H * (S * (S + 1) / 2) * (d // H)),
+            # per causal (draw, head, query, key) element: e^x - 1 and two weighted sums, fp32
+            "dust_attn_key_scores": ("alu", OPS_KEY_SCORE * K * (T // S) * H * (S * (S + 1) / 2),
+                                     1e12, FP32_VALU_PEAK_TOPS, "Tops/s"),
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_error_estimate": _alu(K * T * d, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * d * d),
@@ -377,17 +412,24 @@ class InnerChain(Chain):
         cfg = {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
                "draws": self.K, "draw_block": self.KB, "gamma": self.gamma, "sigma": self.sigma,
                "storage": "bf16 delta_o / g_o / x, fp32 scores, rewards, g_hat, G_W"}
-        if self.attn_values:
+        if self.attn_mode == "values":
             cfg.update({"workload": self.c["name"] + "_attention_values", "heads": self.HEADS,
                         "head_dim": self.d // self.HEADS, "draw_block": self.K,
                         "delta_o": "attention re-run with perturbed values (synthetic weights)",
                         "storage": "bf16 attention weights / g_o / x, fp32 scores, rewards, "
                                    "g_hat, G_W"})
+        elif self.attn_mode == "keys":
+            cfg.update({"workload": self.c["name"] + "_attention_keys", "heads": self.HEADS,
+                        "head_dim": self.d // self.HEADS, "draw_block": self.K,
+                        "softmax_scale": self.tau,
+                        "delta_o": "softmax re-run with perturbed keys (synthetic q, k, v)",
+                        "storage": "bf16 attention weights / q / v / g_o / x, fp32 scores, "
+                                   "rewards, g_hat, G_W"})
         return cfg
 
     def cpu_baseline(self, scale):
         import oracle
-        if self.attn_values:
+        if self.attn_mode is not None:
             return self._cpu_baseline_attention(scale)
         S, d = self.S, self.d
         K_s, T_s = max(8, int(8192 * scale) // 8 * 8), S
@@ -424,15 +466,20 @@ class InnerChain(Chain):
         P = self.P[:1].float().cpu().numpy().astype(np.float64)          # the first sequence
         go = synth.bf16_bits_to_f32(self.gobits[:S]).astype(np.float64)
         t0 = time.perf_counter()
-        c = oracle.attn_value_scores(P, go, K_s, self.sigma, self.seed, self.tag)
+        if self.attn_mode == "keys":
+            q, v = (synth.bf16_bits_to_f32(a[:S]).astype(np.float64) for a in (self.qbits, self.vbits))
+            c = oracle.attn_key_scores(P, q, v, go, K_s, self.sigma, self.tau, self.seed, self.tag)
+        else:
+            c = oracle.attn_value_scores(P, go, K_s, self.sigma, self.seed, self.tag)
         r = oracle.reward_scan(c, S, self.gamma)
         g = oracle.error_estimate(r, d, self.sigma, self.seed, self.tag, K_total=self.K)
         oracle.weight_grad(g, synth.bf16_bits_to_f32(self.xbits[:S]).astype(np.float64))
         dt = time.perf_counter() - t0
         return {"value": K_s * S / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
                 "sample": "%d of %d draws x first %d tokens (one sequence, %d heads): attention "
-                          "value scores, scan, error estimate, G_W; %.1f s"
-                          % (K_s, self.K, S, H, dt)}
+                          "%s scores, scan, error estimate, G_W; %.1f s"
+                          % (K_s, self.K, S, H, "key" if self.attn_mode == "keys" else "value",
+                             dt)}
 
 
 CHAINS = {2: LinearChain, 3: HeadChain, 4: InnerChain, 5: LinearChain}
@@ -462,11 +509,12 @@ def main() -> int:
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
     chain.optimizer = args.optimizer
-    if args.attention_values:
-        if args.workload != 4:
-            print("--attention-values applies to workload 4 only", file=sys.stderr)
+    if args.attention_values or args.attention_keys:
+        if args.workload != 4 or (args.attention_values and args.attention_keys):
+            print("--attention-values or --attention-keys (one of them) applies to workload 4 "
+                  "only", file=sys.stderr)
             return 2
-        chain.attn_values = True
+        chain.attn_mode = "values" if args.attention_values else "keys"
     chain.setup()
     chain.opt_setup()
 
@@ -557,7 +605,7 @@ KERNEL_SOURCES = {
     "dust_error_estimate": "error_estimate.hip",
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
-    "dust_attn_value_scores": "attn_scores.hip",
+    "dust_attn_value_scores": "attn_scores.hip", "dust_attn_key_scores": "attn_scores.hip",
 }
 
 
