@@ -24,12 +24,13 @@
 // (v_mfma_f32_32x32x16_bf16; the noise split into a bf16 high part and a bf16 remainder so that
 // it keeps 16 significant bits): E_st = <a_s, g_t> for values, D_st = <a_s, q_t> for keys. The
 // output tile's layout (lane l holds query l % 32 and 16 of the key rows) lets each lane weight
-// and sum its keys; one lane-half swap (v_permlane32_swap) completes the sum over the 32 keys
-// of two draws at once.
+// and sum its keys; one lane-half swap (v_permlane32_swap) completes two sums over the 32 keys
+// at once (two draws' scores for values, one draw's N1 and N0 for keys).
 //
-// Work layout: a block of 4 waves owns one sequence and 8 draws, two per wave; the block walks
-// heads, then key tiles, then the query tiles at or after the key tile (causal order). Each
-// step's weight tile (widened to fp32) and the query-side bf16 tiles are staged in LDS by the
+// Work layout: a block owns one sequence and 8 draws (values: 4 waves, two draws each; keys: 8
+// waves, one draw each, so that each SIMD holds two waves); the block walks heads, then key
+// tiles, then the query tiles at or after the key tile (causal order). Each step's weight tiles
+// (widened to fp32, the causal mask applied) and query-side bf16 tiles are staged in LDS by the
 // whole block, double-buffered with one barrier per step; the key-side operands (noise, and the
 // values for keys) stay in registers for the whole key tile.
 #include "dust_internal.hpp"
