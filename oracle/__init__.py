@@ -59,6 +59,8 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
                                                ctypes.c_double, _u64, _u32, _u32, _u32, _i64,
                                                ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
                                                _d]
+    lib.dust_or_attn_query_scores.argtypes = lib.dust_or_attn_key_scores.argtypes
+    lib.dust_or_attn_query_scores_at.argtypes = lib.dust_or_attn_key_scores_at.argtypes
     lib.dust_or_sgd_momentum.argtypes = [_d, _d, _d, _i64, ctypes.c_double, ctypes.c_double]
     lib.dust_or_adam.argtypes = [_d, _d, _d, _d, _i64, ctypes.c_double, ctypes.c_double,
                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64]
@@ -264,6 +266,35 @@ def attn_key_scores_at(P, q, v, g_o, k, t, sigma: float, tau: float, seed: int, 
     _load().dust_or_attn_key_scores_at(_p(Pd), _p(qd), _p(vd), _p(gd), H, S, dh, sigma, tau, seed,
                                        tag, draw0, tok0, chan0, _pidx(k), _pidx(t), len(k),
                                        _p(out))
+    return out
+
+
+def attn_query_scores(P, k, v, g_o, K: int, sigma: float, tau: float, seed: int, tag: int,
+                      draw0: int = 0, tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """Scores c [K, T] of K draws perturbing an attention query projection (dust_oracle.c states
+    the formula): P [B, H, S, S] attention weights (query rows), k, v, g_o [T, H*dh], tau the
+    softmax scale."""
+    Pd, kd, vd, gd = _f64(P), _f64(k), _f64(v), _f64(g_o)
+    B, H, S, _ = Pd.shape
+    T = B * S
+    dh = gd.shape[1] // H
+    c = np.empty((K, T), dtype=np.float64)
+    _load().dust_or_attn_query_scores(_p(Pd), _p(kd), _p(vd), _p(gd), K, B, H, S, dh, sigma, tau,
+                                      seed, tag, draw0, tok0, chan0, _p(c))
+    return c
+
+
+def attn_query_scores_at(P, k, v, g_o, kk, t, sigma: float, tau: float, seed: int, tag: int,
+                         draw0: int = 0, tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """attn_query_scores at chosen local (draw, token) pairs."""
+    Pd, kd, vd, gd = _f64(P), _f64(k), _f64(v), _f64(g_o)
+    B, H, S, _ = Pd.shape
+    dh = gd.shape[1] // H
+    kk, t = _idx(kk), _idx(t)
+    out = np.empty(len(kk), dtype=np.float64)
+    _load().dust_or_attn_query_scores_at(_p(Pd), _p(kd), _p(vd), _p(gd), H, S, dh, sigma, tau,
+                                         seed, tag, draw0, tok0, chan0, _pidx(kk), _pidx(t),
+                                         len(kk), _p(out))
     return out
 
 

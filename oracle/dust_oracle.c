@@ -331,6 +331,87 @@ void dust_or_attn_key_scores_at(const double *P, const double *q, const double *
     }
 }
 
+/* Scores of draws that perturb an attention QUERY projection, scored the same way. With
+ * q'_t = q_t + sigma a_t, head h's logit of query t on key s moves by
+ * delta_ts = sigma tau <a_t, k_s>, and the re-run is the softmax re-run above with these shifts:
+ *     P'_ts = P_ts e^{delta_ts} / sum_{s' <= t} P_ts' e^{delta_ts'},
+ *     Delta o_t = sum_{s <= t} (P'_ts - Pbar_ts) v_s,   c_t = -sum_h <Delta o^h_t, g^h_t>.
+ * k, v and g are [T, H dh]; the noise of (token t, head h, column j) is channel chan0 + h dh + j
+ * of token tok0 + t in draw draw0 + i. */
+static double query_score_one(const double *P, const double *k, const double *v,
+                              const double *g, int64_t H, int64_t S, int64_t dh, double sigma,
+                              double tau, uint64_t seed, uint32_t tag, uint32_t draw,
+                              uint32_t tok0, int64_t chan0, int64_t t, double *dl, double *a)
+{
+    const int64_t b = t / S, tl = t % S, d = H * dh;
+    double acc = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+        const double *prow = P + ((b * H + h) * S + tl) * S;
+        for (int64_t j = 0; j < dh; ++j)
+            a[j] = dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + t),
+                                  (uint64_t)(chan0 + h * dh + j));
+        double Z = 0.0, mx = -INFINITY;
+        for (int64_t sl = 0; sl <= tl; ++sl) {
+            double dot = 0.0;
+            for (int64_t j = 0; j < dh; ++j) dot += a[j] * k[(b * S + sl) * d + h * dh + j];
+            dl[sl] = sigma * tau * dot;
+            Z += prow[sl];
+            if (dl[sl] > mx) mx = dl[sl];
+        }
+        if (Z == 0.0) continue;
+        double den = 0.0;
+        for (int64_t sl = 0; sl <= tl; ++sl) den += prow[sl] * exp(dl[sl] - mx);
+        for (int64_t j = 0; j < dh; ++j) {
+            double dO = 0.0;
+            for (int64_t sl = 0; sl <= tl; ++sl)
+                dO += (prow[sl] * exp(dl[sl] - mx) / den - prow[sl] / Z) *
+                      v[(b * S + sl) * d + h * dh + j];
+            acc += dO * g[t * d + h * dh + j];
+        }
+    }
+    return -acc;
+}
+
+void dust_or_attn_query_scores(const double *P, const double *k, const double *v,
+                               const double *g, int64_t K, int64_t B, int64_t H, int64_t S,
+                               int64_t dh, double sigma, double tau, uint64_t seed, uint32_t tag,
+                               uint32_t draw0, uint32_t tok0, int64_t chan0, double *c)
+{
+    const int64_t T = B * S;
+    #pragma omp parallel
+    {
+        double *dl = malloc((size_t)S * sizeof(double));
+        double *a = malloc((size_t)dh * sizeof(double));
+        #pragma omp for collapse(2) schedule(dynamic)
+        for (int64_t i = 0; i < K; ++i)
+            for (int64_t t = 0; t < T; ++t)
+                c[i * T + t] = query_score_one(P, k, v, g, H, S, dh, sigma, tau, seed, tag,
+                                               (uint32_t)(draw0 + i), tok0, chan0, t, dl, a);
+        free(a);
+        free(dl);
+    }
+}
+
+/* The same scores at n chosen (draw, token) pairs: out[m] = c[kk[m]][t[m]]. */
+void dust_or_attn_query_scores_at(const double *P, const double *k, const double *v,
+                                  const double *g, int64_t H, int64_t S, int64_t dh,
+                                  double sigma, double tau, uint64_t seed, uint32_t tag,
+                                  uint32_t draw0, uint32_t tok0, int64_t chan0,
+                                  const int64_t *kk, const int64_t *t, int64_t n, double *out)
+{
+    #pragma omp parallel
+    {
+        double *dl = malloc((size_t)S * sizeof(double));
+        double *a = malloc((size_t)dh * sizeof(double));
+        #pragma omp for schedule(dynamic)
+        for (int64_t m = 0; m < n; ++m)
+            out[m] = query_score_one(P, k, v, g, H, S, dh, sigma, tau, seed, tag,
+                                     (uint32_t)(draw0 + kk[m]), tok0, chan0, t[m], dl, a);
+        free(a);
+        free(dl);
+    }
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Discounted reward r_t = sum_{s >= t, s in t's sequence} gamma^(s - t) c_s (explainer,
  * "Credit assignment"). Tokens are T = B * seg_len, sequence b owns [b*seg_len, (b+1)*seg_len).

@@ -42,6 +42,8 @@ def _causal_weights(g, B, H, S, garbage_above=False):
     (1, 1, 96, 128, 9, 8, 2, 5, True),       # widest heads, three groups of draws
     (1, 4, 64, 48, 4, 4, 0, 0, False),       # three k-slices
     (1, 1, 2048, 16, 2, 0, 0, 0, False),     # long sequence: more than 64 KB of LDS per block
+    (1, 1, 4096, 16, 1, 0, 0, 0, True),      # the longest sequence supported
+    (1, 2, 256, 128, 17, 0, 5, 0, False),    # widest heads, three draw blocks, a ragged one
 ])
 def test_attn_value_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage):
     announce("attn value scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage),))
@@ -91,6 +93,9 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     (1, 2, 1024, 16, 2, 0, 0, 0, False, 0.05, 0.25),     # longest sequence
     (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
     (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
+    (1, 1, 1024, 128, 2, 0, 0, 0, True, 0.02, 0.09),     # longest sequence at the widest heads
+    (1, 1, 512, 80, 3, 0, 0, 0, False, 0.02, 0.11),      # the widest heads with two tiles a step
+    (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
 ])
 def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn key scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))

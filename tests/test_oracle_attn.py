@@ -16,6 +16,9 @@ tau q k^T and of tau q (k + sigma a)^T with numpy, and compare the output change
 product; the first-order term is the textbook softmax Jacobian P_s (delta_sr - P_r); a row's
 weights count only relative to their sum, so rescaling rows changes nothing; sigma = 0 and a
 query that attends only to itself give exactly zero; weights above the diagonal are ignored.
+
+Queries: the same softmax re-run with the logits moved by sigma tau <a_t, k_s> (the noise at the
+query token), pinned the same way against softmax(tau (q + sigma a) k^T).
 """
 import numpy as np
 import pytest
@@ -181,3 +184,65 @@ def test_sampled_key_scores_equal_the_full_array():
     k, t = np.array([0, 2, 1, 2]), np.array([0, 31, 17, 16])
     np.testing.assert_array_equal(
         oracle.attn_key_scores_at(P, q, v, go, k, t, 0.03, 0.35, 11, 5, 2, 7, 16), full[k, t])
+
+
+@pytest.mark.parametrize("B,H,S,dh,K,chan0,draw0,tok0", [
+    (2, 2, 12, 8, 3, 0, 0, 0),
+    (1, 3, 20, 4, 2, 64, 5, 100),
+])
+def test_query_scores_equal_an_explicit_attention_rerun(B, H, S, dh, K, chan0, draw0, tok0):
+    g = np.random.default_rng(69)
+    T, d, sigma, tau, seed, tag = B * S, H * dh, 0.3, 1.0 / np.sqrt(dh), 0x5EEE, 5
+    q, k, v, go = (g.standard_normal((T, d)) for _ in range(4))
+    kT = _heads(k, B, S, H).transpose(0, 1, 3, 2)
+    P = _softmax_causal(tau * _heads(q, B, S, H) @ kT)
+    o = np.einsum("bhts,bhsj->bhtj", P, _heads(v, B, S, H))
+    a = oracle.normals(seed, tag, draw0, tok0, chan0, K, T, d)
+    ref = np.empty((K, T))
+    for i in range(K):
+        Pp = _softmax_causal(tau * _heads(q + sigma * a[i], B, S, H) @ kT)
+        do = np.einsum("bhts,bhsj->bhtj", Pp, _heads(v, B, S, H)) - o
+        ref[i] = -np.einsum("bhtj,bhtj->bt", do, _heads(go, B, S, H)).reshape(T)
+    got = oracle.attn_query_scores(P, k, v, go, K, sigma, tau, seed, tag, draw0, tok0, chan0)
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-12)
+
+
+def test_query_scores_first_order_is_the_softmax_jacobian():
+    g = np.random.default_rng(70)
+    B, H, S, dh, K, tau = 1, 2, 16, 8, 2, 0.4
+    T, d = B * S, H * dh
+    k, v, go = (g.standard_normal((T, d)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    a = oracle.normals(3, 8, 0, 0, 0, K, T, d)
+    kh, vh, gh = _heads(k, B, S, H), _heads(v, B, S, H), _heads(go, B, S, H)
+    u = gh @ vh.transpose(0, 1, 3, 2)
+    lin = np.empty((K, T))
+    for i in range(K):
+        D = tau * _heads(a[i], B, S, H) @ kh.transpose(0, 1, 3, 2)     # d logit_ts / d sigma
+        dP = P * (D - (P * D).sum(-1, keepdims=True))
+        lin[i] = -(dP * u).sum(-1).sum(1).reshape(T)
+    for sigma in (1e-5, 1e-6):
+        got = oracle.attn_query_scores(P, k, v, go, K, sigma, tau, 3, 8) / sigma
+        np.testing.assert_allclose(got, lin, rtol=3 * sigma * 1e2, atol=1e-9)
+
+
+def test_query_scores_row_scale_diagonal_and_zeros():
+    g = np.random.default_rng(71)
+    B, H, S, dh, K, sigma, tau = 2, 2, 12, 4, 2, 0.2, 0.5
+    T, d = B * S, H * dh
+    k, v, go = (g.standard_normal((T, d)) for _ in range(3))
+    P = _causal_weights(g, B, H, S)
+    c = oracle.attn_query_scores(P, k, v, go, K, sigma, tau, 9, 3)
+    scaled = P * np.exp(g.standard_normal((B, H, S, 1)))
+    np.testing.assert_allclose(oracle.attn_query_scores(scaled, k, v, go, K, sigma, tau, 9, 3), c,
+                               rtol=1e-10, atol=1e-13)
+    junk = P + np.triu(np.abs(g.standard_normal((S, S))), 1)[None, None]
+    assert np.array_equal(oracle.attn_query_scores(junk, k, v, go, K, sigma, tau, 9, 3), c)
+    assert np.all(oracle.attn_query_scores(P, k, v, go, K, 0.0, tau, 9, 3) == 0.0)
+    eye = np.broadcast_to(np.eye(S), (B, H, S, S)).copy()
+    assert np.all(oracle.attn_query_scores(eye, k, v, go, K, sigma, tau, 9, 3) == 0.0)
+    assert np.any(c != 0.0)
+    full = oracle.attn_query_scores(P, k, v, go, K, sigma, tau, 9, 3, 2, 7, 16)
+    kk, t = np.array([0, 1, 1]), np.array([0, 23, 12])
+    np.testing.assert_array_equal(
+        oracle.attn_query_scores_at(P, k, v, go, kk, t, sigma, tau, 9, 3, 2, 7, 16), full[kk, t])

@@ -87,6 +87,10 @@ PINS_STEPS = [
     attn.test_key_scores_first_order_is_the_softmax_jacobian,
     attn.test_key_scores_invariant_to_row_scale_and_blind_above_the_diagonal,
     attn.test_key_scores_vanish_at_sigma_zero_and_for_self_attention,
+    lambda: attn.test_query_scores_equal_an_explicit_attention_rerun(2, 2, 12, 8, 3, 0, 0, 0),
+    lambda: attn.test_query_scores_equal_an_explicit_attention_rerun(1, 3, 20, 4, 2, 64, 5, 100),
+    attn.test_query_scores_first_order_is_the_softmax_jacobian,
+    attn.test_query_scores_row_scale_diagonal_and_zeros,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -149,6 +153,17 @@ MUTATIONS = [
      "for (int64_t sl = 0; sl < S; ++sl) {\n            double dot = 0.0;"),
     ("key output change drops the value", "* exp(dl[sl] - mx) / den - prow[sl] / Z) *\n                      v[(b * S + sl) * d + h * dh + j];",
      "* exp(dl[sl] - mx) / den - prow[sl] / Z) *\n                      v[t * d + h * dh + j];"),
+    ("query noise at the sequence start", "a[j] = dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + t),",
+     "a[j] = dust_or_normal(seed, tag, draw, (uint32_t)(tok0 + b * S),"),
+    ("query logit uses the query's own key", "dot += a[j] * k[(b * S + sl) * d + h * dh + j];",
+     "dot += a[j] * k[t * d + h * dh + j];"),
+    ("query logit shift without the softmax scale",
+     "dot += a[j] * k[(b * S + sl) * d + h * dh + j];\n            dl[sl] = sigma * tau * dot;",
+     "dot += a[j] * k[(b * S + sl) * d + h * dh + j];\n            dl[sl] = sigma * dot;"),
+    ("query score sign", "    return -acc;\n}\n\nvoid dust_or_attn_query_scores(",
+     "    return acc;\n}\n\nvoid dust_or_attn_query_scores("),
+    ("query head offset dropped", "(uint64_t)(chan0 + h * dh + j));\n        double Z",
+     "(uint64_t)(chan0 + j));\n        double Z"),
 ]
 
 
