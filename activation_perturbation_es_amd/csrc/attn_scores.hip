@@ -90,7 +90,7 @@ __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uin
 // Staging of one step: QT query tiles, each as 16-byte pieces, P rows first (4 per query row),
 // then the NQ query-side tiles (2 KS per row each); loads into registers, stores to LDS after
 // the step's compute. Only the first ntiles query tiles of a step exist.
-template <int KS, int NQ, uint32_t NT = 256, int QT = 1>
+template <int KS, int NQ, uint32_t NT = 256, int QT = 1, bool TP = false>
 struct Stager {
     static constexpr uint32_t kTilePieces = 128u + 64u * KS * NQ;
     static constexpr uint32_t kPieces = QT * kTilePieces;
@@ -98,12 +98,13 @@ struct Stager {
     static constexpr uint32_t kTileBytes = stage_bytes(KS, NQ);
     u32x4 r[kPerThread];
 
-    // P [B, H, S, S]; the query-side arrays [T, H DH]; query tiles ct .. ct + ntiles - 1 of
-    // sequence b, head h, key tile kt
+    // P [B, H, S, S]: query tiles ct .. ct + ntiles - 1 over key tile kt of sequence b, head h;
+    // the side arrays [T, H DH]: row tiles xt .. xt + ntiles - 1 of the sequence (the query
+    // tiles for value and key scores, the key tile for query scores)
     __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P,
                                          const uint16_t *const (&qs)[NQ], uint32_t b, uint32_t H,
                                          uint32_t S, uint32_t d, uint32_t h, uint32_t kt,
-                                         uint32_t ct, uint32_t ntiles) {
+                                         uint32_t ct, uint32_t ntiles, uint32_t xt) {
         constexpr uint32_t DH = 16u * KS;
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
@@ -116,12 +117,13 @@ struct Stager {
                 r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + qt * 32u + row) * S +
                                         kt * 32u + 8u * seg);
             } else {
+                const uint32_t xr = xt + tile;
                 const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n)
                     if (m == (uint32_t)n)
-                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + qt * 32u + row) * d +
+                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + xr * 32u + row) * d +
                                                 h * DH + 8u * seg);
             }
         }
@@ -129,7 +131,7 @@ struct Stager {
 
     // P widened to fp32 once here for all draws; on a diagonal tile (the step's first tile when
     // mask is set) the keys after the row's query become 0, so later arithmetic needs no causal
-    // test
+    // test. TP stores the tile transposed, [32 keys][32 queries].
     __device__ __forceinline__ void store(uint32_t tid, unsigned char *base, bool mask,
                                           uint32_t ntiles) const {
         constexpr uint32_t GP = g_pitch(KS);
@@ -153,8 +155,14 @@ struct Stager {
 #pragma unroll
                     for (uint32_t e = 0; e < 8u; ++e) f[e] = 8u * seg + e <= row ? f[e] : 0.f;
                 }
-                dst[0] = f32x4{f[0], f[1], f[2], f[3]};
-                dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+                if (TP) {
+#pragma unroll
+                    for (uint32_t e = 0; e < 8u; ++e)
+                        *(float *)(tb + (8u * seg + e) * kPPitch + 4u * row) = f[e];
+                } else {
+                    dst[0] = f32x4{f[0], f[1], f[2], f[3]};
+                    dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+                }
             } else {
                 const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
@@ -220,14 +228,14 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     // Step n's tiles are in LDS stage n % 2; step n + 1's are fetched into registers at the
     // start of step n and stored to the other stage at its end, before the one barrier per step.
     StepOrder<> cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 1);
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 1, 0);
     stg.store(tid, lds, true, 1);
     noise(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;   // uniform across the block
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, 1);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, 1, nx.ct);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -461,7 +469,7 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
     };
 
     StepOrder<QT> cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, min((uint32_t)QT, nt));
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, min((uint32_t)QT, nt), 0);
     stg.store(tid, lds, true, min((uint32_t)QT, nt));
     query_norms(0);
     key_tile(0, 0);
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
         const bool more = nx.h < H;
         const uint32_t ntiles = min((uint32_t)QT, nt - cur.ct);
         const uint32_t nx_tiles = min((uint32_t)QT, nt - nx.ct);
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx_tiles);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx_tiles, nx.ct);
 
         // every tile's products (a tile past the last one computes on stale data, unused)
         const unsigned char *base = lds + st * SB;
@@ -510,6 +518,240 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
     }
     __syncthreads();
     fold_head(H == 1u);
+}
+
+// Query scores: the transpose of the key scores. The noise sits on the query side, so a block
+// walks heads, then query tiles, then the key tiles at or before the query tile, generating the
+// noise of a query tile once; the products D^T = a k^T and U^T = g v^T come out with the query
+// tile's rows in each lane's registers and its key in the lane's column, so every lane keeps
+// the running sums N1, N0 of its 16 query rows in registers over the key tiles and one lane
+// reduction per query tile completes them. NW waves, one draw per wave: 8 (two per SIMD) where
+// the registers allow, 4 for the widest heads.
+template <int KS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
+    const uint16_t *__restrict__ P, const uint16_t *__restrict__ km,
+    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g, float *__restrict__ c,
+    uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
+    uint32_t draw0, uint32_t tok0, uint32_t ndg) {
+    // LDS: two stages of one step's operands (P tile transposed [32 keys][32 queries], k and v
+    // tiles [32 keys][DH]); the query tile's row sums Z and base from waves 0-3, double-buffered
+    // by query tile, [2][Z, base][32]; the key norms |k_s|, double-buffered by head, [2][S].
+    extern __shared__ __align__(16) unsigned char lds[];
+    constexpr uint32_t DH = 16u * KS;
+    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 2);
+    const uint32_t tid = threadIdx.x;
+    const uint32_t wave = wave_in_block();
+    const uint32_t lane = tid & 63u;
+    const uint32_t b = blockIdx.x / ndg;
+    const uint32_t i = (blockIdx.x % ndg) * NW + wave;
+    const uint32_t draw = draw0 + min(i, Kc - 1u);
+    const uint32_t col = lane & 31u, half = lane >> 5;
+    float *ZB = (float *)(lds + 2u * SB);
+    float *KN = ZB + 128u;
+
+    const uint32_t d = H * DH;
+    const uint32_t nt = S / 32u;
+    const uint16_t *const ks_[2] = {km, v};
+    Stager<KS, 2, NW * 64, 1, true> stg;
+
+    // query-side operands of the current query tile: the draw's noise, the output error g, and
+    // the largest noise norm over the tile's 32 queries
+    bf16x8 ahi[KS], alo[KS], gq[KS];
+    float amax = 0.f;
+    auto query_tile = [&](uint32_t h, uint32_t ct) {
+        const uint32_t row = b * S + ct * 32u + col;
+        const uint16_t *grow = g + (uint64_t)row * d + h * DH + 8u * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            gq[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(grow + 16u * ks));
+        float n2;
+        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
+        n2 += __shfl_xor(n2, 32);
+#pragma unroll
+        for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+    };
+    // |k_s| of head h for every key of the sequence
+    auto key_norms = [&](uint32_t h) {
+        float *kn = KN + (h & 1u) * S;
+        for (uint32_t t = tid; t < S; t += NW * 64u) {
+            const uint16_t *krow = km + ((uint64_t)b * S + t) * d + h * DH;
+            float n2 = 0.f;
+#pragma unroll
+            for (uint32_t p = 0; p < 2u * KS; ++p) {
+                const u32x4 w = *(const u32x4 *)(krow + 8u * p);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = __uint_as_float(w[e] << 16);
+                    const float hi = __uint_as_float(w[e] & 0xFFFF0000u);
+                    n2 = __builtin_fmaf(hi, hi, __builtin_fmaf(lo, lo, n2));
+                }
+            }
+            kn[t] = __builtin_sqrtf(n2);
+        }
+    };
+
+    const float lim_cs = ec.lim * 0.999f;
+    const uint32_t lim_bits = __float_as_uint(ec.lim) << 1;
+
+    // running sums of the current query tile: element r is query row 8 (r / 4) + 4 half + r % 4,
+    // summed over this lane's key column
+    float n1[16], n0[16], zs[4], bs[4];
+    // completed sums N1, N0 of the previous query tile (the row each lane holds: see fold)
+    float t1 = 0.f, t0 = 0.f;
+    uint32_t fold_tile = 0xFFFFFFFFu;   // global index h * nt + ct of the tile awaiting its fold
+    auto reset = [&]() {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) n1[r] = n0[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zs[j] = bs[j] = 0.f;
+    };
+    // Sum the running sums over the 32 key columns (lanes of one half); lane l then takes the
+    // totals of row m(l) = 8 ((l & 15) >> 2) + 4 (l >> 5) + (l & 3) when (l & 31) < 16. Waves 0-3
+    // also complete their row sums Z and base and leave them in LDS.
+    auto finish_tile = [&](uint32_t gt) {
+#pragma unroll
+        for (int m = 1; m <= 16; m <<= 1)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                n1[r] += __shfl_xor(n1[r], m);
+                n0[r] += __shfl_xor(n0[r], m);
+            }
+        const uint32_t rr = lane & 15u;
+        t1 = 0.f;
+        t0 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            t1 = rr == (uint32_t)r ? n1[r] : t1;
+            t0 = rr == (uint32_t)r ? n0[r] : t0;
+        }
+        if (wave < 4u) {
+#pragma unroll
+            for (int m = 1; m <= 16; m <<= 1)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    zs[j] += __shfl_xor(zs[j], m);
+                    bs[j] += __shfl_xor(bs[j], m);
+                }
+            // rows 8 wave + 4 half + j, j < 4: lane (half, j) writes them
+            float *zb = ZB + (gt & 1u) * 64u;
+            if ((lane & 31u) < 4u) {
+                const uint32_t j = lane & 3u, m = 8u * wave + 4u * half + j;
+                float z = zs[0], bb = bs[0];
+#pragma unroll
+                for (uint32_t jj = 1; jj < 4u; ++jj) {
+                    z = j == jj ? zs[jj] : z;
+                    bb = j == jj ? bs[jj] : bb;
+                }
+                zb[m] = z;
+                zb[32u + m] = bb;
+            }
+        }
+        fold_tile = gt;
+    };
+    // Fold the completed tile into this wave's draw: (Z N1 - base N0) / (Z (Z + N0)).
+    auto fold = [&]() {
+        if (fold_tile == 0xFFFFFFFFu) return;
+        const uint32_t h = fold_tile / nt, ct = fold_tile % nt;
+        fold_tile = 0xFFFFFFFFu;
+        if (i >= Kc || (lane & 31u) >= 16u) return;
+        const uint32_t m = 8u * ((lane & 15u) >> 2) + 4u * half + (lane & 3u);
+        const float *zb = ZB + (((h * nt + ct) & 1u) * 64u);
+        const float Z = zb[m], bsum = zb[32u + m];
+        const float val = Z > 0.f ? (Z * t1 - bsum * t0) / (Z * (Z + t0)) : 0.f;
+        float *cr = c + (uint64_t)i * T + (uint64_t)b * S + ct * 32u + m;
+        *cr = h == 0 ? -val : *cr - val;
+    };
+
+    // steps: head, query tile ct, key tile kt <= ct
+    uint32_t h = 0, ct = 0, kt = 0;
+    stg.load(tid, P, ks_, b, H, S, d, 0, 0, 0, 1, 0);
+    stg.store(tid, lds, true, 1);
+    key_norms(0);
+    query_tile(0, 0);
+    reset();
+    __syncthreads();
+    for (uint32_t st = 0;; st ^= 1u) {
+        fold();   // the previous query tile's sums, once its row sums are in LDS
+        uint32_t nh = h, nc = ct, nk = kt + 1u;
+        if (nk > ct) {
+            nk = 0;
+            nc = ct + 1u;
+            if (nc == nt) { nc = 0; nh = h + 1u; }
+        }
+        const bool more = nh < H;
+        // the staged key tile is kt; the P tile is (query tile ct, key tile kt)
+        if (more) stg.load(tid, P, ks_, b, H, S, d, nh, nk, nc, 1, nk);   // k, v of key tile nk
+
+        const unsigned char *base = lds + st * SB;
+        const unsigned char *krow = base + 32u * kPPitch + col * GP + 16u * half;
+        const unsigned char *vrow = krow + 32u * GP;
+        f32x16 dd = {}, u = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 kb = *(const bf16x8 *)(krow + 32u * ks);
+            const bf16x8 vb = *(const bf16x8 *)(vrow + 32u * ks);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kb, dd, 0, 0, 0);
+            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gq[ks], vb, u, 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kb, dd, 0, 0, 0);
+        }
+        const float kn = KN[(h & 1u) * S + kt * 32u + col];
+        const unsigned char *prow = base + col * kPPitch + 16u * half;
+        float w[16];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) w[4 * qd + r] = x[r];
+        }
+        bool poly = __builtin_amdgcn_ballot_w64(!(kn * amax <= lim_cs)) == 0;
+        if (!poly) {
+            uint32_t mb = 0;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mb = max(mb, __float_as_uint(dd[r]) << 1);
+            poly = __builtin_amdgcn_ballot_w64(!(mb <= lim_bits)) == 0;
+        }
+        if (poly) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = expm1_poly(dd[r], ec);
+                n1[r] = __builtin_fmaf(w[r] * u[r], e, n1[r]);
+                n0[r] = __builtin_fmaf(w[r], e, n0[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = expm1_any(dd[r], ec);
+                n1[r] = __builtin_fmaf(w[r] * u[r], e, n1[r]);
+                n0[r] = __builtin_fmaf(w[r], e, n0[r]);
+            }
+        }
+        if (wave < 4u) {   // row sums of rows 8 wave .. 8 wave + 7 (this wave's qd)
+#pragma unroll
+            for (uint32_t qd = 0; qd < 4u; ++qd)
+                if (qd == wave) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        zs[j] += w[4 * qd + j];
+                        bs[j] = __builtin_fmaf(w[4 * qd + j], u[4 * qd + j], bs[j]);
+                    }
+                }
+        }
+        if (kt == ct) {   // the query tile is complete
+            finish_tile(h * nt + ct);
+            reset();
+        }
+        if (!more) break;
+        stg.store(tid, lds + (st ^ 1u) * SB, nk == nc, 1);
+        if (nh != h) key_norms(nh);
+        if (nc != ct || nh != h) query_tile(nh, nc);
+        __syncthreads();
+        h = nh;
+        ct = nc;
+        kt = nk;
+    }
+    __syncthreads();
+    fold();
 }
 
 }  // namespace
@@ -592,6 +834,44 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const ui
     }
 #undef DUST_AKS2
 #undef DUST_AKS
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const uint16_t *v,
+                                    const uint16_t *g, float *c, int64_t Kc, int64_t B,
+                                    int64_t H, int64_t S, int64_t dh, int64_t chan0, float sigma,
+                                    float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
+                                    hipStream_t s) {
+    const uint32_t nw = dh <= 96 ? 8u : 4u;   // waves (draws) per block
+    const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
+    const uint32_t blocks = (uint32_t)(B * ndg);
+    // the logit shift is sigma tau <a, k> and the noise comes divided by kNormalScale
+    const double s1 = (double)sigma * (double)softmax_scale * kNormalScale;
+    Expm1Coef ec;
+    ec.s1 = (float)s1;
+    ec.s2 = (float)(s1 * s1 / 2.0);
+    ec.s3 = (float)(s1 * s1 * s1 / 6.0);
+    ec.s4 = (float)(s1 * s1 * s1 * s1 / 24.0);
+    ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
+    ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
+    const uint32_t q0 = (uint32_t)(chan0 / 4);
+    // two stages, the row sums [2][2][32] and the key norms [2][S]
+    const size_t lds = 2 * (size_t)stage_bytes((int)(dh / 16), 2) + (128 + 2 * (size_t)S) * 4;
+#define DUST_AQS(KS, NW)                                                                       \
+    attn_query_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                             \
+        P, k, v, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
+        draw0, tok0, ndg)
+    switch (dh / 16) {
+        case 1: DUST_AQS(1, 8); break;
+        case 2: DUST_AQS(2, 8); break;
+        case 3: DUST_AQS(3, 8); break;
+        case 4: DUST_AQS(4, 8); break;
+        case 5: DUST_AQS(5, 8); break;
+        case 6: DUST_AQS(6, 8); break;
+        case 7: DUST_AQS(7, 4); break;
+        default: DUST_AQS(8, 4); break;
+    }
+#undef DUST_AQS
     return hipGetLastError();
 }
 

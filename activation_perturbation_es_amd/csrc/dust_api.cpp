@@ -389,6 +389,49 @@ int dust_attn_key_scores(const void *P, const void *q, const void *v, const void
                       fn);
 }
 
+int dust_attn_query_scores(const void *P, const void *k, const void *v, const void *g_o,
+                           float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,
+                           int64_t chan0, float sigma, float softmax_scale, uint64_t seed,
+                           uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream) {
+    const char *fn = "dust_attn_query_scores";
+    if (Kc < 0 || B < 0 || H < 0 || S < 0 || dh < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size", fn);
+    if (!std::isfinite(sigma) || !std::isfinite(softmax_scale))
+        return fail(DUST_ERR_INVALID, "%s: sigma and softmax_scale must be finite", fn);
+    if (std::fabs((double)sigma * (double)softmax_scale) > 1048576.0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: |sigma * softmax_scale| beyond 2^20", fn);
+    if (Kc > kMaxIdx || B > kMaxIdx || H > kMaxIdx || S > kMaxIdx || dh > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (int rc = check_noise_ranges(fn, B * S, H * dh, chan0, Kc, draw0, tok0)) return rc;
+    if (Kc == 0 || B == 0 || S == 0) return ok();
+    if (H == 0 || dh == 0) return fail(DUST_ERR_INVALID, "%s: H and dh must be >= 1", fn);
+    if (S % 32 != 0 || S > 4096 || dh % 16 != 0 || dh > 128)
+        return fail(DUST_ERR_UNSUPPORTED,
+                    "%s: S=%lld must be a multiple of 32 up to 4096 and dh=%lld a multiple of 16 "
+                    "up to 128", fn, (long long)S, (long long)dh);
+    if (!P || !k || !v || !g_o || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (((uintptr_t)P & 15u) || ((uintptr_t)k & 15u) || ((uintptr_t)v & 15u) ||
+        ((uintptr_t)g_o & 15u) || !elem_aligned(c, 4))
+        return fail(DUST_ERR_INVALID, "%s: P, k, v and g_o must be 16-byte, c 4-byte aligned",
+                    fn);
+    const int64_t p_bytes = span(B * H, S, S, 2), x_bytes = span(B * S, H * dh, 1, 2);
+    const int64_t c_bytes = span(Kc, B * S, 1, 4);
+    if (p_bytes < 0 || x_bytes < 0 || c_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (B * ((Kc + 3) / 4) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, k, (size_t)x_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, v, (size_t)x_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, g_o, (size_t)x_bytes))
+        return fail(DUST_ERR_INVALID, "%s: c overlaps P, k, v or g_o", fn);
+    return hip_status(dust::launch_attn_query_scores((const uint16_t *)P, (const uint16_t *)k,
+                                                     (const uint16_t *)v, (const uint16_t *)g_o,
+                                                     c, Kc, B, H, S, dh, chan0, sigma,
+                                                     softmax_scale, make_key(seed, tag), draw0,
+                                                     tok0, (hipStream_t)stream),
+                      fn);
+}
+
 int dust_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr, float momentum,
                       void *stream) {
     const char *fn = "dust_sgd_momentum";

@@ -232,6 +232,30 @@ int dust_attn_key_scores(const void *P, const void *q, const void *v, const void
                          uint32_t draw0, uint32_t tok0, void *stream);
 
 /*
+ * dust_attn_query_scores -- loss change of K draws that perturb an attention QUERY projection,
+ * scored through the attention output as above. With q'_t = q_t + sigma a_t, head h's logit of
+ * query t on key s moves by delta_ts = sigma * softmax_scale * <a^h_t, k^h_s>, and the scores
+ * are those of dust_attn_key_scores with these shifts (the softmax re-run relative to the
+ * given weights, each row normalised).
+ *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
+ *           keys s; entries above the diagonal are ignored                              (in)
+ *   k       [B*S, H*dh] bf16 keys, head h in columns h*dh .. h*dh+dh-1                   (in)
+ *   v       [B*S, H*dh] bf16 values                                                      (in)
+ *   g_o     [B*S, H*dh] bf16 estimated error of the attention output                     (in)
+ *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
+ * The noise a of (token t, head h, column j) is channel chan0 + h*dh + j of token tok0 + t
+ * (the query projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
+ * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P, k, v and
+ * g_o 16-byte aligned; sigma and softmax_scale finite with |sigma * softmax_scale| <= 2^20.
+ * c must not overlap the inputs. Precision and the range of the logit shifts as for
+ * dust_attn_key_scores.
+ */
+int dust_attn_query_scores(const void *P, const void *k, const void *v, const void *g_o,
+                           float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,
+                           int64_t chan0, float sigma, float softmax_scale, uint64_t seed,
+                           uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);
+
+/*
  * dust_sgd_momentum -- one SGD-with-momentum step on n fp32 weights, in place.
  * The explainer's section "Results" trains with the estimate through SGD with momentum at a
  * constant learning rate; the step is the textbook heavy ball without dampening:

@@ -13,7 +13,9 @@ two other entry points (dust_noise_inject into zeros, then dust_loss_delta).
 The key scores (a softmax re-run with the logits moved by sigma tau <q_t, a_s>) are compared the
 same way, at the same bar, over the same layouts, with logit shifts both inside and beyond the
 range where the kernel takes e^x - 1 from a polynomial (|x| <= 0.2), and on tiles that mix the
-two; sigma = 0 must give exactly zero and attention to the own token only (nearly) zero.
+two; sigma = 0 must give exactly zero and attention to the own token only (nearly) zero. The
+query scores (shifts sigma tau <a_t, k_s>) are checked the same way, including the widest heads
+(which run 4 waves per block) and the longest sequences.
 """
 import numpy as np
 import pytest
@@ -152,3 +154,52 @@ def test_attn_scores_channels_beyond_32_bits():
     ref = oracle.attn_key_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
                                  bits_to_f64(gb), Kc, sigma, tau, 3, 1, 0, 0, chan0)
     assert frob_rel(host_f32(c), ref) <= 1e-5
+    dust.dust_attn_query_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh,
+                                chan0, sigma, tau, 3, 1, 0, 0)
+    ref = oracle.attn_query_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
+                                   bits_to_f64(gb), Kc, sigma, tau, 3, 1, 0, 0, chan0)
+    assert frob_rel(host_f32(c), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("B,H,S,dh,Kc,chan0,draw0,tok0,garbage,sigma,tau", [
+    (2, 2, 32, 16, 5, 0, 3, 7, False, 0.05, 0.25),       # one tile, ragged draw group
+    (1, 3, 64, 32, 6, 64, 0, 0, True, 0.05, 0.18),       # channel offset, weights above the diagonal
+    (2, 2, 128, 64, 3, 0, 11, 1000, False, 0.01, 0.125), # 4 x 4 tiles, the workload's head width
+    (1, 1, 96, 128, 9, 8, 2, 5, True, 0.02, 0.09),       # widest heads (4 waves a block), 3 blocks
+    (1, 4, 64, 48, 4, 4, 0, 0, False, 0.05, 0.144),      # three k-slices
+    (1, 1, 96, 112, 5, 0, 0, 0, False, 0.05, 0.094),     # seven k-slices (4 waves a block)
+    (1, 1, 4096, 16, 2, 0, 0, 0, False, 0.05, 0.25),     # the longest sequence
+    (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
+    (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
+    (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
+])
+def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
+    announce("attn query scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
+    g = np.random.default_rng(75)
+    T, d, seed, tag = B * S, H * dh, 0xA780, 8
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
+    kb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_query_scores(bf16(Pbits), bf16(kb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh,
+                                chan0, sigma, tau, seed, tag, draw0, tok0)
+    ref = oracle.attn_query_scores(bits_to_f64(Pbits), bits_to_f64(kb), bits_to_f64(vb),
+                                   bits_to_f64(gb), Kc, sigma, tau, seed, tag, draw0, tok0, chan0)
+    err = frob_rel(host_f32(c), ref)
+    print("query scores rel. Frobenius error %.2e" % err)
+    assert err <= 1e-5
+
+
+def test_attn_query_scores_vanish_at_sigma_zero_and_for_self_attention():
+    announce("attn query scores sigma = 0, self attention")
+    B, H, S, dh, Kc = 1, 2, 64, 32, 4
+    T, d = B * S, H * dh
+    g = np.random.default_rng(76)
+    kb, vb, gb = (bf16(rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)))
+                  for _ in range(3))
+    P = bf16(rne_bf16_bits_of_f32(_causal_weights(g, B, H, S).astype(np.float32)))
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_query_scores(P, kb, vb, gb, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
+    assert torch.all(c == 0)
+    eye = bf16(rne_bf16_bits_of_f32(np.broadcast_to(np.eye(S, dtype=np.float32), (B, H, S, S)).copy()))
+    dust.dust_attn_query_scores(eye, kb, vb, gb, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
+    assert float(c.abs().max()) <= 1e-6

@@ -263,6 +263,35 @@ def test_w4_attention_key_scores():
     assert frob_rel(got[k, t], ref) <= 1e-5
 
 
+def test_w4_attention_query_scores():
+    """The attention workload scored through a softmax re-run with perturbed queries (8 heads of
+    64, softmax scale 1/8, bench.py --attention-queries), at full size: all 16384 draws in one
+    call as the benchmark times it, sampled outputs against the oracle."""
+    announce("w4 attention query scores")
+    c = synth.CONFIGS[4]
+    T, d, S, K, sigma = c["T"], c["d"], c["seg_len"], c["K"], c["sigma"]
+    B, H = T // S, 8
+    tau = 1.0 / np.sqrt(d // H)
+    seed, tag = synth.noise_seed(4), synth.NOISE_TAG
+    g = np.random.default_rng(408)
+    z = g.standard_normal((B, H, S, S)).astype(np.float32)
+    z[:, :, np.triu_indices(S, 1)[0], np.triu_indices(S, 1)[1]] = -np.inf
+    z = np.exp(z - z.max(-1, keepdims=True))
+    Pbits = rne_bf16_bits_of_f32((z / z.sum(-1, keepdims=True)).astype(np.float32))
+    del z
+    kb, vb, gb = (synth.normal_bf16(synth.rng(4, j), (T, d)) for j in (4, 5, 1))
+    cd = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_attn_query_scores(bf16(Pbits), bf16(kb), bf16(vb), bf16(gb), cd, K, B, H, S, d // H,
+                                0, sigma, tau, seed, tag, 0, 0)
+    got = host_f32(cd)
+    s = np.random.default_rng(409)
+    k, t = s.integers(0, K, 96), s.integers(0, T, 96)
+    k[:3], t[:3] = [0, K - 1, K - 1], [0, T - 1, S - 1]
+    ref = oracle.attn_query_scores_at(bits_to_f64(Pbits), bits_to_f64(kb), bits_to_f64(vb),
+                                      bits_to_f64(gb), k, t, sigma, tau, seed, tag)
+    assert frob_rel(got[k, t], ref) <= 1e-5
+
+
 # ------------------------------------------------------------------------------ workload 5
 def test_w5_inject_block():
     announce("w5 inject block")
