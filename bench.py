@@ -13,9 +13,9 @@ The perturbed forward of the rest of the model, between the perturbation and the
 is not part of the estimator; its per-token losses are synthetic inputs here.
 --workload 3 / 4 / 5 time the LM-head chunk, the attention k/v inner-product and the 240M-shape
 chains the same way (for the report; the default line is workload 2). With --workload 4,
---attention-values or --attention-keys scores the draws by re-running the attention with
-perturbed values or keys (dust_attn_value_scores / dust_attn_key_scores) instead of streaming a
-synthetic attention-output change.
+--attention-values, --attention-keys or --attention-queries scores the draws by re-running the
+attention with perturbed values, keys or queries (dust_attn_value_scores / _key_scores /
+_query_scores) instead of streaming a synthetic attention-output change.
 
 Metric: draws x tokens per second (K * T / step time). Prints one JSON line with the per-kernel
 HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
@@ -96,6 +96,10 @@ def parse():
                     help="workload 4: score by re-running the softmax with perturbed keys "
                          "(dust_attn_key_scores on synthetic queries, keys and values, 8 heads of "
                          "64) instead of streaming a synthetic attention-output change")
+    ap.add_argument("--attention-queries", action="store_true",
+                    help="workload 4: score by re-running the softmax with perturbed queries "
+                         "(dust_attn_query_scores on synthetic queries, keys and values, 8 heads "
+                         "of 64) instead of streaming a synthetic attention-output change")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -338,15 +342,16 @@ class InnerChain(Chain):
             z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
             self.P = t.softmax(z, -1).to(t.bfloat16)
             del z
-        elif self.attn_mode == "keys":
+        elif self.attn_mode in ("keys", "queries"):
             # queries, keys and values N(0, 1) in bf16; the clean forward's weights are the
             # causal softmax of tau q k^T per head (fp32 on the device, before timing)
             self.tau = 1.0 / np.sqrt(self.d // H)
-            self.qbits, kbits, self.vbits = (synth.normal_bf16(synth.rng(self.cfg_id, j),
-                                                               (self.T, self.d)) for j in (3, 4, 5))
-            self.q, self.v = self.bf(self.qbits), self.bf(self.vbits)
+            self.qbits, self.kbits, self.vbits = (synth.normal_bf16(synth.rng(self.cfg_id, j),
+                                                                    (self.T, self.d))
+                                                  for j in (3, 4, 5))
+            self.q, self.k, self.v = self.bf(self.qbits), self.bf(self.kbits), self.bf(self.vbits)
             heads = lambda a: a.float().reshape(B, S, H, -1).permute(0, 2, 1, 3)
-            z = self.tau * heads(self.q) @ heads(self.bf(kbits)).transpose(-1, -2).contiguous()
+            z = self.tau * heads(self.q) @ heads(self.k).transpose(-1, -2).contiguous()
             z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
             self.P = t.softmax(z, -1).to(t.bfloat16)
             del z
@@ -366,7 +371,7 @@ class InnerChain(Chain):
         self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d, self.d)
         self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
 
-    attn_mode = None   # None, "values" or "keys"
+    attn_mode = None   # None, "values", "keys" or "queries"
     HEADS = 8
 
     def step(self, run, sh):
@@ -379,6 +384,10 @@ class InnerChain(Chain):
             run("dust_attn_key_scores", d.dust_attn_key_scores, self.P, self.q, self.v, self.go,
                 self.cbuf, K, T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma,
                 self.tau, self.seed, self.tag, 0, 0, sh)
+        elif self.attn_mode == "queries":
+            run("dust_attn_query_scores", d.dust_attn_query_scores, self.P, self.k, self.v,
+                self.go, self.cbuf, K, T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0,
+                self.sigma, self.tau, self.seed, self.tag, 0, 0, sh)
         else:
             for blk in range(K // KB):
                 run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do,
@@ -403,6 +412,8 @@ class InnerChain(Chain):
             # per causal (draw, head, query, key) element: e^x - 1 and two weighted sums, fp32
             "dust_attn_key_scores": ("alu", OPS_KEY_SCORE * K * (T // S) * H * (S * (S + 1) / 2),
                                      1e12, FP32_VALU_PEAK_TOPS, "Tops/s"),
+            "dust_attn_query_scores": ("alu", OPS_KEY_SCORE * K * (T // S) * H * (S * (S + 1) / 2),
+                                       1e12, FP32_VALU_PEAK_TOPS, "Tops/s"),
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_error_estimate": _alu(K * T * d, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * d * d),
@@ -424,6 +435,13 @@ class InnerChain(Chain):
                         "softmax_scale": self.tau,
                         "delta_o": "softmax re-run with perturbed keys (synthetic q, k, v)",
                         "storage": "bf16 attention weights / q / v / g_o / x, fp32 scores, "
+                                   "rewards, g_hat, G_W"})
+        elif self.attn_mode == "queries":
+            cfg.update({"workload": self.c["name"] + "_attention_queries", "heads": self.HEADS,
+                        "head_dim": self.d // self.HEADS, "draw_block": self.K,
+                        "softmax_scale": self.tau,
+                        "delta_o": "softmax re-run with perturbed queries (synthetic q, k, v)",
+                        "storage": "bf16 attention weights / k / v / g_o / x, fp32 scores, "
                                    "rewards, g_hat, G_W"})
         return cfg
 
@@ -462,13 +480,19 @@ class InnerChain(Chain):
     def _cpu_baseline_attention(self, scale):
         import oracle
         S, d, H = self.S, self.d, self.HEADS
-        K_s = max(1, int(4 * scale))
+        # about 10 s on 16 cores: the value and key oracles regenerate the noise of every key
+        # for every query (0.5 s per draw), the query oracle once per query (2.5 ms per draw)
+        K_s = max(1, int((128 if self.attn_mode == "queries" else 16) * scale))
         P = self.P[:1].float().cpu().numpy().astype(np.float64)          # the first sequence
         go = synth.bf16_bits_to_f32(self.gobits[:S]).astype(np.float64)
         t0 = time.perf_counter()
         if self.attn_mode == "keys":
             q, v = (synth.bf16_bits_to_f32(a[:S]).astype(np.float64) for a in (self.qbits, self.vbits))
             c = oracle.attn_key_scores(P, q, v, go, K_s, self.sigma, self.tau, self.seed, self.tag)
+        elif self.attn_mode == "queries":
+            k, v = (synth.bf16_bits_to_f32(a[:S]).astype(np.float64) for a in (self.kbits, self.vbits))
+            c = oracle.attn_query_scores(P, k, v, go, K_s, self.sigma, self.tau, self.seed,
+                                         self.tag)
         else:
             c = oracle.attn_value_scores(P, go, K_s, self.sigma, self.seed, self.tag)
         r = oracle.reward_scan(c, S, self.gamma)
@@ -478,7 +502,7 @@ class InnerChain(Chain):
         return {"value": K_s * S / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
                 "sample": "%d of %d draws x first %d tokens (one sequence, %d heads): attention "
                           "%s scores, scan, error estimate, G_W; %.1f s"
-                          % (K_s, self.K, S, H, "key" if self.attn_mode == "keys" else "value",
+                          % (K_s, self.K, S, H, self.attn_mode[:-1].replace("querie", "query"),
                              dt)}
 
 
@@ -509,12 +533,14 @@ def main() -> int:
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
     chain.optimizer = args.optimizer
-    if args.attention_values or args.attention_keys:
-        if args.workload != 4 or (args.attention_values and args.attention_keys):
-            print("--attention-values or --attention-keys (one of them) applies to workload 4 "
-                  "only", file=sys.stderr)
+    modes = [m for m, on in (("values", args.attention_values), ("keys", args.attention_keys),
+                             ("queries", args.attention_queries)) if on]
+    if modes:
+        if args.workload != 4 or len(modes) > 1:
+            print("--attention-values, --attention-keys or --attention-queries (one of them) "
+                  "applies to workload 4 only", file=sys.stderr)
             return 2
-        chain.attn_mode = "values" if args.attention_values else "keys"
+        chain.attn_mode = modes[0]
     chain.setup()
     chain.opt_setup()
 
@@ -606,6 +632,7 @@ KERNEL_SOURCES = {
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
     "dust_attn_value_scores": "attn_scores.hip", "dust_attn_key_scores": "attn_scores.hip",
+    "dust_attn_query_scores": "attn_scores.hip",
 }
 
 
