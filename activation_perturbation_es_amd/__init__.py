@@ -19,7 +19,8 @@ __all__ = [
     "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DustError",
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
     "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam",
-    "dust_attn_value_scores", "dust_attn_key_scores", "dust_attn_query_scores", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
+    "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_key_scores",
+    "dust_attn_query_scores", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
     "dust_status_string", "dust_last_error", "library", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -51,6 +52,7 @@ _SIGNATURES = {
                                     _f32, _f32, _u64, _u32, _u32, _u32, _vp]),
     "dust_attn_query_scores": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
                                       _i64, _f32, _f32, _u64, _u32, _u32, _u32, _vp]),
+    "dust_cosine_terms": (_int, [_vp, _vp, _i64, _vp, _vp]),
     "dust_sgd_momentum": (_int, [_vp, _vp, _vp, _i64, _f32, _f32, _vp]),
     "dust_adam": (_int, [_vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "dust_error_estimate": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
@@ -152,6 +154,10 @@ def dust_attn_query_scores(P, k, v, g_o, c, Kc, B, H, S, dh, chan0, sigma, softm
                            tag, draw0, tok0, stream=None):
     return _call("dust_attn_query_scores", _ptr(P), _ptr(k), _ptr(v), _ptr(g_o), _ptr(c), Kc, B,
                  H, S, dh, chan0, sigma, softmax_scale, seed, tag, draw0, tok0, _stream(stream))
+
+
+def dust_cosine_terms(a, b, n, terms, stream=None):
+    return _call("dust_cosine_terms", _ptr(a), _ptr(b), n, _ptr(terms), _stream(stream))
 
 
 def dust_sgd_momentum(w, g, buf, n, lr, momentum, stream=None):

@@ -432,6 +432,20 @@ int dust_attn_query_scores(const void *P, const void *k, const void *v, const vo
                       fn);
 }
 
+int dust_cosine_terms(const float *a, const float *b, int64_t n, double *terms, void *stream) {
+    const char *fn = "dust_cosine_terms";
+    if (n < 0) return fail(DUST_ERR_INVALID, "%s: negative size n=%lld", fn, (long long)n);
+    if (n == 0) return ok();
+    if (!a || !b || !terms) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(a, 4) || !elem_aligned(b, 4) || !elem_aligned(terms, 8))
+        return fail(DUST_ERR_INVALID, "%s: a and b must be 4-byte, terms 8-byte aligned", fn);
+    if (n > ((int64_t)1 << 40)) return fail(DUST_ERR_UNSUPPORTED, "%s: n beyond 2^40", fn);
+    const size_t nb = (size_t)n * 4;
+    if (ranges_overlap(terms, 24, a, nb) || ranges_overlap(terms, 24, b, nb))
+        return fail(DUST_ERR_INVALID, "%s: terms overlaps a or b", fn);
+    return hip_status(dust::launch_cosine_terms(a, b, n, terms, (hipStream_t)stream), fn);
+}
+
 int dust_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr, float momentum,
                       void *stream) {
     const char *fn = "dust_sgd_momentum";

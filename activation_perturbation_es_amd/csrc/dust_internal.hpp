@@ -77,6 +77,9 @@ hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const 
                                     float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s);
 
+hipError_t launch_cosine_terms(const float *a, const float *b, int64_t n, double *out,
+                               hipStream_t s);
+
 hipError_t launch_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr,
                                float momentum, hipStream_t s);
 

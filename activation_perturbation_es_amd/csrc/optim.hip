@@ -9,6 +9,12 @@
 //         w <- w - (lr / (1 - b1^t)) m / (sqrt(v) / sqrt(1 - b2^t) + eps)
 // Both are pure streams (20 and 28 bytes per weight), so each thread moves one 16-byte piece
 // of every array when the arrays allow it; the step's scalars are formed on the host in fp64.
+//
+// The explainer's hyperparameter screening ranks candidate settings by the cosine between the
+// estimate and the backpropagation gradient on one batch; cosine_terms_kernel forms the three
+// sums that cosine needs, sum a b, sum a^2, sum b^2, in fp64 and in a fixed order (one block:
+// thread t takes the elements t, t + 1024, ... in turn, then a fixed pairwise tree), so the
+// result does not depend on scheduling.
 #include <cmath>
 
 #include "dust_internal.hpp"
@@ -90,7 +96,39 @@ __global__ __launch_bounds__(256) void adam_kernel(float *__restrict__ w,
     }
 }
 
+__global__ __launch_bounds__(1024) void cosine_terms_kernel(const float *__restrict__ a,
+                                                            const float *__restrict__ b,
+                                                            uint64_t n, double *__restrict__ out) {
+    __shared__ double red[3][1024];
+    const uint32_t t = threadIdx.x;
+    double ab = 0.0, aa = 0.0, bb = 0.0;
+    for (uint64_t i = t; i < n; i += 1024u) {
+        const double x = a[i], y = b[i];   // fp32 products are exact in fp64
+        ab = __builtin_fma(x, y, ab);
+        aa = __builtin_fma(x, x, aa);
+        bb = __builtin_fma(y, y, bb);
+    }
+    red[0][t] = ab;
+    red[1][t] = aa;
+    red[2][t] = bb;
+    __syncthreads();
+    for (uint32_t h = 512; h > 0; h >>= 1) {
+        if (t < h) {
+#pragma unroll
+            for (int q = 0; q < 3; ++q) red[q][t] += red[q][t + h];
+        }
+        __syncthreads();
+    }
+    if (t < 3) out[t] = red[t][0];
+}
+
 }  // namespace
+
+hipError_t launch_cosine_terms(const float *a, const float *b, int64_t n, double *out,
+                               hipStream_t s) {
+    cosine_terms_kernel<<<1, 1024, 0, s>>>(a, b, (uint64_t)n, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_sgd_momentum(float *w, const float *g, float *buf, int64_t n, float lr,
                                float momentum, hipStream_t s) {

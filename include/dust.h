@@ -256,6 +256,22 @@ int dust_attn_query_scores(const void *P, const void *k, const void *v, const vo
                            uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);
 
 /*
+ * dust_cosine_terms -- the three sums of the cosine between two fp32 arrays, for screening
+ * hyperparameters (explainer, "The real work": candidate settings are ranked by the cosine
+ * between the estimate and the backpropagation gradient on one batch, and training decides
+ * among the best):
+ *     terms[0] = sum_i a_i b_i,  terms[1] = sum_i a_i^2,  terms[2] = sum_i b_i^2
+ * so that cos(a, b) = terms[0] / sqrt(terms[1] terms[2]).
+ *   a, b    [n] fp32                                                                     (in)
+ *   terms   [3] fp64, device memory                                                     (out)
+ * fp64 accumulation in a fixed order (the result does not depend on scheduling); one block, so
+ * it is meant for a few calls per screening, not for the estimate's inner loop. n == 0 leaves
+ * terms untouched. a, b 4-byte and terms 8-byte aligned; terms must not overlap a or b;
+ * n <= 2^40.
+ */
+int dust_cosine_terms(const float *a, const float *b, int64_t n, double *terms, void *stream);
+
+/*
  * dust_sgd_momentum -- one SGD-with-momentum step on n fp32 weights, in place.
  * The explainer's section "Results" trains with the estimate through SGD with momentum at a
  * constant learning rate; the step is the textbook heavy ball without dampening:

@@ -298,6 +298,12 @@ def attn_query_scores_at(P, k, v, g_o, kk, t, sigma: float, tau: float, seed: in
     return out
 
 
+def cosine_terms(a, b) -> np.ndarray:
+    """(sum a b, sum a^2, sum b^2) of two arrays in fp64: the sums of their cosine."""
+    a, b = _f64(a).ravel(), _f64(b).ravel()
+    return np.array([np.dot(a, b), np.dot(a, a), np.dot(b, b)])
+
+
 def reward_scan(c, seg_len: int, gamma: float) -> np.ndarray:
     """r_t = sum_{s>=t in t's sequence} gamma^(s-t) c_s along the last axis of c [K, T]."""
     c = _f64(c)

@@ -128,6 +128,10 @@ INVALID = [
     ("dust_attn_query_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + 4096, 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "overlap"),
     ("dust_attn_query_scores", (FAKE, None, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "null"),
     ("dust_attn_query_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, float("inf"), 0.25, 1, 1, 0, 0, None), 1, "finite"),
+    ("dust_cosine_terms", (FAKE, FAKE2, 16, FAKE2 + 4100, None), 1, "aligned"),
+    ("dust_cosine_terms", (FAKE, FAKE2, 16, FAKE + 8, None), 1, "overlap"),
+    ("dust_cosine_terms", (FAKE, None, 16, FAKE2 + 4096, None), 1, "null"),
+    ("dust_cosine_terms", (FAKE, FAKE2, -1, FAKE2 + 4096, None), 1, "negative"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, 0.1, -0.5, None), 1, "momentum"),
     ("dust_sgd_momentum", (FAKE, FAKE2, FAKE2 + 4096, 16, float("inf"), 0.9, None), 1, "finite"),
     ("dust_sgd_momentum", (FAKE, FAKE, FAKE2 + 4096, 16, 0.1, 0.9, None), 1, "overlap"),
@@ -160,6 +164,7 @@ ZERO_SIZE = [
     ("dust_attn_value_scores", (None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None)),
     ("dust_attn_key_scores", (None, None, None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None)),
     ("dust_attn_query_scores", (None, None, None, None, None, 3, 0, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None)),
+    ("dust_cosine_terms", (None, None, 0, None, None)),
     ("dust_adam", (None, None, None, None, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, 1, None)),
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, announce, dust, host_f32
+from gpu_helpers import DEV, announce, dust, f32, host_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -86,3 +86,25 @@ def test_optimizer_zero_size_touches_nothing():
     dust.dust_sgd_momentum(w, w, w, 0, 0.1, 0.9)
     dust.dust_adam(w, w, w, w, 0, 0.1, 0.9, 0.999, 1e-8, 0.0, 1)
     assert torch.all(w == 3.0)
+
+
+@pytest.mark.parametrize("n", [1, 1000, 1025, (1 << 22) + 3])
+def test_cosine_terms(n):
+    """dust_cosine_terms against the oracle's fp64 sums: the fp32 products are exact in fp64,
+    only the summation order differs (relative 1e-12 allows n 2^-53 and more)."""
+    announce("cosine terms n=%d" % n)
+    g = np.random.default_rng(91)
+    a = g.standard_normal(n).astype(np.float32)
+    b = (0.3 * a + g.standard_normal(n)).astype(np.float32)
+    t = torch.full((3,), float("nan"), dtype=torch.float64, device=DEV)
+    dust.dust_cosine_terms(f32(a), f32(b), n, t)
+    np.testing.assert_allclose(t.cpu().numpy(), oracle.cosine_terms(a, b), rtol=1e-12, atol=0)
+
+
+def test_cosine_terms_zero_size_and_identical_arrays():
+    t = torch.full((3,), 7.0, dtype=torch.float64, device=DEV)
+    dust.dust_cosine_terms(None, None, 0, t)
+    assert torch.all(t == 7.0)
+    from activation_perturbation_es_amd.screen import cosine
+    x = f32(np.random.default_rng(92).standard_normal(5000).astype(np.float32))
+    assert abs(cosine(x, x) - 1.0) < 1e-14 and abs(cosine(x, -x) + 1.0) < 1e-14

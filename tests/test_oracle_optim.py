@@ -75,3 +75,22 @@ def test_adam_first_step_and_weight_decay_closed_forms():
     # a zero gradient on zero moments leaves only the decay
     w, _, _ = oracle.adam(w0, np.zeros(4), np.zeros(4), np.zeros(4), lr, 0.9, 0.999, eps, 0.5, 3)
     np.testing.assert_allclose(w, w0 * (1 - lr * 0.5), rtol=1e-15)
+
+
+def test_cosine_terms_are_the_exact_sums_and_closed_forms():
+    """The screening cosine's three sums: equal the exactly rounded sums (math.fsum of the exact
+    fp64 products of fp32 inputs); basis vectors, a vector with itself, its negative and an
+    orthogonal pair give the closed forms."""
+    import math
+    g = np.random.default_rng(90)
+    a = g.standard_normal(1001).astype(np.float32).astype(np.float64)
+    b = g.standard_normal(1001).astype(np.float32).astype(np.float64)
+    t = oracle.cosine_terms(a, b)
+    exact = [math.fsum(a * b), math.fsum(a * a), math.fsum(b * b)]
+    np.testing.assert_allclose(t, exact, rtol=1e-13, atol=0)
+    e = np.eye(5)
+    assert list(oracle.cosine_terms(e[1], e[1])) == [1.0, 1.0, 1.0]
+    assert list(oracle.cosine_terms(e[1], e[3])) == [0.0, 1.0, 1.0]
+    x = np.array([3.0, -4.0])
+    assert list(oracle.cosine_terms(x, -x)) == [-25.0, 25.0, 25.0]
+    assert list(oracle.cosine_terms(x, np.array([4.0, 3.0]))) == [0.0, 25.0, 25.0]
