@@ -87,6 +87,20 @@ __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uin
     if (norm2) *norm2 = n2;
 }
 
+// Sum over the 32 lanes of each half of the wave, in every lane: the two quad exchanges, the
+// half-row and row mirrors (DPP, no LDS traffic), then one exchange of rows 16 apart.
+template <int CTRL>
+__device__ __forceinline__ float dpp_shuffled(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float half_wave_sum(float x) {
+    x += dpp_shuffled<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+    x += dpp_shuffled<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+    x += dpp_shuffled<0x141>(x);   // row_half_mirror: lane i <- 7 - i within 8
+    x += dpp_shuffled<0x140>(x);   // row_mirror: lane i <- 15 - i within 16
+    return x + __shfl_xor(x, 16);
+}
+
 // Staging of one step: QT query tiles, each as 16-byte pieces, P rows first (4 per query row),
 // then the NQ query-side tiles (2 KS per row each); loads into registers, stores to LDS after
 // the step's compute. Only the first ntiles query tiles of a step exist.
@@ -611,12 +625,10 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     // also complete their row sums Z and base and leave them in LDS.
     auto finish_tile = [&](uint32_t gt) {
 #pragma unroll
-        for (int m = 1; m <= 16; m <<= 1)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                n1[r] += __shfl_xor(n1[r], m);
-                n0[r] += __shfl_xor(n0[r], m);
-            }
+        for (int r = 0; r < 16; ++r) {
+            n1[r] = half_wave_sum(n1[r]);
+            n0[r] = half_wave_sum(n0[r]);
+        }
         const uint32_t rr = lane & 15u;
         t1 = 0.f;
         t0 = 0.f;
@@ -627,12 +639,10 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         }
         if (wave < 4u) {
 #pragma unroll
-            for (int m = 1; m <= 16; m <<= 1)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    zs[j] += __shfl_xor(zs[j], m);
-                    bs[j] += __shfl_xor(bs[j], m);
-                }
+            for (int j = 0; j < 4; ++j) {
+                zs[j] = half_wave_sum(zs[j]);
+                bs[j] = half_wave_sum(bs[j]);
+            }
             // rows 8 wave + 4 half + j, j < 4: lane (half, j) writes them
             float *zb = ZB + (gt & 1u) * 64u;
             if ((lane & 31u) < 4u) {
@@ -711,20 +721,19 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
             for (int r = 0; r < 16; ++r) mb = max(mb, __float_as_uint(dd[r]) << 1);
             poly = __builtin_amdgcn_ballot_w64(!(mb <= lim_bits)) == 0;
         }
+        // e^x - 1 first, the sums after, so that both forms feed the same accumulators
+        float e[16];
         if (poly) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = expm1_poly(dd[r], ec);
-                n1[r] = __builtin_fmaf(w[r] * u[r], e, n1[r]);
-                n0[r] = __builtin_fmaf(w[r], e, n0[r]);
-            }
+            for (int r = 0; r < 16; ++r) e[r] = expm1_poly(dd[r], ec);
         } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = expm1_any(dd[r], ec);
-                n1[r] = __builtin_fmaf(w[r] * u[r], e, n1[r]);
-                n0[r] = __builtin_fmaf(w[r], e, n0[r]);
-            }
+            for (int r = 0; r < 16; ++r) e[r] = expm1_any(dd[r], ec);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            n1[r] = __builtin_fmaf(w[r] * u[r], e[r], n1[r]);
+            n0[r] = __builtin_fmaf(w[r], e[r], n0[r]);
         }
         if (wave < 4u) {   // row sums of rows 8 wave .. 8 wave + 7 (this wave's qd)
 #pragma unroll
