@@ -101,38 +101,33 @@ __device__ __forceinline__ float half_wave_sum(float x) {
     return x + __shfl_xor(x, 16);
 }
 
-// Staging of one step: QT query tiles, each as 16-byte pieces, P rows first (4 per query row),
-// then the NQ query-side tiles (2 KS per row each); loads into registers, stores to LDS after
-// the step's compute. Only the first ntiles query tiles of a step exist.
-template <int KS, int NQ, uint32_t NT = 256, int QT = 1, bool TP = false>
+// Staging of one step as 16-byte pieces: the P tile's rows first (4 per query row), then the NQ
+// side tiles (2 KS per row each); loads into registers, stores to LDS after the step's compute.
+template <int KS, int NQ, uint32_t NT = 256, bool TP = false>
 struct Stager {
-    static constexpr uint32_t kTilePieces = 128u + 64u * KS * NQ;
-    static constexpr uint32_t kPieces = QT * kTilePieces;
+    static constexpr uint32_t kPieces = 128u + 64u * KS * NQ;
     static constexpr uint32_t kPerThread = (kPieces + NT - 1u) / NT;
-    static constexpr uint32_t kTileBytes = stage_bytes(KS, NQ);
     u32x4 r[kPerThread];
 
-    // P [B, H, S, S]: query tiles ct .. ct + ntiles - 1 over key tile kt of sequence b, head h;
-    // the side arrays [T, H DH]: row tiles xt .. xt + ntiles - 1 of the sequence (the query
-    // tiles for value and key scores, the key tile for query scores)
+    // P [B, H, S, S]: query tile ct over key tile kt of sequence b, head h; the side arrays
+    // [T, H DH]: row tile xt of the sequence (the query tile for value and key scores, the key
+    // tile for query scores)
     __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P,
                                          const uint16_t *const (&qs)[NQ], uint32_t b, uint32_t H,
                                          uint32_t S, uint32_t d, uint32_t h, uint32_t kt,
-                                         uint32_t ct, uint32_t ntiles, uint32_t xt) {
+                                         uint32_t ct, uint32_t xt) {
         constexpr uint32_t DH = 16u * KS;
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
             const uint32_t pc = tid + NT * j;
-            const uint32_t tile = pc / kTilePieces, lp = pc % kTilePieces;
-            if (pc >= kPieces || tile >= ntiles) continue;
-            const uint32_t qt = ct + tile;
-            if (lp < 128u) {
-                const uint32_t row = lp >> 2, seg = lp & 3u;
-                r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + qt * 32u + row) * S +
+            if (pc >= kPieces) continue;
+            if (pc < 128u) {
+                const uint32_t row = pc >> 2, seg = pc & 3u;
+                r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + ct * 32u + row) * S +
                                         kt * 32u + 8u * seg);
             } else {
-                const uint32_t xr = xt + tile;
-                const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
+                const uint32_t xr = xt;
+                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n)
@@ -143,20 +138,17 @@ struct Stager {
         }
     }
 
-    // P widened to fp32 once here for all draws; on a diagonal tile (the step's first tile when
-    // mask is set) the keys after the row's query become 0, so later arithmetic needs no causal
-    // test. TP stores the tile transposed, [32 keys][32 queries].
-    __device__ __forceinline__ void store(uint32_t tid, unsigned char *base, bool mask,
-                                          uint32_t ntiles) const {
+    // P widened to fp32 once here for all draws; on a diagonal tile (mask) the keys after the
+    // row's query become 0, so later arithmetic needs no causal test. TP stores the tile
+    // transposed, [32 keys][32 queries].
+    __device__ __forceinline__ void store(uint32_t tid, unsigned char *tb, bool mask) const {
         constexpr uint32_t GP = g_pitch(KS);
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
             const uint32_t pc = tid + NT * j;
-            const uint32_t tile = pc / kTilePieces, lp = pc % kTilePieces;
-            if (pc >= kPieces || tile >= ntiles) continue;
-            unsigned char *tb = base + tile * kTileBytes;
-            if (lp < 128u) {
-                const uint32_t row = lp >> 2, seg = lp & 3u;
+            if (pc >= kPieces) continue;
+            if (pc < 128u) {
+                const uint32_t row = pc >> 2, seg = pc & 3u;
                 f32x4 *dst = (f32x4 *)(tb + row * kPPitch + 32u * seg);
                 const u32x4 w = r[j];
                 float f[8];
@@ -165,7 +157,7 @@ struct Stager {
                     f[2 * e] = __uint_as_float(w[e] << 16);
                     f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
                 }
-                if (mask && tile == 0) {
+                if (mask) {
 #pragma unroll
                     for (uint32_t e = 0; e < 8u; ++e) f[e] = 8u * seg + e <= row ? f[e] : 0.f;
                 }
@@ -178,7 +170,7 @@ struct Stager {
                     dst[1] = f32x4{f[4], f[5], f[6], f[7]};
                 }
             } else {
-                const uint32_t x = lp - 128u, m = x / (64u * KS), y = x % (64u * KS);
+                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
                 *(u32x4 *)(tb + 32u * kPPitch + (m * 32u + row) * GP + 16u * seg) = r[j];
             }
@@ -186,14 +178,13 @@ struct Stager {
     }
 };
 
-// Steps in the order head, key tile, query tile >= key tile; a step covers QT query tiles.
-template <uint32_t QT = 1>
+// Steps in the order head, key tile, query tile >= key tile.
 struct StepOrder {
     uint32_t h = 0, kt = 0, ct = 0;
     __device__ __forceinline__ StepOrder next(uint32_t nt) const {
         StepOrder n = *this;
-        n.ct = ct + QT;
-        if (n.ct >= nt) {
+        n.ct = ct + 1u;
+        if (n.ct == nt) {
             n.kt = kt + 1u;
             n.ct = n.kt;
             if (n.kt == nt) { n.h = h + 1u; n.kt = 0; n.ct = 0; }
@@ -241,15 +232,15 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
 
     // Step n's tiles are in LDS stage n % 2; step n + 1's are fetched into registers at the
     // start of step n and stored to the other stage at its end, before the one barrier per step.
-    StepOrder<> cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 1, 0);
-    stg.store(tid, lds, true, 1);
+    StepOrder cur;
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.store(tid, lds, true);
     noise(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;   // uniform across the block
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, 1, nx.ct);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -284,7 +275,7 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
                                                          __float_as_uint(partB), false, false);
         cwh[cur.ct * 32u + col] += __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         if (!more) break;
-        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct, 1);
+        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
         if (nx.kt != cur.kt || nx.h != cur.h) noise(nx.h, nx.kt);
         __syncthreads();
         cur = nx;
@@ -320,22 +311,20 @@ __device__ __forceinline__ float expm1_any(float D, const Expm1Coef &e) {
 }
 
 // Key scores, 8 waves per block (two per SIMD, so that one wave's vector work runs under the
-// other's matrix-core work), one draw per wave, one sequence per block, QT query tiles per step
-// (the tiles' product chains are independent, and the vector work of one overlaps the matrix
-// work of the next).
-template <int KS, int QT>
+// other's matrix-core work), one draw per wave, one sequence per block.
+template <int KS>
 __global__ __launch_bounds__(512) void attn_key_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ qm,
     const uint16_t *__restrict__ v, const uint16_t *__restrict__ g, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
-    // LDS: two stages of one step's operands (per query tile: P tile [32 queries][32 keys], q
-    // and g tiles [32 queries][DH]); per wave the head's running sums of its draw, [N1, N0][S];
+    // LDS: two stages of one step's operands (P tile [32 queries][32 keys], q and g tiles
+    // [32 queries][DH]); per wave the head's running sums of its draw, [N1, N0][S];
     // per SIMD (waves 0-3) the partial row sums over the 8 key rows of each tile it owns,
     // [Z, base][S]; the head's query norms |q_t|, [S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
-    constexpr uint32_t GP = g_pitch(KS), TB = stage_bytes(KS, 2), SB = QT * TB;
+    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 2);
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
@@ -354,7 +343,7 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
     const uint16_t *const qs[2] = {qm, g};
-    Stager<KS, 2, 512, QT> stg;
+    Stager<KS, 2, 512> stg;
 
     // key-side operands of the current key tile: the draw's noise and the values, and the
     // largest noise norm over the tile's 32 keys (for the range test of e^x - 1)
@@ -482,9 +471,9 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
         }
     };
 
-    StepOrder<QT> cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, min((uint32_t)QT, nt), 0);
-    stg.store(tid, lds, true, min((uint32_t)QT, nt));
+    StepOrder cur;
+    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.store(tid, lds, true);
     query_norms(0);
     key_tile(0, 0);
     __syncthreads();
@@ -494,38 +483,24 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
             query_norms(cur.h);
             __syncthreads();   // Z and base read, query norms written, before either is used
         }
-        const StepOrder<QT> nx = cur.next(nt);
+        const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;
-        const uint32_t ntiles = min((uint32_t)QT, nt - cur.ct);
-        const uint32_t nx_tiles = min((uint32_t)QT, nt - nx.ct);
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx_tiles, nx.ct);
+        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
-        // every tile's products (a tile past the last one computes on stale data, unused)
         const unsigned char *base = lds + st * SB;
-        f32x16 dd[QT], u[QT];
-#pragma unroll
-        for (int j = 0; j < QT; ++j) {
-            dd[j] = f32x16{};
-            u[j] = f32x16{};
-        }
+        const unsigned char *qrow = base + 32u * kPPitch + col * GP + 16u * half;
+        f32x16 dd = {}, u = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-            for (int j = 0; j < QT; ++j) {
-                const unsigned char *qrow = base + j * TB + 32u * kPPitch + col * GP + 16u * half;
-                const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
-                const bf16x8 gb = *(const bf16x8 *)(qrow + 32u * GP + 32u * ks);
-                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd[j], 0, 0, 0);
-                u[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks], gb, u[j], 0, 0, 0);
-                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd[j], 0, 0, 0);
-            }
+            const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
+            const bf16x8 gb = *(const bf16x8 *)(qrow + 32u * GP + 32u * ks);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd, 0, 0, 0);
+            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks], gb, u, 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd, 0, 0, 0);
         }
-        tile_sums(dd[0], u[0], base, cur.ct, cur.kt == 0);
-#pragma unroll
-        for (int j = 1; j < QT; ++j)
-            if ((uint32_t)j < ntiles) tile_sums(dd[j], u[j], base + j * TB, cur.ct + j, cur.kt == 0);
+        tile_sums(dd, u, base, cur.ct, cur.kt == 0);
         if (!more) break;
-        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct, nx_tiles);
+        stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
         if (nx.kt != cur.kt || nx.h != cur.h) key_tile(nx.h, nx.kt);
         __syncthreads();
         cur = nx;
@@ -566,7 +541,7 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
     const uint16_t *const ks_[2] = {km, v};
-    Stager<KS, 2, NW * 64, 1, true> stg;
+    Stager<KS, 2, NW * 64, true> stg;
 
     // query-side operands of the current query tile: the draw's noise, the output error g, and
     // the largest noise norm over the tile's 32 queries
@@ -675,8 +650,8 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
 
     // steps: head, query tile ct, key tile kt <= ct
     uint32_t h = 0, ct = 0, kt = 0;
-    stg.load(tid, P, ks_, b, H, S, d, 0, 0, 0, 1, 0);
-    stg.store(tid, lds, true, 1);
+    stg.load(tid, P, ks_, b, H, S, d, 0, 0, 0, 0);
+    stg.store(tid, lds, true);
     key_norms(0);
     query_tile(0, 0);
     reset();
@@ -691,7 +666,7 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         }
         const bool more = nh < H;
         // the staged key tile is kt; the P tile is (query tile ct, key tile kt)
-        if (more) stg.load(tid, P, ks_, b, H, S, d, nh, nk, nc, 1, nk);   // k, v of key tile nk
+        if (more) stg.load(tid, P, ks_, b, H, S, d, nh, nk, nc, nk);   // k, v of key tile nk
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *krow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -751,7 +726,7 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
             reset();
         }
         if (!more) break;
-        stg.store(tid, lds + (st ^ 1u) * SB, nk == nc, 1);
+        stg.store(tid, lds + (st ^ 1u) * SB, nk == nc);
         if (nh != h) key_norms(nh);
         if (nc != ct || nh != h) query_tile(nh, nc);
         __syncthreads();
@@ -793,13 +768,11 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
     return hipGetLastError();
 }
 
-// LDS of the key kernel: two stages of QT query tiles, then (8 waves x 2 running sums + 4 x 2
-// row sums + the query norms) x S floats
-size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh, int qt) {
-    return 2 * (size_t)qt * stage_bytes((int)(dh / 16), 2) + (size_t)25 * S * sizeof(float);
+// LDS of the key kernel: two stages, then (8 waves x 2 running sums + 4 x 2 row sums + the
+// query norms) x S floats
+size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
+    return 2 * (size_t)stage_bytes((int)(dh / 16), 2) + (size_t)25 * S * sizeof(float);
 }
-
-constexpr size_t kMaxLds = 160 * 1024;
 
 hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const uint16_t *v,
                                   const uint16_t *g, float *c, int64_t Kc, int64_t B, int64_t H,
@@ -818,30 +791,21 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const ui
     ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
     ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-    // two query tiles per step where their stages fit beside the running sums and their
-    // products fit the registers (dh <= 80)
-    const int qt = dh <= 80 && attn_key_scores_lds_bytes(S, dh, 2) <= kMaxLds ? 2 : 1;
-    const size_t lds = attn_key_scores_lds_bytes(S, dh, qt);
-#define DUST_AKS(KS, QT)                                                                       \
-    attn_key_scores_kernel<KS, QT><<<blocks, 512, lds, s>>>(                                   \
+    const size_t lds = attn_key_scores_lds_bytes(S, dh);
+#define DUST_AKS(KS)                                                                           \
+    attn_key_scores_kernel<KS><<<blocks, 512, lds, s>>>(                                       \
         P, q, v, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
-#define DUST_AKS2(KS)                                                                          \
-    if (qt == 2)                                                                               \
-        DUST_AKS(KS, 2);                                                                       \
-    else                                                                                       \
-        DUST_AKS(KS, 1)
     switch (dh / 16) {
-        case 1: DUST_AKS2(1); break;
-        case 2: DUST_AKS2(2); break;
-        case 3: DUST_AKS2(3); break;
-        case 4: DUST_AKS2(4); break;
-        case 5: DUST_AKS2(5); break;
-        case 6: DUST_AKS(6, 1); break;
-        case 7: DUST_AKS(7, 1); break;
-        default: DUST_AKS(8, 1); break;
+        case 1: DUST_AKS(1); break;
+        case 2: DUST_AKS(2); break;
+        case 3: DUST_AKS(3); break;
+        case 4: DUST_AKS(4); break;
+        case 5: DUST_AKS(5); break;
+        case 6: DUST_AKS(6); break;
+        case 7: DUST_AKS(7); break;
+        default: DUST_AKS(8); break;
     }
-#undef DUST_AKS2
 #undef DUST_AKS
     return hipGetLastError();
 }
