@@ -107,7 +107,7 @@ def parse():
 
 
 def _alu(normals, extra):
-    return ("alu", normals * (OPS_PER_NORMAL + extra), 1e12, VALU_PEAK_TOPS, "Tops/s")
+    return ("alu", normals * (OPS_PER_NORMAL + extra), 1e12, VALU_PEAK_TOPS, "Tops/s", normals)
 
 
 def _hbm(nbytes):
@@ -583,13 +583,15 @@ def main() -> int:
     model.update(chain.opt_model())
     kernels = {}
     for name, ms in per.items():
-        bound, work, scale, peak, unit = model[name]
+        bound, work, scale, peak, unit = model[name][:5]
         avg_ms = float(np.mean(ms))
         ach = work / (avg_ms * 1e-3) / scale
         kernels[name] = {"launches_per_step": len(ms) // args.steps, "avg_ms": round(avg_ms, 5),
                          "ms_per_step": round(sum(ms) / args.steps, 5), "bound": bound,
                          "achieved": round(ach, 3), "peak": peak, "unit": unit,
                          "frac": round(ach / peak, 4)}
+        if len(model[name]) > 5:   # generating kernels: normals per second, free of the op model
+            kernels[name]["normals_per_s"] = float("%.4g" % (model[name][5] / (avg_ms * 1e-3)))
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": dk["achieved"],
