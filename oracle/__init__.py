@@ -60,6 +60,7 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
                                                ctypes.POINTER(_i64), ctypes.POINTER(_i64), _i64,
                                                _d]
     lib.dust_or_attn_query_scores.argtypes = lib.dust_or_attn_key_scores.argtypes
+    lib.dust_or_attn_row_weights.argtypes = [_d, _d, _d, _i64, _i64, _i64, _i64, _d, _d]
     lib.dust_or_attn_query_scores_at.argtypes = lib.dust_or_attn_key_scores_at.argtypes
     lib.dust_or_sgd_momentum.argtypes = [_d, _d, _d, _i64, ctypes.c_double, ctypes.c_double]
     lib.dust_or_adam.argtypes = [_d, _d, _d, _d, _i64, ctypes.c_double, ctypes.c_double,
@@ -267,6 +268,19 @@ def attn_key_scores_at(P, q, v, g_o, k, t, sigma: float, tau: float, seed: int, 
                                        tag, draw0, tok0, chan0, _pidx(k), _pidx(t), len(k),
                                        _p(out))
     return out
+
+
+def attn_row_weights(P, v, g_o):
+    """Draw-independent row weights of the softmax re-run (dust_oracle.c states the formula):
+    W [B, H, S, S] with W_ts = P_ts (Z_t u_ts - base_t) on and below the diagonal, 0 above it,
+    and the causal row sums Z [B, H, S]; P [B, H, S, S], v, g_o [T, H*dh]."""
+    Pd, vd, gd = _f64(P), _f64(v), _f64(g_o)
+    B, H, S, _ = Pd.shape
+    dh = gd.shape[1] // H
+    W = np.empty((B, H, S, S), dtype=np.float64)
+    Z = np.empty((B, H, S), dtype=np.float64)
+    _load().dust_or_attn_row_weights(_p(Pd), _p(vd), _p(gd), B, H, S, dh, _p(W), _p(Z))
+    return W, Z
 
 
 def attn_query_scores(P, k, v, g_o, K: int, sigma: float, tau: float, seed: int, tag: int,

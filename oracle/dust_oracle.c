@@ -412,6 +412,47 @@ void dust_or_attn_query_scores_at(const double *P, const double *k, const double
     }
 }
 
+/* Draw-independent row weights of the softmax re-run. With u_ts = <v^h_s, g^h_t>,
+ * Z_t = sum_{s <= t} P_ts and base_t = sum_{s <= t} P_ts u_ts, the re-run change of head h's
+ * output inner product at query t under logit shifts delta_ts is
+ *     <Delta o_t, g_t> = (base_t + N1_t) / (Z_t + N0_t) - base_t / Z_t
+ *                      = sum_s W_ts (e^{delta_ts} - 1) / (Z_t (Z_t + N0_t)),
+ * N0_t = sum_s P_ts (e^{delta_ts} - 1), N1_t = sum_s P_ts u_ts (e^{delta_ts} - 1), with
+ *     W_ts = P_ts (Z_t u_ts - base_t)  for s <= t,   W_ts = 0 for s > t.
+ * W [B, H, S, S] and Z [B, H, S]; P [B, H, S, S] (entries above the diagonal ignored), v and g
+ * [B S, H dh]. Written out per element, as defined. */
+void dust_or_attn_row_weights(const double *P, const double *v, const double *g, int64_t B,
+                              int64_t H, int64_t S, int64_t dh, double *W, double *Z)
+{
+    const int64_t d = H * dh;
+    #pragma omp parallel for collapse(3) schedule(dynamic)
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h)
+            for (int64_t t = 0; t < S; ++t) {
+                const double *prow = P + ((b * H + h) * S + t) * S;
+                double *wrow = W + ((b * H + h) * S + t) * S;
+                double z = 0.0, base = 0.0;
+                for (int64_t s = 0; s <= t; ++s) {
+                    double u = 0.0;
+                    for (int64_t j = 0; j < dh; ++j)
+                        u += v[(b * S + s) * d + h * dh + j] * g[(b * S + t) * d + h * dh + j];
+                    z += prow[s];
+                    base += prow[s] * u;
+                }
+                for (int64_t s = 0; s < S; ++s) {
+                    if (s > t) {
+                        wrow[s] = 0.0;
+                        continue;
+                    }
+                    double u = 0.0;
+                    for (int64_t j = 0; j < dh; ++j)
+                        u += v[(b * S + s) * d + h * dh + j] * g[(b * S + t) * d + h * dh + j];
+                    wrow[s] = prow[s] * (z * u - base);
+                }
+                Z[(b * H + h) * S + t] = z;
+            }
+}
+
 /* ---------------------------------------------------------------------------------------- */
 /* Discounted reward r_t = sum_{s >= t, s in t's sequence} gamma^(s - t) c_s (explainer,
  * "Credit assignment"). Tokens are T = B * seg_len, sequence b owns [b*seg_len, (b+1)*seg_len).

@@ -246,3 +246,77 @@ def test_query_scores_row_scale_diagonal_and_zeros():
     kk, t = np.array([0, 1, 1]), np.array([0, 23, 12])
     np.testing.assert_array_equal(
         oracle.attn_query_scores_at(P, k, v, go, kk, t, sigma, tau, 9, 3, 2, 7, 16), full[kk, t])
+
+
+# Row weights: the draw-independent part of the softmax re-run that the key and query scorers
+# share. Pinned against an explicit numpy re-run under arbitrary logit shifts, and by their
+# invariants.
+
+@pytest.mark.parametrize("B,H,S,dh", [(2, 2, 12, 8), (1, 3, 20, 4)])
+def test_row_weights_reproduce_an_explicit_softmax_rerun(B, H, S, dh):
+    """For any logit shifts delta, sum_s W_ts (e^delta - 1) / (Z (Z + N0)) is the change of
+    <o_t, g_t> when head h's weights become P e^delta renormalised, against the rows of P
+    normalised by Z (rows are rescaled on purpose so that Z != 1)."""
+    g = np.random.default_rng(70)
+    T, d = B * S, H * dh
+    P = _causal_weights(g, B, H, S) * g.uniform(0.5, 2.0, (B, H, S, 1))
+    v, go = g.standard_normal((T, d)), g.standard_normal((T, d))
+    W, Z = oracle.attn_row_weights(P, v, go)
+    vh, gh = _heads(v, B, S, H), _heads(go, B, S, H)
+    tri = np.tril(np.ones((S, S), dtype=bool))
+    for trial in range(3):
+        delta = np.where(tri, g.standard_normal((B, H, S, S)) * 0.7, 0.0)
+        Pp = P * np.exp(delta) * tri
+        Pp = Pp / Pp.sum(-1, keepdims=True)
+        Pc = P * tri / (P * tri).sum(-1, keepdims=True)
+        ref = np.einsum("bhtj,bhtj->bht", np.einsum("bhts,bhsj->bhtj", Pp - Pc, vh), gh)
+        em1 = np.expm1(delta) * tri
+        N0 = (P * tri * em1).sum(-1)
+        got = (W * em1).sum(-1) / (Z * (Z + N0))
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-13)
+
+
+def test_row_weights_invariants():
+    """Rows of W sum to zero; Z is the causal row sum; W vanishes above the diagonal, for
+    self-attention only (a row with one key has nothing to move toward), and ignores the
+    weights above the diagonal."""
+    g = np.random.default_rng(71)
+    B, H, S, dh = 2, 2, 16, 4
+    T, d = B * S, H * dh
+    P = _causal_weights(g, B, H, S)
+    v, go = g.standard_normal((T, d)), g.standard_normal((T, d))
+    W, Z = oracle.attn_row_weights(P, v, go)
+    scale = np.abs(W).max()
+    assert scale > 0.1
+    np.testing.assert_allclose(W.sum(-1), 0.0, atol=1e-12 * S * scale)
+    np.testing.assert_allclose(Z, np.tril(P).sum(-1), rtol=1e-15)
+    assert np.all(W[..., ~np.tril(np.ones((S, S), dtype=bool))] == 0.0)
+    junk = P + np.triu(g.standard_normal((B, H, S, S)), 1)
+    W2, Z2 = oracle.attn_row_weights(junk, v, go)
+    assert np.array_equal(W2, W) and np.array_equal(Z2, Z)
+    eye = np.broadcast_to(np.eye(S), (B, H, S, S)).copy()
+    We, Ze = oracle.attn_row_weights(eye, v, go)
+    assert np.all(We == 0.0) and np.all(Ze == 1.0)
+
+
+def test_row_weights_recover_the_key_and_query_scores():
+    """The oracle's key and query scores (explicit re-runs) equal the row-weight form under the
+    logit shifts of the same draws: sigma tau <q_t, a_s> for keys, sigma tau <a_t, k_s> for
+    queries, noise from the oracle's generator."""
+    g = np.random.default_rng(72)
+    B, H, S, dh, K = 1, 2, 12, 4, 2
+    T, d, sigma, tau, seed, tag = B * S, H * dh, 0.2, 0.5, 0x5EED, 9
+    q, k, v, go = (g.standard_normal((T, d)) for _ in range(4))
+    P = _softmax_causal(tau * _heads(q, B, S, H) @ _heads(k, B, S, H).transpose(0, 1, 3, 2))
+    W, Z = oracle.attn_row_weights(P, v, go)
+    tri = np.tril(np.ones((S, S), dtype=bool))
+    a = oracle.normals(seed, tag, 0, 0, 0, K, T, d)
+    ck = oracle.attn_key_scores(P, q, v, go, K, sigma, tau, seed, tag)
+    cq = oracle.attn_query_scores(P, k, v, go, K, sigma, tau, seed, tag)
+    for i in range(K):
+        ah = _heads(a[i], B, S, H)
+        for got, delta in ((ck[i], _heads(q, B, S, H) @ ah.transpose(0, 1, 3, 2)),
+                           (cq[i], ah @ _heads(k, B, S, H).transpose(0, 1, 3, 2))):
+            em1 = np.expm1(sigma * tau * delta) * tri
+            val = (W * em1).sum(-1) / (Z * (Z + (P * tri * em1).sum(-1)))   # [B, H, S]
+            np.testing.assert_allclose(got, -val.sum(1).reshape(T), rtol=1e-9, atol=1e-13)

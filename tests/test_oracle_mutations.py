@@ -91,6 +91,8 @@ PINS_STEPS = [
     lambda: attn.test_query_scores_equal_an_explicit_attention_rerun(1, 3, 20, 4, 2, 64, 5, 100),
     attn.test_query_scores_first_order_is_the_softmax_jacobian,
     attn.test_query_scores_row_scale_diagonal_and_zeros,
+    lambda: attn.test_row_weights_reproduce_an_explicit_softmax_rerun(2, 2, 12, 8),
+    attn.test_row_weights_invariants,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -162,6 +164,15 @@ MUTATIONS = [
      "dot += a[j] * k[(b * S + sl) * d + h * dh + j];\n            dl[sl] = sigma * dot;"),
     ("query score sign", "    return -acc;\n}\n\nvoid dust_or_attn_query_scores(",
      "    return acc;\n}\n\nvoid dust_or_attn_query_scores("),
+    ("row weights without the base", "wrow[s] = prow[s] * (z * u - base);",
+     "wrow[s] = prow[s] * (z * u);"),
+    ("row weights without Z", "wrow[s] = prow[s] * (z * u - base);",
+     "wrow[s] = prow[s] * (u - base);"),
+    ("row weights' inner product on the query's value",
+     "u += v[(b * S + s) * d + h * dh + j] * g[(b * S + t) * d + h * dh + j];\n                    wrow",
+     "u += v[(b * S + t) * d + h * dh + j] * g[(b * S + t) * d + h * dh + j];\n                    wrow"),
+    ("row sum includes the diagonal's successor", "for (int64_t s = 0; s <= t; ++s) {\n                    double u = 0.0;",
+     "for (int64_t s = 0; s <= t + (t + 1 < S); ++s) {\n                    double u = 0.0;"),
     ("query head offset dropped", "(uint64_t)(chan0 + h * dh + j));\n        double Z",
      "(uint64_t)(chan0 + j));\n        double Z"),
 ]
