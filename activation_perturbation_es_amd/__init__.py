@@ -19,8 +19,8 @@ __all__ = [
     "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DustError",
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
     "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam",
-    "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_key_scores",
-    "dust_attn_query_scores", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
+    "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_row_weights",
+    "dust_attn_key_scores", "dust_attn_query_scores", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
     "dust_status_string", "dust_last_error", "library", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -48,6 +48,7 @@ _SIGNATURES = {
     "dust_loss_reward": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp]),
     "dust_attn_value_scores": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _f32,
                                       _u64, _u32, _u32, _u32, _vp]),
+    "dust_attn_row_weights": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _vp]),
     "dust_attn_key_scores": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                     _f32, _f32, _u64, _u32, _u32, _u32, _vp]),
     "dust_attn_query_scores": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
@@ -144,15 +145,20 @@ def dust_attn_value_scores(P, g_o, c, Kc, B, H, S, dh, chan0, sigma, seed, tag, 
                  sigma, seed, tag, draw0, tok0, _stream(stream))
 
 
-def dust_attn_key_scores(P, q, v, g_o, c, Kc, B, H, S, dh, chan0, sigma, softmax_scale, seed, tag,
+def dust_attn_row_weights(P, v, g_o, W, Z, B, H, S, dh, stream=None):
+    return _call("dust_attn_row_weights", _ptr(P), _ptr(v), _ptr(g_o), _ptr(W), _ptr(Z), B, H, S,
+                 dh, _stream(stream))
+
+
+def dust_attn_key_scores(P, q, W, Z, c, Kc, B, H, S, dh, chan0, sigma, softmax_scale, seed, tag,
                          draw0, tok0, stream=None):
-    return _call("dust_attn_key_scores", _ptr(P), _ptr(q), _ptr(v), _ptr(g_o), _ptr(c), Kc, B, H,
+    return _call("dust_attn_key_scores", _ptr(P), _ptr(q), _ptr(W), _ptr(Z), _ptr(c), Kc, B, H,
                  S, dh, chan0, sigma, softmax_scale, seed, tag, draw0, tok0, _stream(stream))
 
 
-def dust_attn_query_scores(P, k, v, g_o, c, Kc, B, H, S, dh, chan0, sigma, softmax_scale, seed,
+def dust_attn_query_scores(P, k, W, Z, c, Kc, B, H, S, dh, chan0, sigma, softmax_scale, seed,
                            tag, draw0, tok0, stream=None):
-    return _call("dust_attn_query_scores", _ptr(P), _ptr(k), _ptr(v), _ptr(g_o), _ptr(c), Kc, B,
+    return _call("dust_attn_query_scores", _ptr(P), _ptr(k), _ptr(W), _ptr(Z), _ptr(c), Kc, B,
                  H, S, dh, chan0, sigma, softmax_scale, seed, tag, draw0, tok0, _stream(stream))
 
 

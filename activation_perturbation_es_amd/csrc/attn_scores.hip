@@ -46,14 +46,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint32_t (&w)[4]) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS row pitches (bytes): 32 keys of P as fp32 plus 16 bytes and DH bf16 columns of a
+// LDS row pitches (bytes): 32 keys of P (or W) as fp32 plus 16 bytes and DH bf16 columns of a
 // query-side tile plus 16 bytes, so that the 16-byte fragment reads of 16 consecutive rows fall
 // into distinct banks.
 constexpr uint32_t kPPitch = 144;
 __host__ __device__ constexpr uint32_t g_pitch(int KS) { return 32u * KS + 16u; }
-// one step's operands: P tile and NQ query-side tiles of 32 rows
-__host__ __device__ constexpr uint32_t stage_bytes(int KS, int NQ) {
-    return 32u * (kPPitch + NQ * g_pitch(KS));
+// one step's operands: the P tile, with HW the W tile, and NQ side tiles of 32 rows
+__host__ __device__ constexpr uint32_t stage_bytes(int KS, int NQ, bool HW = false) {
+    return 32u * ((HW ? 2u : 1u) * kPPitch + NQ * g_pitch(KS));
 }
 
 // The A operand of one key row: the noise of key `token` at channels 4 q0 + 16 ks + 8 half ..
@@ -101,46 +101,52 @@ __device__ __forceinline__ float half_wave_sum(float x) {
     return x + __shfl_xor(x, 16);
 }
 
-// Staging of one step as 16-byte pieces: the P tile's rows first (4 per query row), then the NQ
-// side tiles (2 KS per row each); loads into registers, stores to LDS after the step's compute.
-template <int KS, int NQ, uint32_t NT = 256, bool TP = false>
+// Staging of one step as 16-byte pieces: the P tile's rows first (4 per row of 32 bf16), then
+// with HW the W tile's rows (8 per row of 32 fp32), then the NQ side tiles (2 KS per row each);
+// loads into registers, stores to LDS after the step's compute. A stage in LDS holds P
+// [32][kPPitch], with HW W [32][kPPitch], then the side tiles [NQ][32][g_pitch].
+template <int KS, int NQ, uint32_t NT = 256, bool TP = false, bool HW = false>
 struct Stager {
-    static constexpr uint32_t kPieces = 128u + 64u * KS * NQ;
+    static constexpr uint32_t kW = HW ? 256u : 0u;
+    static constexpr uint32_t kPieces = 128u + kW + 64u * KS * NQ;
     static constexpr uint32_t kPerThread = (kPieces + NT - 1u) / NT;
+    static constexpr uint32_t kSide = (HW ? 64u : 32u) * kPPitch;   // bytes before the side tiles
     u32x4 r[kPerThread];
 
-    // P [B, H, S, S]: query tile ct over key tile kt of sequence b, head h; the side arrays
-    // [T, H DH]: row tile xt of the sequence (the query tile for value and key scores, the key
-    // tile for query scores)
-    __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P,
+    // P [B, H, S, S] and W [B, H, S, S]: query tile ct over key tile kt of sequence b, head h;
+    // the side arrays [T, H DH]: row tile xt of the sequence (the query tile for value and key
+    // scores, the key tile for query scores)
+    __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P, const float *Wm,
                                          const uint16_t *const (&qs)[NQ], uint32_t b, uint32_t H,
                                          uint32_t S, uint32_t d, uint32_t h, uint32_t kt,
                                          uint32_t ct, uint32_t xt) {
         constexpr uint32_t DH = 16u * KS;
+        const uint64_t tile = (((uint64_t)b * H + h) * S + ct * 32u) * S + kt * 32u;
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
             const uint32_t pc = tid + NT * j;
             if (pc >= kPieces) continue;
             if (pc < 128u) {
                 const uint32_t row = pc >> 2, seg = pc & 3u;
-                r[j] = *(const u32x4 *)(P + (((uint64_t)b * H + h) * S + ct * 32u + row) * S +
-                                        kt * 32u + 8u * seg);
+                r[j] = *(const u32x4 *)(P + tile + (uint64_t)row * S + 8u * seg);
+            } else if (HW && pc < 128u + kW) {
+                const uint32_t x = pc - 128u, row = x >> 3, seg = x & 7u;
+                r[j] = *(const u32x4 *)(Wm + tile + (uint64_t)row * S + 4u * seg);
             } else {
-                const uint32_t xr = xt;
-                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
+                const uint32_t x = pc - 128u - kW, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n)
                     if (m == (uint32_t)n)
-                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + xr * 32u + row) * d +
+                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + xt * 32u + row) * d +
                                                 h * DH + 8u * seg);
             }
         }
     }
 
     // P widened to fp32 once here for all draws; on a diagonal tile (mask) the keys after the
-    // row's query become 0, so later arithmetic needs no causal test. TP stores the tile
-    // transposed, [32 keys][32 queries].
+    // row's query become 0 in P and W, so later arithmetic needs no causal test. TP stores the
+    // P and W tiles transposed, [32 keys][32 queries].
     __device__ __forceinline__ void store(uint32_t tid, unsigned char *tb, bool mask) const {
         constexpr uint32_t GP = g_pitch(KS);
 #pragma unroll
@@ -169,10 +175,27 @@ struct Stager {
                     dst[0] = f32x4{f[0], f[1], f[2], f[3]};
                     dst[1] = f32x4{f[4], f[5], f[6], f[7]};
                 }
+            } else if (HW && pc < 128u + kW) {
+                const uint32_t x = pc - 128u, row = x >> 3, seg = x & 7u;
+                unsigned char *wt = tb + 32u * kPPitch;
+                const u32x4 w = r[j];
+                float f[4];
+#pragma unroll
+                for (uint32_t e = 0; e < 4u; ++e) {
+                    f[e] = __uint_as_float(w[e]);
+                    if (mask) f[e] = 4u * seg + e <= row ? f[e] : 0.f;
+                }
+                if (TP) {
+#pragma unroll
+                    for (uint32_t e = 0; e < 4u; ++e)
+                        *(float *)(wt + (4u * seg + e) * kPPitch + 4u * row) = f[e];
+                } else {
+                    *(f32x4 *)(wt + row * kPPitch + 16u * seg) = f32x4{f[0], f[1], f[2], f[3]};
+                }
             } else {
-                const uint32_t x = pc - 128u, m = x / (64u * KS), y = x % (64u * KS);
+                const uint32_t x = pc - 128u - kW, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
-                *(u32x4 *)(tb + 32u * kPPitch + (m * 32u + row) * GP + 16u * seg) = r[j];
+                *(u32x4 *)(tb + kSide + (m * 32u + row) * GP + 16u * seg) = r[j];
             }
         }
     }
@@ -233,14 +256,14 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     // Step n's tiles are in LDS stage n % 2; step n + 1's are fetched into registers at the
     // start of step n and stored to the other stage at its end, before the one barrier per step.
     StepOrder cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.load(tid, P, nullptr, qs, b, H, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     noise(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;   // uniform across the block
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
+        if (more) stg.load(tid, P, nullptr, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -310,51 +333,138 @@ __device__ __forceinline__ float expm1_any(float D, const Expm1Coef &e) {
     return fabsf(x) <= kPolyRange ? expm1_poly(D, e) : expf(x) - 1.f;
 }
 
-// Key scores, 8 waves per block (two per SIMD, so that one wave's vector work runs under the
-// other's matrix-core work), one draw per wave, one sequence per block.
+// Row weights of the softmax re-run, shared by the key and query scores. With u_ts = <v_s, g_t>,
+// Z_t = sum_{s <= t} P_ts and base_t = sum_{s <= t} P_ts u_ts, a re-run under logit shifts
+// delta changes the output's inner product at query t by
+//     (Z N1 - base N0) / (Z (Z + N0)) = sum_s W_ts (e^delta_ts - 1) / (Z_t (Z_t + N0_t)),
+//     W_ts = P_ts (Z_t u_ts - base_t),  N0_t = sum_s P_ts (e^delta_ts - 1),
+// and W, Z do not depend on the draw. One wave per tile of 32 queries of one (sequence, head):
+// u on the matrix cores (value rows as the A operand, g rows as B; element r of a lane is key
+// 8 (r / 4) + 4 half + r % 4 of the tile, its query the lane's column), a first pass over the
+// key tiles at or before the query tile sums Z and base, a second writes W; tiles above the
+// diagonal are written as zeros.
 template <int KS>
-__global__ __launch_bounds__(512) void attn_key_scores_kernel(
+__global__ __launch_bounds__(256) void attn_row_weights_kernel(
+    const uint16_t *__restrict__ P, const uint16_t *__restrict__ v,
+    const uint16_t *__restrict__ g, float *__restrict__ W, float *__restrict__ Z, uint32_t H,
+    uint32_t S, uint32_t ntiles) {
+    constexpr uint32_t DH = 16u * KS;
+    const uint32_t lane = threadIdx.x & 63u;
+    const uint32_t gt = blockIdx.x * 4u + wave_in_block();   // query tile over (b, h, ct)
+    if (gt >= ntiles) return;
+    const uint32_t nt = S / 32u, ct = gt % nt, bh = gt / nt, h = bh % H, b = bh / H;
+    const uint32_t col = lane & 31u, half = lane >> 5;
+    const uint32_t d = H * DH;
+    const uint32_t t = ct * 32u + col;   // this lane's query
+    bf16x8 gb[KS];
+    const uint16_t *grow = g + ((uint64_t)b * S + t) * d + h * DH + 8u * half;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+        gb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(grow + 16u * ks));
+    const uint64_t rowoff = (((uint64_t)b * H + h) * S + t) * S;
+    const uint16_t *prow = P + rowoff;
+    float *wrow = W + rowoff;
+
+    auto u_tile = [&](uint32_t kt) {
+        const uint16_t *vrow = v + ((uint64_t)b * S + kt * 32u + col) * d + h * DH + 8u * half;
+        f32x16 u = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8, *(const u32x4 *)(vrow + 16u * ks)), gb[ks], u, 0, 0, 0);
+        return u;
+    };
+    // the lane's weights over its 16 keys of tile kt, 0 past its query
+    auto p_tile = [&](uint32_t kt, float (&p)[16]) {
+#pragma unroll
+        for (uint32_t qd = 0; qd < 4u; ++qd) {
+            const uint2 w = *(const uint2 *)(prow + kt * 32u + 8u * qd + 4u * half);
+            p[4 * qd + 0] = __uint_as_float(w.x << 16);
+            p[4 * qd + 1] = __uint_as_float(w.x & 0xFFFF0000u);
+            p[4 * qd + 2] = __uint_as_float(w.y << 16);
+            p[4 * qd + 3] = __uint_as_float(w.y & 0xFFFF0000u);
+#pragma unroll
+            for (uint32_t r = 0; r < 4u; ++r)
+                p[4 * qd + r] = kt * 32u + 8u * qd + 4u * half + r <= t ? p[4 * qd + r] : 0.f;
+        }
+    };
+
+    float z = 0.f, bs = 0.f;
+    for (uint32_t kt = 0; kt <= ct; ++kt) {
+        const f32x16 u = u_tile(kt);
+        float p[16];
+        p_tile(kt, p);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            z += p[r];
+            bs = __builtin_fmaf(p[r], u[r], bs);
+        }
+    }
+    z += __shfl_xor(z, 32);
+    bs += __shfl_xor(bs, 32);
+    if (half == 0) Z[((uint64_t)b * H + h) * S + t] = z;
+    for (uint32_t kt = 0; kt < nt; ++kt) {
+        float w[16];
+        if (kt <= ct) {
+            const f32x16 u = u_tile(kt);
+            float p[16];
+            p_tile(kt, p);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[r] = p[r] * __builtin_fmaf(z, u[r], -bs);
+        } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w[r] = 0.f;
+        }
+#pragma unroll
+        for (uint32_t qd = 0; qd < 4u; ++qd)
+            *(f32x4 *)(wrow + kt * 32u + 8u * qd + 4u * half) =
+                f32x4{w[4 * qd], w[4 * qd + 1], w[4 * qd + 2], w[4 * qd + 3]};
+    }
+}
+
+// Key scores: NW waves per block (three per SIMD where the registers allow, so that one wave's
+// vector work runs under another's matrix-core work), one draw per wave, one sequence per
+// block. Per step each wave forms D = a q^T on the matrix cores, then per element
+// e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys (one lane-half swap completes
+// both sums) into running sums in LDS; at each head's end every wave folds M / (Z (Z + N0))
+// into its draw's scores.
+template <int KS, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ qm,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g, float *__restrict__ c,
+    const float *__restrict__ Wm, const float *__restrict__ Zm, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
-    // LDS: two stages of one step's operands (P tile [32 queries][32 keys], q and g tiles
-    // [32 queries][DH]); per wave the head's running sums of its draw, [N1, N0][S];
-    // per SIMD (waves 0-3) the partial row sums over the 8 key rows of each tile it owns,
-    // [Z, base][S]; the head's query norms |q_t|, [S].
+    // LDS: two stages of one step's operands (P and W tiles [32 queries][32 keys] in fp32, the
+    // q tile [32 queries][DH]); per wave the head's running sums of its draw, [M, N0][S]; the
+    // head's query norms |q_t|, [S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
-    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 2);
+    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 1, true);
+    using Stg = Stager<KS, 1, NW * 64, false, true>;
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
     // this wave's draw; a draw past the last one is computed with the last draw's noise and
     // not written, so every wave loads and synchronises
-    const uint32_t i = (blockIdx.x % ndg) * 8u + wave;
+    const uint32_t i = (blockIdx.x % ndg) * (uint32_t)NW + wave;
     const uint32_t draw = draw0 + min(i, Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
     float *NN = (float *)(lds + 2u * SB);
-    float *ZB = NN + 16u * S;
-    float *QN = ZB + 8u * S;
-    float *nnw = NN + (wave * 2u + half) * S;          // lanes 0-31 keep N1, lanes 32-63 N0
-    float *zbw = ZB + ((wave & 3u) * 2u + half) * S;   // lanes 0-31 keep Z, lanes 32-63 base
+    float *QN = NN + 2u * NW * S;
+    float *nnw = NN + (wave * 2u + half) * S;   // lanes 0-31 keep M, lanes 32-63 N0
 
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
-    const uint16_t *const qs[2] = {qm, g};
-    Stager<KS, 2, 512> stg;
+    const uint16_t *const qs[1] = {qm};
+    Stg stg;
 
-    // key-side operands of the current key tile: the draw's noise and the values, and the
-    // largest noise norm over the tile's 32 keys (for the range test of e^x - 1)
-    bf16x8 ahi[KS], alo[KS], vb[KS];
+    // key-side operands of the current key tile: the draw's noise and the largest noise norm
+    // over the tile's 32 keys (for the range test of e^x - 1)
+    bf16x8 ahi[KS], alo[KS];
     float amax = 0.f;
     auto key_tile = [&](uint32_t h, uint32_t kt) {
         const uint32_t row = b * S + kt * 32u + col;
-        const uint16_t *vrow = v + (uint64_t)row * d + h * DH + 8u * half;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            vb[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(vrow + 16u * ks));
         float n2;
         noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
         n2 += __shfl_xor(n2, 32);
@@ -364,7 +474,7 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
     };
     // |q_t| of head h for every query of the sequence
     auto query_norms = [&](uint32_t h) {
-        for (uint32_t t = tid; t < S; t += 512u) {
+        for (uint32_t t = tid; t < S; t += NW * 64u) {
             const uint16_t *qrow = qm + ((uint64_t)b * S + t) * d + h * DH;
             float n2 = 0.f;
 #pragma unroll
@@ -381,21 +491,17 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
         }
     };
 
-    // A head is complete: fold its sums into the score of this wave's draw. The first head
-    // stores, later heads add; each lane rereads only what it wrote itself.
-    auto fold_head = [&](bool first) {
+    // Head hd is complete: fold its sums into the score of this wave's draw. Head 0 stores,
+    // later heads add; each lane rereads only what it wrote itself.
+    auto fold_head = [&](uint32_t hd) {
         if (i >= Kc) return;
         float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
-        const float *n1 = NN + (wave * 2u) * S, *n0 = n1 + S;
+        const float *zr = Zm + ((uint64_t)b * H + hd) * S;
+        const float *m1 = NN + (wave * 2u) * S, *n0 = m1 + S;
         for (uint32_t t = lane; t < S; t += 64u) {
-            float Z = 0.f, bs = 0.f;
-#pragma unroll
-            for (uint32_t w = 0; w < 4u; ++w) {
-                Z += ZB[(2u * w) * S + t];
-                bs += ZB[(2u * w + 1u) * S + t];
-            }
-            const float val = Z > 0.f ? (Z * n1[t] - bs * n0[t]) / (Z * (Z + n0[t])) : 0.f;
-            cr[t] = first ? -val : cr[t] - val;
+            const float Z = zr[t];
+            const float val = Z > 0.f ? m1[t] / (Z * (Z + n0[t])) : 0.f;
+            cr[t] = hd == 0 ? -val : cr[t] - val;
         }
     };
 
@@ -406,18 +512,22 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
 
     // One query tile's vector work: e^x - 1 of the products, weighted sums over the tile's keys
     // into the running sums of query tile qt.
-    auto tile_sums = [&](const f32x16 &dd, const f32x16 &u, const unsigned char *tb, uint32_t qt,
-                         bool first) {
+    auto tile_sums = [&](const f32x16 &dd, const unsigned char *tb, uint32_t qt, bool first) {
         const uint32_t tq = qt * 32u + col;
         const float qn = QN[tq];
         // element 4 qd + r is key row 8 qd + 4 half + r of the tile, query column col
         const unsigned char *prow = tb + col * kPPitch + 16u * half;
-        float w[16];
+        const unsigned char *wrow = prow + 32u * kPPitch;
+        float p[16], w[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
             const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
+            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[4 * qd + r] = x[r];
+            for (int r = 0; r < 4; ++r) {
+                p[4 * qd + r] = x[r];
+                w[4 * qd + r] = y[r];
+            }
         }
         bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax <= lim_cs)) == 0;
         if (!poly) {   // the bound is loose: test the products themselves
@@ -426,133 +536,104 @@ __global__ __launch_bounds__(512) void attn_key_scores_kernel(
             for (int r = 0; r < 16; ++r) m = max(m, __float_as_uint(dd[r]) << 1);
             poly = __builtin_amdgcn_ballot_w64(!(m <= lim_bits)) == 0;
         }
-        float n1 = 0.f, n0 = 0.f;
+        // e^x - 1 first, the sums after, so that both forms feed the same accumulators
+        float e[16];
         if (poly) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = expm1_poly(dd[r], ec);
-                n1 = __builtin_fmaf(w[r] * u[r], e, n1);
-                n0 = __builtin_fmaf(w[r], e, n0);
-            }
+            for (int r = 0; r < 16; ++r) e[r] = expm1_poly(dd[r], ec);
         } else {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = expm1_any(dd[r], ec);
-                n1 = __builtin_fmaf(w[r] * u[r], e, n1);
-                n0 = __builtin_fmaf(w[r], e, n0);
-            }
+            for (int r = 0; r < 16; ++r) e[r] = expm1_any(dd[r], ec);
         }
-        // lane-half swap: lanes 0-31 end with N1 over the tile's 32 keys, lanes 32-63 with N0
-        const auto sn = __builtin_amdgcn_permlane32_swap(__float_as_uint(n1), __float_as_uint(n0),
+        float m1 = 0.f, n0 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            m1 = __builtin_fmaf(w[r], e[r], m1);
+            n0 = __builtin_fmaf(p[r], e[r], n0);
+        }
+        // lane-half swap: lanes 0-31 end with M over the tile's 32 keys, lanes 32-63 with N0
+        const auto sn = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(n0),
                                                          false, false);
         const float nn = __uint_as_float(sn[0]) + __uint_as_float(sn[1]);
         if (first)   // a query tile's first key tile of the head starts its sums
             nnw[tq] = nn;
         else
             nnw[tq] += nn;
-        if (wave < 4u) {   // the draw-independent row sums, key rows 8 wave .. 8 wave + 7
-            float zs = 0.f, bs = 0.f;
-#pragma unroll
-            for (uint32_t qd = 0; qd < 4u; ++qd)
-                if (qd == wave) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        zs += w[4 * qd + r];
-                        bs = __builtin_fmaf(w[4 * qd + r], u[4 * qd + r], bs);
-                    }
-                }
-            const auto sz = __builtin_amdgcn_permlane32_swap(__float_as_uint(zs),
-                                                             __float_as_uint(bs), false, false);
-            const float zb = __uint_as_float(sz[0]) + __uint_as_float(sz[1]);
-            if (first)
-                zbw[tq] = zb;
-            else
-                zbw[tq] += zb;
-        }
     };
 
     StepOrder cur;
-    stg.load(tid, P, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.load(tid, P, Wm, qs, b, H, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     query_norms(0);
     key_tile(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         if (cur.kt == 0 && cur.ct == 0 && cur.h > 0) {   // uniform across the block
-            fold_head(cur.h == 1u);
+            fold_head(cur.h - 1u);
             query_norms(cur.h);
-            __syncthreads();   // Z and base read, query norms written, before either is used
+            __syncthreads();   // query norms written before they are used
         }
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;
-        if (more) stg.load(tid, P, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
+        if (more) stg.load(tid, P, Wm, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
         const unsigned char *base = lds + st * SB;
-        const unsigned char *qrow = base + 32u * kPPitch + col * GP + 16u * half;
-        f32x16 dd = {}, u = {};
+        const unsigned char *qrow = base + Stg::kSide + col * GP + 16u * half;
+        f32x16 dd = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
-            const bf16x8 gb = *(const bf16x8 *)(qrow + 32u * GP + 32u * ks);
             dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd, 0, 0, 0);
-            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[ks], gb, u, 0, 0, 0);
             dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd, 0, 0, 0);
         }
-        tile_sums(dd, u, base, cur.ct, cur.kt == 0);
+        tile_sums(dd, base, cur.ct, cur.kt == 0);
         if (!more) break;
         stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
         if (nx.kt != cur.kt || nx.h != cur.h) key_tile(nx.h, nx.kt);
         __syncthreads();
         cur = nx;
     }
-    __syncthreads();
-    fold_head(H == 1u);
+    fold_head(H - 1u);
 }
 
 // Query scores: the transpose of the key scores. The noise sits on the query side, so a block
 // walks heads, then query tiles, then the key tiles at or before the query tile, generating the
-// noise of a query tile once; the products D^T = a k^T and U^T = g v^T come out with the query
-// tile's rows in each lane's registers and its key in the lane's column, so every lane keeps
-// the running sums N1, N0 of its 16 query rows in registers over the key tiles and one lane
-// reduction per query tile completes them. NW waves, one draw per wave: 8 (two per SIMD) where
-// the registers allow, 4 for the widest heads.
+// noise of a query tile once; the product D^T = a k^T comes out with the query tile's rows in
+// each lane's registers and its key in the lane's column, so every lane keeps the running sums
+// M, N0 of its 16 query rows in registers over the key tiles and one lane reduction per query
+// tile completes them. NW waves, one draw per wave.
 template <int KS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ km,
-    const uint16_t *__restrict__ v, const uint16_t *__restrict__ g, float *__restrict__ c,
+    const float *__restrict__ Wm, const float *__restrict__ Zm, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
-    // LDS: two stages of one step's operands (P tile transposed [32 keys][32 queries], k and v
-    // tiles [32 keys][DH]); the query tile's row sums Z and base from waves 0-3, double-buffered
-    // by query tile, [2][Z, base][32]; the key norms |k_s|, double-buffered by head, [2][S].
+    // LDS: two stages of one step's operands (P and W tiles transposed, [32 keys][32 queries]
+    // in fp32, the k tile [32 keys][DH]); the key norms |k_s|, double-buffered by head, [2][S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
-    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 2);
+    constexpr uint32_t GP = g_pitch(KS), SB = stage_bytes(KS, 1, true);
+    using Stg = Stager<KS, 1, NW * 64, true, true>;
     const uint32_t tid = threadIdx.x;
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    const uint32_t i = (blockIdx.x % ndg) * NW + wave;
+    const uint32_t i = (blockIdx.x % ndg) * (uint32_t)NW + wave;
     const uint32_t draw = draw0 + min(i, Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
-    float *ZB = (float *)(lds + 2u * SB);
-    float *KN = ZB + 128u;
+    float *KN = (float *)(lds + 2u * SB);
 
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
-    const uint16_t *const ks_[2] = {km, v};
-    Stager<KS, 2, NW * 64, true> stg;
+    const uint16_t *const ks_[1] = {km};
+    Stg stg;
 
-    // query-side operands of the current query tile: the draw's noise, the output error g, and
-    // the largest noise norm over the tile's 32 queries
-    bf16x8 ahi[KS], alo[KS], gq[KS];
+    // query-side operands of the current query tile: the draw's noise and the largest noise
+    // norm over the tile's 32 queries
+    bf16x8 ahi[KS], alo[KS];
     float amax = 0.f;
     auto query_tile = [&](uint32_t h, uint32_t ct) {
         const uint32_t row = b * S + ct * 32u + col;
-        const uint16_t *grow = g + (uint64_t)row * d + h * DH + 8u * half;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            gq[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(grow + 16u * ks));
         float n2;
         noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
         n2 += __shfl_xor(n2, 32);
@@ -585,79 +666,45 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
 
     // running sums of the current query tile: element r is query row 8 (r / 4) + 4 half + r % 4,
     // summed over this lane's key column
-    float n1[16], n0[16], zs[4], bs[4];
-    // completed sums N1, N0 of the previous query tile (the row each lane holds: see fold)
-    float t1 = 0.f, t0 = 0.f;
-    uint32_t fold_tile = 0xFFFFFFFFu;   // global index h * nt + ct of the tile awaiting its fold
+    float m1[16], n0[16];
     auto reset = [&]() {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) n1[r] = n0[r] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) zs[j] = bs[j] = 0.f;
+        for (int r = 0; r < 16; ++r) m1[r] = n0[r] = 0.f;
     };
-    // Sum the running sums over the 32 key columns (lanes of one half); lane l then takes the
-    // totals of row m(l) = 8 ((l & 15) >> 2) + 4 (l >> 5) + (l & 3) when (l & 31) < 16. Waves 0-3
-    // also complete their row sums Z and base and leave them in LDS.
-    auto finish_tile = [&](uint32_t gt) {
+    // Query tile ct of head h is complete: sum the running sums over the 32 key columns (lanes
+    // of one half); lane l then takes the totals of row m(l) = 8 ((l & 15) >> 2) + 4 (l >> 5) +
+    // (l & 3) when (l & 31) < 16 and folds M / (Z (Z + N0)) into this wave's draw. Head 0
+    // stores, later heads add.
+    auto finish_tile = [&](uint32_t h, uint32_t ct) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            n1[r] = half_wave_sum(n1[r]);
+            m1[r] = half_wave_sum(m1[r]);
             n0[r] = half_wave_sum(n0[r]);
         }
         const uint32_t rr = lane & 15u;
-        t1 = 0.f;
-        t0 = 0.f;
+        float t1 = 0.f, t0 = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            t1 = rr == (uint32_t)r ? n1[r] : t1;
+            t1 = rr == (uint32_t)r ? m1[r] : t1;
             t0 = rr == (uint32_t)r ? n0[r] : t0;
         }
-        if (wave < 4u) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                zs[j] = half_wave_sum(zs[j]);
-                bs[j] = half_wave_sum(bs[j]);
-            }
-            // rows 8 wave + 4 half + j, j < 4: lane (half, j) writes them
-            float *zb = ZB + (gt & 1u) * 64u;
-            if ((lane & 31u) < 4u) {
-                const uint32_t j = lane & 3u, m = 8u * wave + 4u * half + j;
-                float z = zs[0], bb = bs[0];
-#pragma unroll
-                for (uint32_t jj = 1; jj < 4u; ++jj) {
-                    z = j == jj ? zs[jj] : z;
-                    bb = j == jj ? bs[jj] : bb;
-                }
-                zb[m] = z;
-                zb[32u + m] = bb;
-            }
-        }
-        fold_tile = gt;
-    };
-    // Fold the completed tile into this wave's draw: (Z N1 - base N0) / (Z (Z + N0)).
-    auto fold = [&]() {
-        if (fold_tile == 0xFFFFFFFFu) return;
-        const uint32_t h = fold_tile / nt, ct = fold_tile % nt;
-        fold_tile = 0xFFFFFFFFu;
         if (i >= Kc || (lane & 31u) >= 16u) return;
         const uint32_t m = 8u * ((lane & 15u) >> 2) + 4u * half + (lane & 3u);
-        const float *zb = ZB + (((h * nt + ct) & 1u) * 64u);
-        const float Z = zb[m], bsum = zb[32u + m];
-        const float val = Z > 0.f ? (Z * t1 - bsum * t0) / (Z * (Z + t0)) : 0.f;
+        const float Z = Zm[((uint64_t)b * H + h) * S + ct * 32u + m];
+        const float val = Z > 0.f ? t1 / (Z * (Z + t0)) : 0.f;
         float *cr = c + (uint64_t)i * T + (uint64_t)b * S + ct * 32u + m;
         *cr = h == 0 ? -val : *cr - val;
     };
 
     // steps: head, query tile ct, key tile kt <= ct
     uint32_t h = 0, ct = 0, kt = 0;
-    stg.load(tid, P, ks_, b, H, S, d, 0, 0, 0, 0);
+    stg.load(tid, P, Wm, ks_, b, H, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     key_norms(0);
     query_tile(0, 0);
     reset();
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
-        fold();   // the previous query tile's sums, once its row sums are in LDS
         uint32_t nh = h, nc = ct, nk = kt + 1u;
         if (nk > ct) {
             nk = 0;
@@ -665,29 +712,31 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
             if (nc == nt) { nc = 0; nh = h + 1u; }
         }
         const bool more = nh < H;
-        // the staged key tile is kt; the P tile is (query tile ct, key tile kt)
-        if (more) stg.load(tid, P, ks_, b, H, S, d, nh, nk, nc, nk);   // k, v of key tile nk
+        // the staged key tile is kt; the P and W tiles are (query tile ct, key tile kt)
+        if (more) stg.load(tid, P, Wm, ks_, b, H, S, d, nh, nk, nc, nk);   // k of key tile nk
 
         const unsigned char *base = lds + st * SB;
-        const unsigned char *krow = base + 32u * kPPitch + col * GP + 16u * half;
-        const unsigned char *vrow = krow + 32u * GP;
-        f32x16 dd = {}, u = {};
+        const unsigned char *krow = base + Stg::kSide + col * GP + 16u * half;
+        f32x16 dd = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 kb = *(const bf16x8 *)(krow + 32u * ks);
-            const bf16x8 vb = *(const bf16x8 *)(vrow + 32u * ks);
             dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kb, dd, 0, 0, 0);
-            u = __builtin_amdgcn_mfma_f32_32x32x16_bf16(gq[ks], vb, u, 0, 0, 0);
             dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kb, dd, 0, 0, 0);
         }
         const float kn = KN[(h & 1u) * S + kt * 32u + col];
         const unsigned char *prow = base + col * kPPitch + 16u * half;
-        float w[16];
+        const unsigned char *wrow = prow + 32u * kPPitch;
+        float p[16], w[16];
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
             const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
+            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) w[4 * qd + r] = x[r];
+            for (int r = 0; r < 4; ++r) {
+                p[4 * qd + r] = x[r];
+                w[4 * qd + r] = y[r];
+            }
         }
         bool poly = __builtin_amdgcn_ballot_w64(!(kn * amax <= lim_cs)) == 0;
         if (!poly) {
@@ -707,22 +756,11 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            n1[r] = __builtin_fmaf(w[r] * u[r], e[r], n1[r]);
-            n0[r] = __builtin_fmaf(w[r], e[r], n0[r]);
-        }
-        if (wave < 4u) {   // row sums of rows 8 wave .. 8 wave + 7 (this wave's qd)
-#pragma unroll
-            for (uint32_t qd = 0; qd < 4u; ++qd)
-                if (qd == wave) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        zs[j] += w[4 * qd + j];
-                        bs[j] = __builtin_fmaf(w[4 * qd + j], u[4 * qd + j], bs[j]);
-                    }
-                }
+            m1[r] = __builtin_fmaf(w[r], e[r], m1[r]);
+            n0[r] = __builtin_fmaf(p[r], e[r], n0[r]);
         }
         if (kt == ct) {   // the query tile is complete
-            finish_tile(h * nt + ct);
+            finish_tile(h, ct);
             reset();
         }
         if (!more) break;
@@ -734,8 +772,6 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         ct = nc;
         kt = nk;
     }
-    __syncthreads();
-    fold();
 }
 
 }  // namespace
@@ -768,20 +804,32 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
     return hipGetLastError();
 }
 
-// LDS of the key kernel: two stages, then (8 waves x 2 running sums + 4 x 2 row sums + the
-// query norms) x S floats
-size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
-    return 2 * (size_t)stage_bytes((int)(dh / 16), 2) + (size_t)25 * S * sizeof(float);
+hipError_t launch_attn_row_weights(const uint16_t *P, const uint16_t *v, const uint16_t *g,
+                                   float *W, float *Z, int64_t B, int64_t H, int64_t S,
+                                   int64_t dh, hipStream_t s) {
+    const uint32_t ntiles = (uint32_t)(B * H * (S / 32));   // one wave per query tile
+    const uint32_t blocks = (ntiles + 3u) / 4u;
+#define DUST_ARW(KS)                                                                           \
+    attn_row_weights_kernel<KS><<<blocks, 256, 0, s>>>(P, v, g, W, Z, (uint32_t)H, (uint32_t)S, \
+                                                       ntiles)
+    switch (dh / 16) {
+        case 1: DUST_ARW(1); break;
+        case 2: DUST_ARW(2); break;
+        case 3: DUST_ARW(3); break;
+        case 4: DUST_ARW(4); break;
+        case 5: DUST_ARW(5); break;
+        case 6: DUST_ARW(6); break;
+        case 7: DUST_ARW(7); break;
+        default: DUST_ARW(8); break;
+    }
+#undef DUST_ARW
+    return hipGetLastError();
 }
 
-hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const uint16_t *v,
-                                  const uint16_t *g, float *c, int64_t Kc, int64_t B, int64_t H,
-                                  int64_t S, int64_t dh, int64_t chan0, float sigma,
-                                  float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
-                                  hipStream_t s) {
-    const uint32_t ndg = (uint32_t)((Kc + 7) / 8);
-    const uint32_t blocks = (uint32_t)(B * ndg);
-    // the logit shift is sigma tau <q, a> and the noise comes divided by kNormalScale
+namespace {
+
+// e^x - 1 coefficients for logit shifts sigma tau <., .> of noise divided by kNormalScale
+Expm1Coef expm1_coef(float sigma, float softmax_scale) {
     const double s1 = (double)sigma * (double)softmax_scale * kNormalScale;
     Expm1Coef ec;
     ec.s1 = (float)s1;
@@ -790,59 +838,76 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const ui
     ec.s4 = (float)(s1 * s1 * s1 * s1 / 24.0);
     ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
     ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
+    return ec;
+}
+
+// Waves (draws) per block of the key and query kernels: 12 (three per SIMD) where the registers
+// allow it without spilling (key heads up to 96 wide, query heads up to 64), else 8.
+uint32_t key_waves(int64_t dh) { return dh <= 96 ? 12u : 8u; }
+uint32_t query_waves(int64_t dh) { return dh <= 64 ? 12u : 8u; }
+
+}  // namespace
+
+// LDS of the key kernel: two stages, then (NW waves x 2 running sums + the query norms) x S
+size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
+    return 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) +
+           (size_t)(2 * key_waves(dh) + 1) * S * sizeof(float);
+}
+
+hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const float *W,
+                                  const float *Z, float *c, int64_t Kc, int64_t B, int64_t H,
+                                  int64_t S, int64_t dh, int64_t chan0, float sigma,
+                                  float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
+                                  hipStream_t s) {
+    const uint32_t nw = key_waves(dh);
+    const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
+    const uint32_t blocks = (uint32_t)(B * ndg);
+    const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
     const size_t lds = attn_key_scores_lds_bytes(S, dh);
-#define DUST_AKS(KS)                                                                           \
-    attn_key_scores_kernel<KS><<<blocks, 512, lds, s>>>(                                       \
-        P, q, v, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
+#define DUST_AKS(KS, NW)                                                                       \
+    attn_key_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                               \
+        P, q, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
     switch (dh / 16) {
-        case 1: DUST_AKS(1); break;
-        case 2: DUST_AKS(2); break;
-        case 3: DUST_AKS(3); break;
-        case 4: DUST_AKS(4); break;
-        case 5: DUST_AKS(5); break;
-        case 6: DUST_AKS(6); break;
-        case 7: DUST_AKS(7); break;
-        default: DUST_AKS(8); break;
+        case 1: DUST_AKS(1, 12); break;
+        case 2: DUST_AKS(2, 12); break;
+        case 3: DUST_AKS(3, 12); break;
+        case 4: DUST_AKS(4, 12); break;
+        case 5: DUST_AKS(5, 12); break;
+        case 6: DUST_AKS(6, 12); break;
+        case 7: DUST_AKS(7, 8); break;
+        default: DUST_AKS(8, 8); break;
     }
 #undef DUST_AKS
     return hipGetLastError();
 }
 
-hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const uint16_t *v,
-                                    const uint16_t *g, float *c, int64_t Kc, int64_t B,
-                                    int64_t H, int64_t S, int64_t dh, int64_t chan0, float sigma,
+hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const float *W,
+                                    const float *Z, float *c, int64_t Kc, int64_t B, int64_t H,
+                                    int64_t S, int64_t dh, int64_t chan0, float sigma,
                                     float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s) {
-    const uint32_t nw = dh <= 96 ? 8u : 4u;   // waves (draws) per block
+    const uint32_t nw = query_waves(dh);
     const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
     const uint32_t blocks = (uint32_t)(B * ndg);
-    // the logit shift is sigma tau <a, k> and the noise comes divided by kNormalScale
-    const double s1 = (double)sigma * (double)softmax_scale * kNormalScale;
-    Expm1Coef ec;
-    ec.s1 = (float)s1;
-    ec.s2 = (float)(s1 * s1 / 2.0);
-    ec.s3 = (float)(s1 * s1 * s1 / 6.0);
-    ec.s4 = (float)(s1 * s1 * s1 * s1 / 24.0);
-    ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
-    ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
+    const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-    // two stages, the row sums [2][2][32] and the key norms [2][S]
-    const size_t lds = 2 * (size_t)stage_bytes((int)(dh / 16), 2) + (128 + 2 * (size_t)S) * 4;
+    // two stages and the key norms [2][S]
+    const size_t lds = 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) + 2 * (size_t)S * 4;
 #define DUST_AQS(KS, NW)                                                                       \
     attn_query_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                             \
-        P, k, v, g, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
+        P, k, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
     switch (dh / 16) {
-        case 1: DUST_AQS(1, 8); break;
-        case 2: DUST_AQS(2, 8); break;
-        case 3: DUST_AQS(3, 8); break;
-        case 4: DUST_AQS(4, 8); break;
+        case 1: DUST_AQS(1, 12); break;
+        case 2: DUST_AQS(2, 12); break;
+        case 3: DUST_AQS(3, 12); break;
+        case 4: DUST_AQS(4, 12); break;
         case 5: DUST_AQS(5, 8); break;
         case 6: DUST_AQS(6, 8); break;
-        case 7: DUST_AQS(7, 4); break;
-        default: DUST_AQS(8, 4); break;
+        case 7: DUST_AQS(7, 8); break;
+        default: DUST_AQS(8, 8); break;
     }
 #undef DUST_AQS
     return hipGetLastError();

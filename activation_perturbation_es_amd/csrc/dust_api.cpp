@@ -71,6 +71,50 @@ bool ranges_overlap(const void *a, size_t abytes, const void *b, size_t bbytes) 
     return a0 < b0 + bbytes && b0 < a0 + abytes;
 }
 
+// Shared validation of the key and query scores: x is q for keys, k for queries; S_max is the
+// longest sequence the kernel supports.
+int check_softmax_scores(const char *fn, const void *P, const void *x, const float *W,
+                         const float *Z, float *c, int64_t Kc, int64_t B, int64_t H, int64_t S,
+                         int64_t dh, int64_t chan0, float sigma, float softmax_scale,
+                         uint32_t draw0, uint32_t tok0, int64_t S_max, bool *nothing) {
+    *nothing = false;
+    if (Kc < 0 || B < 0 || H < 0 || S < 0 || dh < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size", fn);
+    if (!std::isfinite(sigma) || !std::isfinite(softmax_scale))
+        return fail(DUST_ERR_INVALID, "%s: sigma and softmax_scale must be finite", fn);
+    if (std::fabs((double)sigma * (double)softmax_scale) > 1048576.0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: |sigma * softmax_scale| beyond 2^20", fn);
+    if (Kc > kMaxIdx || B > kMaxIdx || H > kMaxIdx || S > kMaxIdx || dh > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (int rc = check_noise_ranges(fn, B * S, H * dh, chan0, Kc, draw0, tok0)) return rc;
+    if (Kc == 0 || B == 0 || S == 0) {
+        *nothing = true;
+        return ok();
+    }
+    if (H == 0 || dh == 0) return fail(DUST_ERR_INVALID, "%s: H and dh must be >= 1", fn);
+    if (S % 32 != 0 || S > S_max || dh % 16 != 0 || dh > 128)
+        return fail(DUST_ERR_UNSUPPORTED,
+                    "%s: S=%lld must be a multiple of 32 up to %lld and dh=%lld a multiple of 16 "
+                    "up to 128", fn, (long long)S, (long long)S_max, (long long)dh);
+    if (!P || !x || !W || !Z || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (((uintptr_t)P & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)W & 15u) ||
+        !elem_aligned(Z, 4) || !elem_aligned(c, 4))
+        return fail(DUST_ERR_INVALID, "%s: P, the %s, and W must be 16-byte, Z and c 4-byte "
+                    "aligned", fn, S_max == 1024 ? "queries" : "keys");
+    const int64_t p_bytes = span(B * H, S, S, 2), w_bytes = span(B * H, S, S, 4);
+    const int64_t x_bytes = span(B * S, H * dh, 1, 2), z_bytes = span(B * H, S, 1, 4);
+    const int64_t c_bytes = span(Kc, B * S, 1, 4);
+    if (p_bytes < 0 || w_bytes < 0 || x_bytes < 0 || z_bytes < 0 || c_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    if (B * ((Kc + 7) / 8) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, x, (size_t)x_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, W, (size_t)w_bytes) ||
+        ranges_overlap(c, (size_t)c_bytes, Z, (size_t)z_bytes))
+        return fail(DUST_ERR_INVALID, "%s: c overlaps an input", fn);
+    return DUST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -346,87 +390,73 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
                       fn);
 }
 
-int dust_attn_key_scores(const void *P, const void *q, const void *v, const void *g_o, float *c,
-                         int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
-                         float sigma, float softmax_scale, uint64_t seed, uint32_t tag,
-                         uint32_t draw0, uint32_t tok0, void *stream) {
-    const char *fn = "dust_attn_key_scores";
-    if (Kc < 0 || B < 0 || H < 0 || S < 0 || dh < 0)
-        return fail(DUST_ERR_INVALID, "%s: negative size", fn);
-    if (!std::isfinite(sigma) || !std::isfinite(softmax_scale))
-        return fail(DUST_ERR_INVALID, "%s: sigma and softmax_scale must be finite", fn);
-    if (std::fabs((double)sigma * (double)softmax_scale) > 1048576.0)
-        return fail(DUST_ERR_UNSUPPORTED, "%s: |sigma * softmax_scale| beyond 2^20", fn);
-    if (Kc > kMaxIdx || B > kMaxIdx || H > kMaxIdx || S > kMaxIdx || dh > kMaxIdx)
+int dust_attn_row_weights(const void *P, const void *v, const void *g_o, float *W, float *Z,
+                          int64_t B, int64_t H, int64_t S, int64_t dh, void *stream) {
+    const char *fn = "dust_attn_row_weights";
+    if (B < 0 || H < 0 || S < 0 || dh < 0) return fail(DUST_ERR_INVALID, "%s: negative size", fn);
+    if (B > kMaxIdx || H > kMaxIdx || S > kMaxIdx || dh > kMaxIdx)
         return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
-    if (int rc = check_noise_ranges(fn, B * S, H * dh, chan0, Kc, draw0, tok0)) return rc;
-    if (Kc == 0 || B == 0 || S == 0) return ok();
-    if (H == 0 || dh == 0) return fail(DUST_ERR_INVALID, "%s: H and dh must be >= 1", fn);
-    if (S % 32 != 0 || S > 1024 || dh % 16 != 0 || dh > 128)
-        return fail(DUST_ERR_UNSUPPORTED,
-                    "%s: S=%lld must be a multiple of 32 up to 1024 and dh=%lld a multiple of 16 "
-                    "up to 128", fn, (long long)S, (long long)dh);
-    if (!P || !q || !v || !g_o || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
-    if (((uintptr_t)P & 15u) || ((uintptr_t)q & 15u) || ((uintptr_t)v & 15u) ||
-        ((uintptr_t)g_o & 15u) || !elem_aligned(c, 4))
-        return fail(DUST_ERR_INVALID, "%s: P, q, v and g_o must be 16-byte, c 4-byte aligned",
-                    fn);
-    const int64_t p_bytes = span(B * H, S, S, 2), x_bytes = span(B * S, H * dh, 1, 2);
-    const int64_t c_bytes = span(Kc, B * S, 1, 4);
-    if (p_bytes < 0 || x_bytes < 0 || c_bytes < 0)
-        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    if (B * ((Kc + 7) / 8) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
-    if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, q, (size_t)x_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, v, (size_t)x_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, g_o, (size_t)x_bytes))
-        return fail(DUST_ERR_INVALID, "%s: c overlaps P, q, v or g_o", fn);
-    return hip_status(dust::launch_attn_key_scores((const uint16_t *)P, (const uint16_t *)q,
-                                                   (const uint16_t *)v, (const uint16_t *)g_o, c,
-                                                   Kc, B, H, S, dh, chan0, sigma, softmax_scale,
-                                                   make_key(seed, tag), draw0, tok0,
-                                                   (hipStream_t)stream),
-                      fn);
-}
-
-int dust_attn_query_scores(const void *P, const void *k, const void *v, const void *g_o,
-                           float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,
-                           int64_t chan0, float sigma, float softmax_scale, uint64_t seed,
-                           uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream) {
-    const char *fn = "dust_attn_query_scores";
-    if (Kc < 0 || B < 0 || H < 0 || S < 0 || dh < 0)
-        return fail(DUST_ERR_INVALID, "%s: negative size", fn);
-    if (!std::isfinite(sigma) || !std::isfinite(softmax_scale))
-        return fail(DUST_ERR_INVALID, "%s: sigma and softmax_scale must be finite", fn);
-    if (std::fabs((double)sigma * (double)softmax_scale) > 1048576.0)
-        return fail(DUST_ERR_UNSUPPORTED, "%s: |sigma * softmax_scale| beyond 2^20", fn);
-    if (Kc > kMaxIdx || B > kMaxIdx || H > kMaxIdx || S > kMaxIdx || dh > kMaxIdx)
-        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
-    if (int rc = check_noise_ranges(fn, B * S, H * dh, chan0, Kc, draw0, tok0)) return rc;
-    if (Kc == 0 || B == 0 || S == 0) return ok();
+    if (B == 0 || S == 0) return ok();
     if (H == 0 || dh == 0) return fail(DUST_ERR_INVALID, "%s: H and dh must be >= 1", fn);
     if (S % 32 != 0 || S > 4096 || dh % 16 != 0 || dh > 128)
         return fail(DUST_ERR_UNSUPPORTED,
                     "%s: S=%lld must be a multiple of 32 up to 4096 and dh=%lld a multiple of 16 "
                     "up to 128", fn, (long long)S, (long long)dh);
-    if (!P || !k || !v || !g_o || !c) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
-    if (((uintptr_t)P & 15u) || ((uintptr_t)k & 15u) || ((uintptr_t)v & 15u) ||
-        ((uintptr_t)g_o & 15u) || !elem_aligned(c, 4))
-        return fail(DUST_ERR_INVALID, "%s: P, k, v and g_o must be 16-byte, c 4-byte aligned",
+    if (!P || !v || !g_o || !W || !Z) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (((uintptr_t)P & 15u) || ((uintptr_t)v & 15u) || ((uintptr_t)g_o & 15u) ||
+        ((uintptr_t)W & 15u) || !elem_aligned(Z, 4))
+        return fail(DUST_ERR_INVALID, "%s: P, v, g_o and W must be 16-byte, Z 4-byte aligned",
                     fn);
-    const int64_t p_bytes = span(B * H, S, S, 2), x_bytes = span(B * S, H * dh, 1, 2);
-    const int64_t c_bytes = span(Kc, B * S, 1, 4);
-    if (p_bytes < 0 || x_bytes < 0 || c_bytes < 0)
+    if (B * H * (S / 32) > kMaxIdx || B * S > kMaxIdx || H * dh > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    const int64_t p_bytes = span(B * H, S, S, 2), w_bytes = span(B * H, S, S, 4);
+    const int64_t x_bytes = span(B * S, H * dh, 1, 2), z_bytes = span(B * H, S, 1, 4);
+    if (p_bytes < 0 || w_bytes < 0 || x_bytes < 0 || z_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    if (B * ((Kc + 3) / 4) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
-    if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, k, (size_t)x_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, v, (size_t)x_bytes) ||
-        ranges_overlap(c, (size_t)c_bytes, g_o, (size_t)x_bytes))
-        return fail(DUST_ERR_INVALID, "%s: c overlaps P, k, v or g_o", fn);
-    return hip_status(dust::launch_attn_query_scores((const uint16_t *)P, (const uint16_t *)k,
-                                                     (const uint16_t *)v, (const uint16_t *)g_o,
-                                                     c, Kc, B, H, S, dh, chan0, sigma,
+    if (ranges_overlap(W, (size_t)w_bytes, Z, (size_t)z_bytes))
+        return fail(DUST_ERR_INVALID, "%s: W overlaps Z", fn);
+    const void *outs[2] = {W, Z};
+    const size_t out_bytes[2] = {(size_t)w_bytes, (size_t)z_bytes};
+    for (int o = 0; o < 2; ++o)
+        if (ranges_overlap(outs[o], out_bytes[o], P, (size_t)p_bytes) ||
+            ranges_overlap(outs[o], out_bytes[o], v, (size_t)x_bytes) ||
+            ranges_overlap(outs[o], out_bytes[o], g_o, (size_t)x_bytes))
+            return fail(DUST_ERR_INVALID, "%s: W or Z overlaps P, v or g_o", fn);
+    return hip_status(dust::launch_attn_row_weights((const uint16_t *)P, (const uint16_t *)v,
+                                                    (const uint16_t *)g_o, W, Z, B, H, S, dh,
+                                                    (hipStream_t)stream),
+                      fn);
+}
+
+int dust_attn_key_scores(const void *P, const void *q, const float *W, const float *Z, float *c,
+                         int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
+                         float sigma, float softmax_scale, uint64_t seed, uint32_t tag,
+                         uint32_t draw0, uint32_t tok0, void *stream) {
+    const char *fn = "dust_attn_key_scores";
+    bool nothing;
+    if (int rc = check_softmax_scores(fn, P, q, W, Z, c, Kc, B, H, S, dh, chan0, sigma,
+                                      softmax_scale, draw0, tok0, 1024, &nothing))
+        return rc;
+    if (nothing) return ok();
+    return hip_status(dust::launch_attn_key_scores((const uint16_t *)P, (const uint16_t *)q, W, Z,
+                                                   c, Kc, B, H, S, dh, chan0, sigma,
+                                                   softmax_scale, make_key(seed, tag), draw0,
+                                                   tok0, (hipStream_t)stream),
+                      fn);
+}
+
+int dust_attn_query_scores(const void *P, const void *k, const float *W, const float *Z,
+                           float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,
+                           int64_t chan0, float sigma, float softmax_scale, uint64_t seed,
+                           uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream) {
+    const char *fn = "dust_attn_query_scores";
+    bool nothing;
+    if (int rc = check_softmax_scores(fn, P, k, W, Z, c, Kc, B, H, S, dh, chan0, sigma,
+                                      softmax_scale, draw0, tok0, 4096, &nothing))
+        return rc;
+    if (nothing) return ok();
+    return hip_status(dust::launch_attn_query_scores((const uint16_t *)P, (const uint16_t *)k, W,
+                                                     Z, c, Kc, B, H, S, dh, chan0, sigma,
                                                      softmax_scale, make_key(seed, tag), draw0,
                                                      tok0, (hipStream_t)stream),
                       fn);

@@ -65,15 +65,19 @@ hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float 
                                     float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s);
 
-hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const uint16_t *v,
-                                  const uint16_t *g, float *c, int64_t Kc, int64_t B, int64_t H,
+hipError_t launch_attn_row_weights(const uint16_t *P, const uint16_t *v, const uint16_t *g,
+                                   float *W, float *Z, int64_t B, int64_t H, int64_t S,
+                                   int64_t dh, hipStream_t s);
+
+hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const float *W,
+                                  const float *Z, float *c, int64_t Kc, int64_t B, int64_t H,
                                   int64_t S, int64_t dh, int64_t chan0, float sigma,
                                   float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                   hipStream_t s);
 
-hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const uint16_t *v,
-                                    const uint16_t *g, float *c, int64_t Kc, int64_t B,
-                                    int64_t H, int64_t S, int64_t dh, int64_t chan0, float sigma,
+hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const float *W,
+                                    const float *Z, float *c, int64_t Kc, int64_t B, int64_t H,
+                                    int64_t S, int64_t dh, int64_t chan0, float sigma,
                                     float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s);
 

@@ -15,7 +15,8 @@ is not part of the estimator; its per-token losses are synthetic inputs here.
 chains the same way (for the report; the default line is workload 2). With --workload 4,
 --attention-values, --attention-keys or --attention-queries scores the draws by re-running the
 attention with perturbed values, keys or queries (dust_attn_value_scores / _key_scores /
-_query_scores) instead of streaming a synthetic attention-output change.
+_query_scores; keys and queries after dust_attn_row_weights, once per step) instead of
+streaming a synthetic attention-output change.
 
 Metric: draws x tokens per second (K * T / step time). Prints one JSON line with the per-kernel
 HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
@@ -355,6 +356,9 @@ class InnerChain(Chain):
             z.masked_fill_(~t.ones((S, S), dtype=t.bool, device=self.dev).tril(), float("-inf"))
             self.P = t.softmax(z, -1).to(t.bfloat16)
             del z
+            # the draw-independent row weights of the re-run, recomputed in every timed step
+            self.W = self.empty((B, H, S, S), t.float32)
+            self.Z = self.empty((B, H, S), t.float32)
         else:
             # One 512-draw block of the synthetic attention-output change, drawn on the device
             # before timing; every block of the timed step streams this buffer (the kernel's work
@@ -380,14 +384,18 @@ class InnerChain(Chain):
             run("dust_attn_value_scores", d.dust_attn_value_scores, self.P, self.go, self.cbuf, K,
                 T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma, self.seed,
                 self.tag, 0, 0, sh)
-        elif self.attn_mode == "keys":
-            run("dust_attn_key_scores", d.dust_attn_key_scores, self.P, self.q, self.v, self.go,
-                self.cbuf, K, T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0, self.sigma,
-                self.tau, self.seed, self.tag, 0, 0, sh)
-        elif self.attn_mode == "queries":
-            run("dust_attn_query_scores", d.dust_attn_query_scores, self.P, self.k, self.v,
-                self.go, self.cbuf, K, T // self.S, self.HEADS, self.S, self.d // self.HEADS, 0,
-                self.sigma, self.tau, self.seed, self.tag, 0, 0, sh)
+        elif self.attn_mode in ("keys", "queries"):
+            B, H, S, dh = T // self.S, self.HEADS, self.S, self.d // self.HEADS
+            run("dust_attn_row_weights", d.dust_attn_row_weights, self.P, self.v, self.go, self.W,
+                self.Z, B, H, S, dh, sh)
+            if self.attn_mode == "keys":
+                run("dust_attn_key_scores", d.dust_attn_key_scores, self.P, self.q, self.W, self.Z,
+                    self.cbuf, K, B, H, S, dh, 0, self.sigma, self.tau, self.seed, self.tag, 0, 0,
+                    sh)
+            else:
+                run("dust_attn_query_scores", d.dust_attn_query_scores, self.P, self.k, self.W,
+                    self.Z, self.cbuf, K, B, H, S, dh, 0, self.sigma, self.tau, self.seed,
+                    self.tag, 0, 0, sh)
         else:
             for blk in range(K // KB):
                 run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_INNER, None, None, self.do,
@@ -414,6 +422,9 @@ class InnerChain(Chain):
                                      1e12, FP32_VALU_PEAK_TOPS, "Tops/s"),
             "dust_attn_query_scores": ("alu", OPS_KEY_SCORE * K * (T // S) * H * (S * (S + 1) / 2),
                                        1e12, FP32_VALU_PEAK_TOPS, "Tops/s"),
+            # once per estimate: P read once (bf16), W written (fp32, zero above the diagonal)
+            # and Z
+            "dust_attn_row_weights": _hbm((T // S) * H * (6.0 * S * S + 4.0 * S)),
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_error_estimate": _alu(K * T * d, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * d * d),
@@ -434,15 +445,15 @@ class InnerChain(Chain):
                         "head_dim": self.d // self.HEADS, "draw_block": self.K,
                         "softmax_scale": self.tau,
                         "delta_o": "softmax re-run with perturbed keys (synthetic q, k, v)",
-                        "storage": "bf16 attention weights / q / v / g_o / x, fp32 scores, "
-                                   "rewards, g_hat, G_W"})
+                        "storage": "bf16 attention weights / q / v / g_o / x, fp32 row weights, "
+                                   "scores, rewards, g_hat, G_W"})
         elif self.attn_mode == "queries":
             cfg.update({"workload": self.c["name"] + "_attention_queries", "heads": self.HEADS,
                         "head_dim": self.d // self.HEADS, "draw_block": self.K,
                         "softmax_scale": self.tau,
                         "delta_o": "softmax re-run with perturbed queries (synthetic q, k, v)",
-                        "storage": "bf16 attention weights / k / v / g_o / x, fp32 scores, "
-                                   "rewards, g_hat, G_W"})
+                        "storage": "bf16 attention weights / k / v / g_o / x, fp32 row weights, "
+                                   "scores, rewards, g_hat, G_W"})
         return cfg
 
     def cpu_baseline(self, scale):
@@ -634,7 +645,7 @@ KERNEL_SOURCES = {
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
     "dust_attn_value_scores": "attn_scores.hip", "dust_attn_key_scores": "attn_scores.hip",
-    "dust_attn_query_scores": "attn_scores.hip",
+    "dust_attn_query_scores": "attn_scores.hip", "dust_attn_row_weights": "attn_scores.hip",
 }
 
 

@@ -199,6 +199,30 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
                            void *stream);
 
 /*
+ * dust_attn_row_weights -- the draw-independent part of the softmax re-run that
+ * dust_attn_key_scores and dust_attn_query_scores share (explainer, "The real work: suppressing
+ * interference": attention internals are scored through the attention output). For head h of
+ * sequence b, with u_ts = <v^h_s, g^h_t>, Z_t = sum_{s <= t} P_ts and base_t =
+ * sum_{s <= t} P_ts u_ts, a re-run of the weights under logit shifts delta (each row normalised,
+ * as dust_attn_key_scores states) changes <o_t, g_t> by
+ *     sum_s W_ts (e^{delta_ts} - 1) / (Z_t (Z_t + sum_s P_ts (e^{delta_ts} - 1))),
+ *     W_ts = P_ts (Z_t u_ts - base_t) for s <= t,  W_ts = 0 for s > t.
+ * Compute W and Z once per batch of weights; every draw of the key or query scores reuses them.
+ *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
+ *           keys s; entries above the diagonal are ignored                              (in)
+ *   v       [B*S, H*dh] bf16 values, head h in columns h*dh .. h*dh+dh-1                 (in)
+ *   g_o     [B*S, H*dh] bf16 estimated error of the attention output                     (in)
+ *   W       [B, H, S, S] fp32 row weights, zero above the diagonal                      (out)
+ *   Z       [B, H, S] fp32 causal row sums of P                                         (out)
+ * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P, v, g_o
+ * and W 16-byte, Z 4-byte aligned. W and Z must not overlap each other or the inputs. The inner
+ * products u run on the bf16 matrix cores with fp32 accumulation; Z, base and W are fp32.
+ * B = 0 or S = 0 does nothing.
+ */
+int dust_attn_row_weights(const void *P, const void *v, const void *g_o, float *W, float *Z,
+                          int64_t B, int64_t H, int64_t S, int64_t dh, void *stream);
+
+/*
  * dust_attn_key_scores -- loss change of K draws that perturb an attention KEY projection,
  * scored through the attention output (explainer, "The real work: suppressing interference":
  * the inner product of the output's change with the output's estimated error). With
@@ -208,25 +232,26 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
  *     P'_ts = P_ts e^{delta_ts} / sum_{s' <= t} P_ts' e^{delta_ts'},
  *     c[i][t] = -sum_h <sum_{s <= t} (P'_ts - P_ts / Z_t) v^h_s, g^h_t>,  Z_t = sum_{s <= t} P_ts
  * (each row is normalised, so bf16 weights that do not sum to one exactly still give 0 at
- * sigma = 0; a row whose weights sum to zero adds nothing). The call computes the scores
- * without forming the perturbed outputs. Use them as dust_loss_delta's inner-mode scores
- * (dust_reward_scan, then dust_error_estimate with the same seed, tag, draw0, tok0 and chan0
- * and d = H * dh).
+ * sigma = 0; a row whose weights sum to zero adds nothing). The values v and the output error
+ * g_o enter through W and Z of dust_attn_row_weights(P, v, g_o), which the caller computes
+ * first, once for all draws. The call computes the scores without forming the perturbed
+ * outputs. Use them as dust_loss_delta's inner-mode scores (dust_reward_scan, then
+ * dust_error_estimate with the same seed, tag, draw0, tok0 and chan0 and d = H * dh).
  *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
  *           keys s; entries above the diagonal are ignored                              (in)
  *   q       [B*S, H*dh] bf16 queries, head h in columns h*dh .. h*dh+dh-1                (in)
- *   v       [B*S, H*dh] bf16 values                                                      (in)
- *   g_o     [B*S, H*dh] bf16 estimated error of the attention output                     (in)
+ *   W, Z    [B, H, S, S] and [B, H, S] fp32 from dust_attn_row_weights; entries of W above
+ *           the diagonal are ignored                                                    (in)
  *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
  * The noise a of (token s, head h, column j) is channel chan0 + h*dh + j of token tok0 + s
  * (the key projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
- * Supported: S a multiple of 32 and at most 1024, dh a multiple of 16 in [16, 128]; P, q, v and
- * g_o 16-byte aligned; sigma and softmax_scale finite with |sigma * softmax_scale| <= 2^20.
- * c must not overlap the inputs. fp32 accumulation; the noise enters the bf16 matrix cores as
- * a high part plus a remainder (16 significant bits). Logit shifts beyond about 80 overflow
- * e^delta and give non-finite scores.
+ * Supported: S a multiple of 32 and at most 1024, dh a multiple of 16 in [16, 128]; P, q and W
+ * 16-byte, Z and c 4-byte aligned; sigma and softmax_scale finite with
+ * |sigma * softmax_scale| <= 2^20. c must not overlap the inputs. fp32 accumulation; the noise
+ * enters the bf16 matrix cores as a high part plus a remainder (16 significant bits). Logit
+ * shifts beyond about 80 overflow e^delta and give non-finite scores.
  */
-int dust_attn_key_scores(const void *P, const void *q, const void *v, const void *g_o, float *c,
+int dust_attn_key_scores(const void *P, const void *q, const float *W, const float *Z, float *c,
                          int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
                          float sigma, float softmax_scale, uint64_t seed, uint32_t tag,
                          uint32_t draw0, uint32_t tok0, void *stream);
@@ -236,21 +261,21 @@ int dust_attn_key_scores(const void *P, const void *q, const void *v, const void
  * scored through the attention output as above. With q'_t = q_t + sigma a_t, head h's logit of
  * query t on key s moves by delta_ts = sigma * softmax_scale * <a^h_t, k^h_s>, and the scores
  * are those of dust_attn_key_scores with these shifts (the softmax re-run relative to the
- * given weights, each row normalised).
+ * given weights, each row normalised; v and g_o enter through W and Z of
+ * dust_attn_row_weights).
  *   P       [B, H, S, S] bf16 attention weights of the clean forward, row t (query) over
  *           keys s; entries above the diagonal are ignored                              (in)
  *   k       [B*S, H*dh] bf16 keys, head h in columns h*dh .. h*dh+dh-1                   (in)
- *   v       [B*S, H*dh] bf16 values                                                      (in)
- *   g_o     [B*S, H*dh] bf16 estimated error of the attention output                     (in)
+ *   W, Z    [B, H, S, S] and [B, H, S] fp32 from dust_attn_row_weights                   (in)
  *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
  * The noise a of (token t, head h, column j) is channel chan0 + h*dh + j of token tok0 + t
  * (the query projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
- * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P, k, v and
- * g_o 16-byte aligned; sigma and softmax_scale finite with |sigma * softmax_scale| <= 2^20.
- * c must not overlap the inputs. Precision and the range of the logit shifts as for
- * dust_attn_key_scores.
+ * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P, k and W
+ * 16-byte, Z and c 4-byte aligned; sigma and softmax_scale finite with
+ * |sigma * softmax_scale| <= 2^20. c must not overlap the inputs. Precision and the range of the
+ * logit shifts as for dust_attn_key_scores.
  */
-int dust_attn_query_scores(const void *P, const void *k, const void *v, const void *g_o,
+int dust_attn_query_scores(const void *P, const void *k, const float *W, const float *Z,
                            float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,
                            int64_t chan0, float sigma, float softmax_scale, uint64_t seed,
                            uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);

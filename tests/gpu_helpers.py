@@ -62,3 +62,12 @@ def frob_rel(got, ref) -> float:
     ref = np.asarray(ref, dtype=np.float64)
     den = np.linalg.norm(ref)
     return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+
+
+def row_weights(P, v, g_o, B, H, S, dh):
+    """W [B, H, S, S] and Z [B, H, S] of dust_attn_row_weights, on the device (the key and query
+    scorers take them in place of the values and the output error)."""
+    W = torch.full((B, H, S, S), float("nan"), dtype=torch.float32, device=DEV)
+    Z = torch.full((B, H, S), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_attn_row_weights(P, v, g_o, W, Z, B, H, S, dh)
+    return W, Z

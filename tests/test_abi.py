@@ -128,6 +128,19 @@ INVALID = [
     ("dust_attn_query_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + 4096, 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "overlap"),
     ("dust_attn_query_scores", (FAKE, None, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "null"),
     ("dust_attn_query_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, float("inf"), 0.25, 1, 1, 0, 0, None), 1, "finite"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8194, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "aligned"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + 4096 + 65532, 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "overlap"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, 2, 8192, 16, None), 2, "up to 4096"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, 2, 64, 24, None), 2, "multiple of 16"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30) + 8, FAKE2 + (2 << 30), 2, 2, 64, 16, None), 1, "aligned"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30) + 2, 2, 2, 64, 16, None), 1, "aligned"),
+    ("dust_attn_row_weights", (FAKE, FAKE2 + 8, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, 2, 64, 16, None), 1, "aligned"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (1 << 30) + 4096, 2, 2, 64, 16, None), 1, "W overlaps Z"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE + 4096, FAKE2 + (2 << 30), 2, 2, 64, 16, None), 1, "overlaps P"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + 4096, 2, 2, 64, 16, None), 1, "overlaps P"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, None, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, 2, 64, 16, None), 1, "null"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, -1, 64, 16, None), 1, "negative"),
+    ("dust_attn_row_weights", (FAKE, FAKE2, FAKE2 + 8192, FAKE2 + (1 << 30), FAKE2 + (2 << 30), 2, 0, 64, 16, None), 1, "H and dh"),
     ("dust_cosine_terms", (FAKE, FAKE2, 16, FAKE2 + 4100, None), 1, "aligned"),
     ("dust_cosine_terms", (FAKE, FAKE2, 16, FAKE + 8, None), 1, "overlap"),
     ("dust_cosine_terms", (FAKE, None, 16, FAKE2 + 4096, None), 1, "null"),
@@ -162,6 +175,8 @@ ZERO_SIZE = [
     ("dust_loss_reward", (None, None, None, 0, 10, 5, 0.5, None)),
     ("dust_sgd_momentum", (None, None, None, 0, 0.1, 0.9, None)),
     ("dust_attn_value_scores", (None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None)),
+    ("dust_attn_row_weights", (None, None, None, None, None, 0, 2, 64, 16, None)),
+    ("dust_attn_row_weights", (None, None, None, None, None, 2, 2, 0, 16, None)),
     ("dust_attn_key_scores", (None, None, None, None, None, 0, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None)),
     ("dust_attn_query_scores", (None, None, None, None, None, 3, 0, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None)),
     ("dust_cosine_terms", (None, None, 0, None, None)),

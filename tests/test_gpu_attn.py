@@ -1,4 +1,4 @@
-"""GPU parity of dust_attn_value_scores and dust_attn_key_scores with the oracle (MI355X only).
+"""GPU parity of the attention scorers and of their row weights with the oracle (MI355X only).
 
 The scores c = -<Delta o, g_o> of a perturbed attention value projection, computed on the
 device without forming Delta o, are compared with the oracle's fp64 sum element by element at
@@ -15,14 +15,17 @@ same way, at the same bar, over the same layouts, with logit shifts both inside 
 range where the kernel takes e^x - 1 from a polynomial (|x| <= 0.2), and on tiles that mix the
 two; sigma = 0 must give exactly zero and attention to the own token only (nearly) zero. The
 query scores (shifts sigma tau <a_t, k_s>) are checked the same way, including the widest heads
-(which run 4 waves per block) and the longest sequences.
+(which run 8 waves per block instead of 12) and the longest sequences. Both take the values and
+the output error through the row weights W and Z of dust_attn_row_weights, which are themselves
+compared with the oracle's element by element.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_helpers import DEV, announce, bf16, bits_to_f64, dust, f32, frob_rel, host_f32, rne_bf16_bits_of_f32
+from gpu_helpers import (DEV, announce, bf16, bits_to_f64, dust, f32, frob_rel, host_f32,
+                         rne_bf16_bits_of_f32, row_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,8 +109,10 @@ def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, ta
     Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
     qb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
     c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
-    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh, chan0,
-                              sigma, tau, seed, tag, draw0, tok0)
+    Pd = bf16(Pbits)
+    W, Z = row_weights(Pd, bf16(vb), bf16(gb), B, H, S, dh)
+    dust.dust_attn_key_scores(Pd, bf16(qb), W, Z, c, Kc, B, H, S, dh, chan0, sigma, tau, seed, tag,
+                              draw0, tok0)
     ref = oracle.attn_key_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
                                  bits_to_f64(gb), Kc, sigma, tau, seed, tag, draw0, tok0, chan0)
     err = frob_rel(host_f32(c), ref)
@@ -124,16 +129,19 @@ def test_attn_key_scores_vanish_at_sigma_zero_and_for_self_attention():
                   for _ in range(3))
     P = bf16(rne_bf16_bits_of_f32(_causal_weights(g, B, H, S).astype(np.float32)))
     c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
-    dust.dust_attn_key_scores(P, qb, vb, gb, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
+    W, Z = row_weights(P, vb, gb, B, H, S, dh)
+    dust.dust_attn_key_scores(P, qb, W, Z, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
     assert torch.all(c == 0)
     eye = bf16(rne_bf16_bits_of_f32(np.broadcast_to(np.eye(S, dtype=np.float32), (B, H, S, S)).copy()))
-    dust.dust_attn_key_scores(eye, qb, vb, gb, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
+    W, Z = row_weights(eye, vb, gb, B, H, S, dh)
+    dust.dust_attn_key_scores(eye, qb, W, Z, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
     assert float(c.abs().max()) <= 1e-6
 
 
 def test_attn_key_scores_zero_draws_touch_nothing():
     c = torch.full((2, 64), 5.0, device=DEV)
     dust.dust_attn_key_scores(None, None, None, None, c, 0, 2, 2, 32, 16, 0, 0.01, 0.25, 1, 1, 0, 0)
+    dust.dust_attn_query_scores(None, None, None, None, c, 0, 2, 2, 32, 16, 0, 0.01, 0.25, 1, 1, 0, 0)
     assert torch.all(c == 5.0)
 
 
@@ -149,13 +157,14 @@ def test_attn_scores_channels_beyond_32_bits():
     dust.dust_attn_value_scores(bf16(Pbits), bf16(gb), c, Kc, B, H, S, dh, chan0, sigma, 3, 1, 0, 0)
     ref = oracle.attn_value_scores(bits_to_f64(Pbits), bits_to_f64(gb), Kc, sigma, 3, 1, 0, 0, chan0)
     assert frob_rel(host_f32(c), ref) <= 1e-5
-    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh, chan0,
-                              sigma, tau, 3, 1, 0, 0)
+    W, Z = row_weights(bf16(Pbits), bf16(vb), bf16(gb), B, H, S, dh)
+    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), W, Z, c, Kc, B, H, S, dh, chan0, sigma, tau, 3,
+                              1, 0, 0)
     ref = oracle.attn_key_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
                                  bits_to_f64(gb), Kc, sigma, tau, 3, 1, 0, 0, chan0)
     assert frob_rel(host_f32(c), ref) <= 1e-5
-    dust.dust_attn_query_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh,
-                                chan0, sigma, tau, 3, 1, 0, 0)
+    dust.dust_attn_query_scores(bf16(Pbits), bf16(qb), W, Z, c, Kc, B, H, S, dh, chan0, sigma, tau,
+                                3, 1, 0, 0)
     ref = oracle.attn_query_scores(bits_to_f64(Pbits), bits_to_f64(qb), bits_to_f64(vb),
                                    bits_to_f64(gb), Kc, sigma, tau, 3, 1, 0, 0, chan0)
     assert frob_rel(host_f32(c), ref) <= 1e-5
@@ -165,9 +174,9 @@ def test_attn_scores_channels_beyond_32_bits():
     (2, 2, 32, 16, 5, 0, 3, 7, False, 0.05, 0.25),       # one tile, ragged draw group
     (1, 3, 64, 32, 6, 64, 0, 0, True, 0.05, 0.18),       # channel offset, weights above the diagonal
     (2, 2, 128, 64, 3, 0, 11, 1000, False, 0.01, 0.125), # 4 x 4 tiles, the workload's head width
-    (1, 1, 96, 128, 9, 8, 2, 5, True, 0.02, 0.09),       # widest heads (4 waves a block), 3 blocks
+    (1, 1, 96, 128, 9, 8, 2, 5, True, 0.02, 0.09),       # widest heads (8 waves a block), 2 blocks
     (1, 4, 64, 48, 4, 4, 0, 0, False, 0.05, 0.144),      # three k-slices
-    (1, 1, 96, 112, 5, 0, 0, 0, False, 0.05, 0.094),     # seven k-slices (4 waves a block)
+    (1, 1, 96, 112, 5, 0, 0, 0, False, 0.05, 0.094),     # seven k-slices (8 waves a block)
     (1, 1, 4096, 16, 2, 0, 0, 0, False, 0.05, 0.25),     # the longest sequence
     (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
     (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
@@ -180,8 +189,10 @@ def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, 
     Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
     kb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
     c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
-    dust.dust_attn_query_scores(bf16(Pbits), bf16(kb), bf16(vb), bf16(gb), c, Kc, B, H, S, dh,
-                                chan0, sigma, tau, seed, tag, draw0, tok0)
+    Pd = bf16(Pbits)
+    W, Z = row_weights(Pd, bf16(vb), bf16(gb), B, H, S, dh)
+    dust.dust_attn_query_scores(Pd, bf16(kb), W, Z, c, Kc, B, H, S, dh, chan0, sigma, tau, seed,
+                                tag, draw0, tok0)
     ref = oracle.attn_query_scores(bits_to_f64(Pbits), bits_to_f64(kb), bits_to_f64(vb),
                                    bits_to_f64(gb), Kc, sigma, tau, seed, tag, draw0, tok0, chan0)
     err = frob_rel(host_f32(c), ref)
@@ -198,8 +209,44 @@ def test_attn_query_scores_vanish_at_sigma_zero_and_for_self_attention():
                   for _ in range(3))
     P = bf16(rne_bf16_bits_of_f32(_causal_weights(g, B, H, S).astype(np.float32)))
     c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
-    dust.dust_attn_query_scores(P, kb, vb, gb, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
+    W, Z = row_weights(P, vb, gb, B, H, S, dh)
+    dust.dust_attn_query_scores(P, kb, W, Z, c, Kc, B, H, S, dh, 0, 0.0, 0.2, 5, 1, 0, 0)
     assert torch.all(c == 0)
     eye = bf16(rne_bf16_bits_of_f32(np.broadcast_to(np.eye(S, dtype=np.float32), (B, H, S, S)).copy()))
-    dust.dust_attn_query_scores(eye, kb, vb, gb, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
+    W, Z = row_weights(eye, vb, gb, B, H, S, dh)
+    dust.dust_attn_query_scores(eye, kb, W, Z, c, Kc, B, H, S, dh, 0, 0.05, 0.2, 5, 1, 0, 0)
     assert float(c.abs().max()) <= 1e-6
+
+
+@pytest.mark.parametrize("B,H,S,dh,garbage", [
+    (2, 2, 32, 16, False),     # one tile
+    (1, 3, 64, 32, True),      # weights above the diagonal must be ignored
+    (2, 2, 128, 64, False),    # 4 x 4 tiles, the workload's head width
+    (1, 1, 96, 128, True),     # widest heads
+    (1, 4, 64, 48, False),     # three k-slices
+    (1, 1, 4096, 16, False),   # the longest sequence
+    (3, 1, 64, 112, False),    # a partly filled last block of query tiles
+])
+def test_attn_row_weights(B, H, S, dh, garbage):
+    """W and Z of dust_attn_row_weights against the oracle's: relative Frobenius 1e-5 for W (fp32
+    sums of bf16 products over dh and of S weights), 2e-5 per row sum for Z, and W exactly zero
+    above the diagonal."""
+    announce("attn row weights %s" % ((B, H, S, dh, garbage),))
+    g = np.random.default_rng(77)
+    T, d = B * S, H * dh
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
+    vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(2))
+    W, Z = row_weights(bf16(Pbits), bf16(vb), bf16(gb), B, H, S, dh)
+    Wr, Zr = oracle.attn_row_weights(bits_to_f64(Pbits), bits_to_f64(vb), bits_to_f64(gb))
+    Wg, Zg = host_f32(W), host_f32(Z)
+    err = frob_rel(Wg, Wr)
+    print("row weights rel. Frobenius error %.2e" % err)
+    assert err <= 1e-5
+    assert np.all(np.abs(Zg - Zr) <= 2e-5 * np.abs(Zr))
+    assert np.all(Wg[..., ~np.tril(np.ones((S, S), dtype=bool))] == 0.0)
+
+
+def test_attn_row_weights_zero_size_touches_nothing():
+    W = torch.full((2, 2, 32, 32), 5.0, device=DEV)
+    dust.dust_attn_row_weights(None, None, None, W, W, 0, 2, 32, 16)
+    assert torch.all(W == 5.0)

@@ -13,7 +13,7 @@ import torch
 import oracle
 import synth
 from gpu_helpers import (DEV, announce, bf16, bf16_ulp, bits_to_f64, dust, f32, frob_rel,
-                         host_bf16_bits, host_f32, i32, rne_bf16_bits_of_f32)
+                         host_bf16_bits, host_f32, i32, rne_bf16_bits_of_f32, row_weights)
 
 pytestmark = pytest.mark.gpu
 NS = 20000   # sampled elements per check
@@ -252,8 +252,11 @@ def test_w4_attention_key_scores():
     del z
     qb, vb, gb = (synth.normal_bf16(synth.rng(4, j), (T, d)) for j in (3, 4, 1))
     cd = torch.empty((K, T), dtype=torch.float32, device=DEV)
-    dust.dust_attn_key_scores(bf16(Pbits), bf16(qb), bf16(vb), bf16(gb), cd, K, B, H, S, d // H, 0,
-                              sigma, tau, seed, tag, 0, 0)
+    Pd = bf16(Pbits)
+    W, Z = row_weights(Pd, bf16(vb), bf16(gb), B, H, S, d // H)
+    dust.dust_attn_key_scores(Pd, bf16(qb), W, Z, cd, K, B, H, S, d // H, 0, sigma, tau, seed, tag,
+                              0, 0)
+    del W, Z
     got = host_f32(cd)
     s = np.random.default_rng(407)
     k, t = s.integers(0, K, 96), s.integers(0, T, 96)
@@ -281,8 +284,11 @@ def test_w4_attention_query_scores():
     del z
     kb, vb, gb = (synth.normal_bf16(synth.rng(4, j), (T, d)) for j in (4, 5, 1))
     cd = torch.empty((K, T), dtype=torch.float32, device=DEV)
-    dust.dust_attn_query_scores(bf16(Pbits), bf16(kb), bf16(vb), bf16(gb), cd, K, B, H, S, d // H,
-                                0, sigma, tau, seed, tag, 0, 0)
+    Pd = bf16(Pbits)
+    W, Z = row_weights(Pd, bf16(vb), bf16(gb), B, H, S, d // H)
+    dust.dust_attn_query_scores(Pd, bf16(kb), W, Z, cd, K, B, H, S, d // H, 0, sigma, tau, seed,
+                                tag, 0, 0)
+    del W, Z
     got = host_f32(cd)
     s = np.random.default_rng(409)
     k, t = s.integers(0, K, 96), s.integers(0, T, 96)

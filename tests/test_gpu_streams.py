@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import synth
-from gpu_helpers import DEV, announce, bf16, dust, f32
+from gpu_helpers import DEV, announce, bf16, dust, f32, row_weights
 
 pytestmark = pytest.mark.gpu
 
@@ -79,10 +79,14 @@ def test_attention_scorers_repeat_bit_for_bit():
     z.masked_fill_(~torch.ones((S, S), dtype=torch.bool, device=DEV).tril(), float("-inf"))
     P = torch.softmax(z, -1).to(torch.bfloat16)
     q, k, v, go = (torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16) for _ in range(4))
+    W, Z = row_weights(P, v, go, B, H, S, dh)
+    W2, Z2 = row_weights(P, v, go, B, H, S, dh)
+    assert torch.equal(W.view(torch.int32), W2.view(torch.int32))
+    assert torch.equal(Z.view(torch.int32), Z2.view(torch.int32))
     calls = [
         lambda c: dust.dust_attn_value_scores(P, go, c, Kc, B, H, S, dh, 0, 0.05, 3, 1, 0, 0),
-        lambda c: dust.dust_attn_key_scores(P, q, v, go, c, Kc, B, H, S, dh, 0, 0.05, 0.125, 3, 1, 0, 0),
-        lambda c: dust.dust_attn_query_scores(P, k, v, go, c, Kc, B, H, S, dh, 0, 0.05, 0.125, 3, 1, 0, 0),
+        lambda c: dust.dust_attn_key_scores(P, q, W, Z, c, Kc, B, H, S, dh, 0, 0.05, 0.125, 3, 1, 0, 0),
+        lambda c: dust.dust_attn_query_scores(P, k, W, Z, c, Kc, B, H, S, dh, 0, 0.05, 0.125, 3, 1, 0, 0),
     ]
     for call in calls:
         c1 = torch.empty((Kc, T), device=DEV)
