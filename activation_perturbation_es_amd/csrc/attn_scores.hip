@@ -113,34 +113,53 @@ struct Stager {
     static constexpr uint32_t kSide = (HW ? 64u : 32u) * kPPitch;   // bytes before the side tiles
     u32x4 r[kPerThread];
 
-    // P [B, H, S, S] and W [B, H, S, S]: query tile ct over key tile kt of sequence b, head h;
-    // the side arrays [T, H DH]: row tile xt of the sequence (the query tile for value and key
-    // scores, the key tile for query scores)
-    __device__ __forceinline__ void load(uint32_t tid, const uint16_t *P, const float *Wm,
+    const unsigned char *src[kPerThread];   // this thread's piece at tile offset zero
+
+    // The per-thread part of every step's addresses, once per block. P [B, H, S, S] and
+    // W [B, H, S, S] of sequence b; the side arrays [T, H DH] from the sequence's first row.
+    __device__ __forceinline__ void init(uint32_t tid, const uint16_t *P, const float *Wm,
                                          const uint16_t *const (&qs)[NQ], uint32_t b, uint32_t H,
-                                         uint32_t S, uint32_t d, uint32_t h, uint32_t kt,
-                                         uint32_t ct, uint32_t xt) {
-        constexpr uint32_t DH = 16u * KS;
-        const uint64_t tile = (((uint64_t)b * H + h) * S + ct * 32u) * S + kt * 32u;
+                                         uint32_t S, uint32_t d) {
 #pragma unroll
         for (uint32_t j = 0; j < kPerThread; ++j) {
             const uint32_t pc = tid + NT * j;
+            src[j] = (const unsigned char *)P;
             if (pc >= kPieces) continue;
             if (pc < 128u) {
                 const uint32_t row = pc >> 2, seg = pc & 3u;
-                r[j] = *(const u32x4 *)(P + tile + (uint64_t)row * S + 8u * seg);
+                src[j] = (const unsigned char *)(P + ((uint64_t)b * H * S + row) * S + 8u * seg);
             } else if (HW && pc < 128u + kW) {
                 const uint32_t x = pc - 128u, row = x >> 3, seg = x & 7u;
-                r[j] = *(const u32x4 *)(Wm + tile + (uint64_t)row * S + 4u * seg);
+                src[j] = (const unsigned char *)(Wm + ((uint64_t)b * H * S + row) * S + 4u * seg);
             } else {
                 const uint32_t x = pc - 128u - kW, m = x / (64u * KS), y = x % (64u * KS);
                 const uint32_t row = y / (2u * KS), seg = y % (2u * KS);
 #pragma unroll
                 for (int n = 0; n < NQ; ++n)
                     if (m == (uint32_t)n)
-                        r[j] = *(const u32x4 *)(qs[n] + ((uint64_t)b * S + xt * 32u + row) * d +
-                                                h * DH + 8u * seg);
+                        src[j] = (const unsigned char *)(qs[n] + ((uint64_t)b * S + row) * d +
+                                                         8u * seg);
             }
+        }
+    }
+
+    // One step's pieces into registers: query tile ct over key tile kt of head h for P and W,
+    // row tile xt of the side arrays (the query tile for value and key scores, the key tile for
+    // query scores). The kind of piece is the same across a wave (P, W and the side tiles start
+    // at multiples of 64 pieces), so the tile offset is chosen on the scalar unit.
+    __device__ __forceinline__ void load(uint32_t tid, uint32_t S, uint32_t d, uint32_t h,
+                                         uint32_t kt, uint32_t ct, uint32_t xt) {
+        constexpr uint32_t DH = 16u * KS;
+        const uint64_t tile = ((uint64_t)h * S + ct * 32u) * S + kt * 32u;   // elements
+        const uint64_t side = 2u * ((uint64_t)xt * 32u * d + h * DH);         // bytes
+        const uint32_t w0 = __builtin_amdgcn_readfirstlane(tid & ~63u);
+#pragma unroll
+        for (uint32_t j = 0; j < kPerThread; ++j) {
+            const uint32_t pc0 = w0 + NT * j;
+            if (pc0 >= kPieces) continue;
+            const uint64_t off = pc0 < 128u ? 2u * tile : (HW && pc0 < 128u + kW) ? 4u * tile
+                                                                                   : side;
+            r[j] = *(const u32x4 *)(src[j] + off);
         }
     }
 
@@ -256,14 +275,15 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     // Step n's tiles are in LDS stage n % 2; step n + 1's are fetched into registers at the
     // start of step n and stored to the other stage at its end, before the one barrier per step.
     StepOrder cur;
-    stg.load(tid, P, nullptr, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.init(tid, P, nullptr, qs, b, H, S, d);
+    stg.load(tid, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     noise(0, 0);
     __syncthreads();
     for (uint32_t st = 0;; st ^= 1u) {
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;   // uniform across the block
-        if (more) stg.load(tid, P, nullptr, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
+        if (more) stg.load(tid, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *grow = base + 32u * kPPitch + col * GP + 16u * half;
@@ -562,7 +582,8 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     };
 
     StepOrder cur;
-    stg.load(tid, P, Wm, qs, b, H, S, d, 0, 0, 0, 0);
+    stg.init(tid, P, Wm, qs, b, H, S, d);
+    stg.load(tid, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     query_norms(0);
     key_tile(0, 0);
@@ -575,7 +596,7 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         }
         const StepOrder nx = cur.next(nt);
         const bool more = nx.h < H;
-        if (more) stg.load(tid, P, Wm, qs, b, H, S, d, nx.h, nx.kt, nx.ct, nx.ct);
+        if (more) stg.load(tid, S, d, nx.h, nx.kt, nx.ct, nx.ct);
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *qrow = base + Stg::kSide + col * GP + 16u * half;
@@ -698,7 +719,8 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
 
     // steps: head, query tile ct, key tile kt <= ct
     uint32_t h = 0, ct = 0, kt = 0;
-    stg.load(tid, P, Wm, ks_, b, H, S, d, 0, 0, 0, 0);
+    stg.init(tid, P, Wm, ks_, b, H, S, d);
+    stg.load(tid, S, d, 0, 0, 0, 0);
     stg.store(tid, lds, true);
     key_norms(0);
     query_tile(0, 0);
@@ -713,7 +735,7 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         }
         const bool more = nh < H;
         // the staged key tile is kt; the P and W tiles are (query tile ct, key tile kt)
-        if (more) stg.load(tid, P, Wm, ks_, b, H, S, d, nh, nk, nc, nk);   // k of key tile nk
+        if (more) stg.load(tid, S, d, nh, nk, nc, nk);   // k of key tile nk
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *krow = base + Stg::kSide + col * GP + 16u * half;
