@@ -101,6 +101,7 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     (1, 1, 1024, 128, 2, 0, 0, 0, True, 0.02, 0.09),     # longest sequence at the widest heads
     (1, 1, 512, 80, 3, 0, 0, 0, False, 0.02, 0.11),      # the widest heads with two tiles a step
     (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
+    (1, 1, 1024, 96, 13, 0, 0, 0, True, 0.02, 0.1),      # 12 waves at their largest LDS, 12 + 1 draws
 ])
 def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn key scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
@@ -181,6 +182,8 @@ def test_attn_scores_channels_beyond_32_bits():
     (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
     (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
     (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
+    (1, 1, 2048, 64, 13, 0, 0, 0, True, 0.02, 0.125),    # 12 waves, long sequence, 12 + 1 draws
+    (1, 1, 128, 80, 9, 0, 0, 0, False, 0.05, 0.11),      # the narrowest heads on 8 waves
 ])
 def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn query scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
@@ -226,6 +229,7 @@ def test_attn_query_scores_vanish_at_sigma_zero_and_for_self_attention():
     (1, 4, 64, 48, False),     # three k-slices
     (1, 1, 4096, 16, False),   # the longest sequence
     (3, 1, 64, 112, False),    # a partly filled last block of query tiles
+    (1, 2, 1024, 96, True),    # six k-slices, long sequence
 ])
 def test_attn_row_weights(B, H, S, dh, garbage):
     """W and Z of dust_attn_row_weights against the oracle's: relative Frobenius 1e-5 for W (fp32
