@@ -1,8 +1,8 @@
-// Inner-product scores of a perturbed attention value or key projection (gfx950).
+// Inner-product scores of a perturbed attention value, key or query projection (gfx950).
 //
 // Explainer cnblogs.com/32bin/p/23212811, "The real work: suppressing interference": attention
 // internals are scored through the attention output, by the inner product of the output's
-// change with the output's estimated error g. Neither kernel forms Delta o (K x T x d values).
+// change with the output's estimated error g. No kernel forms Delta o (K x T x d values).
 //
 // Values. When the value projection's output is perturbed, v'_s = v_s + sigma a_s, the attention
 // weights P of the clean forward stay as they are (they come from queries and keys), so the
@@ -17,22 +17,26 @@
 // u_ts = <v_s, g_t>, base_t = sum_s P_ts u_ts, N0_t = sum_s P_ts (e^delta_ts - 1) and
 // N1_t = sum_s P_ts (e^delta_ts - 1) u_ts, the change of the output's inner product is
 //     <Delta o_t, g_t> = (base + N1) / (Z + N0) - base / Z = (Z N1 - base N0) / (Z (Z + N0)),
-// a form whose terms are all O(sigma), so nothing cancels at the O(1) level.
+// a form whose terms are all O(sigma), so nothing cancels at the O(1) level. Its numerator is
+// sum_s W_ts (e^delta_ts - 1) with W_ts = P_ts (Z_t u_ts - base_t), which does not depend on the
+// draw: the row-weights kernel forms W and Z once, and per draw and element the scorers need
+// only e^delta - 1 and two fused multiply-adds. Queries (q'_t = q_t + sigma a_t) are the same
+// re-run with delta_ts = sigma tau <a_t, k_s>.
 //
-// Both kernels regenerate the noise of one tile of 32 keys once per draw, and for every later
-// tile of 32 queries form the 32 x 32 key-query inner products on the matrix cores
+// The scorers regenerate the noise of one tile of 32 tokens once per draw, and for every tile
+// of 32 tokens it meets form the 32 x 32 inner products on the matrix cores
 // (v_mfma_f32_32x32x16_bf16; the noise split into a bf16 high part and a bf16 remainder so that
-// it keeps 16 significant bits): E_st = <a_s, g_t> for values, D_st = <a_s, q_t> for keys. The
-// output tile's layout (lane l holds query l % 32 and 16 of the key rows) lets each lane weight
-// and sum its keys; one lane-half swap (v_permlane32_swap) completes two sums over the 32 keys
-// at once (two draws' scores for values, one draw's N1 and N0 for keys).
+// it keeps 16 significant bits): E_st = <a_s, g_t> for values, D_st = <a_s, q_t> for keys,
+// D_ts = <a_t, k_s> for queries. The output tile's layout (lane l holds column l % 32 and 16 of
+// the rows) lets each lane weight and sum its elements; lane-half swaps (v_permlane32_swap) or
+// DPP row exchanges complete the sums over the tile.
 //
-// Work layout: a block owns one sequence and 8 draws (values: 4 waves, two draws each; keys: 8
-// waves, one draw each, so that each SIMD holds two waves); the block walks heads, then key
-// tiles, then the query tiles at or after the key tile (causal order). Each step's weight tiles
-// (widened to fp32, the causal mask applied) and query-side bf16 tiles are staged in LDS by the
-// whole block, double-buffered with one barrier per step; the key-side operands (noise, and the
-// values for keys) stay in registers for the whole key tile.
+// Work layout: a block owns one sequence and several draws (values: 4 waves, two draws each;
+// keys and queries: 12 waves, or 8 for wide heads, one draw each, so that each SIMD holds three
+// or two waves); the block walks heads, then tiles in causal order. Each step's weight tiles
+// (widened to fp32, the causal mask applied) and bf16 side tiles are staged in LDS by the whole
+// block, double-buffered with one barrier per step; the operands of the outer tile (noise) stay
+// in registers across its inner tiles.
 #include "dust_internal.hpp"
 
 namespace dust {
