@@ -91,18 +91,49 @@ __device__ __forceinline__ void noise_fragments(const Key &key, uint32_t q0, uin
     if (norm2) *norm2 = n2;
 }
 
-// Sum over the 32 lanes of each half of the wave, in every lane: the two quad exchanges, the
-// half-row and row mirrors (DPP, no LDS traffic), then one exchange of rows 16 apart.
+// The value of another lane of the same DPP row (CTRL: a DPP row or quad pattern; no LDS traffic).
 template <int CTRL>
 __device__ __forceinline__ float dpp_shuffled(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float half_wave_sum(float x) {
-    x += dpp_shuffled<0xB1>(x);    // quad_perm [1, 0, 3, 2]
-    x += dpp_shuffled<0x4E>(x);    // quad_perm [2, 3, 0, 1]
-    x += dpp_shuffled<0x141>(x);   // row_half_mirror: lane i <- 7 - i within 8
-    x += dpp_shuffled<0x140>(x);   // row_mirror: lane i <- 15 - i within 16
-    return x + __shfl_xor(x, 16);
+
+// Sums over the 32 lanes of each half of the wave of 32 values per lane, transposed: afterwards
+// lane l holds the total of v[l & 31] over its half. Each stage pairs every lane with a lane of
+// the other class and halves the slots: the lane keeps the slot of its class, sends the other
+// and adds what its partner sends for the same slot. Classes and exchanges: lane bit 4 (rows 16
+// apart, v_permlane16_swap, which exchanges and sums a pair of slots in two instructions), then
+// within each row of 16 the mirror (bit 3), the half mirror (bit 2) and the quad exchanges
+// (bits 1 and 0), all DPP.
+__device__ __forceinline__ float half_wave_transpose_sum(const float (&v)[32], uint32_t lane) {
+    float a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]),
+                                                         __float_as_uint(v[i + 16]), false, false);
+        a[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const bool c3 = (lane & 8u) != 0, c2 = (lane & 4u) != 0, c1 = (lane & 2u) != 0,
+               c0 = (lane & 1u) != 0;
+    float b8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float keep = c3 ? a[i + 8] : a[i], send = c3 ? a[i] : a[i + 8];
+        b8[i] = keep + dpp_shuffled<0x140>(send);   // row_mirror: lane 15 - p of the row
+    }
+    float b4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float keep = c2 ? b8[i + 4] : b8[i], send = c2 ? b8[i] : b8[i + 4];
+        b4[i] = keep + dpp_shuffled<0x141>(send);   // row_half_mirror: lane 7 - p of the half row
+    }
+    float b2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const float keep = c1 ? b4[i + 2] : b4[i], send = c1 ? b4[i] : b4[i + 2];
+        b2[i] = keep + dpp_shuffled<0x4E>(send);    // quad_perm [2, 3, 0, 1]
+    }
+    const float keep = c0 ? b2[1] : b2[0], send = c0 ? b2[0] : b2[1];
+    return keep + dpp_shuffled<0xB1>(send);         // quad_perm [1, 0, 3, 2]
 }
 
 // Staging of one step as 16-byte pieces: the P tile's rows first (4 per row of 32 bf16), then
@@ -701,18 +732,19 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     // (l & 3) when (l & 31) < 16 and folds M / (Z (Z + N0)) into this wave's draw. Head 0
     // stores, later heads add.
     auto finish_tile = [&](uint32_t h, uint32_t ct) {
+        // transposed sum over the 32 lanes of each half: lane l ends with the total of slot
+        // l & 31 of v = (M of rows 0..15, N0 of rows 0..15)
+        float v[32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            m1[r] = half_wave_sum(m1[r]);
-            n0[r] = half_wave_sum(n0[r]);
+            v[r] = m1[r];
+            v[16 + r] = n0[r];
         }
-        const uint32_t rr = lane & 15u;
-        float t1 = 0.f, t0 = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            t1 = rr == (uint32_t)r ? m1[r] : t1;
-            t0 = rr == (uint32_t)r ? n0[r] : t0;
-        }
+        const float x = half_wave_transpose_sum(v, lane);
+        // M and N0 of row lane & 15 sit in lanes 16 apart
+        const float other = __shfl_xor(x, 16);
+        const bool hi16 = (lane & 16u) != 0;
+        const float t1 = hi16 ? other : x, t0 = hi16 ? x : other;
         if (i >= Kc || (lane & 31u) >= 16u) return;
         const uint32_t m = 8u * ((lane & 15u) >> 2) + 4u * half + (lane & 3u);
         const float Z = Zm[((uint64_t)b * H + h) * S + ct * 32u + m];
