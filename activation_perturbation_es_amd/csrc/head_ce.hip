@@ -65,7 +65,9 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
         if (x > mr) {
             sr = sr * fast_exp(mr - x) + 1.f;
             mr = x;
-        } else {
+        } else if (x != -INFINITY) {
+            // a masked (-inf) logit adds nothing; without this test one met before any finite
+            // logit would form e^{-inf - (-inf)} = NaN
             sr += fast_exp(x - mr);
         }
     }

@@ -341,6 +341,33 @@ def test_head_ce_chunk(T, V, v0, C, Kc):
     assert np.abs(host_f32(lc) - ref_c).max() <= 1e-4
 
 
+@pytest.mark.parametrize("V,v0,C", [(700, 256, 256), (300, 0, 100)])
+def test_head_ce_chunk_masked_logits(V, v0, C):
+    """Masked vocabulary entries (logit -inf) outside the chunk, at the lowest ids so that a lane
+    meets them before any finite logit, and inside the chunk: they contribute nothing to the
+    log-sum-exp, as in the oracle."""
+    announce("head_ce_chunk masked %s" % ((V, v0, C),))
+    g = np.random.default_rng(31)
+    T, Kc, seed, tag, sigma = 9, 20, 77, 3, 0.3
+    z = (g.standard_normal((T, V)) * np.sqrt(2)).astype(np.float32)
+    z[:, :200 if v0 >= 200 else 0] = -np.inf          # every lane's first logits, out of chunk
+    z[1:, v0 + C:v0 + C + 70] = -np.inf                # a run after the chunk
+    z[2, v0 + 5:v0 + 9] = -np.inf                      # inside the chunk
+    z[3, :] = -np.inf
+    z[3, v0 + 3] = 1.5                                 # one finite logit, inside the chunk
+    tgt = g.integers(v0, v0 + C, T).astype(np.int32)
+    tgt[2] = v0 + 10
+    tgt[3] = v0 + 3
+    tgt[4] = v0 + C + 80 if v0 + C + 80 < V else 0    # a finite target outside the chunk
+    lp = torch.full((Kc, T), float("nan"), device=DEV)
+    lc = torch.full((T,), float("nan"), device=DEV)
+    dust.dust_head_ce_chunk(f32(z), i32(tgt), lp, lc, T, V, v0, C, Kc, sigma, seed, tag, 0, 0)
+    ref_p, ref_c = oracle.head_ce_chunk(z, tgt, v0, C, Kc, sigma, seed, tag, 0, 0)
+    assert np.all(np.isfinite(ref_p)) and np.all(np.isfinite(ref_c))
+    assert np.abs(host_f32(lp) - ref_p).max() <= 1e-4
+    assert np.abs(host_f32(lc) - ref_c).max() <= 1e-4
+
+
 def test_head_ce_bad_target_gives_nan():
     T, V = 4, 64
     z = np.zeros((T, V), dtype=np.float32)

@@ -18,6 +18,7 @@ import pytest
 import oracle
 import test_oracle_attn as attn
 import test_oracle_generator as gen
+import test_oracle_helpers as helpers
 import test_oracle_optim as optim
 import test_oracle_steps as steps
 
@@ -93,6 +94,10 @@ PINS_STEPS = [
     attn.test_query_scores_row_scale_diagonal_and_zeros,
     lambda: attn.test_row_weights_reproduce_an_explicit_softmax_rerun(2, 2, 12, 8),
     attn.test_row_weights_invariants,
+    helpers.test_round_bf16_equals_exhaustive_nearest_even_on_ties_subnormals_and_overflow,
+    helpers.test_round_bf16_equals_torch_on_fp32_values,
+    lambda: helpers.test_normals_at_equals_slices_of_bulk_normals(3, 7, 2**32 + 8),
+    lambda: helpers.test_head_ce_at_equals_torch_cross_entropy_of_perturbed_logits(64, 12, 20),
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -173,6 +178,17 @@ MUTATIONS = [
      "u += v[(b * S + t) * d + h * dh + j] * g[(b * S + t) * d + h * dh + j];\n                    wrow"),
     ("row sum includes the diagonal's successor", "for (int64_t s = 0; s <= t; ++s) {\n                    double u = 0.0;",
      "for (int64_t s = 0; s <= t + (t + 1 < S); ++s) {\n                    double u = 0.0;"),
+    ("bf16 ties away from zero", "(rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0))",
+     "(rem >= 0.5)"),
+    ("bf16 subnormals at fp32's spacing", "if (qexp < -133) qexp = -133;", "if (qexp < -149) qexp = -149;"),
+    ("bf16 overflow saturates", "v = INFINITY;   /* beyond", "v = 3.3895313892515355e38;   /* beyond"),
+    ("sampled normals ignore draw0", "out[m] = dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),",
+     "out[m] = dust_or_normal(seed, tag, (uint32_t)(k[m]),"),
+    ("sampled normals drop the channel offset", "(uint64_t)(chan0 + j[m]));", "(uint64_t)(j[m]));"),
+    ("sampled head loss: target not perturbed", "if (zj > mx) mx = zj;\n            if (j == y) zy = zj;",
+     "if (zj > mx) mx = zj;\n            if (j == y) zy = z[j];"),
+    ("sampled head loss: chunk off by one", "if (j >= v0 && j < v0 + C)\n                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),\n                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);\n            if (zj > mx)",
+     "if (j > v0 && j < v0 + C)\n                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),\n                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);\n            if (zj > mx)"),
     ("query head offset dropped", "(uint64_t)(chan0 + h * dh + j));\n        double Z",
      "(uint64_t)(chan0 + j));\n        double Z"),
 ]
