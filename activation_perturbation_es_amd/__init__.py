@@ -20,7 +20,8 @@ __all__ = [
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
     "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam",
     "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_row_weights",
-    "dust_attn_key_scores", "dust_attn_query_scores", "dust_weight_grad", "dust_head_ce_chunk", "dust_noise_words",
+    "dust_attn_key_scores", "dust_attn_query_scores", "dust_weight_grad",
+    "dust_weight_grad_noalloc", "dust_head_ce_chunk", "dust_noise_words",
     "dust_status_string", "dust_last_error", "library", "LIB_PATH", "EXPORTED_SYMBOLS",
 ]
 
@@ -60,6 +61,7 @@ _SIGNATURES = {
                                    _u32, _u32, _int, _vp]),
     "dust_weight_grad_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "dust_weight_grad": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, ctypes.c_size_t, _vp]),
+    "dust_weight_grad_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
     "dust_head_ce_chunk": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _u64,
                                   _u32, _u32, _u32, _vp]),
     "dust_noise_words": (_int, [_vp, _i64, _i64, _i64, _u32, _u64, _u32, _u32, _u32, _vp]),
@@ -193,6 +195,11 @@ def dust_weight_grad_workspace(T, d_out, d_in) -> int:
 def dust_weight_grad(g_hat_t_bf16, x_bf16, G, T, d_out, d_in, workspace, ws_bytes, stream=None):
     return _call("dust_weight_grad", _ptr(g_hat_t_bf16), _ptr(x_bf16), _ptr(G), T, d_out, d_in,
                  _ptr(workspace), ws_bytes, _stream(stream))
+
+
+def dust_weight_grad_noalloc(g_hat_t_bf16, x_bf16, G, T, d_out, d_in, stream=None):
+    return _call("dust_weight_grad_noalloc", _ptr(g_hat_t_bf16), _ptr(x_bf16), _ptr(G), T, d_out,
+                 d_in, _stream(stream))
 
 
 def dust_head_ce_chunk(logits, targets, loss_pert, loss_clean, T, V, v0, C, Kc, sigma, seed, tag,

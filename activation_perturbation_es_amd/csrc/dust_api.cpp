@@ -316,26 +316,30 @@ size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in) {
     return dust::weight_grad_workspace_bytes(T, d_out, d_in);
 }
 
-int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
-                     int64_t d_out, int64_t d_in, void *workspace, size_t ws_bytes,
-                     void *stream) {
-    const char *fn = "dust_weight_grad";
+// Checks shared by dust_weight_grad and dust_weight_grad_noalloc (everything but the
+// workspace). *nothing is set when the call has no work (d_out or d_in zero).
+int check_weight_grad(const char *fn, const void *g_hat_t_bf16, const void *x_bf16, float *G,
+                      int64_t T, int64_t d_out, int64_t d_in, bool *nothing) {
+    *nothing = false;
     if (T < 0 || d_out < 0 || d_in < 0)
         return fail(DUST_ERR_INVALID, "%s: negative size (T=%lld d_out=%lld d_in=%lld)", fn,
                     (long long)T, (long long)d_out, (long long)d_in);
-    if (d_out == 0 || d_in == 0) return ok();
+    if (d_out == 0 || d_in == 0) {
+        *nothing = true;
+        return ok();
+    }
     if (!G || (T > 0 && (!g_hat_t_bf16 || !x_bf16)))
         return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
     if (!elem_aligned(G, 4) || (T > 0 && (!elem_aligned(g_hat_t_bf16, 2) || !elem_aligned(x_bf16, 2))))
         return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
     if (T > kMaxIdx || d_out > kMaxIdx || d_in > kMaxIdx || d_out * d_in > 256 * kMaxIdx)
         return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
-    const size_t need = dust::weight_grad_workspace_bytes(T, d_out, d_in);
-    if (need > 0 && (workspace == nullptr || ws_bytes < need))
-        return fail(DUST_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
-                    workspace ? ws_bytes : (size_t)0);
-    if (need > 0 && ((uintptr_t)workspace & 15u))
-        return fail(DUST_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    return DUST_OK;
+}
+
+// The array-size and G-overlap checks of the weight gradient (after the workspace checks).
+int check_weight_grad_arrays(const char *fn, const void *g_hat_t_bf16, const void *x_bf16,
+                             float *G, int64_t T, int64_t d_out, int64_t d_in) {
     const int64_t G_bytes = span(d_out, d_in, 1, 4);
     const int64_t a_bytes = span(d_out, T, 1, 2), b_bytes = span(T, d_in, 1, 2);
     if (G_bytes < 0 || a_bytes < 0 || b_bytes < 0)
@@ -343,6 +347,26 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
     if (T > 0 && (ranges_overlap(G, (size_t)G_bytes, g_hat_t_bf16, (size_t)a_bytes) ||
                   ranges_overlap(G, (size_t)G_bytes, x_bf16, (size_t)b_bytes)))
         return fail(DUST_ERR_INVALID, "%s: G overlaps an input", fn);
+    return DUST_OK;
+}
+
+int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
+                     int64_t d_out, int64_t d_in, void *workspace, size_t ws_bytes,
+                     void *stream) {
+    const char *fn = "dust_weight_grad";
+    bool nothing;
+    if (int rc = check_weight_grad(fn, g_hat_t_bf16, x_bf16, G, T, d_out, d_in, &nothing))
+        return rc;
+    if (nothing) return ok();
+    const size_t need = dust::weight_grad_workspace_bytes(T, d_out, d_in);
+    if (need > 0 && (workspace == nullptr || ws_bytes < need))
+        return fail(DUST_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", fn, need,
+                    workspace ? ws_bytes : (size_t)0);
+    if (need > 0 && ((uintptr_t)workspace & 15u))
+        return fail(DUST_ERR_INVALID, "%s: workspace must be 16-byte aligned", fn);
+    if (int rc = check_weight_grad_arrays(fn, g_hat_t_bf16, x_bf16, G, T, d_out, d_in)) return rc;
+    const int64_t G_bytes = span(d_out, d_in, 1, 4);
+    const int64_t a_bytes = span(d_out, T, 1, 2), b_bytes = span(T, d_in, 1, 2);
     if (need > 0 && ranges_overlap(G, (size_t)G_bytes, workspace, need))
         return fail(DUST_ERR_INVALID, "%s: G overlaps the workspace", fn);
     if (need > 0 && T > 0 &&
@@ -352,6 +376,33 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
     return hip_status(dust::launch_weight_grad((const uint16_t *)g_hat_t_bf16,
                                                (const uint16_t *)x_bf16, G, T, d_out, d_in,
                                                workspace, (hipStream_t)stream),
+                      fn);
+}
+
+int dust_weight_grad_noalloc(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
+                             int64_t d_out, int64_t d_in, void *stream) {
+    const char *fn = "dust_weight_grad_noalloc";
+    bool nothing;
+    if (int rc = check_weight_grad(fn, g_hat_t_bf16, x_bf16, G, T, d_out, d_in, &nothing))
+        return rc;
+    if (nothing) return ok();
+    const size_t need = dust::weight_grad_workspace_bytes(T, d_out, d_in);
+    if (need > dust::weight_grad_scratch_bytes())
+        return fail(DUST_ERR_UNSUPPORTED,
+                    "%s: this shape needs %zu bytes of split partial sums, beyond the %zu-byte "
+                    "per-device scratch; use dust_weight_grad with a workspace", fn, need,
+                    dust::weight_grad_scratch_bytes());
+    if (int rc = check_weight_grad_arrays(fn, g_hat_t_bf16, x_bf16, G, T, d_out, d_in)) return rc;
+    void *scratch = nullptr;
+    if (need > 0) {
+        const hipError_t e = dust::weight_grad_scratch(&scratch);
+        if (e != hipSuccess)
+            return fail(DUST_ERR_HIP, "%s: scratch address lookup failed: %s", fn,
+                        hipGetErrorString(e));
+    }
+    return hip_status(dust::launch_weight_grad((const uint16_t *)g_hat_t_bf16,
+                                               (const uint16_t *)x_bf16, G, T, d_out, d_in,
+                                               scratch, (hipStream_t)stream),
                       fn);
 }
 

@@ -94,6 +94,11 @@ hipError_t launch_adam(float *w, const float *g, float *m, float *v, int64_t n, 
 hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, int64_t T,
                               int64_t d_out, int64_t d_in, void *workspace, hipStream_t s);
 
+// The per-device scratch array of dust_weight_grad_noalloc: its size, and the calling thread's
+// current device's address of it (looked up on the first call per device, then cached).
+size_t weight_grad_scratch_bytes();
+hipError_t weight_grad_scratch(void **ptr);
+
 hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
                                 float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
                                 int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,

@@ -18,6 +18,8 @@
 // transposed 4 x 8 in registers. Both split the token axis across blocks so that the 256 CUs fill;
 // the split partial sums go to a workspace and are added in split order by a second kernel, so
 // results are deterministic.
+#include <mutex>
+
 #include "dust_internal.hpp"
 
 namespace dust {
@@ -480,6 +482,38 @@ size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in) {
     const SplitPlan p = plan_split(T, d_out, d_in);
     if (p.splits <= 1) return 0;
     return (size_t)p.splits * (size_t)d_out * (size_t)d_in * sizeof(float);
+}
+
+// Split partial sums of dust_weight_grad_noalloc, for callers that cannot allocate: one array
+// per GPU, loaded with the code object and held until the process ends. Host code never passes
+// the array's name to a kernel (on the host it names a stand-in, not device memory): the device
+// address of each GPU's copy is looked up once per device and used instead.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t weight_grad_scratch_bytes() { return kScratchBytes; }
+
+hipError_t weight_grad_scratch(void **ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr || ((uintptr_t)p & 255u)) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, int64_t T,

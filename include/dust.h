@@ -25,7 +25,8 @@
  *     returns DUST_ERR_WORKSPACE; a failed launch
  *     returns DUST_ERR_HIP. dust_last_error() then holds a one-line description for the
  *     calling thread. Nothing is enqueued when a call fails validation.
- *   - Entry points are re-entrant and keep no state between calls.
+ *   - Entry points are re-entrant and keep no state between calls (except the scratch array of
+ *     dust_weight_grad_noalloc, which is stated there).
  *
  * Noise (shared by inject, error estimate and head chunk; regenerated, never stored).
  *   The explainer draws a_t ~ N(0, I) independently per token and per draw and adds sigma*a_t
@@ -171,6 +172,22 @@ size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in);
 int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
                      int64_t d_out, int64_t d_in, void *workspace, size_t ws_bytes,
                      void *stream);
+
+/*
+ * dust_weight_grad_noalloc -- dust_weight_grad without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): same arguments, result and kernels, with the split partial sums in a
+ * scratch array of 64 MiB that the library holds on each GPU it runs on until the process ends.
+ * The call allocates and frees nothing. Shapes whose partial sums exceed the scratch (when
+ * dust_weight_grad_workspace(T, d_out, d_in) > 64 MiB) return DUST_ERR_UNSUPPORTED; the MLP
+ * shapes 2048 x 512 and 4096 x 1024 over 16384 tokens need exactly 64 MiB, and shapes that need
+ * no workspace (e.g. 4096 x 4096) use none. Every split partial the kernels read is written by
+ * the same call first, so nothing needs clearing between calls. All calls on one GPU share its
+ * scratch: two calls that overlap in time on one GPU (e.g. on two streams) race and give wrong
+ * results; calls serialised on one stream are safe. DUST_ERR_HIP if the scratch's device address cannot be looked up.
+ */
+int dust_weight_grad_noalloc(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
+                             int64_t d_out, int64_t d_in, void *stream);
 
 /*
  * dust_attn_value_scores -- loss change of K draws that perturb an attention VALUE projection,
