@@ -2,27 +2,27 @@
 """Throughput of the Dust estimator chain on one MI355X.
 
 One step = one whole estimate, with every input resident in HBM before the timed region. The
-default workload is the MLP up-projection 512 -> 2048 of the 8-layer width-512 GPT
-(T = 16 x 1024 tokens, K = 64 draws, gamma = 0, sigma = 0.01):
-    dust_noise_inject   (all 64 draws in one call, [64, 16384, 2048] bf16 perturbed outputs)
-    dust_loss_reward    (loss change and reward scan in one pass, [64, 16384]; --unfused runs
+default workload is the largest one that fits one GPU: the MLP up-projection 1024 -> 4096 of the
+~240M-parameter GPT shape (T = 16 x 1024 tokens, K = 1024 draws, gamma = 0, sigma = 0.01):
+    dust_noise_inject   (32 calls of 32 draws, [32, 16384, 4096] bf16 perturbed outputs each)
+    dust_loss_reward    (loss change and reward scan in one pass, [1024, 16384]; --unfused runs
                          dust_loss_delta and dust_reward_scan instead)
-    dust_error_estimate (g_hat [16384, 2048] fp32 + its bf16 transpose)
-    dust_weight_grad    (G_W [2048, 512], bf16 matrix cores)
+    dust_error_estimate (g_hat [16384, 4096] fp32 + its bf16 transpose)
+    dust_weight_grad    (G_W [4096, 1024], bf16 matrix cores)
 The perturbed forward of the rest of the model, between the perturbation and the loss change,
 is not part of the estimator; its per-token losses are synthetic inputs here.
---workload 3 / 4 / 5 time the LM-head chunk, the attention k/v inner-product and the 240M-shape
-chains the same way (for the report; the default line is workload 2). With --workload 4,
---attention-values, --attention-keys or --attention-queries scores the draws by re-running the
-attention with perturbed values, keys or queries (dust_attn_value_scores / _key_scores /
-_query_scores; keys and queries after dust_attn_row_weights, once per step) instead of
-streaming a synthetic attention-output change.
+--workload 2 / 3 / 4 time the MLP up-projection 512 -> 2048 (K = 64), the LM-head chunk and the
+attention k/v inner-product chains the same way. With --workload 4, --attention-values,
+--attention-keys or --attention-queries scores the draws by re-running the attention with
+perturbed values, keys or queries (dust_attn_value_scores / _key_scores / _query_scores; keys and
+queries after dust_attn_row_weights, once per step) instead of streaming a synthetic
+attention-output change.
 
 Metric: draws x tokens per second (K * T / step time). Prints one JSON line with the per-kernel
 HIP-event durations measured inside the timed region, the roofline of the dominant kernel, and
 the CPU oracle's throughput on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--workload 2] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 30] [--workload 5] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -42,6 +42,10 @@ import synth  # noqa: E402
 
 METRIC = "Dust estimator draws·tokens/sec on 1 GPU + % of HBM/MFMA roofline"
 UNIT = "draws·tokens/s"
+# What the path computes in: bf16 activations, perturbed outputs and matrix-core operands (the
+# weight-gradient contraction runs on the bf16 matrix cores), fp32 noise, scores, rewards,
+# output error and every accumulation; the generator itself is 32-bit integer arithmetic.
+DTYPE = "bf16 storage and MFMA operands, fp32 accumulate"
 
 # MI355X published peaks
 HBM_PEAK_GBS = 8000.0
@@ -80,7 +84,7 @@ def parse():
     # the shader clock takes tens of milliseconds under load to settle; 30 untimed steps put the
     # timed ones in steady state (about +1 % against 3 on the headline workload)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", type=int, default=2, choices=(2, 3, 4, 5))
+    ap.add_argument("--workload", type=int, default=5, choices=(2, 3, 4, 5))
     ap.add_argument("--cpu-scale", type=float, default=1.0,
                     help="scale of the CPU oracle's sample (1.0 = about 10-30 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,6 +524,11 @@ class InnerChain(Chain):
 CHAINS = {2: LinearChain, 3: HeadChain, 4: InnerChain, 5: LinearChain}
 
 
+def cfg_name(chain) -> str:
+    """The workload name the bench line carries (and profiles/traffic.json is keyed by)."""
+    return chain.config()["workload"]
+
+
 def main() -> int:
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -613,13 +622,14 @@ def main() -> int:
     traffic_file = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(traffic_file):
         with open(traffic_file) as f:
-            tr = json.load(f)
-        if (tr.get("kernel") == dominant and tr.get("workload") == chain.c["name"]
-                and tr.get("build") == _kernel_build_id(dominant)):
+            tr = json.load(f).get(cfg_name(chain), {})
+        if tr.get("kernel") == dominant and tr.get("build") == _kernel_build_id(dominant):
             roofline["traffic"] = tr.get("bytes_per_launch")
 
     cfg = chain.config()
     cfg["parallelism"] = "single GPU"
+    cfg["precision"] = ("bf16 activations, perturbed outputs and matrix-core operands; fp32 "
+                        "noise, scores, rewards, output error and accumulation")
     if args.workload != 4:
         cfg["loss_to_reward"] = "one kernel" if chain.fused else "two kernels"
     if chain.optimizer != "none":
@@ -627,7 +637,7 @@ def main() -> int:
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": UNIT, "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE,
         "data": "synthetic", "config": cfg, "roofline": roofline, "kernels": kernels,
     }
     if not args.no_cpu_baseline:
