@@ -155,6 +155,33 @@ def test_reward_scan(K, T, S, gamma):
     assert np.all(np.abs(got - ref) <= 1e-5 * bound + 1e-30)
 
 
+# more (draw, sequence) units than the chip keeps waves resident: every wave walks several units
+# (whole sequences in registers, or streamed chunk by chunk past 4 chunks), in place or not
+MANY_UNITS = [(6000, 64, 32), (9000, 1300, 1300), (20000, 67, 67), (700, 16384, 1024)]
+
+
+@pytest.mark.parametrize("K,T,S", MANY_UNITS)
+@pytest.mark.parametrize("gamma", [0.0, 0.9])
+def test_reward_scan_many_units_per_wave(K, T, S, gamma):
+    announce("reward_scan many units %s" % ((K, T, S, gamma),))
+    g = np.random.default_rng(27)
+    c = g.standard_normal((K, T)).astype(np.float32)
+    r = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_reward_scan(f32(c), r, K, T, S, gamma)
+    got = host_f32(r)
+    ref = oracle.reward_scan(c, S, gamma)
+    if gamma == 0.0:
+        assert np.array_equal(got, c)
+    assert frob_rel(got, ref) <= 1e-5
+    bound = oracle.reward_scan(np.abs(c), S, gamma)
+    assert np.all(np.abs(got - ref) <= 1e-5 * bound + 1e-30)
+    lc = g.standard_normal(T).astype(np.float32)
+    buf = f32(c)
+    dust.dust_loss_reward(f32(lc), buf, buf, K, T, S, gamma)   # fused, in place
+    ref_f = oracle.reward_scan(oracle.loss_delta_loss(lc, c), S, gamma)
+    assert frob_rel(host_f32(buf), ref_f) <= 1e-5
+
+
 def test_reward_scan_in_place():
     announce("reward_scan in place")
     K, T, S, gamma = 3, 2048, 1024, 0.99
