@@ -192,3 +192,134 @@ def test_estimate_converges_to_its_credit_assignment_limit(layer):
     to_true = [_cos(_estimate(net, K, 1.0), G_true) for K in KS]
     print("%s gamma 1.0: cos to autograd %s" % (layer, np.round(to_true, 4)))
     assert all(b > a for a, b in zip(to_true, to_true[1:])) and to_true[-1] >= 0.7
+
+
+# ------------------------------------------------------------------------------ layer-type groups
+# The explainer ("The real work: suppressing interference") perturbs several layers of one type
+# in the same forward, each with its own noise, and gives every layer type its own forward and
+# its own sigma. Here both blocks' MLP up-projections form one group: one forward per draw
+# perturbs both, under distinct tags, and each layer's estimate is formed from the same per-token
+# loss changes. To first order in sigma the other layer's noise adds a zero-mean term to every
+# loss change, so it adds variance but no bias: at a fixed population the group's cosines sit
+# below the single-layer ones (a larger c in the law cos(K) = c_max / sqrt(1 + c/K) of "Gradients
+# grow"), while the fitted c_max stays that of the single layer -- the estimate recovers with K.
+# A second layer type in the same forward at its own, larger sigma (block 1's attention value
+# projection) swamps the group's loss changes: that is why layer types get separate forwards.
+GROUP_TAGS = {"fc0": 11, "fc1": 12, "v1": 13}
+GROUP_KS = (256, 1024, 4096, 16384)
+
+
+class GroupNet:
+    """The harness forward with optional noise on block 0's and block 1's MLP up-projection
+    outputs and on block 1's attention values."""
+
+    def __init__(self):
+        self.P, self.tok, self.tgt = _model()
+
+    def forward(self, n=1, W=None, noise=None):
+        """Per-token losses [n, T] of n copies of the batch, and the clean inputs of the two
+        up-projections; noise maps a layer ('fc0', 'fc1', 'v1') to [n*B, S, width] additions."""
+        P, W, noise = self.P, W or {}, noise or {}
+        h = (P["emb"][self.tok] + P["pos"][None]).repeat(n, 1, 1)
+        a = _ln(h)
+        q, k, v = (a @ P["qkv0"].T).split(DM, -1)
+        h = h + _attend(q, k, v) @ P["ao0"].T
+        x0 = _ln(h)
+        y0 = x0 @ W.get("fc0", P["fc0"]).T
+        if "fc0" in noise:
+            y0 = y0 + noise["fc0"]
+        h = h + torch.nn.functional.gelu(y0) @ P["pr0"].T
+        a = _ln(h)
+        q, k, v = (a @ P["qkv1"].T).split(DM, -1)
+        if "v1" in noise:
+            v = v + noise["v1"]
+        h = h + _attend(q, k, v) @ P["ao1"].T
+        x1 = _ln(h)
+        y1 = x1 @ W.get("fc1", P["fc1"]).T
+        if "fc1" in noise:
+            y1 = y1 + noise["fc1"]
+        h = h + torch.nn.functional.gelu(y1) @ P["pr1"].T
+        z = _ln(h) @ P["head"].T
+        l = torch.nn.functional.cross_entropy(z.reshape(-1, V), self.tgt.repeat(n, 1).reshape(-1),
+                                              reduction="none").reshape(n, T)
+        return l, x0, x1
+
+
+def _group_truth(net):
+    W = {k: net.P[k].clone().requires_grad_(True) for k in ("fc0", "fc1")}
+    l, _, _ = net.forward(W=W)
+    l.sum().backward()
+    return {k: W[k].grad.double().cpu().numpy() for k in W}
+
+
+def _group_estimate(net, K, sigmas, estimated, chunk=512):
+    """One forward per draw with every layer in `sigmas` perturbed (its own tag and sigma); the
+    library's chain turns the shared loss changes into each estimated layer's weight gradient."""
+    width = {"fc0": DF, "fc1": DF, "v1": DM}
+    with torch.no_grad():
+        lc, x0, x1 = net.forward()
+        lc = lc[0].contiguous()
+        xs = {"fc0": x0, "fc1": x1}
+        lp = torch.empty((K, T), dtype=torch.float32, device=DEV)
+        for k0 in range(0, K, chunk):
+            kc = min(chunk, K - k0)
+            noise = {}
+            for layer, sg in sigmas.items():
+                d = width[layer]
+                zero = torch.zeros((T, d), dtype=torch.float32, device=DEV)
+                a = torch.empty((kc, T, d), dtype=torch.float32, device=DEV)
+                dust.dust_noise_inject(zero, a, dust.DUST_F32, T, d, d, 0, kc, sg, SEED,
+                                       GROUP_TAGS[layer], k0, 0)          # sigma a, draws k0..
+                noise[layer] = a.reshape(kc * B, S, d)
+            lp[k0:k0 + kc] = net.forward(kc, noise=noise)[0]
+        r = torch.empty_like(lp)
+        dust.dust_loss_reward(lc, lp, r, K, T, S, 0.0)
+        out = {}
+        for layer in estimated:
+            d, sg = width[layer], sigmas[layer]
+            gh = torch.empty((T, d), dtype=torch.float32, device=DEV)
+            ght = torch.empty((d, T), dtype=torch.bfloat16, device=DEV)
+            dust.dust_error_estimate(r, gh, ght, K, K, T, d, 0, sg, SEED, GROUP_TAGS[layer], 0, 0, 0)
+            xb = xs[layer].reshape(T, DM).to(torch.bfloat16).contiguous()
+            G = torch.empty((d, DM), dtype=torch.float32, device=DEV)
+            ws_bytes = dust.dust_weight_grad_workspace(T, d, DM)
+            ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=DEV)
+            dust.dust_weight_grad(ght, xb, G, T, d, DM, ws, ws_bytes)
+            out[layer] = G
+        torch.cuda.synchronize()
+        return {k: v.double().cpu().numpy() for k, v in out.items()}
+
+
+def test_layer_type_group_interference():
+    announce("gpt layer-type group")
+    net = GroupNet()
+    G_true = _group_truth(net)
+    law = lambda K, cm, c: cm / np.sqrt(1 + c / K)
+    runs = {
+        "alone": {layer: [_group_estimate(net, K, {layer: SIGMA}, [layer])[layer]
+                          for K in GROUP_KS] for layer in ("fc0", "fc1")},
+        "group": [_group_estimate(net, K, {"fc0": SIGMA, "fc1": SIGMA}, ["fc0", "fc1"])
+                  for K in GROUP_KS],
+        "mixed": [_group_estimate(net, K, {"fc0": SIGMA, "fc1": SIGMA, "v1": 0.3},
+                                  ["fc0", "fc1"]) for K in GROUP_KS[:3]],
+    }
+    for layer in ("fc0", "fc1"):
+        alone = np.array([_cos(G, G_true[layer]) for G in runs["alone"][layer]])
+        group = np.array([_cos(run[layer], G_true[layer]) for run in runs["group"]])
+        mixed = np.array([_cos(run[layer], G_true[layer]) for run in runs["mixed"]])
+        fa, _ = curve_fit(law, np.array(GROUP_KS, float), alone, p0=(1.0, 100.0),
+                          bounds=([0.0, 0.0], [2.0, 1e9]))
+        fg, _ = curve_fit(law, np.array(GROUP_KS, float), group, p0=(1.0, 100.0),
+                          bounds=([0.0, 0.0], [2.0, 1e9]))
+        print("%s: alone cos %s (c_max %.3f, c %.0f); group cos %s (c_max %.3f, c %.0f); "
+              "with attention values at sigma 0.3 in the same forward: cos %s"
+              % (layer, np.round(alone, 4), fa[0], fa[1], np.round(group, 4), fg[0], fg[1],
+                 np.round(mixed, 4)))
+        # interference: lower cosines at every population up to 4096 draws, a larger c
+        assert np.all(group[:3] < alone[:3])
+        assert fg[1] > 1.3 * fa[1]
+        # no bias: the group's estimate recovers with K towards the single layer's limit
+        assert all(b > a for a, b in zip(group, group[1:]))
+        assert abs(fg[0] - fa[0]) <= 0.02
+        # another layer type at a larger sigma in the same forward swamps the group
+        assert mixed[-1] < 0.5 * group[2]
