@@ -93,6 +93,12 @@ def _configure(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.dust_or_head_ce_at.argtypes = [_d, ctypes.POINTER(ctypes.c_int32), _i64, _i64, _i64, _i64,
                                        ctypes.c_double, _u64, _u32, _u32, _u32, _pi64, _pi64, _i64,
                                        _d]
+    lib.dust_or_activation.argtypes = [ctypes.c_double, ctypes.c_int]
+    lib.dust_or_activation.restype = ctypes.c_double
+    lib.dust_or_perturbed_linear.argtypes = [_d, _d, _i64, _i64, _i64, _i64, _i64, ctypes.c_double,
+                                             _u64, _u32, _u32, _u32, ctypes.c_int, _d]
+    lib.dust_or_perturbed_rows_at.argtypes = [_d, _i64, _i64, ctypes.c_double, _u64, _u32, _u32,
+                                              _u32, ctypes.c_int, _pi64, _pi64, _i64, _d]
     lib.dust_or_threads.restype = ctypes.c_int
     lib.dust_or_round_bf16.argtypes = [ctypes.c_double]
     lib.dust_or_round_bf16.restype = ctypes.c_double
@@ -386,6 +392,41 @@ def head_ce_at(logits, targets, v0: int, C: int, k, t, sigma: float, seed: int, 
     _load().dust_or_head_ce_at(_p(z), y.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), T, V, v0, C,
                                sigma, seed, tag, draw0, tok0, _pidx(k), _pidx(t), len(k), _p(out))
     return out
+
+
+ACT_NONE, ACT_RELU, ACT_RELU2, ACT_GELU_TANH = 0, 1, 2, 3
+
+
+def activation(x, act: int) -> np.ndarray:
+    """Elementwise activation (dust_oracle.c states the four forms) of an array, fp64."""
+    f = np.vectorize(lambda v: _load().dust_or_activation(v, act), otypes=[np.float64])
+    return f(_f64(x))
+
+
+def perturbed_linear(y, w, K: int, sigma: float, seed: int, tag: int, act: int, draw0: int = 0,
+                     tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """out[k][t][n] = sum_j act(y[t][j] + sigma a^{(draw0+k)}_{tok0+t, chan0+j}) w[n][j]: the next
+    linear layer applied to the activated perturbed output (explainer, "The real work", first
+    measure). y [T, d], w [n_out, d] -> [K, T, n_out], fp64."""
+    y, w = _f64(y), _f64(w)
+    T, d = y.shape
+    n_out = w.shape[0]
+    out = np.empty((K, T, n_out), dtype=np.float64)
+    _load().dust_or_perturbed_linear(_p(y), _p(w), T, d, n_out, chan0, K, sigma, seed, tag, draw0,
+                                     tok0, act, _p(out))
+    return out
+
+
+def perturbed_rows_at(y, k, t, sigma: float, seed: int, tag: int, act: int, draw0: int = 0,
+                      tok0: int = 0, chan0: int = 0) -> np.ndarray:
+    """act(y[t] + sigma a^{(draw0+k)}_{tok0+t}) for chosen (k, t) pairs: rows [m, d], fp64."""
+    y = _f64(y)
+    d = y.shape[1]
+    k, t = _idx(k), _idx(t)
+    rows = np.empty((len(k), d), dtype=np.float64)
+    _load().dust_or_perturbed_rows_at(_p(y), d, chan0, sigma, seed, tag, draw0, tok0, act,
+                                      _pidx(k), _pidx(t), len(k), _p(rows))
+    return rows
 
 
 def round_bf16(x) -> np.ndarray:

@@ -623,6 +623,69 @@ void dust_or_adam(double *w, const double *g, double *m, double *v, int64_t n, d
 }
 
 /* ---------------------------------------------------------------------------------------- */
+/* The first operation of a perturbed re-run from a layer onward (explainer, "The real work:
+ * suppressing interference", first measure: the network is re-run from the perturbed layer on):
+ * the next linear layer applied to the activated perturbed output,
+ *     out[k][t][n] = sum_j act(y[t][j] + sigma a^{(draw0+k)}_{tok0+t, chan0+j}) w[n][j],
+ * i.e. the perturbation of dust_or_noise_inject, an elementwise activation, and a matrix
+ * product with the next layer's weight w [n_out, d] (row n = output n). act: 0 identity,
+ * 1 ReLU max(x, 0), 2 squared ReLU max(x, 0)^2, 3 GELU in its tanh form
+ * 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). The pages name no activation; these are the
+ * common choices for a transformer MLP. */
+double dust_or_activation(double x, int act)
+{
+    if (act == 1) return x > 0.0 ? x : 0.0;
+    if (act == 2) return x > 0.0 ? x * x : 0.0;
+    if (act == 3) {
+        const double u = sqrt(2.0 / 3.14159265358979323846) * (x + 0.044715 * x * x * x);
+        return 0.5 * x * (1.0 + tanh(u));
+    }
+    return x;
+}
+
+/* out [K, T, n_out]; y [T, d]; w [n_out, d]. */
+void dust_or_perturbed_linear(const double *y, const double *w, int64_t T, int64_t d,
+                              int64_t n_out, int64_t chan0, int64_t K, double sigma,
+                              uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                              int act, double *out)
+{
+    #pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t t = 0; t < T; ++t) {
+            double *row = (double *)malloc((size_t)d * sizeof(double));
+            for (int64_t j = 0; j < d; ++j)
+                row[j] = dust_or_activation(
+                    y[t * d + j] + sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k),
+                                                          (uint32_t)(tok0 + t),
+                                                          (uint64_t)(chan0 + j)),
+                    act);
+            for (int64_t n = 0; n < n_out; ++n) {
+                double acc = 0.0;
+                for (int64_t j = 0; j < d; ++j) acc += row[j] * w[n * d + j];
+                out[(k * T + t) * n_out + n] = acc;
+            }
+            free(row);
+        }
+}
+
+/* The activated perturbed rows act(y[t] + sigma a^{(draw0+k)}_t) [d] at chosen (k, t) pairs:
+ * rows [m, d], for checks of the full-size product at sampled rows. */
+void dust_or_perturbed_rows_at(const double *y, int64_t d, int64_t chan0, double sigma,
+                               uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                               int act, const int64_t *k, const int64_t *t, int64_t m,
+                               double *rows)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t q = 0; q < m; ++q)
+        for (int64_t j = 0; j < d; ++j)
+            rows[q * d + j] = dust_or_activation(
+                y[t[q] * d + j] + sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[q]),
+                                                         (uint32_t)(tok0 + t[q]),
+                                                         (uint64_t)(chan0 + j)),
+                act);
+}
+
+/* ---------------------------------------------------------------------------------------- */
 /* Round a double to the nearest bfloat16 value (8 significant bits, fp32 exponent range),
  * ties to even, returned as a double. Used to state what a bf16 output must hold. */
 double dust_or_round_bf16(double x)

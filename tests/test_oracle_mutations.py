@@ -20,6 +20,7 @@ import test_oracle_attn as attn
 import test_oracle_generator as gen
 import test_oracle_helpers as helpers
 import test_oracle_optim as optim
+import test_oracle_perturbed_linear as plin
 import test_oracle_steps as steps
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -98,6 +99,11 @@ PINS_STEPS = [
     helpers.test_round_bf16_equals_torch_on_fp32_values,
     lambda: helpers.test_normals_at_equals_slices_of_bulk_normals(3, 7, 2**32 + 8),
     lambda: helpers.test_head_ce_at_equals_torch_cross_entropy_of_perturbed_logits(64, 12, 20),
+    lambda: plin.test_activation_equals_torch(*plin.ACTS[2]),
+    lambda: plin.test_activation_equals_torch(*plin.ACTS[3]),
+    lambda: plin.test_perturbed_linear_equals_torch_linear_of_explicit_inputs(*plin.ACTS[3], 7, 300, 2**32 + 64),
+    plin.test_sigma_zero_is_the_clean_product_and_the_output_is_affine_in_sigma,
+    plin.test_sampled_rows_equal_the_bulk_operand,
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -189,6 +195,15 @@ MUTATIONS = [
      "if (zj > mx) mx = zj;\n            if (j == y) zy = z[j];"),
     ("sampled head loss: chunk off by one", "if (j >= v0 && j < v0 + C)\n                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),\n                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);\n            if (zj > mx)",
      "if (j > v0 && j < v0 + C)\n                zj += sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[m]),\n                                             (uint32_t)(tok0 + t[m]), (uint64_t)j);\n            if (zj > mx)"),
+    ("activation before the noise", "row[j] = dust_or_activation(\n                    y[t * d + j] + sigma",
+     "row[j] = dust_or_activation(y[t * d + j], act) + sigma * dust_or_activation(\n                    sigma"),
+    ("next layer's weight transposed", "acc += row[j] * w[n * d + j];", "acc += row[j] * w[(j % n_out) * d + n % d];"),
+    ("perturbed product drops the token offset", "(uint32_t)(tok0 + t),\n                                                          (uint64_t)(chan0 + j)),\n                    act);",
+     "(uint32_t)(t),\n                                                          (uint64_t)(chan0 + j)),\n                    act);"),
+    ("gelu cubic coefficient", "(x + 0.044715 * x * x * x)", "(x + 0.04 * x * x * x)"),
+    ("squared relu left linear", "if (act == 2) return x > 0.0 ? x * x : 0.0;", "if (act == 2) return x > 0.0 ? x : 0.0;"),
+    ("sampled perturbed rows ignore draw0", "sigma * dust_or_normal(seed, tag, (uint32_t)(draw0 + k[q]),",
+     "sigma * dust_or_normal(seed, tag, (uint32_t)(k[q]),"),
     ("query head offset dropped", "(uint64_t)(chan0 + h * dh + j));\n        double Z",
      "(uint64_t)(chan0 + j));\n        double Z"),
 ]
