@@ -16,7 +16,8 @@ import os
 
 __all__ = [
     "DUST_OK", "DUST_ERR_INVALID", "DUST_ERR_UNSUPPORTED", "DUST_ERR_WORKSPACE", "DUST_ERR_HIP",
-    "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DustError",
+    "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DUST_ACT_NONE",
+    "DUST_ACT_RELU", "DUST_ACT_RELU2", "DUST_ACT_GELU_TANH", "DustError", "dust_perturbed_linear",
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
     "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam",
     "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_row_weights",
@@ -28,6 +29,7 @@ __all__ = [
 DUST_OK, DUST_ERR_INVALID, DUST_ERR_UNSUPPORTED, DUST_ERR_WORKSPACE, DUST_ERR_HIP = 0, 1, 2, 3, 4
 DUST_F32, DUST_BF16 = 0, 1
 DUST_DELTA_LOSS, DUST_DELTA_INNER = 0, 1
+DUST_ACT_NONE, DUST_ACT_RELU, DUST_ACT_RELU2, DUST_ACT_GELU_TANH = 0, 1, 2, 3
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdust.so")
 
@@ -44,6 +46,8 @@ _SIGNATURES = {
     "dust_last_error": (ctypes.c_char_p, []),
     "dust_noise_inject": (_int, [_vp, _vp, _int, _i64, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                  _u32, _u32, _vp]),
+    "dust_perturbed_linear": (_int, [_vp, _vp, _vp, _int, _int, _i64, _i64, _i64, _i64, _i64,
+                                     _f32, _u64, _u32, _u32, _u32, _vp]),
     "dust_loss_delta": (_int, [_int, _vp, _vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _vp]),
     "dust_reward_scan": (_int, [_vp, _vp, _i64, _i64, _i64, _f32, _vp]),
     "dust_loss_reward": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _f32, _vp]),
@@ -129,6 +133,12 @@ def dust_noise_inject(y, y_pert, dtype, T, d, ld_y, chan0, Kc, sigma, seed, tag,
                       stream=None):
     return _call("dust_noise_inject", _ptr(y), _ptr(y_pert), dtype, T, d, ld_y, chan0, Kc, sigma,
                  seed, tag, draw0, tok0, _stream(stream))
+
+
+def dust_perturbed_linear(y, w, out, out_dtype, act, T, d, n_out, chan0, Kc, sigma, seed, tag,
+                          draw0, tok0, stream=None):
+    return _call("dust_perturbed_linear", _ptr(y), _ptr(w), _ptr(out), out_dtype, act, T, d, n_out,
+                 chan0, Kc, sigma, seed, tag, draw0, tok0, _stream(stream))
 
 
 def dust_loss_delta(mode, loss_clean, loss_pert, delta_o, g_o, io_dtype, c, Kc, T, d,

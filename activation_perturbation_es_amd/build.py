@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libdust.so")
 INCLUDE = os.path.join(ROOT, "include")
 
 SOURCES = ["dust_api.cpp", "noise.hip", "delta_scan.hip", "error_estimate.hip",
-           "weight_grad.hip", "head_ce.hip", "optim.hip", "attn_scores.hip"]
+           "weight_grad.hip", "head_ce.hip", "optim.hip", "attn_scores.hip",
+           "perturbed_linear.hip"]
 HEADERS = [os.path.join(CSRC, h) for h in ("dust_noise.hpp", "dust_internal.hpp")] + \
           [os.path.join(INCLUDE, "dust.h")]
 

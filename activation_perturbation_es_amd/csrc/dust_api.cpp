@@ -379,6 +379,51 @@ int dust_weight_grad(const void *g_hat_t_bf16, const void *x_bf16, float *G, int
                       fn);
 }
 
+int dust_perturbed_linear(const void *y, const void *w, void *out, int out_dtype, int act,
+                          int64_t T, int64_t d, int64_t n_out, int64_t chan0, int64_t Kc,
+                          float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                          uint32_t tok0, void *stream) {
+    const char *fn = "dust_perturbed_linear";
+    if (out_dtype != DUST_F32 && out_dtype != DUST_BF16)
+        return fail(DUST_ERR_INVALID, "%s: out_dtype=%d is not DUST_F32 or DUST_BF16", fn,
+                    out_dtype);
+    if (act < DUST_ACT_NONE || act > DUST_ACT_GELU_TANH)
+        return fail(DUST_ERR_INVALID, "%s: act=%d is not a dust_activation", fn, act);
+    if (T < 0 || d < 0 || n_out < 0 || Kc < 0)
+        return fail(DUST_ERR_INVALID, "%s: negative size", fn);
+    if (!std::isfinite(sigma)) return fail(DUST_ERR_INVALID, "%s: sigma must be finite", fn);
+    if (T > kMaxIdx || d > kMaxIdx || n_out > kMaxIdx || Kc > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: sizes beyond 2^31 are not supported", fn);
+    if (int rc = check_noise_ranges(fn, T, d, chan0, Kc, draw0, tok0)) return rc;
+    if (Kc == 0 || T == 0 || n_out == 0) return ok();
+    if (d == 0 || d % 64 != 0 || n_out % 32 != 0)
+        return fail(DUST_ERR_UNSUPPORTED,
+                    "%s: d=%lld must be a positive multiple of 64 and n_out=%lld of 32", fn,
+                    (long long)d, (long long)n_out);
+    if (d > ((int64_t)1 << 23))
+        return fail(DUST_ERR_UNSUPPORTED, "%s: d beyond 2^23 is not supported", fn);
+    if (!y || !w || !out) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    const size_t es = out_dtype == DUST_BF16 ? 2 : 4;
+    if (((uintptr_t)y & 15u) || ((uintptr_t)w & 15u) || !elem_aligned(out, es))
+        return fail(DUST_ERR_INVALID, "%s: y and w must be 16-byte aligned, out element-aligned",
+                    fn);
+    const int64_t y_bytes = span(T, d, 1, 2), w_bytes = span(n_out, d, 1, 2);
+    const int64_t o_bytes = span(Kc, T, n_out, (int64_t)es);
+    if (y_bytes < 0 || w_bytes < 0 || o_bytes < 0)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
+    const int64_t blocks = Kc * ((T + 127) / 128) * ((n_out + 511) / 512);
+    if (blocks > kMaxIdx)
+        return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large; split the draws", fn);
+    if (ranges_overlap(out, (size_t)o_bytes, y, (size_t)y_bytes) ||
+        ranges_overlap(out, (size_t)o_bytes, w, (size_t)w_bytes))
+        return fail(DUST_ERR_INVALID, "%s: out overlaps an input", fn);
+    return hip_status(dust::launch_perturbed_linear((const uint16_t *)y, (const uint16_t *)w, out,
+                                                    out_dtype == DUST_BF16, act, T, d, n_out,
+                                                    chan0, Kc, sigma, make_key(seed, tag), draw0,
+                                                    tok0, (hipStream_t)stream),
+                      fn);
+}
+
 int dust_weight_grad_noalloc(const void *g_hat_t_bf16, const void *x_bf16, float *G, int64_t T,
                              int64_t d_out, int64_t d_in, void *stream) {
     const char *fn = "dust_weight_grad_noalloc";

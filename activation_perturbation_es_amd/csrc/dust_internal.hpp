@@ -99,6 +99,11 @@ hipError_t launch_weight_grad(const uint16_t *gt, const uint16_t *x, float *G, i
 size_t weight_grad_scratch_bytes();
 hipError_t weight_grad_scratch(void **ptr);
 
+hipError_t launch_perturbed_linear(const uint16_t *y, const uint16_t *w, void *out, bool out_bf16,
+                                   int act, int64_t T, int64_t d, int64_t n_out, int64_t chan0,
+                                   int64_t Kc, float sigma, Key key, uint32_t draw0,
+                                   uint32_t tok0, hipStream_t s);
+
 hipError_t launch_head_ce_chunk(const float *logits, const int32_t *targets, float *loss_pert,
                                 float *loss_clean, int64_t T, int64_t V, int64_t v0, int64_t C,
                                 int64_t Kc, float sigma, Key key, uint32_t draw0, uint32_t tok0,

@@ -105,6 +105,12 @@ def parse():
                     help="workload 4: score by re-running the softmax with perturbed queries "
                          "(dust_attn_query_scores on synthetic queries, keys and values, 8 heads "
                          "of 64) instead of streaming a synthetic attention-output change")
+    ap.add_argument("--downstream", choices=("none", "fused", "unfused"), default="none",
+                    help="workloads 2 and 5: also run the first operation of the perturbed "
+                         "forward, the down-projection of the activated perturbed outputs "
+                         "(GELU, then [d_in x d_out]): 'fused' with dust_perturbed_linear "
+                         "(noise regenerated in the matrix-core operand path, y' never written), "
+                         "'unfused' as dust_noise_inject + torch GELU + torch matmul")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -189,12 +195,29 @@ class LinearChain(Chain):
         self.G = self.empty((self.d_out, self.d_in), t.float32)
         self.ws_bytes = self.dust.dust_weight_grad_workspace(self.T, self.d_out, self.d_in)
         self.ws = self.empty(max(self.ws_bytes, 16), t.uint8)
+        if self.downstream != "none":
+            # the next layer: the MLP down-projection [d_in, d_out], W ~ N(0, 1/d_out), bf16
+            self.wnbits = synth.normal_bf16(synth.rng(self.cfg_id, 8), (self.d_in, self.d_out),
+                                            1.0 / np.sqrt(self.d_out))
+            self.wn = self.bf(self.wnbits)
+            self.dbuf = self.empty((self.KB, self.T, self.d_in), t.bfloat16)
+
+    downstream = "none"   # "none", "fused" or "unfused"
 
     def step(self, run, sh):
-        d, T, K, KB = self.dust, self.T, self.K, self.KB
+        d, T, K, KB, t = self.dust, self.T, self.K, self.KB, self.torch
         for blk in range(K // KB):
+            if self.downstream == "fused":
+                run("dust_perturbed_linear", d.dust_perturbed_linear, self.y, self.wn, self.dbuf,
+                    d.DUST_BF16, d.DUST_ACT_GELU_TANH, T, self.d_out, self.d_in, 0, KB, self.sigma,
+                    self.seed, self.tag, blk * KB, 0, sh)
+                continue
             run("dust_noise_inject", d.dust_noise_inject, self.y, self.ybuf, d.DUST_BF16, T, self.d_out,
                 self.d_out, 0, KB, self.sigma, self.seed, self.tag, blk * KB, 0, sh)
+            if self.downstream == "unfused":
+                run("torch_gelu_matmul", lambda: t.matmul(
+                    t.nn.functional.gelu(self.ybuf, approximate="tanh"), self.wn.t(),
+                    out=self.dbuf))
         if self.fused:
             run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.rbuf, K, T, self.S,
                 self.gamma, sh)
@@ -220,12 +243,22 @@ class LinearChain(Chain):
             "dust_loss_reward": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_error_estimate": _alu(K * T * do, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * do * self.d_in),
+            # the down-projection of the block's activated perturbed outputs
+            "dust_perturbed_linear": _mfma(2.0 * self.KB * T * do * self.d_in),
+            "torch_gelu_matmul": _mfma(2.0 * self.KB * T * do * self.d_in),
         }
 
     def config(self):
-        return {"workload": self.c["name"], "d_in": self.d_in, "d_out": self.d_out, "tokens": self.T,
-                "seq_len": self.S, "draws": self.K, "gamma": self.gamma, "sigma": self.sigma,
-                "inject_block": self.KB, "storage": "bf16 activations, fp32 rewards/g_hat/G_W"}
+        cfg = {"workload": self.c["name"], "d_in": self.d_in, "d_out": self.d_out, "tokens": self.T,
+               "seq_len": self.S, "draws": self.K, "gamma": self.gamma, "sigma": self.sigma,
+               "inject_block": self.KB, "storage": "bf16 activations, fp32 rewards/g_hat/G_W"}
+        if self.downstream != "none":
+            cfg["workload"] += "_downstream_" + self.downstream
+            cfg["downstream"] = ("GELU (tanh form) then the down-projection [%d x %d], bf16 out, "
+                                 "%s" % (self.d_in, self.d_out,
+                                         "dust_perturbed_linear" if self.downstream == "fused"
+                                         else "dust_noise_inject + torch gelu + torch matmul"))
+        return cfg
 
     def cpu_baseline(self, scale):
         """The oracle's chain (as it stands) on whole sequences with all K draws (workload 2) or
@@ -236,12 +269,19 @@ class LinearChain(Chain):
             K_s, T_s = self.K, min(self.T, max(S, int(16 * S * scale) // S * S))
         else:
             K_s, T_s = max(4, int(512 * scale) // 4 * 4), S
+        if self.downstream != "none":
+            K_s = max(1, int(64 * scale))  # the product costs d_out d_in multiply-adds per token
         KB = min(self.KB, K_s)
         y = synth.bf16_bits_to_f32(self.ybits[:T_s]).astype(np.float64)
         x = synth.bf16_bits_to_f32(self.xbits[:T_s]).astype(np.float64)
         oracle.threads()
         t0 = time.perf_counter()
         for b in range(K_s // KB):
+            if self.downstream != "none":
+                oracle.perturbed_linear(y, synth.bf16_bits_to_f32(self.wnbits).astype(np.float64),
+                                        KB, self.sigma, self.seed, self.tag, oracle.ACT_GELU_TANH,
+                                        draw0=b * KB)
+                continue
             oracle.noise_inject(y, self.sigma, KB, self.seed, self.tag, draw0=b * KB)
         r = oracle.reward_scan(oracle.loss_delta_loss(self.lc_h[:T_s], self.lp_h[:K_s, :T_s]), S, self.gamma)
         g = oracle.error_estimate(r, self.d_out, self.sigma, self.seed, self.tag, K_total=self.K)
@@ -249,8 +289,10 @@ class LinearChain(Chain):
         dt = time.perf_counter() - t0
         return {"value": K_s * T_s / dt, "unit": UNIT, "cores": oracle.threads(), "kind": "oracle",
                 "sample": "%d of %d draws x first %d of %d tokens (%d whole sequences), whole chain "
-                          "incl. the full G_W contraction over those tokens; %.1f s"
-                          % (K_s, self.K, T_s, self.T, T_s // S, dt)}
+                          "incl. %sthe full G_W contraction over those tokens; %.1f s"
+                          % (K_s, self.K, T_s, self.T, T_s // S,
+                             "the down-projection of the perturbed outputs and "
+                             if self.downstream != "none" else "", dt)}
 
 
 class HeadChain(Chain):
@@ -552,6 +594,11 @@ def main() -> int:
 
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
+    if args.downstream != "none":
+        if args.workload not in (2, 5):
+            print("--downstream applies to the MLP workloads 2 and 5 only", file=sys.stderr)
+            return 2
+        chain.downstream = args.downstream
     chain.optimizer = args.optimizer
     modes = [m for m, on in (("values", args.attention_values), ("keys", args.attention_keys),
                              ("queries", args.attention_queries)) if on]
@@ -656,6 +703,7 @@ KERNEL_SOURCES = {
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
     "dust_attn_value_scores": "attn_scores.hip", "dust_attn_key_scores": "attn_scores.hip",
     "dust_attn_query_scores": "attn_scores.hip", "dust_attn_row_weights": "attn_scores.hip",
+    "dust_perturbed_linear": "perturbed_linear.hip",
 }
 
 

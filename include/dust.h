@@ -68,6 +68,13 @@ typedef enum { DUST_F32 = 0, DUST_BF16 = 1 } dust_dtype;
 
 typedef enum { DUST_DELTA_LOSS = 0, DUST_DELTA_INNER = 1 } dust_delta_mode;
 
+/* Elementwise activation applied to a perturbed output before the next linear layer
+ * (dust_perturbed_linear). GELU is the tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+typedef enum {
+    DUST_ACT_NONE = 0, DUST_ACT_RELU = 1, DUST_ACT_RELU2 = 2 /* max(x, 0)^2 */,
+    DUST_ACT_GELU_TANH = 3
+} dust_activation;
+
 /* Static name of a status code ("DUST_OK", ...). Never NULL. */
 const char *dust_status_string(int status);
 
@@ -88,6 +95,30 @@ const char *dust_last_error(void);
 int dust_noise_inject(const void *y, void *y_pert, int dtype, int64_t T, int64_t d,
                       int64_t ld_y, int64_t chan0, int64_t Kc, float sigma, uint64_t seed,
                       uint32_t tag, uint32_t draw0, uint32_t tok0, void *stream);
+
+/*
+ * dust_perturbed_linear -- the next linear layer applied to the perturbed outputs of a block of
+ * draws, without writing them. Explainer, "The real work: suppressing interference" (first
+ * measure): a perturbed layer is scored by re-running the network from that layer onward; the
+ * first operation of that re-run, for a layer followed by an activation and a linear map
+ * (e.g. an MLP up-projection followed by the down-projection), is
+ *     out[k][t][n] = sum_j act(y[t][j] + sigma * a^{(draw0+k)}_{tok0+t, chan0+j}) * w[n][j]
+ * with the noise of dust_noise_inject (same seed, tag, draw0, tok0, chan0 give the same
+ * y'), regenerated on the fly, so the [Kc, T, d] perturbed outputs never reach memory.
+ *   y       [T, d] bf16 clean layer output                                             (in)
+ *   w       [n_out, d] bf16 weight of the next linear layer (row n = output n)         (in)
+ *   out     [Kc, T, n_out] of out_dtype (DUST_F32 or DUST_BF16, nearest even)          (out)
+ *   act     a dust_activation
+ * act(y + sigma a) is formed in fp32 and rounded to bf16 (nearest even) as the matrix-core
+ * operand; products accumulate in fp32. Requires d a multiple of 64 (at most 2^23), n_out a
+ * multiple of 32, y and w 16-byte aligned,
+ * out element-aligned, sigma finite; out must not overlap y or w. Kc == 0 or T == 0 or
+ * n_out == 0 does nothing.
+ */
+int dust_perturbed_linear(const void *y, const void *w, void *out, int out_dtype, int act,
+                          int64_t T, int64_t d, int64_t n_out, int64_t chan0, int64_t Kc,
+                          float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                          uint32_t tok0, void *stream);
 
 /*
  * dust_loss_delta -- per-token score of every draw, c [Kc, T] fp32 (out).
