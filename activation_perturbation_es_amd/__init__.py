@@ -19,7 +19,8 @@ __all__ = [
     "DUST_F32", "DUST_BF16", "DUST_DELTA_LOSS", "DUST_DELTA_INNER", "DUST_ACT_NONE",
     "DUST_ACT_RELU", "DUST_ACT_RELU2", "DUST_ACT_GELU_TANH", "DustError", "dust_perturbed_linear",
     "dust_noise_inject", "dust_loss_delta", "dust_reward_scan", "dust_loss_reward",
-    "dust_error_estimate", "dust_weight_grad_workspace", "dust_sgd_momentum", "dust_adam",
+    "dust_error_estimate", "dust_error_estimate_losses", "dust_weight_grad_workspace",
+    "dust_sgd_momentum", "dust_adam",
     "dust_cosine_terms", "dust_attn_value_scores", "dust_attn_row_weights",
     "dust_attn_key_scores", "dust_attn_query_scores", "dust_weight_grad",
     "dust_weight_grad_noalloc", "dust_head_ce_chunk", "dust_noise_words",
@@ -63,6 +64,8 @@ _SIGNATURES = {
     "dust_adam": (_int, [_vp, _vp, _vp, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _i64, _vp]),
     "dust_error_estimate": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32, _u64, _u32,
                                    _u32, _u32, _int, _vp]),
+    "dust_error_estimate_losses": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _f32,
+                                          _u64, _u32, _u32, _u32, _int, _vp]),
     "dust_weight_grad_workspace": (ctypes.c_size_t, [_i64, _i64, _i64]),
     "dust_weight_grad": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp, ctypes.c_size_t, _vp]),
     "dust_weight_grad_noalloc": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _vp]),
@@ -196,6 +199,13 @@ def dust_error_estimate(r, g_hat, g_hat_t_bf16, K, K_total, T, d, chan0, sigma, 
                         tok0, accumulate, stream=None):
     return _call("dust_error_estimate", _ptr(r), _ptr(g_hat), _ptr(g_hat_t_bf16), K, K_total, T, d,
                  chan0, sigma, seed, tag, draw0, tok0, int(accumulate), _stream(stream))
+
+
+def dust_error_estimate_losses(loss_clean, loss_pert, g_hat, g_hat_t_bf16, K, K_total, T, d, chan0,
+                               sigma, seed, tag, draw0, tok0, accumulate, stream=None):
+    return _call("dust_error_estimate_losses", _ptr(loss_clean), _ptr(loss_pert), _ptr(g_hat),
+                 _ptr(g_hat_t_bf16), K, K_total, T, d, chan0, sigma, seed, tag, draw0, tok0,
+                 int(accumulate), _stream(stream))
 
 
 def dust_weight_grad_workspace(T, d_out, d_in) -> int:

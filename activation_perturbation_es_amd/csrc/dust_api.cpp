@@ -272,11 +272,17 @@ int dust_loss_reward(const float *loss_clean, const float *loss_pert, float *r, 
                       fn);
 }
 
-int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_t K,
-                        int64_t K_total, int64_t T, int64_t d, int64_t chan0, float sigma,
-                        uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
-                        int accumulate, void *stream) {
-    const char *fn = "dust_error_estimate";
+}  // extern "C"
+
+namespace {
+
+// dust_error_estimate (lc == nullptr: r holds the rewards) and dust_error_estimate_losses (r
+// holds the perturbed losses, lc the clean ones).
+int error_estimate_call(const char *fn, const float *lc, const float *r, float *g_hat,
+                        void *g_hat_t_bf16, int64_t K, int64_t K_total, int64_t T, int64_t d,
+                        int64_t chan0, float sigma, uint64_t seed, uint32_t tag, uint32_t draw0,
+                        uint32_t tok0, int accumulate, void *stream, bool losses) {
+    const char *rname = losses ? "loss_pert" : "r";
     if (K < 0 || T < 0 || d < 0)
         return fail(DUST_ERR_INVALID, "%s: negative size (K=%lld T=%lld d=%lld)", fn,
                     (long long)K, (long long)T, (long long)d);
@@ -287,8 +293,9 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
         return fail(DUST_ERR_INVALID, "%s: sigma must be finite and > 0", fn);
     if (int rc = check_noise_ranges(fn, T, d, chan0, K, draw0, tok0)) return rc;
     if (T == 0 || d == 0) return ok();
-    if (!g_hat || (K > 0 && !r)) return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
-    if (!elem_aligned(g_hat, 4) || (r && !elem_aligned(r, 4)) ||
+    if (!g_hat || (K > 0 && !r) || (losses && K > 0 && !lc))
+        return fail(DUST_ERR_INVALID, "%s: null pointer", fn);
+    if (!elem_aligned(g_hat, 4) || (r && !elem_aligned(r, 4)) || (lc && !elem_aligned(lc, 4)) ||
         (g_hat_t_bf16 && !elem_aligned(g_hat_t_bf16, 2)))
         return fail(DUST_ERR_INVALID, "%s: pointers must be aligned to the element size", fn);
     if (T > kMaxIdx || d > kMaxIdx || K > kMaxIdx)
@@ -299,13 +306,39 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
     if (r_bytes < 0 || g_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
     if (r && ranges_overlap(r, (size_t)r_bytes, g_hat, (size_t)g_bytes))
-        return fail(DUST_ERR_INVALID, "%s: r and g_hat overlap", fn);
+        return fail(DUST_ERR_INVALID, "%s: %s and g_hat overlap", fn, rname);
+    if (lc && ranges_overlap(lc, (size_t)T * 4, g_hat, (size_t)g_bytes))
+        return fail(DUST_ERR_INVALID, "%s: loss_clean and g_hat overlap", fn);
     if (g_hat_t_bf16 && ranges_overlap(g_hat_t_bf16, (size_t)g_bytes / 2, g_hat, (size_t)g_bytes))
         return fail(DUST_ERR_INVALID, "%s: g_hat_t_bf16 and g_hat overlap", fn);
-    return hip_status(dust::launch_error_estimate(r, g_hat, (uint16_t *)g_hat_t_bf16, K, K_total, T,
-                                                  d, chan0, sigma, make_key(seed, tag), draw0,
-                                                  tok0, accumulate != 0, (hipStream_t)stream),
+    return hip_status(dust::launch_error_estimate_losses(losses ? lc : nullptr, r, g_hat,
+                                                         (uint16_t *)g_hat_t_bf16, K, K_total, T,
+                                                         d, chan0, sigma, make_key(seed, tag),
+                                                         draw0, tok0, accumulate != 0,
+                                                         (hipStream_t)stream),
                       fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_t K,
+                        int64_t K_total, int64_t T, int64_t d, int64_t chan0, float sigma,
+                        uint64_t seed, uint32_t tag, uint32_t draw0, uint32_t tok0,
+                        int accumulate, void *stream) {
+    return error_estimate_call("dust_error_estimate", nullptr, r, g_hat, g_hat_t_bf16, K, K_total,
+                               T, d, chan0, sigma, seed, tag, draw0, tok0, accumulate, stream,
+                               false);
+}
+
+int dust_error_estimate_losses(const float *loss_clean, const float *loss_pert, float *g_hat,
+                               void *g_hat_t_bf16, int64_t K, int64_t K_total, int64_t T,
+                               int64_t d, int64_t chan0, float sigma, uint64_t seed, uint32_t tag,
+                               uint32_t draw0, uint32_t tok0, int accumulate, void *stream) {
+    return error_estimate_call("dust_error_estimate_losses", loss_clean, loss_pert, g_hat,
+                               g_hat_t_bf16, K, K_total, T, d, chan0, sigma, seed, tag, draw0,
+                               tok0, accumulate, stream, true);
 }
 
 size_t dust_weight_grad_workspace(int64_t T, int64_t d_out, int64_t d_in) {

@@ -58,6 +58,13 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
                                  float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                  bool accumulate, hipStream_t s);
 
+// The estimate with the rewards of gamma = 0 formed on load as lc[t] - lp[i][t] (lp in place of
+// r); lc == nullptr reads the rewards r themselves (launch_error_estimate).
+hipError_t launch_error_estimate_losses(const float *lc, const float *lp, float *g, uint16_t *gt,
+                                        int64_t K, int64_t K_total, int64_t T, int64_t d,
+                                        int64_t chan0, float sigma, Key key, uint32_t draw0,
+                                        uint32_t tok0, bool accumulate, hipStream_t s);
+
 size_t weight_grad_workspace_bytes(int64_t T, int64_t d_out, int64_t d_in);
 
 hipError_t launch_attn_value_scores(const uint16_t *P, const uint16_t *g, float *c, int64_t Kc,

@@ -10,14 +10,19 @@
 // kernel is bound by the generator's ALU work. The draw sum runs in fp32 in draw order per
 // element; the optional bf16 transpose g_hat^T [d, T] is written from the same registers, so
 // the contraction kernel reads its A operand K-contiguous.
+// LOSSES (gamma = 0 only): the kernel reads the perturbed losses instead of the rewards and forms
+// r = c = l_clean - l_pert on load (the same fp32 subtraction as the loss-change kernel; with
+// gamma = 0 the reward is the score), so the K x T scores and rewards are never stored. gfx950
+// has no scalar floating-point unit, so this costs one vector subtraction per token and draw.
 #include "dust_internal.hpp"
 
 namespace dust {
 namespace {
 
-template <int TPW, bool VEC>
+template <int TPW, bool VEC, bool LOSSES>
 __global__ __launch_bounds__(256) void error_estimate_kernel(
-    const float *__restrict__ r, float *__restrict__ g, uint16_t *__restrict__ gt, uint32_t K,
+    const float *__restrict__ r, const float *__restrict__ lc, float *__restrict__ g,
+    uint16_t *__restrict__ gt, uint32_t K,
     uint32_t T, uint32_t d, uint32_t q0, float scale, Key key, uint32_t draw0, uint32_t tok0,
     int accumulate, uint32_t n_ctiles) {
     // Consecutive logical waves share g_hat^T lines (neighbouring token tiles) and reward rows
@@ -53,6 +58,9 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
         }
     };
     const float *rp = r + t0;
+    float lcv[TPW];   // LOSSES: the clean losses of the tile's tokens
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) lcv[tt] = (LOSSES && tt < (int)ntok) ? lc[t0 + tt] : 0.f;
     if (ntok == TPW) {
         // whole tile: a draw's TPW rewards are one contiguous row piece, fetched by one scalar
         // load one draw ahead of their use
@@ -61,7 +69,7 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
         for (uint32_t i = 0; i < K; ++i) {
             float rv[TPW];
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) rv[tt] = next[tt];
+            for (int tt = 0; tt < TPW; ++tt) rv[tt] = LOSSES ? lcv[tt] - next[tt] : next[tt];
             if (i + 1 < K) next = *(const f32xT *)(rp + (uint64_t)(i + 1) * T);
             accumulate_draw(draw0 + i, rv);
         }
@@ -69,7 +77,8 @@ __global__ __launch_bounds__(256) void error_estimate_kernel(
         for (uint32_t i = 0; i < K; ++i, rp += T) {
             float rv[TPW];
 #pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) rv[tt] = (tt < (int)ntok) ? rp[tt] : 0.f;
+            for (int tt = 0; tt < TPW; ++tt)
+                rv[tt] = (tt < (int)ntok) ? (LOSSES ? lcv[tt] - rp[tt] : rp[tt]) : 0.f;
             accumulate_draw(draw0 + i, rv);
         }
     }
@@ -144,6 +153,14 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
                                  int64_t K_total, int64_t T, int64_t d, int64_t chan0,
                                  float sigma, Key key, uint32_t draw0, uint32_t tok0,
                                  bool accumulate, hipStream_t s) {
+    return launch_error_estimate_losses(nullptr, r, g, gt, K, K_total, T, d, chan0, sigma, key,
+                                        draw0, tok0, accumulate, s);
+}
+
+hipError_t launch_error_estimate_losses(const float *lc, const float *r, float *g, uint16_t *gt,
+                                        int64_t K, int64_t K_total, int64_t T, int64_t d,
+                                        int64_t chan0, float sigma, Key key, uint32_t draw0,
+                                        uint32_t tok0, bool accumulate, hipStream_t s) {
     if (K == 0 && !accumulate) {
         const uint64_t n = (uint64_t)T * (uint64_t)d;
         zero_estimate_kernel<<<(uint32_t)((n + 255) / 256), 256, 0, s>>>(g, gt, n);
@@ -160,15 +177,21 @@ hipError_t launch_error_estimate(const float *r, float *g, uint16_t *gt, int64_t
     const uint64_t waves = (uint64_t)((T + tpw - 1) / tpw) * n_ctiles;
     const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-#define DUST_EE(TP, V)                                                                         \
-    error_estimate_kernel<TP, V><<<blocks, 256, 0, s>>>(r, g, gt, (uint32_t)K, (uint32_t)T,    \
-                                                        (uint32_t)d, q0, scale, key, draw0,    \
-                                                        tok0, accumulate ? 1 : 0, n_ctiles)
-    if (vec) {
-        if (tpw == 8) DUST_EE(8, true); else DUST_EE(4, true);
-    } else {
-        if (tpw == 8) DUST_EE(8, false); else DUST_EE(4, false);
-    }
+#define DUST_EE(TP, V, L)                                                                      \
+    error_estimate_kernel<TP, V, L><<<blocks, 256, 0, s>>>(r, lc, g, gt, (uint32_t)K,          \
+                                                           (uint32_t)T, (uint32_t)d, q0, scale, \
+                                                           key, draw0, tok0,                   \
+                                                           accumulate ? 1 : 0, n_ctiles)
+#define DUST_EE_TV(L)                                                                          \
+    do {                                                                                       \
+        if (vec) {                                                                             \
+            if (tpw == 8) DUST_EE(8, true, L); else DUST_EE(4, true, L);                       \
+        } else {                                                                               \
+            if (tpw == 8) DUST_EE(8, false, L); else DUST_EE(4, false, L);                     \
+        }                                                                                      \
+    } while (0)
+    if (lc != nullptr) DUST_EE_TV(true); else DUST_EE_TV(false);
+#undef DUST_EE_TV
 #undef DUST_EE
     return hipGetLastError();
 }

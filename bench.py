@@ -111,6 +111,10 @@ def parse():
                          "(GELU, then [d_in x d_out]): 'fused' with dust_perturbed_linear "
                          "(noise regenerated in the matrix-core operand path, y' never written), "
                          "'unfused' as dust_noise_inject + torch GELU + torch matmul")
+    ap.add_argument("--fold", action="store_true",
+                    help="loss-scored workloads with gamma = 0 (2, 3, 5): form the scores inside "
+                         "the error estimate (dust_error_estimate_losses) instead of running "
+                         "dust_loss_reward first")
     ap.add_argument("--unfused", action="store_true",
                     help="loss mode: run the loss change and the reward scan as two kernels "
                          "instead of dust_loss_reward")
@@ -138,6 +142,7 @@ class Chain:
         self.c = synth.CONFIGS[cfg_id]
         self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
         self.fused = True   # loss mode: scores and rewards in one pass (dust_loss_reward)
+        self.fold = False   # gamma = 0: scores formed inside the error estimate
 
     # ---- optional optimizer step on the estimate (dust_sgd_momentum / dust_adam)
     optimizer = "none"
@@ -218,16 +223,21 @@ class LinearChain(Chain):
                 run("torch_gelu_matmul", lambda: t.matmul(
                     t.nn.functional.gelu(self.ybuf, approximate="tanh"), self.wn.t(),
                     out=self.dbuf))
-        if self.fused:
-            run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.rbuf, K, T, self.S,
-                self.gamma, sh)
+        if self.fold:
+            run("dust_error_estimate_losses", d.dust_error_estimate_losses, self.lc, self.lp,
+                self.gh, self.ght, K, K, T, self.d_out, 0, self.sigma, self.seed, self.tag, 0, 0,
+                0, sh)
         else:
-            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None,
-                None, d.DUST_F32, self.cbuf, K, T, 0, sh)
-            run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.rbuf, K, T, self.S,
-                self.gamma, sh)
-        run("dust_error_estimate", d.dust_error_estimate, self.rbuf, self.gh, self.ght, K, K, T,
-            self.d_out, 0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
+            if self.fused:
+                run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.rbuf, K, T,
+                    self.S, self.gamma, sh)
+            else:
+                run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp,
+                    None, None, d.DUST_F32, self.cbuf, K, T, 0, sh)
+                run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.rbuf, K, T, self.S,
+                    self.gamma, sh)
+            run("dust_error_estimate", d.dust_error_estimate, self.rbuf, self.gh, self.ght, K, K,
+                T, self.d_out, 0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
         run("dust_weight_grad", d.dust_weight_grad, self.ght, self.x, self.G, T, self.d_out, self.d_in,
             self.ws, self.ws_bytes, sh)
 
@@ -242,6 +252,7 @@ class LinearChain(Chain):
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_loss_reward": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_error_estimate": _alu(K * T * do, OPS_EE_EXTRA),
+            "dust_error_estimate_losses": _alu(K * T * do, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * do * self.d_in),
             # the down-projection of the block's activated perturbed outputs
             "dust_perturbed_linear": _mfma(2.0 * self.KB * T * do * self.d_in),
@@ -321,16 +332,21 @@ class HeadChain(Chain):
         d, T, K = self.dust, self.T, self.K
         run("dust_head_ce_chunk", d.dust_head_ce_chunk, self.z, self.tgt, self.lp, self.lc, T, self.V,
             self.v0, self.C, K, self.sigma, self.seed, self.tag, 0, 0, sh)
-        if self.fused:
-            run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.cbuf, K, T, self.S,
-                self.gamma, sh)
+        if self.fold:
+            run("dust_error_estimate_losses", d.dust_error_estimate_losses, self.lc, self.lp,
+                self.gh, self.ght, K, K, T, self.C, self.v0, self.sigma, self.seed, self.tag, 0, 0,
+                0, sh)
         else:
-            run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp, None,
-                None, d.DUST_F32, self.cbuf, K, T, 0, sh)
-            run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S,
-                self.gamma, sh)
-        run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K, T, self.C,
-            self.v0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
+            if self.fused:
+                run("dust_loss_reward", d.dust_loss_reward, self.lc, self.lp, self.cbuf, K, T,
+                    self.S, self.gamma, sh)
+            else:
+                run("dust_loss_delta", d.dust_loss_delta, d.DUST_DELTA_LOSS, self.lc, self.lp,
+                    None, None, d.DUST_F32, self.cbuf, K, T, 0, sh)
+                run("dust_reward_scan", d.dust_reward_scan, self.cbuf, self.cbuf, K, T, self.S,
+                    self.gamma, sh)
+            run("dust_error_estimate", d.dust_error_estimate, self.cbuf, self.gh, self.ght, K, K,
+                T, self.C, self.v0, self.sigma, self.seed, self.tag, 0, 0, 0, sh)
         run("dust_weight_grad", d.dust_weight_grad, self.ght, self.h, self.G, T, self.C, self.H,
             self.ws, self.ws_bytes, sh)
 
@@ -345,6 +361,7 @@ class HeadChain(Chain):
             "dust_reward_scan": _hbm(8.0 * K * T),
             "dust_loss_reward": _hbm((8.0 + 4.0 / K) * K * T),
             "dust_error_estimate": _alu(K * T * C, OPS_EE_EXTRA),
+            "dust_error_estimate_losses": _alu(K * T * C, OPS_EE_EXTRA),
             "dust_weight_grad": _mfma(2.0 * T * C * self.H),
         }
 
@@ -594,6 +611,12 @@ def main() -> int:
 
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
+    if args.fold:
+        if args.workload not in (2, 3, 5) or chain.c["gamma"] != 0.0:
+            print("--fold applies to the loss-scored workloads with gamma = 0 (2, 3, 5)",
+                  file=sys.stderr)
+            return 2
+        chain.fold = True
     if args.downstream != "none":
         if args.workload not in (2, 5):
             print("--downstream applies to the MLP workloads 2 and 5 only", file=sys.stderr)
@@ -678,7 +701,8 @@ def main() -> int:
     cfg["precision"] = ("bf16 activations, perturbed outputs and matrix-core operands; fp32 "
                         "noise, scores, rewards, output error and accumulation")
     if args.workload != 4:
-        cfg["loss_to_reward"] = "one kernel" if chain.fused else "two kernels"
+        cfg["loss_to_reward"] = ("inside the error estimate" if chain.fold else
+                                 "one kernel" if chain.fused else "two kernels")
     if chain.optimizer != "none":
         cfg["optimizer"] = chain.optimizer
     line = {
@@ -698,7 +722,7 @@ def main() -> int:
 KERNEL_SOURCES = {
     "dust_noise_inject": "noise.hip", "dust_loss_delta": "delta_scan.hip",
     "dust_reward_scan": "delta_scan.hip", "dust_loss_reward": "delta_scan.hip",
-    "dust_error_estimate": "error_estimate.hip",
+    "dust_error_estimate": "error_estimate.hip", "dust_error_estimate_losses": "error_estimate.hip",
     "dust_weight_grad": "weight_grad.hip", "dust_head_ce_chunk": "head_ce.hip",
     "dust_sgd_momentum": "optim.hip", "dust_adam": "optim.hip",
     "dust_attn_value_scores": "attn_scores.hip", "dust_attn_key_scores": "attn_scores.hip",

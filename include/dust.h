@@ -183,6 +183,23 @@ int dust_error_estimate(const float *r, float *g_hat, void *g_hat_t_bf16, int64_
                         int accumulate, void *stream);
 
 /*
+ * dust_error_estimate_losses -- dust_loss_delta (loss mode), dust_reward_scan with gamma = 0 and
+ * dust_error_estimate in one pass (explainer, "Credit assignment": with gamma = 0 a token's
+ * reward is its own loss reduction c = l_clean - l_pert):
+ *     g_hat[t][j] = -(1 / (K_total * sigma)) * sum_{i < K} (loss_clean[t] - loss_pert[i][t])
+ *                   * a^{(draw0+i)}_{t, chan0+j}
+ * The scores are formed on load (the same fp32 subtraction as dust_loss_delta) and never
+ * stored, so no [K, T] score or reward array is needed; the result equals dust_loss_delta
+ * followed by dust_error_estimate bit for bit. Arguments as dust_error_estimate, with
+ *   loss_clean  [T] fp32, loss_pert [K, T] fp32                                          (in)
+ * in place of r. Only gamma = 0: a discounted reward needs the scan (dust_loss_reward).
+ */
+int dust_error_estimate_losses(const float *loss_clean, const float *loss_pert, float *g_hat,
+                               void *g_hat_t_bf16, int64_t K, int64_t K_total, int64_t T,
+                               int64_t d, int64_t chan0, float sigma, uint64_t seed, uint32_t tag,
+                               uint32_t draw0, uint32_t tok0, int accumulate, void *stream);
+
+/*
  * dust_weight_grad_workspace -- bytes of device workspace dust_weight_grad needs for this
  * shape (0 when none, and for shapes dust_weight_grad rejects). Host-only; never fails.
  */

@@ -101,6 +101,10 @@ INVALID = [
     ("dust_weight_grad", (None, FAKE2, FAKE2 + (1 << 30), 64, 8, 8, None, 0, None), 1, "null"),
     ("dust_weight_grad", (FAKE, FAKE2, FAKE, 64, 8, 8, None, 0, None), 1, "overlap"),
     ("dust_weight_grad", (FAKE, FAKE2, FAKE2 + (1 << 30), 4096, 256, 256, FAKE2, 1 << 30, None), 1, "workspace overlaps"),
+    ("dust_error_estimate_losses", (None, FAKE, FAKE2, None, 4, 4, 64, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "null"),
+    ("dust_error_estimate_losses", (FAKE, FAKE, FAKE2, None, 4, 2, 64, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "K_total"),
+    ("dust_error_estimate_losses", (FAKE, FAKE2, FAKE2, None, 4, 4, 64, 8, 0, 0.1, 1, 1, 0, 0, 0, None), 1, "overlap"),
+    ("dust_error_estimate_losses", (FAKE, FAKE, FAKE2, None, 4, 4, 64, 8, 0, 0.0, 1, 1, 0, 0, 0, None), 1, "sigma"),
     ("dust_weight_grad_noalloc", (FAKE, FAKE2, FAKE2 + (1 << 32), 16384, 768, 11008, None), 2, "scratch"),
     ("dust_weight_grad_noalloc", (FAKE, FAKE2, FAKE2 + (1 << 32), -1, 8, 8, None), 1, "negative"),
     ("dust_weight_grad_noalloc", (None, FAKE2, FAKE2 + (1 << 32), 64, 8, 8, None), 1, "null"),
@@ -188,6 +192,7 @@ ZERO_SIZE = [
     ("dust_error_estimate", (None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_weight_grad", (None, None, None, 64, 0, 8, None, 0, None)),
     ("dust_weight_grad_noalloc", (None, None, None, 64, 0, 8, None)),
+    ("dust_error_estimate_losses", (None, None, None, None, 4, 4, 0, 8, 0, 0.1, 1, 1, 0, 0, 0, None)),
     ("dust_head_ce_chunk", (None, None, None, None, 0, 100, 0, 8, 2, 0.1, 1, 1, 0, 0, None)),
     ("dust_noise_words", (None, 0, 4, 4, 0, 1, 1, 0, 0, None)),
 ]

@@ -341,6 +341,39 @@ def test_weight_grad_zero_tokens_writes_zero():
     assert torch.all(G == 0)
 
 
+# ------------------------------------------------------------------------------ scores folded into the estimate
+@pytest.mark.parametrize("K,T,d,chan0,draw0,tok0", [
+    (5, 96, 256, 0, 0, 0),
+    (7, 37, 70, 8, 3, 11),        # ragged token tile and channel group
+    (33, 4096, 512, 4, 100, 0),   # several channel tiles, 8-token tiles
+])
+def test_error_estimate_losses_equals_loss_delta_then_estimate(K, T, d, chan0, draw0, tok0):
+    announce("error_estimate_losses %s" % ((K, T, d, chan0, draw0, tok0),))
+    g = np.random.default_rng(33)
+    seed, tag, sigma = 0x5EED, 2, 0.05
+    lc = (8.0 + g.standard_normal(T)).astype(np.float32)
+    lp = (lc + 0.05 * g.standard_normal((K, T))).astype(np.float32)
+    c = torch.empty((K, T), dtype=torch.float32, device=DEV)
+    dust.dust_loss_delta(dust.DUST_DELTA_LOSS, f32(lc), f32(lp), None, None, dust.DUST_F32, c, K, T, 0)
+    g1 = torch.empty((T, d), device=DEV)
+    t1 = torch.empty((d, T), dtype=torch.bfloat16, device=DEV)
+    dust.dust_error_estimate(c, g1, t1, K, 2 * K, T, d, chan0, sigma, seed, tag, draw0, tok0, 0)
+    g2 = torch.full((T, d), float("nan"), device=DEV)
+    t2 = torch.empty((d, T), dtype=torch.bfloat16, device=DEV)
+    dust.dust_error_estimate_losses(f32(lc), f32(lp), g2, t2, K, 2 * K, T, d, chan0, sigma, seed,
+                                    tag, draw0, tok0, 0)
+    assert torch.equal(g1, g2) and torch.equal(t1.view(torch.int16), t2.view(torch.int16))
+    # a second block of draws accumulated, as with chunked populations
+    dust.dust_error_estimate_losses(f32(lc), f32(lp), g2, None, K, 2 * K, T, d, chan0, sigma, seed,
+                                    tag, draw0 + K, tok0, 1)
+    # the second block's draws draw0 + K .. reuse the same losses
+    ref = (oracle.error_estimate(oracle.loss_delta_loss(lc, lp), d, sigma, seed, tag, draw0=draw0,
+                                 tok0=tok0, chan0=chan0, K_total=2 * K)
+           + oracle.error_estimate(oracle.loss_delta_loss(lc, lp), d, sigma, seed, tag,
+                                   draw0=draw0 + K, tok0=tok0, chan0=chan0, K_total=2 * K))
+    assert frob_rel(host_f32(g2), ref) <= 1e-5
+
+
 # ------------------------------------------------------------------------------ LM-head chunk
 @pytest.mark.parametrize("T,V,v0,C,Kc", [
     (37, 1000, 200, 300, 5),
