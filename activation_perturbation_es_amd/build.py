@@ -48,6 +48,22 @@ def _compile(src: str) -> str:
     return obj
 
 
+PROBES_SRC = "probes.hip"
+PROBES_LIB = os.path.join(PKG, "libdust_probes.so")
+
+
+def build_probes() -> str:
+    """Compile the ceiling probes (bench.py --ceilings) into libdust_probes.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    tmp = PROBES_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBES_SRC), "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (PROBES_SRC, " ".join(cmd), r.stderr))
+    os.replace(tmp, PROBES_LIB)
+    return PROBES_LIB
+
+
 def build(force: bool = True) -> str:
     """Compile every source and link libdust.so. Always recompiles when force is True."""
     os.makedirs(BUILD, exist_ok=True)

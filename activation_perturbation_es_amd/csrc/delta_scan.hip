@@ -271,36 +271,31 @@ __global__ __launch_bounds__(256) void loss_delta_inner_long_kernel(const void *
 }
 
 // ---------------------------------------------------------------- reverse segmented gamma-scan
-// A unit is one (draw, sequence) pair. The grid holds at most as many waves as the chip keeps
-// resident (nwaves); wave w takes units w, w + nwaves, w + 2 nwaves, ... so that every wave is
-// started once and the whole array streams in one round, and a wave's next unit is loaded while
-// the current one is scanned and stored (sequences of up to 4 chunks; longer ones stream chunk
-// by chunk). A sequence is processed in chunks of 64*VEC elements from its end towards its
-// start. Inside a chunk each lane owns VEC consecutive elements and forms their local suffix
-// sums; the lanes then combine with a Hillis-Steele scan over the affine carry (the block of
-// lane l+off contributes gamma^(VEC*off) times its running sum), and the value at the chunk's
-// first element is carried into the next chunk. gamma powers come from repeated squaring:
-// gp[b] = gamma^(VEC * 2^b).
+// One wave per (draw, sequence). The sequence is processed in chunks of 64*VEC elements from its
+// end towards its start. Inside a chunk each lane owns VEC consecutive elements and forms their
+// local suffix sums; the lanes then combine with a Hillis-Steele scan over the affine carry
+// (the block of lane l+off contributes gamma^(VEC*off) times its running sum), and the value at
+// the chunk's first element is carried into the next chunk. gamma powers come from repeated
+// squaring: gp[b] = gamma^(VEC * 2^b).
 // LOSSES: the scores are not read but formed on load from the losses, c = l_clean - l_pert
 // (c then points at l_pert [K, T] and lc at l_clean [T]); the same fp32 subtraction as the
 // loss-change kernel, so the fused rewards equal the two-kernel ones bit for bit.
 template <int VEC, bool LOSSES>
 __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, const float *lc,
                                                           float *r, uint32_t K, uint32_t T,
-                                                          uint32_t seg_len, float gamma,
-                                                          uint32_t nwaves) {
+                                                          uint32_t seg_len, float gamma) {
     const uint32_t nseg = T / seg_len;
-    const uint64_t units = (uint64_t)K * nseg;
-    const uint32_t w0 = blockIdx.x * 4u + wave_in_block();
-    if (w0 >= nwaves) return;
+    const uint64_t w = (uint64_t)blockIdx.x * 4u + wave_in_block();
+    if (w >= (uint64_t)K * nseg) return;
+    const uint32_t i = (uint32_t)(w / nseg);
+    const uint32_t b = (uint32_t)(w % nseg);
     const uint32_t lane = threadIdx.x & 63u;
-    // the VEC scores of positions pos .. pos+VEC-1 of unit u's sequence
-    auto load = [&](uint64_t u, int64_t pos, float (&v)[VEC]) {
-        const uint32_t i = (uint32_t)(u / nseg), b = (uint32_t)(u % nseg);
-        const uint64_t at = (uint64_t)i * T + (uint64_t)b * seg_len + pos;
-        const float *lseg = lc + (uint64_t)b * seg_len;
+    const uint64_t seg_base = (uint64_t)i * T + (uint64_t)b * seg_len;
+    const float *lseg = lc + (uint64_t)b * seg_len;   // l_clean of this sequence (LOSSES)
+    // the VEC scores of sequence positions pos .. pos+VEC-1
+    auto load = [&](int64_t pos, float (&v)[VEC]) {
         if constexpr (VEC == 4) {
-            const f32x4 x = *(const f32x4 *)(c + at);
+            const f32x4 x = *(const f32x4 *)(c + seg_base + pos);
             if constexpr (LOSSES) {
                 const f32x4 l = *(const f32x4 *)(lseg + pos);
 #pragma unroll
@@ -310,7 +305,7 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, const 
                 for (int e = 0; e < 4; ++e) v[e] = x[e];
             }
         } else {
-            v[0] = LOSSES ? lseg[pos] - c[at] : c[at];
+            v[0] = LOSSES ? lseg[pos] - c[seg_base + pos] : c[seg_base + pos];
         }
     };
 
@@ -332,10 +327,40 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, const 
     }
 
     constexpr uint32_t CH = 64u * VEC;
+    // Sequences of up to PRE chunks are loaded up front (all loads in flight at once); longer
+    // ones stream chunk by chunk.
     constexpr uint32_t PRE = 4;
-    // Scan one chunk given this lane's VEC scores, the carry from the chunk after it; store it
-    // and return the carry into the chunk before it.
-    auto scan_chunk = [&](uint64_t u, int64_t pos, float (&v)[VEC], float carry) {
+    float pre[PRE][VEC];
+    const bool preload = seg_len <= PRE * CH;
+    if (preload) {
+#pragma unroll
+        for (uint32_t ch = 0; ch < PRE; ++ch) {
+            const int64_t pos = (int64_t)seg_len - (int64_t)(ch + 1) * CH + (int64_t)lane * VEC;
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) pre[ch][e] = 0.f;
+            if (ch * CH < seg_len && pos >= 0) load(pos, pre[ch]);
+        }
+    }
+    float carry = 0.f;  // r at the first element after the current chunk (0 past the end)
+    for (uint32_t done = 0, ch = 0; done < seg_len; done += CH, ++ch) {
+        // chunk covers sequence positions [seg_len - done - CH, seg_len - done)
+        const int64_t start = (int64_t)seg_len - (int64_t)done - (int64_t)CH;
+        const int64_t pos = start + (int64_t)lane * VEC;   // first element of this lane
+        float v[VEC];
+        const bool in = pos >= 0;    // with VEC > 1, seg_len % VEC == 0, so a lane is all in or out
+        if (preload) {
+#pragma unroll
+            for (uint32_t q = 0; q < PRE; ++q)
+                if (q == ch) {
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) v[e] = pre[q][e];
+                }
+        } else if (in) {
+            load(pos, v);
+        } else {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = 0.f;
+        }
         // local suffix sums inside the lane
 #pragma unroll
         for (int e = VEC - 2; e >= 0; --e) v[e] = __builtin_fmaf(gamma, v[e + 1], v[e]);
@@ -353,67 +378,15 @@ __global__ __launch_bounds__(256) void reward_scan_kernel(const float *c, const 
         after = __builtin_fmaf(glane, carry, after);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) v[e] = __builtin_fmaf(gpow[VEC - e], after, v[e]);
-        if (pos >= 0) {   // with VEC > 1, seg_len % VEC == 0, so a lane is all in or out
-            const uint32_t i = (uint32_t)(u / nseg), b = (uint32_t)(u % nseg);
-            float *dst = r + (uint64_t)i * T + (uint64_t)b * seg_len + pos;
+        if (in) {
             if constexpr (VEC == 4) {
                 const f32x4 o = {v[0], v[1], v[2], v[3]};
-                *(f32x4 *)dst = o;
+                *(f32x4 *)(r + seg_base + pos) = o;
             } else {
-                dst[0] = v[0];
+                r[seg_base + pos] = v[0];
             }
         }
-        return __shfl(v[0], 0);
-    };
-
-    if (seg_len <= PRE * CH) {
-        // whole sequences in registers: all of a unit's loads are issued at once, and the next
-        // unit's loads are issued before the current unit is scanned
-        auto load_unit = [&](uint64_t u, float (&pre)[PRE][VEC]) {
-#pragma unroll
-            for (uint32_t ch = 0; ch < PRE; ++ch) {
-                const int64_t pos = (int64_t)seg_len - (int64_t)(ch + 1) * CH + (int64_t)lane * VEC;
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) pre[ch][e] = 0.f;
-                if (ch * CH < seg_len && pos >= 0) load(u, pos, pre[ch]);
-            }
-        };
-        auto scan_unit = [&](uint64_t u, float (&pre)[PRE][VEC]) {
-            float carry = 0.f;  // r at the first element after the current chunk (0 past the end)
-#pragma unroll
-            for (uint32_t ch = 0; ch < PRE; ++ch) {
-                if (ch * CH >= seg_len) break;
-                const int64_t pos = (int64_t)seg_len - (int64_t)(ch + 1) * CH + (int64_t)lane * VEC;
-                carry = scan_chunk(u, pos, pre[ch], carry);
-            }
-        };
-        float bufa[PRE][VEC], bufb[PRE][VEC];
-        uint64_t u = w0;
-        load_unit(u, bufa);
-        for (;;) {
-            const uint64_t u1 = u + nwaves;
-            if (u1 < units) load_unit(u1, bufb);
-            scan_unit(u, bufa);
-            if (u1 >= units) break;
-            const uint64_t u2 = u1 + nwaves;
-            if (u2 < units) load_unit(u2, bufa);
-            scan_unit(u1, bufb);
-            if (u2 >= units) break;
-            u = u2;
-        }
-    } else {
-        for (uint64_t u = w0; u < units; u += nwaves) {
-            float carry = 0.f;
-            for (uint32_t done = 0; done < seg_len; done += CH) {
-                // chunk covers sequence positions [seg_len - done - CH, seg_len - done)
-                const int64_t pos = (int64_t)seg_len - (int64_t)done - (int64_t)CH + (int64_t)lane * VEC;
-                float v[VEC];
-#pragma unroll
-                for (int e = 0; e < VEC; ++e) v[e] = 0.f;
-                if (pos >= 0) load(u, pos, v);
-                carry = scan_chunk(u, pos, v, carry);
-            }
-        }
+        carry = __shfl(v[0], 0);
     }
 }
 
@@ -488,44 +461,22 @@ hipError_t launch_reward_scan(const float *c, float *r, int64_t K, int64_t T, in
     return launch_loss_reward(nullptr, c, r, K, T, seg_len, gamma, s);
 }
 
-// Waves of one scan instantiation the current device keeps resident at once (its compute units
-// times the blocks of 4 waves each holds at that kernel's register use), queried once.
-template <int VEC, bool LOSSES>
-int64_t scan_resident_waves() {
-    static const int64_t waves = [] {
-        int dev = 0, cus = 0, per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reward_scan_kernel<VEC, LOSSES>,
-                                                         256, 0) != hipSuccess ||
-            cus <= 0 || per_cu <= 0)
-            return (int64_t)256 * 4 * 4;   // a conservative round if the queries fail
-        return (int64_t)cus * per_cu * 4;
-    }();
-    return waves;
-}
-
-template <int VEC, bool LOSSES>
-hipError_t launch_scan(const float *lc, const float *c, float *r, int64_t K, int64_t T,
-                       int64_t seg_len, float gamma, hipStream_t s) {
-    const int64_t units = K * (T / seg_len);
-    const int64_t resident = scan_resident_waves<VEC, LOSSES>();
-    const uint32_t nwaves = (uint32_t)(units < resident ? units : resident);
-    const uint32_t blocks = (nwaves + 3u) / 4u;
-    reward_scan_kernel<VEC, LOSSES><<<blocks, 256, 0, s>>>(c, lc, r, (uint32_t)K, (uint32_t)T,
-                                                           (uint32_t)seg_len, gamma, nwaves);
-    return hipGetLastError();
-}
-
 hipError_t launch_loss_reward(const float *lc, const float *c, float *r, int64_t K, int64_t T,
                               int64_t seg_len, float gamma, hipStream_t s) {
+    const int64_t waves = K * (T / seg_len);
+    const uint32_t blocks = (uint32_t)((waves + 3) / 4);
     const bool vec = (seg_len % 4 == 0) && aligned16(c) && aligned16(r) &&
                      (lc == nullptr || aligned16(lc));
-    if (lc != nullptr)
-        return vec ? launch_scan<4, true>(lc, c, r, K, T, seg_len, gamma, s)
-                   : launch_scan<1, true>(lc, c, r, K, T, seg_len, gamma, s);
-    return vec ? launch_scan<4, false>(lc, c, r, K, T, seg_len, gamma, s)
-               : launch_scan<1, false>(lc, c, r, K, T, seg_len, gamma, s);
+#define DUST_SCAN(V, L)                                                                        \
+    reward_scan_kernel<V, L><<<blocks, 256, 0, s>>>(c, lc, r, (uint32_t)K, (uint32_t)T,        \
+                                                    (uint32_t)seg_len, gamma)
+    if (lc != nullptr) {
+        if (vec) DUST_SCAN(4, true); else DUST_SCAN(1, true);
+    } else {
+        if (vec) DUST_SCAN(4, false); else DUST_SCAN(1, false);
+    }
+#undef DUST_SCAN
+    return hipGetLastError();
 }
 
 }  // namespace dust

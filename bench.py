@@ -88,6 +88,11 @@ def parse():
     ap.add_argument("--cpu-scale", type=float, default=1.0,
                     help="scale of the CPU oracle's sample (1.0 = about 10-30 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of an estimate, measure the denominators the design notes read "
+                         "fractions against: a 1 GiB device copy (GB/s), the library's noise "
+                         "generator alone (normals/s) and back-to-back bf16 MFMAs on random "
+                         "operands (TFLOP/s); prints one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--optimizer", choices=("none", "sgd", "adam"), default="none",
@@ -583,6 +588,60 @@ class InnerChain(Chain):
 CHAINS = {2: LinearChain, 3: HeadChain, 4: InnerChain, 5: LinearChain}
 
 
+def ceilings(torch, dev) -> dict:
+    """The measured ceilings: a device copy, the noise generator alone and the matrix cores alone
+    (activation_perturbation_es_amd/csrc/probes.hip), each run until the clock has settled and
+    then timed with HIP events; medians of 10 launches."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "activation_perturbation_es_amd", "libdust_probes.so"))
+    lib.dust_probe_generator.argtypes = [ctypes.c_void_p, ctypes.c_uint32, ctypes.c_uint32,
+                                         ctypes.c_void_p]
+    lib.dust_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint32,
+                                    ctypes.c_uint32, ctypes.c_void_p]
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, warm=20, n=10):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return float(np.median(ts))
+
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)          # 1 GiB
+    b = torch.empty_like(a)
+    t_copy = timed(lambda: b.copy_(a))
+    del a, b
+    gb, gd = 8192, 2048                                                 # 32 waves per CU
+    gout = torch.empty(gb * 256, dtype=torch.float32, device=dev)
+    t_gen = timed(lambda: lib.dust_probe_generator(gout.data_ptr(), gb, gd, sh))
+    mb, mi = 256, 8192                                                  # one wave per SIMD
+    src = torch.randn(mb * 256 * 16, device=dev).to(torch.bfloat16)
+    mout = torch.empty(mb * 256, dtype=torch.float32, device=dev)
+    t_mfma = timed(lambda: lib.dust_probe_mfma(src.data_ptr(), mout.data_ptr(), mb, mi, sh))
+    normals = gb * 256 * 4 * gd
+    flops = mb * 4 * mi * 16 * 32768
+    copy_gbs = 2.0 * (1 << 30) / t_copy / 1e9
+    return {
+        "device_copy": {"GB_per_s": round(copy_gbs, 1), "frac_of_hbm_peak":
+                        round(copy_gbs / HBM_PEAK_GBS, 4), "bytes_moved": 2 * (1 << 30)},
+        "noise_generator": {"normals_per_s": float("%.4g" % (normals / t_gen)),
+                            "ops_per_s_at_13_per_normal": float("%.4g" % (13 * normals / t_gen)),
+                            "frac_of_valu_peak": round(13 * normals / t_gen / 1e12 / VALU_PEAK_TOPS, 4),
+                            "normals": normals},
+        "mfma_bf16_random_operands": {"TFLOP_per_s": round(flops / t_mfma / 1e12, 1),
+                                      "frac_of_peak": round(flops / t_mfma / 1e12 /
+                                                            BF16_MFMA_PEAK_TFLOPS, 4),
+                                      "flops": flops},
+    }
+
+
 def cfg_name(chain) -> str:
     """The workload name the bench line carries (and profiles/traffic.json is keyed by)."""
     return chain.config()["workload"]
@@ -602,6 +661,9 @@ def main() -> int:
     import activation_perturbation_es_amd as dust
 
     dev = "cuda:0"
+    if args.ceilings:
+        print(json.dumps({"ceilings": ceilings(torch, dev), "n_gpus": 1}), flush=True)
+        return 0
     if args.calibrate_copy:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         b = torch.empty_like(a)

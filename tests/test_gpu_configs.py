@@ -181,6 +181,38 @@ def test_w4_inner_scores():
     assert frob_rel(host_f32(cd), ref) <= 1e-5
 
 
+def test_w4_inner_scores_bench_launch():
+    """The attention workload's inner-product scores in the bench's own launch: 512 draws at the
+    full T x d (the kernel splits the draws 8 ways at this size). The 4.3-billion-element output
+    change is built on the device by plain torch from a host block D [7, T, d]:
+    delta_o[i][s] = D[i % 7][(s - i) mod T] (a per-draw roll, so every (draw, token) pair is
+    distinct); sampled scores are checked against the oracle on the host copy of D."""
+    announce("w4 inner scores, 512-draw launch")
+    c = synth.CONFIGS[4]
+    T, d, std, Kb = c["T"], c["d"], c["delta_o_std"], 512
+    g = synth.rng(4, 3)
+    go = synth.normal_bf16(g, (T, d))
+    D = synth.normal_bf16(g, (7, T, d), std)
+    Dd = bf16(D)
+    do = torch.empty((Kb, T, d), dtype=torch.bfloat16, device=DEV)
+    for i in range(Kb):
+        do[i] = torch.roll(Dd[i % 7], shifts=i, dims=0)
+    del Dd
+    cd = torch.full((Kb, T), float("nan"), dtype=torch.float32, device=DEV)
+    dust.dust_loss_delta(dust.DUST_DELTA_INNER, None, None, do, bf16(go), dust.DUST_BF16, cd, Kb,
+                         T, d)
+    got = host_f32(cd)
+    del do
+    assert np.all(np.isfinite(got))
+    rs = np.random.default_rng(406)
+    k = np.concatenate([[0, Kb - 1, 7, 255], rs.integers(0, Kb, 60)])
+    t = np.concatenate([[0, T - 1, 16383, 8192], rs.integers(0, T, 60)])
+    ref = np.array([oracle.loss_delta_inner(bits_to_f64(D[i % 7][(s - i) % T])[None, None, :],
+                                            bits_to_f64(go[s])[None, :])[0, 0]
+                    for i, s in zip(k, t)])
+    assert frob_rel(got[k, t], ref) <= 1e-5
+
+
 def test_w4_scan():
     announce("w4 scan")
     c = synth.CONFIGS[4]
