@@ -628,7 +628,9 @@ def ceilings(torch, dev) -> dict:
     normals = gb * 256 * 4 * gd
     flops = mb * 4 * mi * 16 * 32768
     copy_gbs = 2.0 * (1 << 30) / t_copy / 1e9
+    clock = clock_under_load(torch, dev, lib, timed)
     return {
+        "clock_under_load": clock,
         "device_copy": {"GB_per_s": round(copy_gbs, 1), "frac_of_hbm_peak":
                         round(copy_gbs / HBM_PEAK_GBS, 4), "bytes_moved": 2 * (1 << 30)},
         "noise_generator": {"normals_per_s": float("%.4g" % (normals / t_gen)),
@@ -640,6 +642,50 @@ def ceilings(torch, dev) -> dict:
                                                             BF16_MFMA_PEAK_TFLOPS, 4),
                                       "flops": flops},
     }
+
+
+def clock_under_load(torch, dev, lib, timed) -> dict:
+    """Shader clock and rates while four waves per CU issue MFMAs and four read LDS (or idle),
+    and while all eight read LDS: per-wave s_memtime cycles over s_memrealtime ticks, averaged
+    over the 256 blocks (one per CU) of the last of the timed launches."""
+    import ctypes
+    lib.dust_probe_clock.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
+    lib.dust_probe_wallclock_khz.restype = ctypes.c_int
+    khz = lib.dust_probe_wallclock_khz()
+    if khz <= 0:
+        raise RuntimeError("hipDeviceAttributeWallClockRate unavailable")
+    sh = torch.cuda.current_stream().cuda_stream
+    blocks, iters = 256, 4000
+    out = torch.zeros(blocks * 8 * 2, dtype=torch.int64, device=dev)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    # (name, MFMA waves, LDS bytes per LDS wave per iteration, LDS waves)
+    modes = [("mfma_alone", 4, 0, 0), ("mfma_with_lds_b128_reads", 4, 16384, 4),
+             ("mfma_with_lds_tr_reads", 4, 16384, 4), ("lds_b128_reads_alone", 0, 8192, 8),
+             ("lds_tr_reads_alone", 0, 8192, 8)]
+    res = {}
+    for mode, (name, mw, lbytes, lw) in enumerate(modes):
+        rc = []
+        timed(lambda: rc.append(lib.dust_probe_clock(mode, out.data_ptr(), sink.data_ptr(),
+                                                     blocks, iters, sh)), warm=5, n=5)
+        if any(rc):
+            raise RuntimeError("dust_probe_clock failed: %r" % rc)
+        o = out.view(blocks, 8, 2).double()
+        waves = slice(0, 4) if mw else slice(0, 8)
+        cyc = o[:, waves, 0].mean().item()
+        sec = o[:, waves, 1].mean().item() / (khz * 1e3)
+        r = {"clock_GHz": round(cyc / sec / 1e9, 3)}
+        if mw:
+            fl = blocks * mw * iters * 16 * 32768
+            r["mfma_TFLOP_per_s"] = round(fl / sec / 1e12, 1)
+            r["mfma_frac_of_peak"] = round(fl / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        if lw:
+            lo = slice(4, 8) if mw else slice(0, 8)
+            lcyc = o[:, lo, 0].mean().item()
+            r["lds_bytes_per_clock_per_CU"] = round(lw * lbytes * iters / lcyc, 1)
+        res[name] = r
+    res["wallclock_kHz"] = khz
+    return res
 
 
 def cfg_name(chain) -> str:
