@@ -38,7 +38,9 @@ __global__ __launch_bounds__(256) void head_ce_kernel(
     uint32_t tok0) {
     __shared__ __align__(16) float part_lds[4][kBatch][kRow];
     __shared__ float xsel_lds[4][kBatch];
-    const uint32_t t = blockIdx.x * 4u + wave_in_block();
+    // tokens dealt to the XCDs in contiguous ranges, so that each 128-byte line of a draw's
+    // loss row (32 tokens, 8 blocks) is written whole by one L2
+    const uint32_t t = xcd_logical_block(blockIdx.x, gridDim.x) * 4u + wave_in_block();
     if (t >= T) return;
     const uint32_t lane = threadIdx.x & 63u;
     const float *z = logits + (uint64_t)t * V;
