@@ -67,7 +67,9 @@ __device__ __forceinline__ uint32_t mix32(uint32_t x) {
 
 // MODE 0: waves 0-3 MFMA, waves 4-7 idle; 1: waves 4-7 read 16 KB of LDS per iteration with
 // ds_read_b128; 2: the same with ds_read_b64_tr_b16; 3: all 8 waves ds_read_b128, 8 KB per
-// iteration; 4: all 8 waves ds_read_b64_tr_b16, 8 KB per iteration. MFMA waves issue 16
+// iteration; 4: all 8 waves ds_read_b64_tr_b16, 8 KB per iteration; 5: waves 0-3 MFMA, waves
+// 4-7 run the noise generator (two Philox calls = 8 normals per lane per iteration); 6: the
+// generator waves alone (waves 0-3 idle). MFMA waves issue 16
 // v_mfma_f32_32x32x16_bf16 per iteration on 8 accumulators (512 cycles at full rate). LDS
 // reads: 16 consecutive bytes (b128) or 8 (tr) per lane, every wave in its own 8 KB window
 // shifted by 16 bytes per iteration, so that the reads are free of bank conflicts.
@@ -82,7 +84,7 @@ __global__ __launch_bounds__(512, 1) void clock_probe_kernel(unsigned long long 
     const unsigned long long c0 = __builtin_amdgcn_s_memtime();
     const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
     float s = 0.f;
-    if (MODE <= 2 && wave < 4u) {
+    if ((MODE <= 2 || MODE == 5) && wave < 4u) {
         u32x4 ua, ub;
         for (uint32_t k = 0; k < 4u; ++k) {   // random finite bf16 pairs
             ua[k] = mix32(blockIdx.x * 4096u + threadIdx.x * 8u + k) & 0xBFFFBFFFu;
@@ -138,6 +140,17 @@ __global__ __launch_bounds__(512, 1) void clock_probe_kernel(unsigned long long 
 #pragma unroll
         for (uint32_t j = 1; j < per; ++j) y ^= x[j];
         s = (float)(y[0] ^ y[1] ^ y[2] ^ y[3]);
+    } else if ((MODE == 5 || MODE == 6) && wave >= 4u) {
+        const Key key{0x0D057005u, 0u, 1u};
+        const uint32_t token = blockIdx.x * 4u + (wave - 4u);
+        for (uint32_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (uint32_t h = 0; h < 2u; ++h) {
+                Polar p[2];
+                noise4_polar<true>(key, lane + 64u * h, token, it, p);
+                s += p[0].rho * (p[0].c + p[0].s) + p[1].rho * (p[1].c + p[1].s);
+            }
+        }
     }
     const unsigned long long c1 = __builtin_amdgcn_s_memtime();
     const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
@@ -179,6 +192,8 @@ int dust_probe_clock(int mode, unsigned long long *out, float *sink, uint32_t bl
     case 2: dust::clock_probe_kernel<2><<<blocks, 512, 0, s>>>(out, sink, iters); break;
     case 3: dust::clock_probe_kernel<3><<<blocks, 512, 0, s>>>(out, sink, iters); break;
     case 4: dust::clock_probe_kernel<4><<<blocks, 512, 0, s>>>(out, sink, iters); break;
+    case 5: dust::clock_probe_kernel<5><<<blocks, 512, 0, s>>>(out, sink, iters); break;
+    case 6: dust::clock_probe_kernel<6><<<blocks, 512, 0, s>>>(out, sink, iters); break;
     default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

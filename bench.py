@@ -645,9 +645,10 @@ def ceilings(torch, dev) -> dict:
 
 
 def clock_under_load(torch, dev, lib, timed) -> dict:
-    """Shader clock and rates while four waves per CU issue MFMAs and four read LDS (or idle),
-    and while all eight read LDS: per-wave s_memtime cycles over s_memrealtime ticks, averaged
-    over the 256 blocks (one per CU) of the last of the timed launches."""
+    """Shader clock and rates while four waves per CU issue MFMAs and four others read LDS, run
+    the noise generator or idle, and while LDS reads or the generator run alone: per-wave
+    s_memtime cycles over s_memrealtime ticks, averaged over the 256 blocks (one per CU) of the
+    last of the timed launches."""
     import ctypes
     lib.dust_probe_clock.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_uint32, ctypes.c_uint32, ctypes.c_void_p]
@@ -662,7 +663,8 @@ def clock_under_load(torch, dev, lib, timed) -> dict:
     # (name, MFMA waves, LDS bytes per LDS wave per iteration, LDS waves)
     modes = [("mfma_alone", 4, 0, 0), ("mfma_with_lds_b128_reads", 4, 16384, 4),
              ("mfma_with_lds_tr_reads", 4, 16384, 4), ("lds_b128_reads_alone", 0, 8192, 8),
-             ("lds_tr_reads_alone", 0, 8192, 8)]
+             ("lds_tr_reads_alone", 0, 8192, 8), ("mfma_with_generator", 4, 0, 0),
+             ("generator_alone", 0, 0, 0)]
     res = {}
     for mode, (name, mw, lbytes, lw) in enumerate(modes):
         rc = []
@@ -671,7 +673,8 @@ def clock_under_load(torch, dev, lib, timed) -> dict:
         if any(rc):
             raise RuntimeError("dust_probe_clock failed: %r" % rc)
         o = out.view(blocks, 8, 2).double()
-        waves = slice(0, 4) if mw else slice(0, 8)
+        gen = name in ("mfma_with_generator", "generator_alone")
+        waves = slice(0, 4) if mw else (slice(4, 8) if gen else slice(0, 8))
         cyc = o[:, waves, 0].mean().item()
         sec = o[:, waves, 1].mean().item() / (khz * 1e3)
         r = {"clock_GHz": round(cyc / sec / 1e9, 3)}
@@ -679,6 +682,10 @@ def clock_under_load(torch, dev, lib, timed) -> dict:
             fl = blocks * mw * iters * 16 * 32768
             r["mfma_TFLOP_per_s"] = round(fl / sec / 1e12, 1)
             r["mfma_frac_of_peak"] = round(fl / sec / 1e12 / BF16_MFMA_PEAK_TFLOPS, 4)
+        if gen:   # 4 generator waves, 64 lanes, 8 normals per lane per iteration
+            gsec = o[:, 4:8, 1].mean().item() / (khz * 1e3)
+            r["generator_normals_per_s"] = float("%.4g" % (blocks * 4 * 64 * 8 * iters / gsec))
+            r["generator_clock_GHz"] = round(o[:, 4:8, 0].mean().item() / gsec / 1e9, 3)
         if lw:
             lo = slice(4, 8) if mw else slice(0, 8)
             lcyc = o[:, lo, 0].mean().item()
