@@ -555,7 +555,13 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         const float *m1 = NN + (wave * 2u) * S, *n0 = m1 + S;
         for (uint32_t t = lane; t < S; t += 64u) {
             const float Z = zr[t];
-            const float val = Z > 0.f ? m1[t] / (Z * (Z + n0[t])) : 0.f;
+            // The form loses precision where the shifts move the row's mass far: Z + N0 below
+            // Z / 2 comes from cancellation; above 2^20 Z the shifts are large enough for the
+            // noise's 16 significant bits to show in e^delta, and near 1e30 they approach its
+            // range. Such a query is left NaN, and the repair pass recomputes it.
+            const float zn = Z + n0[t], den = Z * zn;
+            const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
+            const float val = !(Z > 0.f) ? 0.f : exact ? m1[t] / den : __builtin_nanf("");
             cr[t] = hd == 0 ? -val : cr[t] - val;
         }
     };
@@ -748,7 +754,10 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
         if (i >= Kc || (lane & 31u) >= 16u) return;
         const uint32_t m = 8u * ((lane & 15u) >> 2) + 4u * half + (lane & 3u);
         const float Z = Zm[((uint64_t)b * H + h) * S + ct * 32u + m];
-        const float val = Z > 0.f ? t1 / (Z * (Z + t0)) : 0.f;
+        // far-moved rows: repaired as in the key scores
+        const float zn = Z + t0, den = Z * zn;
+        const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
+        const float val = !(Z > 0.f) ? 0.f : exact ? t1 / den : __builtin_nanf("");
         float *cr = c + (uint64_t)i * T + (uint64_t)b * S + ct * 32u + m;
         *cr = h == 0 ? -val : *cr - val;
     };
@@ -887,6 +896,124 @@ hipError_t launch_attn_row_weights(const uint16_t *P, const uint16_t *v, const u
 namespace {
 
 // e^x - 1 coefficients for logit shifts sigma tau <., .> of noise divided by kNormalScale
+// Repair pass of the key and query scores. The fast pass's form is exact only while the shifts
+// keep the row's perturbed mass sum_s P_ts e^delta_ts near Z_t: far below it, Z + N0 comes from
+// cancellation; far above it, the noise's 16 significant bits show in e^delta, and shifts
+// beyond about 88 overflow it. The fast pass leaves such queries
+// NaN (as any non-finite input would), and here one block per (draw, sequence) finds them
+// (nothing else is touched) and recomputes their scores from the definition with the row
+// maximum subtracted, head by head:
+//     <Delta o_t, g_t> = sum_s W_ts e^{delta_ts - m} / (Z_t sum_s P_ts e^{delta_ts - m}),
+// m the running maximum of delta_ts over the keys with P_ts > 0 (the sum of W_ts over a row is
+// zero, which makes this equal to the fast pass's form), rescaling both sums when m grows. A
+// thread owns one query of a group of 256 and holds its query-side vector (q_t for keys, the
+// noise a_t for queries) in registers; the block stages the key-side vectors of one 32-key tile
+// (the noise a_s for keys, k_s for queries) in LDS. The noise is taken in fp32 (the fast pass
+// rounds it to 16 significant bits). KEYS: the noise is on the keys.
+template <int KS, bool KEYS>
+__global__ __launch_bounds__(256) void attn_softmax_repair_kernel(
+    const uint16_t *__restrict__ P, const uint16_t *__restrict__ xm, const float *__restrict__ Wm,
+    const float *__restrict__ Zm, float *__restrict__ c, uint32_t Kc, uint32_t B, uint32_t H,
+    uint32_t S, uint32_t q0, float s1, Key key, uint32_t draw0, uint32_t tok0) {
+    constexpr uint32_t DH = 16u * KS;
+    __shared__ float tile[32][DH + 1];
+    __shared__ uint8_t bad[4096];
+    __shared__ float total[4096];
+    const uint32_t tid = threadIdx.x;
+    const uint32_t T = B * S, d = H * DH;
+    const uint64_t pairs = (uint64_t)Kc * B;
+    for (uint64_t pr = blockIdx.x; pr < pairs; pr += gridDim.x) {
+        const uint32_t i = (uint32_t)(pr % Kc), b = (uint32_t)(pr / Kc);
+        float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
+        int found = 0;
+        for (uint32_t t = tid; t < S; t += 256u) {
+            const bool nf = !__builtin_isfinite(cr[t]);
+            bad[t] = nf ? 1 : 0;
+            total[t] = 0.f;
+            found |= nf ? 1 : 0;
+        }
+        if (!__syncthreads_or(found)) continue;   // uniform: the pair is fine
+        const uint32_t draw = draw0 + i;
+        for (uint32_t h = 0; h < H; ++h) {
+            const uint32_t qh = q0 + h * (DH / 4u);
+            for (uint32_t g0 = 0; g0 < S; g0 += 256u) {
+                const uint32_t t = g0 + tid;
+                const bool mine = t < S && bad[t];
+                if (!__syncthreads_or(mine ? 1 : 0)) continue;
+                float qv[DH];
+                if (mine) {
+                    if constexpr (KEYS) {
+                        const uint16_t *row = xm + ((uint64_t)b * S + t) * d + h * DH;
+#pragma unroll
+                        for (uint32_t j = 0; j < DH; ++j) qv[j] = bf16_to_f32(row[j]);
+                    } else {
+#pragma unroll
+                        for (uint32_t j = 0; j < DH; j += 4u) {
+                            Polar pp[2];
+                            noise4_polar<false>(key, qh + j / 4u, tok0 + b * S + t, draw, pp);
+                            qv[j] = pp[0].rho * pp[0].c;
+                            qv[j + 1] = pp[0].rho * pp[0].s;
+                            qv[j + 2] = pp[1].rho * pp[1].c;
+                            qv[j + 3] = pp[1].rho * pp[1].s;
+                        }
+                    }
+                }
+                float m = -__builtin_huge_valf(), num = 0.f, den = 0.f;
+                const uint32_t tlast = min(S, g0 + 256u) - 1u;
+                const uint64_t rbase = (((uint64_t)b * H + h) * S + t) * S;
+                for (uint32_t k0 = 0; k0 <= tlast; k0 += 32u) {
+                    __syncthreads();   // the previous tile is no longer read
+                    for (uint32_t e = tid; e < 32u * (DH / 4u); e += 256u) {
+                        const uint32_t r = e / (DH / 4u), j = 4u * (e % (DH / 4u));
+                        const uint32_t sk = k0 + r;
+                        if constexpr (KEYS) {
+                            Polar pp[2];
+                            noise4_polar<false>(key, qh + j / 4u, tok0 + b * S + sk, draw, pp);
+                            tile[r][j] = pp[0].rho * pp[0].c;
+                            tile[r][j + 1] = pp[0].rho * pp[0].s;
+                            tile[r][j + 2] = pp[1].rho * pp[1].c;
+                            tile[r][j + 3] = pp[1].rho * pp[1].s;
+                        } else {
+                            const uint16_t *row = xm + ((uint64_t)b * S + sk) * d + h * DH + j;
+#pragma unroll
+                            for (uint32_t u = 0; u < 4u; ++u) tile[r][j + u] = bf16_to_f32(row[u]);
+                        }
+                    }
+                    __syncthreads();
+                    if (!mine || k0 > t) continue;
+                    const uint32_t rend = min(32u, t - k0 + 1u);
+                    for (uint32_t r = 0; r < rend; ++r) {
+                        const uint32_t sk = k0 + r;
+                        const float pw = bf16_to_f32(P[rbase + sk]);
+                        if (!(pw > 0.f)) continue;   // adds nothing to either sum
+                        float dot = 0.f;
+#pragma unroll
+                        for (uint32_t j = 0; j < DH; ++j) dot = __builtin_fmaf(qv[j], tile[r][j], dot);
+                        const float delta = s1 * dot;
+                        if (delta > m) {
+                            const float sc = __expf(m - delta);
+                            num *= sc;
+                            den *= sc;
+                            m = delta;
+                        }
+                        const float e = __expf(delta - m);
+                        num = __builtin_fmaf(Wm[rbase + sk], e, num);
+                        den = __builtin_fmaf(pw, e, den);
+                    }
+                }
+                if (mine) {
+                    const float Z = Zm[((uint64_t)b * H + h) * S + t];
+                    total[t] -= (Z > 0.f && den > 0.f) ? num / (Z * den) : 0.f;
+                }
+            }
+        }
+        __syncthreads();
+        for (uint32_t t = tid; t < S; t += 256u)
+            if (bad[t]) cr[t] = total[t];
+        __syncthreads();   // bad and total are reused by the next pair
+    }
+}
+
 Expm1Coef expm1_coef(float sigma, float softmax_scale) {
     const double s1 = (double)sigma * (double)softmax_scale * kNormalScale;
     Expm1Coef ec;
@@ -900,8 +1027,14 @@ Expm1Coef expm1_coef(float sigma, float softmax_scale) {
 }
 
 // Waves (draws) per block of the key and query kernels: 12 (three per SIMD) where the registers
-// allow it without spilling (key heads up to 96 wide, query heads up to 64), else 8.
-uint32_t key_waves(int64_t dh) { return dh <= 96 ? 12u : 8u; }
+// allow it without spilling (key heads up to 96 wide, query heads up to 64), else 8. The key
+// kernel keeps two running sums per wave and query position in LDS, so longer sequences take
+// fewer waves: 4 up to S = 2048, 2 up to 4096.
+uint32_t key_waves(int64_t dh, int64_t S) {
+    if (S > 2048) return 2u;
+    if (S > 1024) return 4u;
+    return dh <= 96 ? 12u : 8u;
+}
 uint32_t query_waves(int64_t dh) { return dh <= 64 ? 12u : 8u; }
 
 }  // namespace
@@ -909,7 +1042,34 @@ uint32_t query_waves(int64_t dh) { return dh <= 64 ? 12u : 8u; }
 // LDS of the key kernel: two stages, then (NW waves x 2 running sums + the query norms) x S
 size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
     return 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) +
-           (size_t)(2 * key_waves(dh) + 1) * S * sizeof(float);
+           (size_t)(2 * key_waves(dh, S) + 1) * S * sizeof(float);
+}
+
+// The repair pass after a key or query scores launch (see attn_softmax_repair_kernel): one block
+// per (draw, sequence), at most 4096 blocks walking the pairs.
+template <bool KEYS>
+static hipError_t launch_softmax_repair(const uint16_t *P, const uint16_t *x, const float *W,
+                                 const float *Z, float *c, int64_t Kc, int64_t B, int64_t H,
+                                 int64_t S, int64_t dh, uint32_t q0, float s1, Key key,
+                                 uint32_t draw0, uint32_t tok0, hipStream_t s) {
+    const uint64_t pairs = (uint64_t)Kc * (uint64_t)B;
+    const uint32_t blocks = (uint32_t)(pairs < 4096u ? pairs : 4096u);
+#define DUST_REP(KS)                                                                           \
+    attn_softmax_repair_kernel<KS, KEYS><<<blocks, 256, 0, s>>>(                               \
+        P, x, W, Z, c, (uint32_t)Kc, (uint32_t)B, (uint32_t)H, (uint32_t)S, q0, s1, key, draw0, \
+        tok0)
+    switch (dh / 16) {
+        case 1: DUST_REP(1); break;
+        case 2: DUST_REP(2); break;
+        case 3: DUST_REP(3); break;
+        case 4: DUST_REP(4); break;
+        case 5: DUST_REP(5); break;
+        case 6: DUST_REP(6); break;
+        case 7: DUST_REP(7); break;
+        default: DUST_REP(8); break;
+    }
+#undef DUST_REP
+    return hipGetLastError();
 }
 
 hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const float *W,
@@ -917,7 +1077,7 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const fl
                                   int64_t S, int64_t dh, int64_t chan0, float sigma,
                                   float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                   hipStream_t s) {
-    const uint32_t nw = key_waves(dh);
+    const uint32_t nw = key_waves(dh, S);
     const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
     const uint32_t blocks = (uint32_t)(B * ndg);
     const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
@@ -927,18 +1087,28 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const fl
     attn_key_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                               \
         P, q, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
+#define DUST_AKS_NW(KS, NW0)                                                                   \
+    do {                                                                                       \
+        if (nw == 2u) DUST_AKS(KS, 2);                                                         \
+        else if (nw == 4u) DUST_AKS(KS, 4);                                                    \
+        else DUST_AKS(KS, NW0);                                                                \
+    } while (0)
     switch (dh / 16) {
-        case 1: DUST_AKS(1, 12); break;
-        case 2: DUST_AKS(2, 12); break;
-        case 3: DUST_AKS(3, 12); break;
-        case 4: DUST_AKS(4, 12); break;
-        case 5: DUST_AKS(5, 12); break;
-        case 6: DUST_AKS(6, 12); break;
-        case 7: DUST_AKS(7, 8); break;
-        default: DUST_AKS(8, 8); break;
+        case 1: DUST_AKS_NW(1, 12); break;
+        case 2: DUST_AKS_NW(2, 12); break;
+        case 3: DUST_AKS_NW(3, 12); break;
+        case 4: DUST_AKS_NW(4, 12); break;
+        case 5: DUST_AKS_NW(5, 12); break;
+        case 6: DUST_AKS_NW(6, 12); break;
+        case 7: DUST_AKS_NW(7, 8); break;
+        default: DUST_AKS_NW(8, 8); break;
     }
+#undef DUST_AKS_NW
 #undef DUST_AKS
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_softmax_repair<true>(P, q, W, Z, c, Kc, B, H, S, dh, q0, ec.s1, key, draw0,
+                                       tok0, s);
 }
 
 hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const float *W,
@@ -968,7 +1138,10 @@ hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const 
         default: DUST_AQS(8, 8); break;
     }
 #undef DUST_AQS
-    return hipGetLastError();
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_softmax_repair<false>(P, k, W, Z, c, Kc, B, H, S, dh, q0, ec.s1, key, draw0,
+                                        tok0, s);
 }
 
 }  // namespace dust

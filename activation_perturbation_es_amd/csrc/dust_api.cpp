@@ -76,7 +76,8 @@ bool ranges_overlap(const void *a, size_t abytes, const void *b, size_t bbytes) 
 int check_softmax_scores(const char *fn, const void *P, const void *x, const float *W,
                          const float *Z, float *c, int64_t Kc, int64_t B, int64_t H, int64_t S,
                          int64_t dh, int64_t chan0, float sigma, float softmax_scale,
-                         uint32_t draw0, uint32_t tok0, int64_t S_max, bool *nothing) {
+                         uint32_t draw0, uint32_t tok0, const char *xname, bool *nothing) {
+    constexpr int64_t S_max = 4096;
     *nothing = false;
     if (Kc < 0 || B < 0 || H < 0 || S < 0 || dh < 0)
         return fail(DUST_ERR_INVALID, "%s: negative size", fn);
@@ -100,13 +101,14 @@ int check_softmax_scores(const char *fn, const void *P, const void *x, const flo
     if (((uintptr_t)P & 15u) || ((uintptr_t)x & 15u) || ((uintptr_t)W & 15u) ||
         !elem_aligned(Z, 4) || !elem_aligned(c, 4))
         return fail(DUST_ERR_INVALID, "%s: P, the %s, and W must be 16-byte, Z and c 4-byte "
-                    "aligned", fn, S_max == 1024 ? "queries" : "keys");
+                    "aligned", fn, xname);
     const int64_t p_bytes = span(B * H, S, S, 2), w_bytes = span(B * H, S, S, 4);
     const int64_t x_bytes = span(B * S, H * dh, 1, 2), z_bytes = span(B * H, S, 1, 4);
     const int64_t c_bytes = span(Kc, B * S, 1, 4);
     if (p_bytes < 0 || w_bytes < 0 || x_bytes < 0 || z_bytes < 0 || c_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    if (B * ((Kc + 7) / 8) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    // blocks of 2 to 12 draws each
+    if (B * ((Kc + 1) / 2) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
     if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
         ranges_overlap(c, (size_t)c_bytes, x, (size_t)x_bytes) ||
         ranges_overlap(c, (size_t)c_bytes, W, (size_t)w_bytes) ||
@@ -508,7 +510,8 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
     const int64_t c_bytes = span(Kc, B * S, 1, 4);
     if (p_bytes < 0 || g_bytes < 0 || c_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    if (B * ((Kc + 7) / 8) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
+    // blocks of 2 to 12 draws each
+    if (B * ((Kc + 1) / 2) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
     if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
         ranges_overlap(c, (size_t)c_bytes, g_o, (size_t)g_bytes))
         return fail(DUST_ERR_INVALID, "%s: c overlaps P or g_o", fn);
@@ -564,7 +567,7 @@ int dust_attn_key_scores(const void *P, const void *q, const float *W, const flo
     const char *fn = "dust_attn_key_scores";
     bool nothing;
     if (int rc = check_softmax_scores(fn, P, q, W, Z, c, Kc, B, H, S, dh, chan0, sigma,
-                                      softmax_scale, draw0, tok0, 1024, &nothing))
+                                      softmax_scale, draw0, tok0, "queries", &nothing))
         return rc;
     if (nothing) return ok();
     return hip_status(dust::launch_attn_key_scores((const uint16_t *)P, (const uint16_t *)q, W, Z,
@@ -581,7 +584,7 @@ int dust_attn_query_scores(const void *P, const void *k, const float *W, const f
     const char *fn = "dust_attn_query_scores";
     bool nothing;
     if (int rc = check_softmax_scores(fn, P, k, W, Z, c, Kc, B, H, S, dh, chan0, sigma,
-                                      softmax_scale, draw0, tok0, 4096, &nothing))
+                                      softmax_scale, draw0, tok0, "keys", &nothing))
         return rc;
     if (nothing) return ok();
     return hip_status(dust::launch_attn_query_scores((const uint16_t *)P, (const uint16_t *)k, W,

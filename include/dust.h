@@ -310,11 +310,16 @@ int dust_attn_row_weights(const void *P, const void *v, const void *g_o, float *
  *   c       [Kc, B*S] fp32 scores of draws draw0 .. draw0+Kc-1                          (out)
  * The noise a of (token s, head h, column j) is channel chan0 + h*dh + j of token tok0 + s
  * (the key projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
- * Supported: S a multiple of 32 and at most 1024, dh a multiple of 16 in [16, 128]; P, q and W
+ * Supported: S a multiple of 32 and at most 4096 (sequences longer than 1024 run fewer draws per
+ * block, 4 up to 2048 and 2 beyond), dh a multiple of 16 in [16, 128]; P, q and W
  * 16-byte, Z and c 4-byte aligned; sigma and softmax_scale finite with
  * |sigma * softmax_scale| <= 2^20. c must not overlap the inputs. fp32 accumulation; the noise
- * enters the bf16 matrix cores as a high part plus a remainder (16 significant bits). Logit
- * shifts beyond about 80 overflow e^delta and give non-finite scores.
+ * enters the bf16 matrix cores as a high part plus a remainder (16 significant bits). The fast
+ * pass forms e^delta - 1 directly, which is accurate while the shifts leave the row's mass
+ * sum_s P_ts e^delta_ts between Z_t / 2 and 2^20 Z_t (and below 10^30 / Z_t); any other query
+ * (large shifts) is recomputed, in the same call, by an exact pass that subtracts its row
+ * maximum and takes the noise in fp32 (one block per draw and sequence holding such a query;
+ * slower, but the scores stay finite and accurate for finite inputs).
  */
 int dust_attn_key_scores(const void *P, const void *q, const float *W, const float *Z, float *c,
                          int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh, int64_t chan0,
@@ -337,8 +342,8 @@ int dust_attn_key_scores(const void *P, const void *q, const float *W, const flo
  * (the query projection's output channels; see "Noise"). Sequences are the B rows of S tokens.
  * Supported: S a multiple of 32 and at most 4096, dh a multiple of 16 in [16, 128]; P, k and W
  * 16-byte, Z and c 4-byte aligned; sigma and softmax_scale finite with
- * |sigma * softmax_scale| <= 2^20. c must not overlap the inputs. Precision and the range of the
- * logit shifts as for dust_attn_key_scores.
+ * |sigma * softmax_scale| <= 2^20. c must not overlap the inputs. Precision, and the exact pass
+ * for large logit shifts, as for dust_attn_key_scores.
  */
 int dust_attn_query_scores(const void *P, const void *k, const float *W, const float *Z,
                            float *c, int64_t Kc, int64_t B, int64_t H, int64_t S, int64_t dh,

@@ -122,7 +122,7 @@ INVALID = [
     ("dust_attn_value_scores", (FAKE, FAKE2, FAKE, 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "overlap"),
     ("dust_attn_value_scores", (None, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 1, 1, 0, 0, None), 1, "null"),
     ("dust_attn_value_scores", (FAKE, FAKE2, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 2, 0.01, 1, 1, 0, 0, None), 1, "chan0"),
-    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 2048, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 2, "up to 1024"),
+    ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 8192, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 2, "up to 4096"),
     ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 144, 0, 0.01, 0.25, 1, 1, 0, 0, None), 2, "multiple of 16"),
     ("dust_attn_key_scores", (FAKE + 8, FAKE2, FAKE2 + 4096, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "aligned"),
     ("dust_attn_key_scores", (FAKE, FAKE2, FAKE2 + 4104, FAKE2 + 8192, FAKE2 + (1 << 30), 4, 2, 2, 64, 16, 0, 0.01, 0.25, 1, 1, 0, 0, None), 1, "aligned"),

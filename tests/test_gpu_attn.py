@@ -102,6 +102,9 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     (1, 1, 512, 80, 3, 0, 0, 0, False, 0.02, 0.11),      # the widest heads with two tiles a step
     (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
     (1, 1, 1024, 96, 13, 0, 0, 0, True, 0.02, 0.1),      # 12 waves at their largest LDS, 12 + 1 draws
+    (1, 2, 2048, 16, 5, 0, 1, 0, False, 0.05, 0.25),     # 4 waves per block, 4 + 1 draws
+    (1, 1, 4096, 16, 3, 4, 0, 0, True, 0.05, 0.25),      # 2 waves per block, 2 + 1 draws
+    (1, 1, 4096, 128, 2, 0, 0, 0, False, 0.02, 0.09),    # the widest heads at the longest sequence
 ])
 def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn key scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
@@ -200,6 +203,58 @@ def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, 
                                    bits_to_f64(gb), Kc, sigma, tau, seed, tag, draw0, tok0, chan0)
     err = frob_rel(host_f32(c), ref)
     print("query scores rel. Frobenius error %.2e" % err)
+    assert err <= 1e-5
+
+
+def _max_shift(x64, B, H, S, dh, Kc, sigma, tau, seed, tag, noise_on_keys):
+    """Largest |sigma tau <q_t, a_s>| (or <a_t, k_s>) over the causal pairs, from the oracle's
+    normals: how far the draws reach beyond e^delta's fp32 range."""
+    a = oracle.normals(seed, tag, 0, 0, 0, Kc, B * S, H * dh)
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            xs = x64[b * S:(b + 1) * S, h * dh:(h + 1) * dh]
+            for k in range(Kc):
+                an = a[k, b * S:(b + 1) * S, h * dh:(h + 1) * dh]
+                D = xs @ an.T if noise_on_keys else an @ xs.T      # [query, key]
+                worst = max(worst, float(np.abs(np.tril(D)).max()))
+    return abs(sigma * tau) * worst
+
+
+@pytest.mark.parametrize("which,B,H,S,dh,Kc,garbage,sigma,tau,reach", [
+    ("keys", 1, 2, 64, 32, 4, False, 40.0, 0.18, 100),     # nearly every query beyond e^x's range
+    ("queries", 1, 2, 64, 32, 4, False, 40.0, 0.18, 100),
+    ("keys", 1, 2, 64, 32, 4, False, 10.0, 0.18, 20),      # within range, rows' mass far below Z
+    ("queries", 1, 2, 64, 32, 4, False, 10.0, 0.18, 20),
+    ("keys", 2, 1, 96, 16, 5, True, 26.0, 0.25, 100),      # some queries of some draws
+    ("queries", 2, 1, 96, 16, 5, True, 26.0, 0.25, 100),
+    ("keys", 1, 1, 288, 128, 3, False, 30.0, 0.09, 100),   # two groups of queries, the widest heads
+    ("queries", 1, 1, 288, 128, 3, False, 30.0, 0.09, 100),
+    ("keys", 1, 1, 2048, 16, 3, False, 24.0, 0.25, 100),   # a long sequence on 4 waves a block
+])
+def test_attn_softmax_scores_beyond_exp_range(which, B, H, S, dh, Kc, garbage, sigma, tau, reach):
+    """Large logit shifts: past fp32's e^x range, or moving a row's mass far below Z (where the
+    fast form cancels). The fast pass marks those queries and the exact pass with the row maximum
+    subtracted recomputes them; every score finite, and equal to the oracle's (which subtracts
+    the row maximum throughout)."""
+    announce("attn %s scores beyond e^x %s" % (which, (B, H, S, dh, Kc, garbage, sigma, tau)))
+    g = np.random.default_rng(78)
+    T, d, seed, tag = B * S, H * dh, 0xA781, 9
+    Pbits = rne_bf16_bits_of_f32(_causal_weights(g, B, H, S, garbage).astype(np.float32))
+    xb, vb, gb = (rne_bf16_bits_of_f32(g.standard_normal((T, d)).astype(np.float32)) for _ in range(3))
+    assert _max_shift(bits_to_f64(xb), B, H, S, dh, Kc, sigma, tau, seed, tag, which == "keys") > reach
+    c = torch.full((Kc, T), float("nan"), dtype=torch.float32, device=DEV)
+    Pd = bf16(Pbits)
+    W, Z = row_weights(Pd, bf16(vb), bf16(gb), B, H, S, dh)
+    fn = dust.dust_attn_key_scores if which == "keys" else dust.dust_attn_query_scores
+    fn(Pd, bf16(xb), W, Z, c, Kc, B, H, S, dh, 0, sigma, tau, seed, tag, 0, 0)
+    of = oracle.attn_key_scores if which == "keys" else oracle.attn_query_scores
+    ref = of(bits_to_f64(Pbits), bits_to_f64(xb), bits_to_f64(vb), bits_to_f64(gb), Kc, sigma, tau,
+             seed, tag, 0, 0, 0)
+    got = host_f32(c)
+    assert np.all(np.isfinite(got))
+    err = frob_rel(got, ref)
+    print("%s scores beyond e^x: rel. Frobenius error %.2e" % (which, err))
     assert err <= 1e-5
 
 
