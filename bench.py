@@ -144,7 +144,7 @@ class Chain:
 
     def __init__(self, cfg_id, dust, torch, dev):
         self.cfg_id, self.dust, self.torch, self.dev = cfg_id, dust, torch, dev
-        self.c = synth.CONFIGS[cfg_id]
+        self.c = synth.WORKLOADS[cfg_id]
         self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
         self.fused = True   # loss mode: scores and rewards in one pass (dust_loss_reward)
         self.fold = False   # gamma = 0: scores formed inside the error estimate

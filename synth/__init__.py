@@ -13,7 +13,7 @@ from __future__ import annotations
 import numpy as np
 
 # Workload definitions (sizes are element counts).
-CONFIGS = {
+WORKLOADS = {
     # Tiny CPU-checkable model: linear 64 -> 64 (fp32) feeding a fixed LM head 64 -> 256.
     1: dict(name="tiny_linear_64x64_head256", d_in=64, d_out=64, V=256, T=128, seg_len=128,
             K=16, sigma=0.01, gammas=(0.0, 0.9)),
@@ -87,7 +87,7 @@ def losses(g: np.random.Generator, K: int, T: int):
 def tiny_model(cfg: int = 1):
     """Workload 1: W ~ N(0, 1/64) [d_out, d_in], H ~ N(0, 1/64) [V, d_out], x ~ N(0, 1)
     [T, d_in], targets uniform in [0, V). All fp32."""
-    c = CONFIGS[cfg]
+    c = WORKLOADS[cfg]
     g = rng(cfg)
     W = normal_f32(g, (c["d_out"], c["d_in"]), 1.0 / 8.0)
     H = normal_f32(g, (c["V"], c["d_out"]), 1.0 / 8.0)

@@ -34,7 +34,7 @@ def _cos(a, b):
 @pytest.mark.parametrize("gamma", [0.0, 0.9])
 def test_tiny_chain(gamma):
     announce("tiny chain gamma=%g" % gamma)
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS[1]
     T, d_in, d_out, K, sigma, S = cfg["T"], cfg["d_in"], cfg["d_out"], cfg["K"], cfg["sigma"], cfg["seg_len"]
     seed, tag = synth.noise_seed(1), synth.NOISE_TAG
     W, H, x, tgt = synth.tiny_model()

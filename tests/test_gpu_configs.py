@@ -1,7 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configurations the benchmark times, on
 sampled outputs the oracle computes one by one (MI355X only).
 
-Workloads (see synth.CONFIGS): 2 = MLP up-projection 512 -> 2048, T = 16384, K = 64;
+Workloads (see synth.WORKLOADS): 2 = MLP up-projection 512 -> 2048, T = 16384, K = 64;
 3 = LM-head chunk [0, 1024) of V = 4096, T = 16384, K = 1024; 4 = attention k/v 512 -> 512
 scored by inner products, gamma = 0.99, K = 16384 in blocks of 512; 5 = MLP up-projection
 1024 -> 4096, T = 16384, K = 1024. Tolerances are those of test_gpu_parity.py.
@@ -26,7 +26,7 @@ def _gather_bits(t: torch.Tensor, *idx) -> np.ndarray:
 
 
 def _check_inject_block(cfg, d_key):
-    c = synth.CONFIGS[cfg]
+    c = synth.WORKLOADS[cfg]
     T, d, sigma, Kb = c["T"], c[d_key], c["sigma"], c["inject_block"]
     draw0 = c["K"] - Kb                         # last block of the population
     seed, tag = synth.noise_seed(cfg), synth.NOISE_TAG
@@ -46,7 +46,7 @@ def _check_inject_block(cfg, d_key):
 
 
 def _check_error_estimate(cfg, K, T, d, chan0=0):
-    sigma, seed, tag = synth.CONFIGS[cfg]["sigma"], synth.noise_seed(cfg), synth.NOISE_TAG
+    sigma, seed, tag = synth.WORKLOADS[cfg]["sigma"], synth.noise_seed(cfg), synth.NOISE_TAG
     r = synth.normal_f32(synth.rng(cfg, 3), (K, T), 0.01)
     gh = torch.empty((T, d), dtype=torch.float32, device=DEV)
     gt = torch.empty((d, T), dtype=torch.bfloat16, device=DEV)
@@ -85,7 +85,7 @@ def test_w2_inject_block():
 
 def test_w2_loss_delta_and_scan():
     announce("w2 loss delta + scan")
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     K, T, S = c["K"], c["T"], c["seg_len"]
     lc, lp = synth.losses(synth.rng(2, 2), K, T)
     cd = torch.empty((K, T), dtype=torch.float32, device=DEV)
@@ -102,20 +102,20 @@ def test_w2_loss_delta_and_scan():
 
 def test_w2_error_estimate():
     announce("w2 error estimate")
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     _check_error_estimate(2, c["K"], c["T"], c["d_out"])
 
 
 def test_w2_weight_grad():
     announce("w2 weight grad")
-    c = synth.CONFIGS[2]
+    c = synth.WORKLOADS[2]
     _check_weight_grad(2, c["T"], c["d_out"], c["d_in"], 256)
 
 
 # ------------------------------------------------------------------------------ workload 3
 def test_w3_head_chunk():
     announce("w3 head chunk")
-    c = synth.CONFIGS[3]
+    c = synth.WORKLOADS[3]
     T, V, v0, C, K, sigma = c["T"], c["V"], c["v0"], c["C"], c["K"], c["sigma"]
     seed, tag = synth.noise_seed(3), synth.NOISE_TAG
     g = synth.rng(3, 1)
@@ -136,13 +136,13 @@ def test_w3_head_chunk():
 
 def test_w3_error_estimate():
     announce("w3 error estimate")
-    c = synth.CONFIGS[3]
+    c = synth.WORKLOADS[3]
     _check_error_estimate(3, c["K"], c["T"], c["C"], chan0=c["v0"])
 
 
 def test_w3_weight_grad():
     announce("w3 weight grad")
-    c = synth.CONFIGS[3]
+    c = synth.WORKLOADS[3]
     _check_weight_grad(3, c["T"], c["C"], c["hidden"], 256)
 
 
@@ -151,7 +151,7 @@ def test_w4_delta_o_block_generation():
     """The synthetic attention-output change of one 512-draw block, N(0, 1e-4) in bf16, drawn on
     the device from its own Philox tag."""
     announce("w4 delta_o block")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, Kb, std = c["T"], c["d"], c["draw_block"], c["delta_o_std"]
     seed = synth.noise_seed(4)
     zero = torch.zeros((T, d), dtype=torch.bfloat16, device=DEV)
@@ -169,7 +169,7 @@ def test_w4_delta_o_block_generation():
 
 def test_w4_inner_scores():
     announce("w4 inner scores")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, std = c["T"], c["d"], c["delta_o_std"]
     Kb = 8
     g = synth.rng(4, 1)
@@ -188,7 +188,7 @@ def test_w4_inner_scores_bench_launch():
     delta_o[i][s] = D[i % 7][(s - i) mod T] (a per-draw roll, so every (draw, token) pair is
     distinct); sampled scores are checked against the oracle on the host copy of D."""
     announce("w4 inner scores, 512-draw launch")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, std, Kb = c["T"], c["d"], c["delta_o_std"], 512
     g = synth.rng(4, 3)
     go = synth.normal_bf16(g, (T, d))
@@ -215,7 +215,7 @@ def test_w4_inner_scores_bench_launch():
 
 def test_w4_scan():
     announce("w4 scan")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     K, T, S, gamma = c["K"], c["T"], c["seg_len"], c["gamma"]
     cc = synth.normal_f32(synth.rng(4, 2), (K, T))
     r = torch.empty((K, T), dtype=torch.float32, device=DEV)
@@ -229,13 +229,13 @@ def test_w4_scan():
 
 def test_w4_error_estimate():
     announce("w4 error estimate")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     _check_error_estimate(4, c["K"], c["T"], c["d"])
 
 
 def test_w4_weight_grad():
     announce("w4 weight grad")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     _check_weight_grad(4, c["T"], c["d"], c["d"], 512)
 
 
@@ -244,7 +244,7 @@ def test_w4_attention_value_scores():
     (8 heads of 64, bench.py --attention-values), at full size: all 16384 draws in one call as
     the benchmark times it, sampled outputs against the oracle."""
     announce("w4 attention value scores")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, S, K, sigma = c["T"], c["d"], c["seg_len"], c["K"], c["sigma"]
     B, H = T // S, 8
     seed, tag = synth.noise_seed(4), synth.NOISE_TAG
@@ -271,7 +271,7 @@ def test_w4_attention_key_scores():
     64, softmax scale 1/8, bench.py --attention-keys), at full size: all 16384 draws in one call
     as the benchmark times it, sampled outputs against the oracle."""
     announce("w4 attention key scores")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, S, K, sigma = c["T"], c["d"], c["seg_len"], c["K"], c["sigma"]
     B, H = T // S, 8
     tau = 1.0 / np.sqrt(d // H)
@@ -303,7 +303,7 @@ def test_w4_attention_query_scores():
     64, softmax scale 1/8, bench.py --attention-queries), at full size: all 16384 draws in one
     call as the benchmark times it, sampled outputs against the oracle."""
     announce("w4 attention query scores")
-    c = synth.CONFIGS[4]
+    c = synth.WORKLOADS[4]
     T, d, S, K, sigma = c["T"], c["d"], c["seg_len"], c["K"], c["sigma"]
     B, H = T // S, 8
     tau = 1.0 / np.sqrt(d // H)
@@ -338,7 +338,7 @@ def test_w5_inject_block():
 
 def test_w5_loss_reward():
     announce("w5 loss -> reward")
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS[5]
     K, T, S = c["K"], c["T"], c["seg_len"]
     lc, lp = synth.losses(synth.rng(5, 2), K, T)
     rf = torch.empty((K, T), dtype=torch.float32, device=DEV)
@@ -348,13 +348,13 @@ def test_w5_loss_reward():
 
 def test_w5_error_estimate():
     announce("w5 error estimate")
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS[5]
     _check_error_estimate(5, c["K"], c["T"], c["d_out"])
 
 
 def test_w5_weight_grad():
     announce("w5 weight grad")
-    c = synth.CONFIGS[5]
+    c = synth.WORKLOADS[5]
     _check_weight_grad(5, c["T"], c["d_out"], c["d_in"], 128)
 
 

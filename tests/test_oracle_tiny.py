@@ -19,7 +19,7 @@ from scipy.optimize import curve_fit
 import oracle
 import synth
 
-CFG = synth.CONFIGS[1]
+CFG = synth.WORKLOADS[1]
 
 
 def _estimate(W, H, x, tgt, K, gamma, seed, block=512):
