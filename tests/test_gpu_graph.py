@@ -79,3 +79,75 @@ def test_captured_chain_replays_like_eager(T, d_out, d_in, K, S, gamma):
         torch.cuda.synchronize()
         for k in OUTS:
             assert torch.equal(buf[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
+
+
+def _attention(buf, stream):
+    B, H, S, dh, Kc, sigma, tau, seed, tag = buf["shape"]
+    dust.dust_attn_row_weights(buf["P"], buf["v"], buf["g"], buf["W"], buf["Z"], B, H, S, dh, stream)
+    dust.dust_attn_key_scores(buf["P"], buf["q"], buf["W"], buf["Z"], buf["ck"], Kc, B, H, S, dh, 0,
+                              sigma, tau, seed, tag, 0, 0, stream)
+    dust.dust_attn_query_scores(buf["P"], buf["k"], buf["W"], buf["Z"], buf["cq"], Kc, B, H, S, dh,
+                                0, sigma, tau, seed, tag + 1, 0, 0, stream)
+    dust.dust_attn_value_scores(buf["P"], buf["g"], buf["cv"], Kc, B, H, S, dh, 0, sigma, seed,
+                                tag + 2, 0, 0, stream)
+    dust.dust_perturbed_linear(buf["y"], buf["wn"], buf["po"], dust.DUST_F32, dust.DUST_ACT_GELU_TANH,
+                               B * S, H * dh, 64, 0, Kc, sigma, seed, tag + 3, 0, 0, stream)
+
+
+def _attention_buffers(B, H, S, dh, Kc, sigma, tau, rng_seed):
+    g = np.random.default_rng(rng_seed)
+    T, d = B * S, H * dh
+    z = g.standard_normal((B, H, S, S))
+    z = np.where(np.tril(np.ones((S, S), dtype=bool)), z, -np.inf)
+    P = np.exp(z - z.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    nb = lambda shape: bf16(synth.normal_bf16(g, shape))
+    return {
+        "shape": (B, H, S, dh, Kc, sigma, tau, 0xBEEF, 21),
+        "P": torch.from_numpy(P.astype(np.float32)).to(DEV).to(torch.bfloat16).contiguous(),
+        "q": nb((T, d)), "k": nb((T, d)), "v": nb((T, d)), "g": nb((T, d)), "y": nb((T, d)),
+        "wn": nb((64, d)),
+        "W": torch.empty((B, H, S, S), dtype=torch.float32, device=DEV),
+        "Z": torch.empty((B, H, S), dtype=torch.float32, device=DEV),
+        "ck": torch.empty((Kc, T), dtype=torch.float32, device=DEV),
+        "cq": torch.empty((Kc, T), dtype=torch.float32, device=DEV),
+        "cv": torch.empty((Kc, T), dtype=torch.float32, device=DEV),
+        "po": torch.empty((Kc, T, 64), dtype=torch.float32, device=DEV),
+    }
+
+
+AOUTS = ("W", "Z", "ck", "cq", "cv", "po")
+
+
+@pytest.mark.parametrize("sigma", [0.05, 20.0])   # the second sends rows through the repair pass
+def test_captured_attention_scores_replay_like_eager(sigma):
+    """Row weights, the three attention scorers (the key and query scores with their repair pass)
+    and the perturbed down-projection, captured and replayed: bit-identical to the eager calls."""
+    announce("graph replay attention sigma=%g" % sigma)
+    B, H, S, dh, Kc, tau = 1, 2, 128, 32, 6, 0.18
+    buf = _attention_buffers(B, H, S, dh, Kc, sigma, tau, 43)
+    _attention(buf, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    ref = {k: buf[k].clone() for k in AOUTS}
+    for k in ("ck", "cq", "cv"):
+        assert torch.isfinite(ref[k]).all(), k
+
+    side = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        _attention(buf, side.cuda_stream)
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            _attention(buf, side.cuda_stream)
+    torch.cuda.synchronize()
+
+    other = _attention_buffers(B, H, S, dh, Kc, sigma / 2, tau, 44)
+    for rep in range(3):
+        for k in AOUTS:
+            buf[k].view(torch.uint8).fill_(0xFF)
+        _attention(other, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in AOUTS:
+            assert torch.equal(buf[k].view(torch.uint8), ref[k].view(torch.uint8)), (rep, k)
