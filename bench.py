@@ -85,6 +85,9 @@ def parse():
     # timed ones in steady state (about +1 % against 3 on the headline workload)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=5, choices=(2, 3, 4, 5))
+    ap.add_argument("--draw-block", type=int, default=0,
+                    help="draws per perturbation call of workloads 2 and 5 (a divisor of K; "
+                         "default: the workload's own block)")
     ap.add_argument("--cpu-scale", type=float, default=1.0,
                     help="scale of the CPU oracle's sample (1.0 = about 10-30 s on 16 cores)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,6 +151,7 @@ class Chain:
         self.seed, self.tag = synth.noise_seed(cfg_id), synth.NOISE_TAG
         self.fused = True   # loss mode: scores and rewards in one pass (dust_loss_reward)
         self.fold = False   # gamma = 0: scores formed inside the error estimate
+        self.draw_block = 0  # draws per perturbation call (0: the workload's own)
 
     # ---- optional optimizer step on the estimate (dust_sgd_momentum / dust_adam)
     optimizer = "none"
@@ -191,6 +195,10 @@ class LinearChain(Chain):
         c, t = self.c, self.torch
         self.T, self.d_in, self.d_out, self.K = c["T"], c["d_in"], c["d_out"], c["K"]
         self.KB, self.S, self.gamma, self.sigma = c["inject_block"], c["seg_len"], c["gamma"], c["sigma"]
+        if self.draw_block:
+            if self.K % self.draw_block:
+                raise SystemExit("--draw-block must divide K = %d" % self.K)
+            self.KB = self.draw_block
         g = synth.rng(self.cfg_id, 1)
         self.ybits = synth.normal_bf16(g, (self.T, self.d_out))
         self.xbits = synth.normal_bf16(g, (self.T, self.d_in))
@@ -726,6 +734,11 @@ def main() -> int:
 
     chain = CHAINS[args.workload](args.workload, dust, torch, dev)
     chain.fused = not args.unfused
+    if args.draw_block:
+        if args.workload not in (2, 5):
+            print("--draw-block applies to the MLP workloads 2 and 5 only", file=sys.stderr)
+            return 2
+        chain.draw_block = args.draw_block
     if args.fold:
         if args.workload not in (2, 3, 5) or chain.c["gamma"] != 0.0:
             print("--fold applies to the loss-scored workloads with gamma = 0 (2, 3, 5)",
