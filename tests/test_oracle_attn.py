@@ -320,3 +320,35 @@ def test_row_weights_recover_the_key_and_query_scores():
             em1 = np.expm1(sigma * tau * delta) * tri
             val = (W * em1).sum(-1) / (Z * (Z + (P * tri * em1).sum(-1)))   # [B, H, S]
             np.testing.assert_allclose(got, -val.sum(1).reshape(T), rtol=1e-9, atol=1e-13)
+
+
+@pytest.mark.parametrize("which", ["keys", "queries"])
+@pytest.mark.parametrize("sigma", [30.0, 300.0])
+def test_key_and_query_scores_at_large_shifts(which, sigma):
+    """Logit shifts of hundreds (sigma = 300 reaches past fp64's e^x range, about 709): the
+    oracle's re-run, which subtracts each row's maximum, equals the explicit numpy re-run, and
+    every score is finite."""
+    B, H, S, dh, K = 1, 2, 16, 8, 3
+    g = np.random.default_rng(70)
+    T, d, tau, seed, tag = B * S, H * dh, 1.0 / np.sqrt(dh), 0x5EEF, 6
+    q, k, v, go = (g.standard_normal((T, d)) for _ in range(4))
+    kT = _heads(k, B, S, H).transpose(0, 1, 3, 2)
+    P = _softmax_causal(tau * _heads(q, B, S, H) @ kT)
+    o = np.einsum("bhts,bhsj->bhtj", P, _heads(v, B, S, H))
+    a = oracle.normals(seed, tag, 0, 0, 0, K, T, d)
+    ref = np.empty((K, T))
+    worst = 0.0
+    for i in range(K):
+        if which == "keys":
+            z = tau * _heads(q, B, S, H) @ _heads(k + sigma * a[i], B, S, H).transpose(0, 1, 3, 2)
+        else:
+            z = tau * _heads(q + sigma * a[i], B, S, H) @ kT
+        worst = max(worst, float(np.abs(np.tril(z[0, 0] - (tau * _heads(q, B, S, H) @ kT)[0, 0])).max()))
+        do = np.einsum("bhts,bhsj->bhtj", _softmax_causal(z), _heads(v, B, S, H)) - o
+        ref[i] = -np.einsum("bhtj,bhtj->bt", do, _heads(go, B, S, H)).reshape(T)
+    if sigma == 300.0:
+        assert worst > 709.0
+    f = oracle.attn_key_scores if which == "keys" else oracle.attn_query_scores
+    got = f(P, q if which == "keys" else k, v, go, K, sigma, tau, seed, tag, 0, 0, 0)
+    assert np.all(np.isfinite(got))
+    np.testing.assert_allclose(got, ref, rtol=1e-9, atol=1e-9)
