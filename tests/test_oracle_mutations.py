@@ -104,6 +104,8 @@ PINS_STEPS = [
     lambda: plin.test_perturbed_linear_equals_torch_linear_of_explicit_inputs(*plin.ACTS[3], 7, 300, 2**32 + 64),
     plin.test_sigma_zero_is_the_clean_product_and_the_output_is_affine_in_sigma,
     plin.test_sampled_rows_equal_the_bulk_operand,
+    lambda: attn.test_key_and_query_scores_at_large_shifts("keys", 300.0),
+    lambda: attn.test_key_and_query_scores_at_large_shifts("queries", 300.0),
 ]
 
 # (id, text in dust_oracle.c, replacement)
@@ -206,6 +208,11 @@ MUTATIONS = [
      "sigma * dust_or_normal(seed, tag, (uint32_t)(k[q]),"),
     ("query head offset dropped", "(uint64_t)(chan0 + h * dh + j));\n        double Z",
      "(uint64_t)(chan0 + j));\n        double Z"),
+    ("key re-run without the row maximum", "            Z += prow[sl];\n            if (dl[sl] > mx) mx = dl[sl];",
+     "            Z += prow[sl];\n            if (dl[sl] > mx) mx = 0.0;"),
+    ("query re-run without the row maximum",
+     "dot += a[j] * k[(b * S + sl) * d + h * dh + j];\n            dl[sl] = sigma * tau * dot;\n            Z += prow[sl];\n            if (dl[sl] > mx) mx = dl[sl];",
+     "dot += a[j] * k[(b * S + sl) * d + h * dh + j];\n            dl[sl] = sigma * tau * dot;\n            Z += prow[sl];\n            if (dl[sl] > mx) mx = 0.0;"),
 ]
 
 
