@@ -32,8 +32,10 @@
 // DPP row exchanges complete the sums over the tile.
 //
 // Work layout: a block owns one sequence and several draws (values: 4 waves, two draws each;
-// keys and queries: 12 waves, or 8 for wide heads, one draw each, so that each SIMD holds three
-// or two waves); the block walks heads, then tiles in causal order. Each step's weight tiles
+// keys and queries: 8 waves of two draws each for heads up to 64 wide, so that the operands a
+// wave reads from LDS serve two draws, else one draw per wave and, for keys, 12 waves where the
+// registers allow; long sequences take fewer draws per block, as the key scores' running sums
+// fill the LDS); the block walks heads, then tiles in causal order. Each step's weight tiles
 // (widened to fp32, the causal mask applied) and bf16 side tiles are staged in LDS by the whole
 // block, double-buffered with one barrier per step; the operands of the outer tile (noise) stay
 // in registers across its inner tiles.
@@ -477,20 +479,20 @@ __global__ __launch_bounds__(256) void attn_row_weights_kernel(
     }
 }
 
-// Key scores: NW waves per block (three per SIMD where the registers allow, so that one wave's
-// vector work runs under another's matrix-core work), one draw per wave, one sequence per
-// block. Per step each wave forms D = a q^T on the matrix cores, then per element
-// e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys (one lane-half swap completes
-// both sums) into running sums in LDS; at each head's end every wave folds M / (Z (Z + N0))
-// into its draw's scores.
-template <int KS, int NW>
+// Key scores: NW waves per block, DPW draws per wave, one sequence per block. Per step each wave
+// forms D = a q^T of each of its draws on the matrix cores (the q tile read from LDS once for
+// all of them), then per element e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys
+// (one lane-half swap completes both sums) into running sums in LDS; at each head's end every
+// wave folds M / (Z (Z + N0)) into its draws' scores. Two draws per wave halve the LDS reads and
+// the staging per draw: the P, W and q tiles of a step are read once for both draws.
+template <int KS, int NW, int DPW>
 __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ qm,
     const float *__restrict__ Wm, const float *__restrict__ Zm, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
     // LDS: two stages of one step's operands (P and W tiles [32 queries][32 keys] in fp32, the
-    // q tile [32 queries][DH]); per wave the head's running sums of its draw, [M, N0][S]; the
+    // q tile [32 queries][DH]); per draw of every wave the head's running sums, [M, N0][S]; the
     // head's query norms |q_t|, [S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
@@ -500,32 +502,38 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    // this wave's draw; a draw past the last one is computed with the last draw's noise and
+    // this wave's draws; a draw past the last one is computed with the last draw's noise and
     // not written, so every wave loads and synchronises
-    const uint32_t i = (blockIdx.x % ndg) * (uint32_t)NW + wave;
-    const uint32_t draw = draw0 + min(i, Kc - 1u);
+    const uint32_t i0 = ((blockIdx.x % ndg) * (uint32_t)NW + wave) * (uint32_t)DPW;
     const uint32_t col = lane & 31u, half = lane >> 5;
     float *NN = (float *)(lds + 2u * SB);
-    float *QN = NN + 2u * NW * S;
-    float *nnw = NN + (wave * 2u + half) * S;   // lanes 0-31 keep M, lanes 32-63 N0
+    float *QN = NN + 2u * NW * DPW * S;
+    // running sums of draw j: lanes 0-31 keep M, lanes 32-63 N0
+    auto nnw = [&](int j) { return NN + ((wave * DPW + (uint32_t)j) * 2u + half) * S; };
 
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
     const uint16_t *const qs[1] = {qm};
     Stg stg;
 
-    // key-side operands of the current key tile: the draw's noise and the largest noise norm
+    // key-side operands of the current key tile, per draw: the noise and the largest noise norm
     // over the tile's 32 keys (for the range test of e^x - 1)
-    bf16x8 ahi[KS], alo[KS];
-    float amax = 0.f;
+    bf16x8 ahi[DPW][KS], alo[DPW][KS];
+    float amax[DPW];
     auto key_tile = [&](uint32_t h, uint32_t kt) {
         const uint32_t row = b * S + kt * 32u + col;
-        float n2;
-        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
-        n2 += __shfl_xor(n2, 32);
 #pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
-        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+        for (int j = 0; j < DPW; ++j) {
+            const uint32_t draw = draw0 + min(i0 + (uint32_t)j, Kc - 1u);
+            float n2;
+            noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi[j], alo[j],
+                                &n2);
+            n2 += __shfl_xor(n2, 32);
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+            amax[j] = __uint_as_float(
+                __builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+        }
     };
     // |q_t| of head h for every query of the sequence
     auto query_norms = [&](uint32_t h) {
@@ -546,23 +554,28 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         }
     };
 
-    // Head hd is complete: fold its sums into the score of this wave's draw. Head 0 stores,
+    // Head hd is complete: fold its sums into the scores of this wave's draws. Head 0 stores,
     // later heads add; each lane rereads only what it wrote itself.
     auto fold_head = [&](uint32_t hd) {
-        if (i >= Kc) return;
-        float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
         const float *zr = Zm + ((uint64_t)b * H + hd) * S;
-        const float *m1 = NN + (wave * 2u) * S, *n0 = m1 + S;
-        for (uint32_t t = lane; t < S; t += 64u) {
-            const float Z = zr[t];
-            // The form loses precision where the shifts move the row's mass far: Z + N0 below
-            // Z / 2 comes from cancellation; above 2^20 Z the shifts are large enough for the
-            // noise's 16 significant bits to show in e^delta, and near 1e30 they approach its
-            // range. Such a query is left NaN, and the repair pass recomputes it.
-            const float zn = Z + n0[t], den = Z * zn;
-            const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
-            const float val = !(Z > 0.f) ? 0.f : exact ? m1[t] / den : __builtin_nanf("");
-            cr[t] = hd == 0 ? -val : cr[t] - val;
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) {
+            const uint32_t i = i0 + (uint32_t)j;
+            if (i >= Kc) break;
+            float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
+            const float *m1 = NN + ((wave * DPW + (uint32_t)j) * 2u) * S, *n0 = m1 + S;
+            for (uint32_t t = lane; t < S; t += 64u) {
+                const float Z = zr[t];
+                // The form loses precision where the shifts move the row's mass far: Z + N0
+                // below Z / 2 comes from cancellation; above 2^20 Z the shifts are large enough
+                // for the noise's 16 significant bits to show in e^delta, and near 1e30 they
+                // approach its range. Such a query is left NaN, and the repair pass recomputes
+                // it.
+                const float zn = Z + n0[t], den = Z * zn;
+                const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
+                const float val = !(Z > 0.f) ? 0.f : exact ? m1[t] / den : __builtin_nanf("");
+                cr[t] = hd == 0 ? -val : cr[t] - val;
+            }
         }
     };
 
@@ -571,26 +584,12 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const float lim_cs = ec.lim * 0.999f;
     const uint32_t lim_bits = __float_as_uint(ec.lim) << 1;   // |x| bits shifted past the sign
 
-    // One query tile's vector work: e^x - 1 of the products, weighted sums over the tile's keys
-    // into the running sums of query tile qt.
-    auto tile_sums = [&](const f32x16 &dd, const unsigned char *tb, uint32_t qt, bool first) {
-        const uint32_t tq = qt * 32u + col;
-        const float qn = QN[tq];
-        // element 4 qd + r is key row 8 qd + 4 half + r of the tile, query column col
-        const unsigned char *prow = tb + col * kPPitch + 16u * half;
-        const unsigned char *wrow = prow + 32u * kPPitch;
-        float p[16], w[16];
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
-            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[4 * qd + r] = x[r];
-                w[4 * qd + r] = y[r];
-            }
-        }
-        bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax <= lim_cs)) == 0;
+    // One query tile's vector work for draw j: e^x - 1 of the products, weighted sums over the
+    // tile's keys into the running sums of query tq (p, w: the tile's weights of this lane,
+    // element 4 qd + r being key row 8 qd + 4 half + r of the tile, query column col).
+    auto tile_sums = [&](const f32x16 &dd, const float (&p)[16], const float (&w)[16], float qn,
+                         int j, uint32_t tq, bool first) {
+        bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax[j] <= lim_cs)) == 0;
         if (!poly) {   // the bound is loose: test the products themselves
             uint32_t m = 0;
 #pragma unroll
@@ -616,10 +615,11 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         const auto sn = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(n0),
                                                          false, false);
         const float nn = __uint_as_float(sn[0]) + __uint_as_float(sn[1]);
+        float *nw = nnw(j);
         if (first)   // a query tile's first key tile of the head starts its sums
-            nnw[tq] = nn;
+            nw[tq] = nn;
         else
-            nnw[tq] += nn;
+            nw[tq] += nn;
     };
 
     StepOrder cur;
@@ -641,14 +641,36 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *qrow = base + Stg::kSide + col * GP + 16u * half;
-        f32x16 dd = {};
+        f32x16 dd[DPW];
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) dd[j] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
-            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd, 0, 0, 0);
-            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < DPW; ++j)
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[j][ks], qb, dd[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < DPW; ++j)
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[j][ks], qb, dd[j], 0, 0, 0);
         }
-        tile_sums(dd, base, cur.ct, cur.kt == 0);
+        const uint32_t tq = cur.ct * 32u + col;
+        const float qn = QN[tq];
+        const unsigned char *prow = base + col * kPPitch + 16u * half;
+        const unsigned char *wrow = prow + 32u * kPPitch;
+        float p[16], w[16];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
+            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[4 * qd + r] = x[r];
+                w[4 * qd + r] = y[r];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) tile_sums(dd[j], p, w, qn, j, tq, cur.kt == 0);
         if (!more) break;
         stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
         if (nx.kt != cur.kt || nx.h != cur.h) key_tile(nx.h, nx.kt);
@@ -663,8 +685,9 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
 // noise of a query tile once; the product D^T = a k^T comes out with the query tile's rows in
 // each lane's registers and its key in the lane's column, so every lane keeps the running sums
 // M, N0 of its 16 query rows in registers over the key tiles and one lane reduction per query
-// tile completes them. NW waves, one draw per wave.
-template <int KS, int NW>
+// tile completes them. NW waves, DPW draws per wave (two read each step's k, P and W tiles from
+// LDS once for both draws).
+template <int KS, int NW, int DPW>
 __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ km,
     const float *__restrict__ Wm, const float *__restrict__ Zm, float *__restrict__ c,
@@ -680,8 +703,7 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    const uint32_t i = (blockIdx.x % ndg) * (uint32_t)NW + wave;
-    const uint32_t draw = draw0 + min(i, Kc - 1u);
+    const uint32_t i0 = ((blockIdx.x % ndg) * (uint32_t)NW + wave) * (uint32_t)DPW;
     const uint32_t col = lane & 31u, half = lane >> 5;
     float *KN = (float *)(lds + 2u * SB);
 
@@ -690,18 +712,24 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const uint16_t *const ks_[1] = {km};
     Stg stg;
 
-    // query-side operands of the current query tile: the draw's noise and the largest noise
+    // query-side operands of the current query tile, per draw: the noise and the largest noise
     // norm over the tile's 32 queries
-    bf16x8 ahi[KS], alo[KS];
-    float amax = 0.f;
+    bf16x8 ahi[DPW][KS], alo[DPW][KS];
+    float amax[DPW];
     auto query_tile = [&](uint32_t h, uint32_t ct) {
         const uint32_t row = b * S + ct * 32u + col;
-        float n2;
-        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
-        n2 += __shfl_xor(n2, 32);
 #pragma unroll
-        for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
-        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+        for (int j = 0; j < DPW; ++j) {
+            const uint32_t draw = draw0 + min(i0 + (uint32_t)j, Kc - 1u);
+            float n2;
+            noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi[j], alo[j],
+                                &n2);
+            n2 += __shfl_xor(n2, 32);
+#pragma unroll
+            for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+            amax[j] = __uint_as_float(
+                __builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
+        }
     };
     // |k_s| of head h for every key of the sequence
     auto key_norms = [&](uint32_t h) {
@@ -726,31 +754,34 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
     const float lim_cs = ec.lim * 0.999f;
     const uint32_t lim_bits = __float_as_uint(ec.lim) << 1;
 
-    // running sums of the current query tile: element r is query row 8 (r / 4) + 4 half + r % 4,
-    // summed over this lane's key column
-    float m1[16], n0[16];
+    // running sums of the current query tile, per draw: element r is query row
+    // 8 (r / 4) + 4 half + r % 4, summed over this lane's key column
+    float m1[DPW][16], n0[DPW][16];
     auto reset = [&]() {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) m1[r] = n0[r] = 0.f;
+        for (int j = 0; j < DPW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m1[j][r] = n0[j][r] = 0.f;
     };
-    // Query tile ct of head h is complete: sum the running sums over the 32 key columns (lanes
-    // of one half); lane l then takes the totals of row m(l) = 8 ((l & 15) >> 2) + 4 (l >> 5) +
-    // (l & 3) when (l & 31) < 16 and folds M / (Z (Z + N0)) into this wave's draw. Head 0
-    // stores, later heads add.
-    auto finish_tile = [&](uint32_t h, uint32_t ct) {
+    // Query tile ct of head h is complete: sum the running sums of draw j over the 32 key
+    // columns (lanes of one half); lane l then takes the totals of row m(l) = 8 ((l & 15) >> 2) +
+    // 4 (l >> 5) + (l & 3) when (l & 31) < 16 and folds M / (Z (Z + N0)) into the draw's score.
+    // Head 0 stores, later heads add.
+    auto finish_tile = [&](uint32_t h, uint32_t ct, int j) {
         // transposed sum over the 32 lanes of each half: lane l ends with the total of slot
         // l & 31 of v = (M of rows 0..15, N0 of rows 0..15)
         float v[32];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            v[r] = m1[r];
-            v[16 + r] = n0[r];
+            v[r] = m1[j][r];
+            v[16 + r] = n0[j][r];
         }
         const float x = half_wave_transpose_sum(v, lane);
         // M and N0 of row lane & 15 sit in lanes 16 apart
         const float other = __shfl_xor(x, 16);
         const bool hi16 = (lane & 16u) != 0;
         const float t1 = hi16 ? other : x, t0 = hi16 ? x : other;
+        const uint32_t i = i0 + (uint32_t)j;
         if (i >= Kc || (lane & 31u) >= 16u) return;
         const uint32_t m = 8u * ((lane & 15u) >> 2) + 4u * half + (lane & 3u);
         const float Z = Zm[((uint64_t)b * H + h) * S + ct * 32u + m];
@@ -784,12 +815,18 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *krow = base + Stg::kSide + col * GP + 16u * half;
-        f32x16 dd = {};
+        f32x16 dd[DPW];
+#pragma unroll
+        for (int j = 0; j < DPW; ++j) dd[j] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 kb = *(const bf16x8 *)(krow + 32u * ks);
-            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], kb, dd, 0, 0, 0);
-            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], kb, dd, 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < DPW; ++j)
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[j][ks], kb, dd[j], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < DPW; ++j)
+                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[j][ks], kb, dd[j], 0, 0, 0);
         }
         const float kn = KN[(h & 1u) * S + kt * 32u + col];
         const unsigned char *prow = base + col * kPPitch + 16u * half;
@@ -805,29 +842,33 @@ __global__ __launch_bounds__(NW * 64) void attn_query_scores_kernel(
                 w[4 * qd + r] = y[r];
             }
         }
-        bool poly = __builtin_amdgcn_ballot_w64(!(kn * amax <= lim_cs)) == 0;
-        if (!poly) {
-            uint32_t mb = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mb = max(mb, __float_as_uint(dd[r]) << 1);
-            poly = __builtin_amdgcn_ballot_w64(!(mb <= lim_bits)) == 0;
-        }
-        // e^x - 1 first, the sums after, so that both forms feed the same accumulators
-        float e[16];
-        if (poly) {
+        for (int j = 0; j < DPW; ++j) {
+            bool poly = __builtin_amdgcn_ballot_w64(!(kn * amax[j] <= lim_cs)) == 0;
+            if (!poly) {
+                uint32_t mb = 0;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) e[r] = expm1_poly(dd[r], ec);
-        } else {
+                for (int r = 0; r < 16; ++r) mb = max(mb, __float_as_uint(dd[j][r]) << 1);
+                poly = __builtin_amdgcn_ballot_w64(!(mb <= lim_bits)) == 0;
+            }
+            // e^x - 1 first, the sums after, so that both forms feed the same accumulators
+            float e[16];
+            if (poly) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) e[r] = expm1_any(dd[r], ec);
-        }
+                for (int r = 0; r < 16; ++r) e[r] = expm1_poly(dd[j][r], ec);
+            } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            m1[r] = __builtin_fmaf(w[r], e[r], m1[r]);
-            n0[r] = __builtin_fmaf(p[r], e[r], n0[r]);
+                for (int r = 0; r < 16; ++r) e[r] = expm1_any(dd[j][r], ec);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                m1[j][r] = __builtin_fmaf(w[r], e[r], m1[j][r]);
+                n0[j][r] = __builtin_fmaf(p[r], e[r], n0[j][r]);
+            }
         }
         if (kt == ct) {   // the query tile is complete
-            finish_tile(h, ct);
+#pragma unroll
+            for (int j = 0; j < DPW; ++j) finish_tile(h, ct, j);
             reset();
         }
         if (!more) break;
@@ -1033,16 +1074,23 @@ Expm1Coef expm1_coef(float sigma, float softmax_scale) {
 uint32_t key_waves(int64_t dh, int64_t S) {
     if (S > 2048) return 2u;
     if (S > 1024) return 4u;
-    return dh <= 96 ? 12u : 8u;
+    return dh <= 64 || dh > 96 ? 8u : 12u;
 }
-uint32_t query_waves(int64_t dh) { return dh <= 64 ? 12u : 8u; }
+// draws per wave of the key kernel: two up to 1024 tokens and heads up to 64 wide (wider heads'
+// stages and two draws' running sums would exceed the LDS)
+uint32_t key_draws_per_wave(int64_t S, int64_t dh) { return S <= 1024 && dh <= 64 ? 2u : 1u; }
+uint32_t query_waves(int64_t) { return 8u; }
+// draws per wave of the query kernel: two for heads up to 64 wide (the registers of two draws'
+// noise fragments and running sums of wider heads would spill)
+uint32_t query_draws_per_wave(int64_t dh) { return dh <= 64 ? 2u : 1u; }
 
 }  // namespace
 
-// LDS of the key kernel: two stages, then (NW waves x 2 running sums + the query norms) x S
+// LDS of the key kernel: two stages, then (NW waves x DPW draws x 2 running sums + the query
+// norms) x S
 size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
     return 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) +
-           (size_t)(2 * key_waves(dh, S) + 1) * S * sizeof(float);
+           (size_t)(2 * key_waves(dh, S) * key_draws_per_wave(S, dh) + 1) * S * sizeof(float);
 }
 
 // The repair pass after a key or query scores launch (see attn_softmax_repair_kernel): one block
@@ -1077,31 +1125,31 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const fl
                                   int64_t S, int64_t dh, int64_t chan0, float sigma,
                                   float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                   hipStream_t s) {
-    const uint32_t nw = key_waves(dh, S);
-    const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
+    const uint32_t nw = key_waves(dh, S), dpw = key_draws_per_wave(S, dh);
+    const uint32_t ndg = (uint32_t)((Kc + nw * dpw - 1) / (nw * dpw));
     const uint32_t blocks = (uint32_t)(B * ndg);
     const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
     const size_t lds = attn_key_scores_lds_bytes(S, dh);
-#define DUST_AKS(KS, NW)                                                                       \
-    attn_key_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                               \
+#define DUST_AKS(KS, NW, DPW)                                                                  \
+    attn_key_scores_kernel<KS, NW, DPW><<<blocks, NW * 64, lds, s>>>(                          \
         P, q, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
-#define DUST_AKS_NW(KS, NW0)                                                                   \
+#define DUST_AKS_NW(KS, NW0, DPW0)                                                             \
     do {                                                                                       \
-        if (nw == 2u) DUST_AKS(KS, 2);                                                         \
-        else if (nw == 4u) DUST_AKS(KS, 4);                                                    \
-        else DUST_AKS(KS, NW0);                                                                \
+        if (nw == 2u) DUST_AKS(KS, 2, 1);                                                      \
+        else if (nw == 4u) DUST_AKS(KS, 4, 1);                                                 \
+        else DUST_AKS(KS, NW0, DPW0);                                                          \
     } while (0)
     switch (dh / 16) {
-        case 1: DUST_AKS_NW(1, 12); break;
-        case 2: DUST_AKS_NW(2, 12); break;
-        case 3: DUST_AKS_NW(3, 12); break;
-        case 4: DUST_AKS_NW(4, 12); break;
-        case 5: DUST_AKS_NW(5, 12); break;
-        case 6: DUST_AKS_NW(6, 12); break;
-        case 7: DUST_AKS_NW(7, 8); break;
-        default: DUST_AKS_NW(8, 8); break;
+        case 1: DUST_AKS_NW(1, 8, 2); break;
+        case 2: DUST_AKS_NW(2, 8, 2); break;
+        case 3: DUST_AKS_NW(3, 8, 2); break;
+        case 4: DUST_AKS_NW(4, 8, 2); break;
+        case 5: DUST_AKS_NW(5, 12, 1); break;
+        case 6: DUST_AKS_NW(6, 12, 1); break;
+        case 7: DUST_AKS_NW(7, 8, 1); break;
+        default: DUST_AKS_NW(8, 8, 1); break;
     }
 #undef DUST_AKS_NW
 #undef DUST_AKS
@@ -1116,26 +1164,26 @@ hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const 
                                     int64_t S, int64_t dh, int64_t chan0, float sigma,
                                     float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s) {
-    const uint32_t nw = query_waves(dh);
-    const uint32_t ndg = (uint32_t)((Kc + nw - 1) / nw);
+    const uint32_t nw = query_waves(dh), dpw = query_draws_per_wave(dh);
+    const uint32_t ndg = (uint32_t)((Kc + nw * dpw - 1) / (nw * dpw));
     const uint32_t blocks = (uint32_t)(B * ndg);
     const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
     // two stages and the key norms [2][S]
     const size_t lds = 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) + 2 * (size_t)S * 4;
-#define DUST_AQS(KS, NW)                                                                       \
-    attn_query_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                             \
+#define DUST_AQS(KS, NW, DPW)                                                                  \
+    attn_query_scores_kernel<KS, NW, DPW><<<blocks, NW * 64, lds, s>>>(                        \
         P, k, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
     switch (dh / 16) {
-        case 1: DUST_AQS(1, 12); break;
-        case 2: DUST_AQS(2, 12); break;
-        case 3: DUST_AQS(3, 12); break;
-        case 4: DUST_AQS(4, 12); break;
-        case 5: DUST_AQS(5, 8); break;
-        case 6: DUST_AQS(6, 8); break;
-        case 7: DUST_AQS(7, 8); break;
-        default: DUST_AQS(8, 8); break;
+        case 1: DUST_AQS(1, 8, 2); break;
+        case 2: DUST_AQS(2, 8, 2); break;
+        case 3: DUST_AQS(3, 8, 2); break;
+        case 4: DUST_AQS(4, 8, 2); break;
+        case 5: DUST_AQS(5, 8, 1); break;
+        case 6: DUST_AQS(6, 8, 1); break;
+        case 7: DUST_AQS(7, 8, 1); break;
+        default: DUST_AQS(8, 8, 1); break;
     }
 #undef DUST_AQS
     const hipError_t e = hipGetLastError();
