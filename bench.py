@@ -72,9 +72,9 @@ OPS_PER_NORMAL = 8.5 + 3.5
 OPS_INJECT_EXTRA = 2.0    # half the coefficient x radius multiply, fma with y, half a bf16 pack
 OPS_EE_EXTRA = 1.5        # half the reward x radius multiply, fma into the accumulator
 OPS_HEAD_EXTRA = 3.5      # half the coefficient x radius multiply, multiply, exp2, fma
-# Key scores, per (draw, head, query, key <= query): e^x - 1 of the logit shift by a degree-5
-# polynomial (4 fma + 1 multiply) and the two weighted sums N1, N0 (2 fma).
-OPS_KEY_SCORE = 7.0
+# Key scores, per (draw, head, query, key <= query): e^x - 1 of the logit shift (x + x^2 q(x),
+# q a quadratic: 3 fma + 1 multiply) and the two weighted sums N1, N0 (2 fma).
+OPS_KEY_SCORE = 6.0
 
 
 def parse():
