@@ -368,20 +368,17 @@ __global__ __launch_bounds__(256) void attn_value_scores_kernel(
     }
 }
 
-// e^x - 1 with x = s1 D, in three ranges:
-//  - |x| <= kPolyRange: x + x^2 q(x), the leading term exact and q the quadratic that minimises
-//    the largest relative error over the range (fitted by linear programming on a dense grid);
-//    evaluated in D by Horner's rule, three fused multiply-adds and a multiply, it stays within
-//    8.5e-7 of e^x - 1 in fp32 (the fit alone 7.0e-7), and its error falls like x^4 towards 0;
-//  - |x| <= kTaylorRange: the degree-5 Taylor polynomial (within 4.8e-7 of the result);
-//  - beyond: exp(x) - 1, relative error below 1e-6 there.
-constexpr float kPolyRange = 0.15f, kTaylorRange = 0.2f;
+// e^x - 1 with x = s1 D: for |x| <= kPolyRange, x + x^2 q(x), the leading term exact and q the
+// quadratic that minimises the largest relative error over the range (fitted by linear
+// programming on a dense grid); evaluated in D by Horner's rule, three fused multiply-adds and a
+// multiply, it stays within 8.5e-7 of e^x - 1 in fp32 (the fit alone 7.0e-7), and its error falls
+// like x^4 towards 0. Beyond, exp(x) - 1, within about 1e-6 of the result there.
+constexpr float kPolyRange = 0.15f;
 constexpr double kExpm1Q0 = 0.50000103352597824, kExpm1Q1 = 0.16682308873996046,
                  kExpm1Q2 = 0.0416364346995442;
 struct Expm1Coef {
-    float s1, a2, a3, a4;    // s1^k q_{k-2}: the fast form in D
-    float s2, s3, s4, s5;    // s1^k / k!: the Taylor polynomial in D
-    float lim;               // kPolyRange / |s1|: |D| up to lim takes the fast form
+    float s1, a2, a3, a4;    // s1 and s1^k q_{k-2}: the polynomial in D
+    float lim;               // kPolyRange / |s1|: |D| up to lim takes the polynomial
 };
 
 __device__ __forceinline__ float expm1_poly(float D, const Expm1Coef &e) {
@@ -391,19 +388,9 @@ __device__ __forceinline__ float expm1_poly(float D, const Expm1Coef &e) {
     return D * p;
 }
 
-__device__ __forceinline__ float expm1_taylor(float D, const Expm1Coef &e) {
-    float p = __builtin_fmaf(D, e.s5, e.s4);
-    p = __builtin_fmaf(D, p, e.s3);
-    p = __builtin_fmaf(D, p, e.s2);
-    p = __builtin_fmaf(D, p, e.s1);
-    return D * p;
-}
-
 __device__ __forceinline__ float expm1_any(float D, const Expm1Coef &e) {
     const float x = e.s1 * D;
-    return fabsf(x) <= kPolyRange     ? expm1_poly(D, e)
-           : fabsf(x) <= kTaylorRange ? expm1_taylor(D, e)
-                                      : expf(x) - 1.f;
+    return fabsf(x) <= kPolyRange ? expm1_poly(D, e) : expf(x) - 1.f;
 }
 
 // Row weights of the softmax re-run, shared by the key and query scores. With u_ts = <v_s, g_t>,
@@ -495,20 +482,20 @@ __global__ __launch_bounds__(256) void attn_row_weights_kernel(
     }
 }
 
-// Key scores: NW waves per block, DPW draws per wave, one sequence per block. Per step each wave
-// forms D = a q^T of each of its draws on the matrix cores (the q tile read from LDS once for
-// all of them), then per element e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys
-// (one lane-half swap completes both sums) into running sums in LDS; at each head's end every
-// wave folds M / (Z (Z + N0)) into its draws' scores. Two draws per wave halve the LDS reads and
-// the staging per draw: the P, W and q tiles of a step are read once for both draws.
-template <int KS, int NW, int DPW>
+// Key scores: NW waves per block (three per SIMD where the registers allow, so that one wave's
+// vector work runs under another's matrix-core work), one draw per wave, one sequence per
+// block. Per step each wave forms D = a q^T on the matrix cores, then per element
+// e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys (one lane-half swap completes
+// both sums) into running sums in LDS; at each head's end every wave folds M / (Z (Z + N0))
+// into its draw's scores.
+template <int KS, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const uint16_t *__restrict__ P, const uint16_t *__restrict__ qm,
     const float *__restrict__ Wm, const float *__restrict__ Zm, float *__restrict__ c,
     uint32_t Kc, uint32_t T, uint32_t H, uint32_t S, uint32_t q0, Expm1Coef ec, Key key,
     uint32_t draw0, uint32_t tok0, uint32_t ndg) {
     // LDS: two stages of one step's operands (P and W tiles [32 queries][32 keys] in fp32, the
-    // q tile [32 queries][DH]); per draw of every wave the head's running sums, [M, N0][S]; the
+    // q tile [32 queries][DH]); per wave the head's running sums of its draw, [M, N0][S]; the
     // head's query norms |q_t|, [S].
     extern __shared__ __align__(16) unsigned char lds[];
     constexpr uint32_t DH = 16u * KS;
@@ -518,38 +505,32 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const uint32_t wave = wave_in_block();
     const uint32_t lane = tid & 63u;
     const uint32_t b = blockIdx.x / ndg;
-    // this wave's draws; a draw past the last one is computed with the last draw's noise and
+    // this wave's draw; a draw past the last one is computed with the last draw's noise and
     // not written, so every wave loads and synchronises
-    const uint32_t i0 = ((blockIdx.x % ndg) * (uint32_t)NW + wave) * (uint32_t)DPW;
+    const uint32_t i = (blockIdx.x % ndg) * (uint32_t)NW + wave;
+    const uint32_t draw = draw0 + min(i, Kc - 1u);
     const uint32_t col = lane & 31u, half = lane >> 5;
     float *NN = (float *)(lds + 2u * SB);
-    float *QN = NN + 2u * NW * DPW * S;
-    // running sums of draw j: lanes 0-31 keep M, lanes 32-63 N0
-    auto nnw = [&](int j) { return NN + ((wave * DPW + (uint32_t)j) * 2u + half) * S; };
+    float *QN = NN + 2u * NW * S;
+    float *nnw = NN + (wave * 2u + half) * S;   // lanes 0-31 keep M, lanes 32-63 N0
 
     const uint32_t d = H * DH;
     const uint32_t nt = S / 32u;
     const uint16_t *const qs[1] = {qm};
     Stg stg;
 
-    // key-side operands of the current key tile, per draw: the noise and the largest noise norm
+    // key-side operands of the current key tile: the draw's noise and the largest noise norm
     // over the tile's 32 keys (for the range test of e^x - 1)
-    bf16x8 ahi[DPW][KS], alo[DPW][KS];
-    float amax[DPW];
+    bf16x8 ahi[KS], alo[KS];
+    float amax = 0.f;
     auto key_tile = [&](uint32_t h, uint32_t kt) {
         const uint32_t row = b * S + kt * 32u + col;
+        float n2;
+        noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi, alo, &n2);
+        n2 += __shfl_xor(n2, 32);
 #pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-            const uint32_t draw = draw0 + min(i0 + (uint32_t)j, Kc - 1u);
-            float n2;
-            noise_fragments<KS>(key, q0 + h * (DH / 4u), half, tok0 + row, draw, ahi[j], alo[j],
-                                &n2);
-            n2 += __shfl_xor(n2, 32);
-#pragma unroll
-            for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
-            amax[j] = __uint_as_float(
-                __builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
-        }
+        for (int m = 16; m >= 1; m >>= 1) n2 = fmaxf(n2, __shfl_xor(n2, m));
+        amax = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(__builtin_sqrtf(n2))));
     };
     // |q_t| of head h for every query of the sequence
     auto query_norms = [&](uint32_t h) {
@@ -570,28 +551,23 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         }
     };
 
-    // Head hd is complete: fold its sums into the scores of this wave's draws. Head 0 stores,
+    // Head hd is complete: fold its sums into the score of this wave's draw. Head 0 stores,
     // later heads add; each lane rereads only what it wrote itself.
     auto fold_head = [&](uint32_t hd) {
+        if (i >= Kc) return;
+        float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
         const float *zr = Zm + ((uint64_t)b * H + hd) * S;
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) {
-            const uint32_t i = i0 + (uint32_t)j;
-            if (i >= Kc) break;
-            float *cr = c + (uint64_t)i * T + (uint64_t)b * S;
-            const float *m1 = NN + ((wave * DPW + (uint32_t)j) * 2u) * S, *n0 = m1 + S;
-            for (uint32_t t = lane; t < S; t += 64u) {
-                const float Z = zr[t];
-                // The form loses precision where the shifts move the row's mass far: Z + N0
-                // below Z / 2 comes from cancellation; above 2^20 Z the shifts are large enough
-                // for the noise's 16 significant bits to show in e^delta, and near 1e30 they
-                // approach its range. Such a query is left NaN, and the repair pass recomputes
-                // it.
-                const float zn = Z + n0[t], den = Z * zn;
-                const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
-                const float val = !(Z > 0.f) ? 0.f : exact ? m1[t] / den : __builtin_nanf("");
-                cr[t] = hd == 0 ? -val : cr[t] - val;
-            }
+        const float *m1 = NN + (wave * 2u) * S, *n0 = m1 + S;
+        for (uint32_t t = lane; t < S; t += 64u) {
+            const float Z = zr[t];
+            // The form loses precision where the shifts move the row's mass far: Z + N0 below
+            // Z / 2 comes from cancellation; above 2^20 Z the shifts are large enough for the
+            // noise's 16 significant bits to show in e^delta, and near 1e30 they approach its
+            // range. Such a query is left NaN, and the repair pass recomputes it.
+            const float zn = Z + n0[t], den = Z * zn;
+            const bool exact = zn >= 0.5f * Z && zn <= 1048576.f * Z && den < 1e30f;
+            const float val = !(Z > 0.f) ? 0.f : exact ? m1[t] / den : __builtin_nanf("");
+            cr[t] = hd == 0 ? -val : cr[t] - val;
         }
     };
 
@@ -600,12 +576,26 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
     const float lim_cs = ec.lim * 0.999f;
     const uint32_t lim_bits = __float_as_uint(ec.lim) << 1;   // |x| bits shifted past the sign
 
-    // One query tile's vector work for draw j: e^x - 1 of the products, weighted sums over the
-    // tile's keys into the running sums of query tq (p, w: the tile's weights of this lane,
-    // element 4 qd + r being key row 8 qd + 4 half + r of the tile, query column col).
-    auto tile_sums = [&](const f32x16 &dd, const float (&p)[16], const float (&w)[16], float qn,
-                         int j, uint32_t tq, bool first) {
-        bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax[j] <= lim_cs)) == 0;
+    // One query tile's vector work: e^x - 1 of the products, weighted sums over the tile's keys
+    // into the running sums of query tile qt.
+    auto tile_sums = [&](const f32x16 &dd, const unsigned char *tb, uint32_t qt, bool first) {
+        const uint32_t tq = qt * 32u + col;
+        const float qn = QN[tq];
+        // element 4 qd + r is key row 8 qd + 4 half + r of the tile, query column col
+        const unsigned char *prow = tb + col * kPPitch + 16u * half;
+        const unsigned char *wrow = prow + 32u * kPPitch;
+        float p[16], w[16];
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+            const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
+            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[4 * qd + r] = x[r];
+                w[4 * qd + r] = y[r];
+            }
+        }
+        bool poly = __builtin_amdgcn_ballot_w64(!(qn * amax <= lim_cs)) == 0;
         if (!poly) {   // the bound is loose: test the products themselves
             uint32_t m = 0;
 #pragma unroll
@@ -631,11 +621,10 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
         const auto sn = __builtin_amdgcn_permlane32_swap(__float_as_uint(m1), __float_as_uint(n0),
                                                          false, false);
         const float nn = __uint_as_float(sn[0]) + __uint_as_float(sn[1]);
-        float *nw = nnw(j);
         if (first)   // a query tile's first key tile of the head starts its sums
-            nw[tq] = nn;
+            nnw[tq] = nn;
         else
-            nw[tq] += nn;
+            nnw[tq] += nn;
     };
 
     StepOrder cur;
@@ -657,36 +646,14 @@ __global__ __launch_bounds__(NW * 64) void attn_key_scores_kernel(
 
         const unsigned char *base = lds + st * SB;
         const unsigned char *qrow = base + Stg::kSide + col * GP + 16u * half;
-        f32x16 dd[DPW];
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) dd[j] = f32x16{};
+        f32x16 dd = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 qb = *(const bf16x8 *)(qrow + 32u * ks);
-#pragma unroll
-            for (int j = 0; j < DPW; ++j)
-                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[j][ks], qb, dd[j], 0, 0, 0);
-#pragma unroll
-            for (int j = 0; j < DPW; ++j)
-                dd[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[j][ks], qb, dd[j], 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahi[ks], qb, dd, 0, 0, 0);
+            dd = __builtin_amdgcn_mfma_f32_32x32x16_bf16(alo[ks], qb, dd, 0, 0, 0);
         }
-        const uint32_t tq = cur.ct * 32u + col;
-        const float qn = QN[tq];
-        const unsigned char *prow = base + col * kPPitch + 16u * half;
-        const unsigned char *wrow = prow + 32u * kPPitch;
-        float p[16], w[16];
-#pragma unroll
-        for (int qd = 0; qd < 4; ++qd) {
-            const f32x4 x = *(const f32x4 *)(prow + 32u * qd);
-            const f32x4 y = *(const f32x4 *)(wrow + 32u * qd);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[4 * qd + r] = x[r];
-                w[4 * qd + r] = y[r];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < DPW; ++j) tile_sums(dd[j], p, w, qn, j, tq, cur.kt == 0);
+        tile_sums(dd, base, cur.ct, cur.kt == 0);
         if (!more) break;
         stg.store(tid, lds + (st ^ 1u) * SB, nx.kt == nx.ct);
         if (nx.kt != cur.kt || nx.h != cur.h) key_tile(nx.h, nx.kt);
@@ -1078,40 +1045,61 @@ Expm1Coef expm1_coef(float sigma, float softmax_scale) {
     ec.a2 = (float)(s1 * s1 * kExpm1Q0);
     ec.a3 = (float)(s1 * s1 * s1 * kExpm1Q1);
     ec.a4 = (float)(s1 * s1 * s1 * s1 * kExpm1Q2);
-    ec.s2 = (float)(s1 * s1 / 2.0);
-    ec.s3 = (float)(s1 * s1 * s1 / 6.0);
-    ec.s4 = (float)(s1 * s1 * s1 * s1 / 24.0);
-    ec.s5 = (float)(s1 * s1 * s1 * s1 * s1 / 120.0);
     ec.lim = s1 == 0.0 ? __builtin_huge_valf() : (float)((double)kPolyRange / fabs(s1));
     return ec;
 }
 
-// Waves per block of the key and query kernels: 8 (two per SIMD) with two draws each for heads up
-// to 64 wide; for wider heads one draw per wave, and for keys 12 waves (three per SIMD) where the
-// registers allow it without spilling (heads up to 96 wide). The key kernel keeps two running
-// sums per draw and query position in LDS, so longer sequences take fewer draws: 4 waves of one
-// up to S = 2048, 2 up to 4096.
-uint32_t key_waves(int64_t dh, int64_t S) {
-    if (S > 2048) return 2u;
-    if (S > 1024) return 4u;
-    return dh <= 64 || dh > 96 ? 8u : 12u;
+// Layout of a key or query scores launch: nw waves per block, dpw draws per wave. One draw per
+// wave keeps three waves on each SIMD (12 per block) where the registers allow it (key heads up
+// to 80 wide, query heads up to 64), else 8 waves; the key kernel keeps two running sums per draw
+// and query position in LDS, so its longer sequences take fewer draws per block: 4 waves up to
+// S = 2048, 2 up to 4096. For heads up to 64 wide (and keys up to S = 1024) 8 waves of two draws
+// each are the alternative: each step's operands, read from LDS once, serve two draws, but with
+// two waves per SIMD a draw costs about 5 % more (measured with all 16384 draws of the attention
+// workload in one launch). A launch takes the layout whose grid, in whole rounds of one block
+// per CU (the LDS or registers admit one), ends sooner: 512 draws over 16 sequences fill 256 CUs
+// in 2 rounds of 16 draws per block, against 2.7 of 12.
+struct ScoreLayout {
+    uint32_t nw, dpw;
+};
+
+uint32_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        return 256u;
+    return (uint32_t)n;
 }
-// draws per wave of the key kernel: two up to 1024 tokens and heads up to 64 wide (wider heads'
-// stages and two draws' running sums would exceed the LDS)
-uint32_t key_draws_per_wave(int64_t S, int64_t dh) { return S <= 1024 && dh <= 64 ? 2u : 1u; }
-uint32_t query_waves(int64_t) { return 8u; }
-// draws per wave of the query kernel: two for heads up to 64 wide (the registers of two draws'
-// noise fragments and running sums of wider heads would spill)
-uint32_t query_draws_per_wave(int64_t dh) { return dh <= 64 ? 2u : 1u; }
+
+// Rounds x draws per block, in twentieths of one-draw-per-wave time.
+uint64_t layout_cost(int64_t B, int64_t Kc, uint32_t draws_per_block, uint32_t cus,
+                     uint32_t per_draw) {
+    const uint64_t blocks = (uint64_t)B * (uint64_t)((Kc + draws_per_block - 1) / draws_per_block);
+    return (blocks + cus - 1) / cus * draws_per_block * per_draw;
+}
+
+ScoreLayout choose_layout(ScoreLayout one, bool two_ok, int64_t B, int64_t Kc) {
+    if (!two_ok) return one;
+    const uint32_t cus = device_cus();
+    const ScoreLayout two = {8u, 2u};
+    return layout_cost(B, Kc, two.nw * two.dpw, cus, 21u) <
+                   layout_cost(B, Kc, one.nw * one.dpw, cus, 20u)
+               ? two
+               : one;
+}
+
+ScoreLayout key_layout(int64_t S, int64_t dh) {
+    if (S > 2048) return {2u, 1u};
+    if (S > 1024) return {4u, 1u};
+    return {dh <= 80 ? 12u : 8u, 1u};
+}
+
+ScoreLayout query_layout(int64_t B, int64_t Kc, int64_t dh) {
+    return choose_layout({dh <= 64 ? 12u : 8u, 1u}, dh <= 64, B, Kc);
+}
 
 }  // namespace
-
-// LDS of the key kernel: two stages, then (NW waves x DPW draws x 2 running sums + the query
-// norms) x S
-size_t attn_key_scores_lds_bytes(int64_t S, int64_t dh) {
-    return 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) +
-           (size_t)(2 * key_waves(dh, S) * key_draws_per_wave(S, dh) + 1) * S * sizeof(float);
-}
 
 // The repair pass after a key or query scores launch (see attn_softmax_repair_kernel): one block
 // per (draw, sequence), at most 4096 blocks walking the pairs.
@@ -1145,31 +1133,33 @@ hipError_t launch_attn_key_scores(const uint16_t *P, const uint16_t *q, const fl
                                   int64_t S, int64_t dh, int64_t chan0, float sigma,
                                   float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                   hipStream_t s) {
-    const uint32_t nw = key_waves(dh, S), dpw = key_draws_per_wave(S, dh);
-    const uint32_t ndg = (uint32_t)((Kc + nw * dpw - 1) / (nw * dpw));
+    const ScoreLayout ly = key_layout(S, dh);
+    const uint32_t ndg = (uint32_t)((Kc + ly.nw - 1) / ly.nw);
     const uint32_t blocks = (uint32_t)(B * ndg);
     const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
-    const size_t lds = attn_key_scores_lds_bytes(S, dh);
-#define DUST_AKS(KS, NW, DPW)                                                                  \
-    attn_key_scores_kernel<KS, NW, DPW><<<blocks, NW * 64, lds, s>>>(                          \
+    // two stages, then (waves x 2 running sums + the query norms) x S
+    const size_t lds = 2 * (size_t)stage_bytes((int)(dh / 16), 1, true) +
+                       (size_t)(2 * ly.nw + 1) * S * sizeof(float);
+#define DUST_AKS(KS, NW)                                                                       \
+    attn_key_scores_kernel<KS, NW><<<blocks, NW * 64, lds, s>>>(                               \
         P, q, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
-#define DUST_AKS_NW(KS, NW0, DPW0)                                                             \
+#define DUST_AKS_NW(KS, NW0)                                                                   \
     do {                                                                                       \
-        if (nw == 2u) DUST_AKS(KS, 2, 1);                                                      \
-        else if (nw == 4u) DUST_AKS(KS, 4, 1);                                                 \
-        else DUST_AKS(KS, NW0, DPW0);                                                          \
+        if (ly.nw == 2u) DUST_AKS(KS, 2);                                                      \
+        else if (ly.nw == 4u) DUST_AKS(KS, 4);                                                 \
+        else DUST_AKS(KS, NW0);                                                                \
     } while (0)
     switch (dh / 16) {
-        case 1: DUST_AKS_NW(1, 8, 2); break;
-        case 2: DUST_AKS_NW(2, 8, 2); break;
-        case 3: DUST_AKS_NW(3, 8, 2); break;
-        case 4: DUST_AKS_NW(4, 8, 2); break;
-        case 5: DUST_AKS_NW(5, 12, 1); break;
-        case 6: DUST_AKS_NW(6, 12, 1); break;
-        case 7: DUST_AKS_NW(7, 8, 1); break;
-        default: DUST_AKS_NW(8, 8, 1); break;
+        case 1: DUST_AKS_NW(1, 12); break;
+        case 2: DUST_AKS_NW(2, 12); break;
+        case 3: DUST_AKS_NW(3, 12); break;
+        case 4: DUST_AKS_NW(4, 12); break;
+        case 5: DUST_AKS_NW(5, 12); break;
+        case 6: DUST_AKS_NW(6, 8); break;
+        case 7: DUST_AKS_NW(7, 8); break;
+        default: DUST_AKS_NW(8, 8); break;
     }
 #undef DUST_AKS_NW
 #undef DUST_AKS
@@ -1184,8 +1174,8 @@ hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const 
                                     int64_t S, int64_t dh, int64_t chan0, float sigma,
                                     float softmax_scale, Key key, uint32_t draw0, uint32_t tok0,
                                     hipStream_t s) {
-    const uint32_t nw = query_waves(dh), dpw = query_draws_per_wave(dh);
-    const uint32_t ndg = (uint32_t)((Kc + nw * dpw - 1) / (nw * dpw));
+    const ScoreLayout ly = query_layout(B, Kc, dh);
+    const uint32_t ndg = (uint32_t)((Kc + ly.nw * ly.dpw - 1) / (ly.nw * ly.dpw));
     const uint32_t blocks = (uint32_t)(B * ndg);
     const Expm1Coef ec = expm1_coef(sigma, softmax_scale);
     const uint32_t q0 = (uint32_t)(chan0 / 4);
@@ -1195,16 +1185,22 @@ hipError_t launch_attn_query_scores(const uint16_t *P, const uint16_t *k, const 
     attn_query_scores_kernel<KS, NW, DPW><<<blocks, NW * 64, lds, s>>>(                        \
         P, k, W, Z, c, (uint32_t)Kc, (uint32_t)(B * S), (uint32_t)H, (uint32_t)S, q0, ec, key,  \
         draw0, tok0, ndg)
+#define DUST_AQS2(KS)                                                                          \
+    do {                                                                                       \
+        if (ly.dpw == 2u) DUST_AQS(KS, 8, 2);                                                  \
+        else DUST_AQS(KS, 12, 1);                                                              \
+    } while (0)
     switch (dh / 16) {
-        case 1: DUST_AQS(1, 8, 2); break;
-        case 2: DUST_AQS(2, 8, 2); break;
-        case 3: DUST_AQS(3, 8, 2); break;
-        case 4: DUST_AQS(4, 8, 2); break;
+        case 1: DUST_AQS2(1); break;
+        case 2: DUST_AQS2(2); break;
+        case 3: DUST_AQS2(3); break;
+        case 4: DUST_AQS2(4); break;
         case 5: DUST_AQS(5, 8, 1); break;
         case 6: DUST_AQS(6, 8, 1); break;
         case 7: DUST_AQS(7, 8, 1); break;
         default: DUST_AQS(8, 8, 1); break;
     }
+#undef DUST_AQS2
 #undef DUST_AQS
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -99,9 +99,9 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     (1, 2, 64, 32, 4, 0, 0, 0, False, 1.5, 0.18),        # large shifts: e^x - 1 from exp
     (1, 2, 128, 32, 4, 0, 0, 0, False, 0.15, 0.18),      # tiles that mix both forms
     (1, 1, 1024, 128, 2, 0, 0, 0, True, 0.02, 0.09),     # longest sequence at the widest heads
-    (1, 1, 512, 80, 3, 0, 0, 0, False, 0.02, 0.11),      # the widest heads with two tiles a step
+    (1, 1, 512, 80, 3, 0, 0, 0, False, 0.02, 0.11),      # the widest heads on 12 waves
     (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
-    (1, 1, 1024, 96, 13, 0, 0, 0, True, 0.02, 0.1),      # 12 waves at their largest LDS, 12 + 1 draws
+    (1, 1, 1024, 96, 13, 0, 0, 0, True, 0.02, 0.1),      # 8 waves of one draw: 8 + 5 draws
     (1, 2, 2048, 16, 5, 0, 1, 0, False, 0.05, 0.25),     # 4 waves per block, 4 + 1 draws
     (1, 1, 4096, 16, 3, 4, 0, 0, True, 0.05, 0.25),      # 2 waves per block, 2 + 1 draws
     (1, 1, 4096, 128, 2, 0, 0, 0, False, 0.02, 0.09),    # the widest heads at the longest sequence
