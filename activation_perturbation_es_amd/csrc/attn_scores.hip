@@ -32,10 +32,10 @@
 // DPP row exchanges complete the sums over the tile.
 //
 // Work layout: a block owns one sequence and several draws (values: 4 waves, two draws each;
-// keys and queries: 8 waves of two draws each for heads up to 64 wide, so that the operands a
-// wave reads from LDS serve two draws, else one draw per wave and, for keys, 12 waves where the
-// registers allow; long sequences take fewer draws per block, as the key scores' running sums
-// fill the LDS); the block walks heads, then tiles in causal order. Each step's weight tiles
+// keys and queries: 12 waves of one draw where the registers allow, else 8, and for queries 8
+// waves of two draws when that grid ends sooner; long sequences take fewer key draws per block,
+// as the key scores' running sums fill the LDS); the block walks heads, then tiles in causal
+// order. Each step's weight tiles
 // (widened to fp32, the causal mask applied) and bf16 side tiles are staged in LDS by the whole
 // block, double-buffered with one barrier per step; the operands of the outer tile (noise) stay
 // in registers across its inner tiles.
