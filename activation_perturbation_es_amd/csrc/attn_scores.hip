@@ -39,6 +39,8 @@
 // (widened to fp32, the causal mask applied) and bf16 side tiles are staged in LDS by the whole
 // block, double-buffered with one barrier per step; the operands of the outer tile (noise) stay
 // in registers across its inner tiles.
+#include <atomic>
+
 #include "dust_internal.hpp"
 
 namespace dust {
@@ -1063,12 +1065,22 @@ struct ScoreLayout {
     uint32_t nw, dpw;
 };
 
+// Compute units of the current device, asked once per device (a lost race stores the same
+// value twice); 256 if the runtime cannot tell.
 uint32_t device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+    constexpr int kMaxDevices = 64;
+    static std::atomic<uint32_t> cached[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256u;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const uint32_t c = cached[dev].load(std::memory_order_relaxed);
+        if (c != 0u) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
-        return 256u;
+        n = 256;
+    if (dev >= 0 && dev < kMaxDevices) cached[dev].store((uint32_t)n, std::memory_order_relaxed);
     return (uint32_t)n;
 }
 

@@ -105,7 +105,7 @@ def test_attn_value_scores_zero_draws_touch_nothing():
     (1, 2, 2048, 16, 5, 0, 1, 0, False, 0.05, 0.25),     # 4 waves per block, 4 + 1 draws
     (1, 1, 4096, 16, 3, 4, 0, 0, True, 0.05, 0.25),      # 2 waves per block, 2 + 1 draws
     (1, 1, 4096, 128, 2, 0, 0, 0, False, 0.02, 0.09),    # the widest heads at the longest sequence
-    (1, 1, 1024, 64, 33, 0, 5, 0, False, 0.01, 0.125),   # 8 waves of two draws: 16 + 16 + 1 draws
+    (1, 1, 1024, 64, 33, 0, 5, 0, False, 0.01, 0.125),   # 33 draws: 12 + 12 + 9
 ])
 def test_attn_key_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn key scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
@@ -188,7 +188,10 @@ def test_attn_scores_channels_beyond_32_bits():
     (2, 1, 32, 64, 17, 4, 9, 3, False, 0.05, 0.125),     # one tile per sequence, ragged blocks
     (1, 1, 2048, 64, 13, 0, 0, 0, True, 0.02, 0.125),    # long sequence, 13 draws in one block
     (1, 1, 128, 80, 9, 0, 0, 0, False, 0.05, 0.11),      # the narrowest heads of one draw a wave
-    (1, 1, 1024, 64, 33, 0, 5, 0, False, 0.01, 0.125),   # 8 waves of two draws: 16 + 16 + 1 draws
+    (1, 1, 1024, 64, 33, 0, 5, 0, False, 0.01, 0.125),   # 33 draws: 12 + 12 + 9
+    # 16 sequences x 200 draws: on 256 compute units 8 waves of two draws end in one round of
+    # blocks against two for 12 waves of one, so this launch takes the two-draw layout
+    (16, 1, 64, 64, 200, 0, 3, 0, False, 0.05, 0.125),
 ])
 def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn query scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
