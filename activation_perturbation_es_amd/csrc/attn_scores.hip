@@ -484,8 +484,8 @@ __global__ __launch_bounds__(256) void attn_row_weights_kernel(
     }
 }
 
-// Key scores: NW waves per block (three per SIMD where the registers allow, so that one wave's
-// vector work runs under another's matrix-core work), one draw per wave, one sequence per
+// Key scores: NW waves per block (three per SIMD where the registers allow, so that fp32 FMAs
+// of two waves can issue together), one draw per wave, one sequence per
 // block. Per step each wave forms D = a q^T on the matrix cores, then per element
 // e = e^{s D} - 1 and M += W e, N0 += P e over the tile's keys (one lane-half swap completes
 // both sums) into running sums in LDS; at each head's end every wave folds M / (Z (Z + N0))
@@ -1055,8 +1055,8 @@ Expm1Coef expm1_coef(float sigma, float softmax_scale) {
 // wave keeps three waves on each SIMD (12 per block) where the registers allow it (key heads up
 // to 80 wide, query heads up to 64), else 8 waves; the key kernel keeps two running sums per draw
 // and query position in LDS, so its longer sequences take fewer draws per block: 4 waves up to
-// S = 2048, 2 up to 4096. For heads up to 64 wide (and keys up to S = 1024) 8 waves of two draws
-// each are the alternative: each step's operands, read from LDS once, serve two draws, but with
+// S = 2048, 2 up to 4096. For query heads up to 64 wide 8 waves of two draws each are the
+// alternative: each step's operands, read from LDS once, serve two draws, but with
 // two waves per SIMD a draw costs about 5 % more (measured with all 16384 draws of the attention
 // workload in one launch). A launch takes the layout whose grid, in whole rounds of one block
 // per CU (the LDS or registers admit one), ends sooner: 512 draws over 16 sequences fill 256 CUs
