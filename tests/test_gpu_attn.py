@@ -189,9 +189,10 @@ def test_attn_scores_channels_beyond_32_bits():
     (1, 1, 2048, 64, 13, 0, 0, 0, True, 0.02, 0.125),    # long sequence, 13 draws in one block
     (1, 1, 128, 80, 9, 0, 0, 0, False, 0.05, 0.11),      # the narrowest heads of one draw a wave
     (1, 1, 1024, 64, 33, 0, 5, 0, False, 0.01, 0.125),   # 33 draws: 12 + 12 + 9
-    # 16 sequences x 200 draws: on 256 compute units 8 waves of two draws end in one round of
-    # blocks against two for 12 waves of one, so this launch takes the two-draw layout
-    (16, 1, 64, 64, 200, 0, 3, 0, False, 0.05, 0.125),
+    # 16 sequences x 201 draws: on 256 compute units 8 waves of two draws end in one round of
+    # blocks against two for 12 waves of one, so this launch takes the two-draw layout; the
+    # odd count leaves one wave with its second draw past the last
+    (16, 1, 64, 64, 201, 0, 3, 0, False, 0.05, 0.125),
 ])
 def test_attn_query_scores(B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau):
     announce("attn query scores %s" % ((B, H, S, dh, Kc, chan0, draw0, tok0, garbage, sigma, tau),))
