@@ -178,6 +178,11 @@ class Chain:
         n = self.G.numel()
         return {"dust_sgd_momentum": _hbm(20.0 * n), "dust_adam": _hbm(28.0 * n)}
 
+    def serial_roofs(self):
+        """Kernels whose matrix-core and vector work do not overlap on this part: the sum of the
+        two at their published peaks, ms per launch."""
+        return {}
+
     def bf(self, bits):
         return self.torch.from_numpy(bits.view(np.int16)).to(self.dev).view(self.torch.bfloat16)
 
@@ -506,6 +511,16 @@ class InnerChain(Chain):
             "dust_weight_grad": _mfma(2.0 * T * d * d),
         }
 
+    def serial_roofs(self):
+        # key and query scores: the fp32 element work at the fp32 vector peak plus the logit
+        # shifts' products as executed (the noise's high part and remainder: 4 dh flops per causal
+        # element) at the bf16 peak
+        T, K, S, H = self.T, self.K, self.S, self.HEADS
+        elems = K * (T // S) * H * (S * (S + 1) / 2)
+        ms = 1e3 * (OPS_KEY_SCORE * elems / (FP32_VALU_PEAK_TOPS * 1e12) +
+                    4.0 * (self.d // H) * elems / (BF16_MFMA_PEAK_TFLOPS * 1e12))
+        return {"dust_attn_key_scores": ms, "dust_attn_query_scores": ms}
+
     def config(self):
         cfg = {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
                "draws": self.K, "draw_block": self.KB, "gamma": self.gamma, "sigma": self.sigma,
@@ -799,6 +814,7 @@ def main() -> int:
         per.setdefault(name, []).append(e0.elapsed_time(e1))
     model = chain.model()
     model.update(chain.opt_model())
+    serial = chain.serial_roofs()
     kernels = {}
     for name, ms in per.items():
         bound, work, scale, peak, unit = model[name][:5]
@@ -810,6 +826,9 @@ def main() -> int:
                          "frac": round(ach / peak, 4)}
         if len(model[name]) > 5:   # generating kernels: normals per second, free of the op model
             kernels[name]["normals_per_s"] = float("%.4g" % (model[name][5] / (avg_ms * 1e-3)))
+        if name in serial:
+            kernels[name]["serial_roof_ms"] = round(serial[name], 3)
+            kernels[name]["serial_frac"] = round(serial[name] / avg_ms, 4)
     dominant = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dominant]
     roofline = {"kernel": dominant, "bound": dk["bound"], "achieved": dk["achieved"],
