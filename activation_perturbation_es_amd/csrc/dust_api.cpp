@@ -107,7 +107,7 @@ int check_softmax_scores(const char *fn, const void *P, const void *x, const flo
     const int64_t c_bytes = span(Kc, B * S, 1, 4);
     if (p_bytes < 0 || w_bytes < 0 || x_bytes < 0 || z_bytes < 0 || c_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    // blocks of 2 to 16 draws each
+    // every layout puts at least 2 draws in a block
     if (B * ((Kc + 1) / 2) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
     if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
         ranges_overlap(c, (size_t)c_bytes, x, (size_t)x_bytes) ||
@@ -510,7 +510,7 @@ int dust_attn_value_scores(const void *P, const void *g_o, float *c, int64_t Kc,
     const int64_t c_bytes = span(Kc, B * S, 1, 4);
     if (p_bytes < 0 || g_bytes < 0 || c_bytes < 0)
         return fail(DUST_ERR_UNSUPPORTED, "%s: arrays beyond 2^62 bytes", fn);
-    // blocks of 2 to 16 draws each
+    // every layout puts at least 2 draws in a block
     if (B * ((Kc + 1) / 2) > kMaxIdx) return fail(DUST_ERR_UNSUPPORTED, "%s: grid too large", fn);
     if (ranges_overlap(c, (size_t)c_bytes, P, (size_t)p_bytes) ||
         ranges_overlap(c, (size_t)c_bytes, g_o, (size_t)g_bytes))
