@@ -35,10 +35,9 @@
 // keys and queries: 12 waves of one draw where the registers allow, else 8, and for queries 8
 // waves of two draws when that grid ends sooner; long sequences take fewer key draws per block,
 // as the key scores' running sums fill the LDS); the block walks heads, then tiles in causal
-// order. Each step's weight tiles
-// (widened to fp32, the causal mask applied) and bf16 side tiles are staged in LDS by the whole
-// block, double-buffered with one barrier per step; the operands of the outer tile (noise) stay
-// in registers across its inner tiles.
+// order. Each step's weight tiles (widened to fp32, the causal mask applied) and bf16 side tiles
+// are staged in LDS by the whole block, double-buffered with one barrier per step; the operands
+// of the outer tile (noise) stay in registers across its inner tiles.
 #include <atomic>
 
 #include "dust_internal.hpp"
