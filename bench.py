@@ -290,14 +290,14 @@ class LinearChain(Chain):
         return cfg
 
     def cpu_baseline(self, scale):
-        """The oracle's chain (as it stands) on whole sequences with all K draws (workload 2) or
-        on a draw subset (workload 5)."""
+        """The oracle's chain (as it stands) on whole sequences with all K draws: several
+        sequences at workload 2, one at workload 5 (a subset of the draws when scale < 1)."""
         import oracle
         S = self.S
         if self.cfg_id == 2:
             K_s, T_s = self.K, min(self.T, max(S, int(16 * S * scale) // S * S))
         else:
-            K_s, T_s = max(4, int(512 * scale) // 4 * 4), S
+            K_s, T_s = min(self.K, max(4, int(1024 * scale) // 4 * 4)), S
         if self.downstream != "none":
             K_s = max(1, int(64 * scale))  # the product costs d_out d_in multiply-adds per token
         KB = min(self.KB, K_s)
