@@ -120,11 +120,14 @@ AOUTS = ("W", "Z", "ck", "cq", "cv", "po")
 
 
 @pytest.mark.parametrize("sigma", [0.05, 20.0])   # the second sends rows through the repair pass
-def test_captured_attention_scores_replay_like_eager(sigma):
+# the second shape (16 sequences x 201 draws) runs the query scores on 8 waves of two draws on a
+# 256-CU device, the first on 12 waves of one
+@pytest.mark.parametrize("B,H,S,dh,Kc", [(1, 2, 128, 32, 6), (16, 2, 64, 32, 201)])
+def test_captured_attention_scores_replay_like_eager(sigma, B, H, S, dh, Kc):
     """Row weights, the three attention scorers (the key and query scores with their repair pass)
     and the perturbed down-projection, captured and replayed: bit-identical to the eager calls."""
-    announce("graph replay attention sigma=%g" % sigma)
-    B, H, S, dh, Kc, tau = 1, 2, 128, 32, 6, 0.18
+    announce("graph replay attention sigma=%g shape %s" % (sigma, (B, H, S, dh, Kc)))
+    tau = 0.18
     buf = _attention_buffers(B, H, S, dh, Kc, sigma, tau, 43)
     _attention(buf, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
