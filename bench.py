@@ -179,8 +179,8 @@ class Chain:
         return {"dust_sgd_momentum": _hbm(20.0 * n), "dust_adam": _hbm(28.0 * n)}
 
     def serial_roofs(self):
-        """Kernels whose matrix-core and vector work do not overlap on this part: the sum of the
-        two at their published peaks, ms per launch."""
+        """Kernels whose matrix-core and vector work do not overlap on this part: the sum of
+        their parts at the published peaks, ms per launch."""
         return {}
 
     def bf(self, bits):
@@ -512,14 +512,19 @@ class InnerChain(Chain):
         }
 
     def serial_roofs(self):
-        # key and query scores: the fp32 element work at the fp32 vector peak plus the logit
-        # shifts' products as executed (the noise's high part and remainder: 4 dh flops per causal
-        # element) at the bf16 peak
+        # The attention scorers, each part at its published peak: the products of the causal
+        # elements as executed (the noise's high part and remainder: 4 dh flops per element) on
+        # the matrix cores, the per-element fp32 work on the vector units (6 ops for the key and
+        # query scores, 1 fma for the value scores), and the noise, K T d normals regenerated
+        # once each at the generator's 12 operations
         T, K, S, H = self.T, self.K, self.S, self.HEADS
         elems = K * (T // S) * H * (S * (S + 1) / 2)
-        ms = 1e3 * (OPS_KEY_SCORE * elems / (FP32_VALU_PEAK_TOPS * 1e12) +
-                    4.0 * (self.d // H) * elems / (BF16_MFMA_PEAK_TFLOPS * 1e12))
-        return {"dust_attn_key_scores": ms, "dust_attn_query_scores": ms}
+        common = (4.0 * (self.d // H) * elems / (BF16_MFMA_PEAK_TFLOPS * 1e12) +
+                  OPS_PER_NORMAL * K * T * self.d / (VALU_PEAK_TOPS * 1e12))
+        ms_kq = 1e3 * (common + OPS_KEY_SCORE * elems / (FP32_VALU_PEAK_TOPS * 1e12))
+        ms_v = 1e3 * (common + elems / (FP32_VALU_PEAK_TOPS * 1e12))
+        return {"dust_attn_key_scores": ms_kq, "dust_attn_query_scores": ms_kq,
+                "dust_attn_value_scores": ms_v}
 
     def config(self):
         cfg = {"workload": self.c["name"], "d": self.d, "tokens": self.T, "seq_len": self.S,
